@@ -1,0 +1,180 @@
+"""Seeded synthetic workloads for the strided-layout GEMM.
+
+This module holds only random draws, their rounding to the storage formats
+(numpy's float16 cast and torch's float8_e4m3fn cast, both round-to-nearest-
+even) and the strides that lay them out.  It holds none of the GEMM's
+arithmetic: no decoding, no products, no sums.  Both the HIP path and the CPU
+oracle are fed from here, so they see identical bytes.
+
+Recipe: ``numpy.random.default_rng(seed)`` (PCG64), draws in fp64 in the
+order A, B, C, SFA, SFB.  Each operand is drawn in its storage order (so a
+transposed view is a real transposed layout of the same draws), then rounded.
+Scale exponents are integers uniform in [-4, 4] stored as E8M0 bytes e + 127.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+
+@dataclass
+class HostOperand:
+    """A host operand: raw codes (uint16 fp16 bits, uint8 E4M3/E8M0 bytes)
+    in a flat storage array, and the (batch?, rows, cols) view with element
+    strides."""
+    storage: np.ndarray
+    shape: Tuple[int, ...]
+    strides: Tuple[int, ...]
+    kind: str  # 'f16' | 'e4m3' | 'e8m0'
+
+    @property
+    def view(self) -> np.ndarray:
+        it = self.storage.itemsize
+        return np.lib.stride_tricks.as_strided(
+            self.storage, shape=self.shape, strides=tuple(s * it for s in self.strides),
+            writeable=False)
+
+
+@dataclass
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    batch: int
+    a: HostOperand
+    b: HostOperand
+    c: Optional[HostOperand] = None
+    sfa: Optional[HostOperand] = None
+    sfb: Optional[HostOperand] = None
+    block_k: int = 32
+    d_shape: Tuple[int, ...] = ()
+    d_strides: Tuple[int, ...] = ()
+    meta: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def mx(self) -> bool:
+        return self.sfa is not None
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.M * self.N * self.K
+
+
+def _draw(rng: np.random.Generator, dist: str, n: int) -> np.ndarray:
+    if dist == "uniform":
+        return rng.uniform(-1.0, 1.0, n)
+    if dist == "normal":
+        return rng.standard_normal(n)
+    if dist.startswith("int"):  # "int4": integers uniform in [-4, 4]
+        r = int(dist[3:])
+        return rng.integers(-r, r + 1, n).astype(np.float64)
+    raise ValueError(dist)
+
+
+def _f16_codes(x: np.ndarray) -> np.ndarray:
+    return x.astype(np.float16).view(np.uint16)
+
+
+def _e4m3_codes(x: np.ndarray) -> np.ndarray:
+    import torch  # the cast rounds to nearest even; clamp first so it saturates
+    t = torch.from_numpy(np.clip(x, -448.0, 448.0).astype(np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def matrix(rng, dist: str, batch: Optional[int], rows: int, cols: int, major: str,
+           kind: str = "f16") -> HostOperand:
+    """Draw a (batch?, rows, cols) operand.  ``major='row'``: cols contiguous
+    (strides (rows*cols, cols, 1)); ``major='col'``: rows contiguous (strides
+    (rows*cols, 1, rows)), i.e. the stride-swapped view of a stored
+    (cols, rows) matrix."""
+    nb = batch or 1
+    x = _draw(rng, dist, nb * rows * cols)
+    codes = _e4m3_codes(x) if kind == "e4m3" else _f16_codes(x)
+    if major == "row":
+        st = (rows * cols, cols, 1)
+    elif major == "col":
+        st = (rows * cols, 1, rows)
+    else:
+        raise ValueError(major)
+    if batch is None:
+        return HostOperand(codes, (rows, cols), st[1:], kind)
+    return HostOperand(codes, (batch, rows, cols), st, kind)
+
+
+def scales(rng, batch: Optional[int], rows: int, kblocks: int, lo: int = -4, hi: int = 4) -> HostOperand:
+    e = rng.integers(lo, hi + 1, (batch or 1) * rows * kblocks)
+    codes = (e + 127).astype(np.uint8)
+    if batch is None:
+        return HostOperand(codes, (rows, kblocks), (kblocks, 1), "e8m0")
+    return HostOperand(codes, (batch, rows, kblocks), (rows * kblocks, kblocks, 1), "e8m0")
+
+
+def gemm_workload(name: str, M: int, N: int, K: int, *, seed: int, dist: str = "normal",
+                  batch: Optional[int] = None, a_major: str = "row", b_major: str = "row",
+                  with_c: bool = False, c_dist: Optional[str] = None, mx: bool = False,
+                  block_k: int = 32, rng: Optional[np.random.Generator] = None,
+                  scale_range: Tuple[int, int] = (-4, 4)) -> Workload:
+    """A generic seeded GEMM problem.  ``a_major``/``b_major`` say which of
+    the two matrix dimensions is contiguous: 'row' = K-contiguous (TN
+    convention), 'col' = M- (or N-) contiguous."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    kind = "e4m3" if mx else "f16"
+    a = matrix(rng, dist, batch, M, K, a_major, kind)
+    b = matrix(rng, dist, batch, N, K, b_major, kind)
+    c = matrix(rng, c_dist or dist, batch, M, N, "row") if with_c else None
+    sfa = sfb = None
+    if mx:
+        kb = -(-K // block_k)
+        sfa = scales(rng, batch, M, kb, *scale_range)
+        sfb = scales(rng, batch, N, kb, *scale_range)
+    if batch is None:
+        d_shape, d_strides = (M, N), (N, 1)
+    else:
+        d_shape, d_strides = (batch, M, N), (M * N, N, 1)
+    return Workload(name, M, N, K, batch or 1, a, b, c, sfa, sfb, block_k, d_shape, d_strides)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads
+# ---------------------------------------------------------------------------
+
+def config1() -> Workload:
+    """fp16 TN 256^3, uniform[-1,1], C = 0, seed 0."""
+    return gemm_workload("fp16_tn_256", 256, 256, 256, seed=0, dist="uniform")
+
+
+def config2(n: int = 4096, with_c: bool = True) -> Workload:
+    """fp16 TN n^3 with C, all normal(0,1), seed 1 (n = 4096; 8192 for the
+    large square case)."""
+    return gemm_workload(f"fp16_tn_{n}" + ("_c" if with_c else ""), n, n, n, seed=1,
+                         dist="normal", with_c=with_c)
+
+
+def config3() -> Tuple[Workload, Workload]:
+    """Ragged and skinny fp16 TN, uniform[-1,1], C = 0; one generator with
+    seed 2 draws (4000,3000,2056) first, then (8192,128,8192)."""
+    rng = np.random.default_rng(2)
+    w1 = gemm_workload("fp16_tn_4000x3000x2056", 4000, 3000, 2056, seed=2, dist="uniform", rng=rng)
+    w2 = gemm_workload("fp16_tn_8192x128x8192", 8192, 128, 8192, seed=2, dist="uniform", rng=rng)
+    return w1, w2
+
+
+def config4(case: str = "NN") -> Workload:
+    """Batch 64 of 512^3, seed 3, normal(0,1), C = 0.  A is the stride-swapped
+    view (M contiguous, strides (M*K, 1, M)).  'NN': B is K-contiguous;
+    'NT': B is N-contiguous (strides (N*K, 1, N)).  'TN'/'TT' are the other two
+    combinations with a K-contiguous A."""
+    a_major = "col" if case[0] == "N" else "row"
+    b_major = "row" if case[1] == "N" else "col"
+    return gemm_workload(f"fp16_batched64_512_{case}", 512, 512, 512, seed=3, dist="normal",
+                         batch=64, a_major=a_major, b_major=b_major)
+
+
+def config5(n: int = 8192) -> Workload:
+    """MXFP8: E4M3 data from normal(0,1), one E8M0 scale per 32 K per row,
+    exponents uniform in [-4, 4], C = 0, seed 4."""
+    return gemm_workload(f"mxfp8_tn_{n}", n, n, n, seed=4, dist="normal", mx=True)

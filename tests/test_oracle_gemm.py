@@ -1,0 +1,261 @@
+"""Pins of the GEMM oracle (oracle/gemm_ref.c) against independent sources.
+
+* codecs: exhaustively against numpy float16 and torch float8 conversions;
+* GEMM: against numpy fp64 matmul on small-integer data where every product
+  and partial sum is exact (so any summation order gives the same bits),
+  through transposed, batched and broadcast views;
+* closed forms: A = 0 gives C, A = I gives B^T + C, one-hot A and B hit one
+  element;
+* MX: unit scales reduce to the fp16 GEMM of the decoded E4M3 values, and a
+  +1 on one E8M0 byte doubles exactly that block's contribution;
+* the acceptance bound on hand-made cases.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import gemm as G
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    G.build()
+
+
+# ---------------------------------------------------------------- codecs
+
+def test_f16_decode_all_codes():
+    codes = np.arange(65536, dtype=np.uint16)
+    ref = codes.view(np.float16).astype(np.float64)
+    got = np.array([G.f16_decode(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_f16_encode_matches_numpy_rne():
+    rng = np.random.default_rng(123)
+    xs = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        rng.uniform(-70000, 70000, 2000),
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 65536.0, 1e9, -1e9, 2.0 ** -24, 2.0 ** -25,
+         3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, np.inf, -np.inf],
+    ])
+    # every exact midpoint between adjacent finite fp16 values (tie cases)
+    pos = np.arange(0, 0x7c00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2
+    xs = np.concatenate([xs, mids, -mids])
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float16).view(np.uint16)
+    got = np.array([G.f16_encode(float(x)) for x in xs], dtype=np.uint16)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(xs[i], got[i], ref[i]) for i in bad[:5]]
+
+
+def test_e4m3_decode_all_codes():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([G.e4m3_decode(i) for i in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2  # S.1111.111
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_e8m0_decode_all_codes():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([G.e8m0_decode(i) for i in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127
+
+
+# ---------------------------------------------------------------- helpers
+
+def f16(x):
+    return np.asarray(x, np.float64).astype(np.float16).view(np.uint16)
+
+
+def dec(codes):
+    return np.asarray(codes, np.uint16).view(np.float16).astype(np.float64)
+
+
+def strided(storage, shape, strides):
+    it = storage.itemsize
+    return np.lib.stride_tricks.as_strided(storage, shape=shape, strides=[s * it for s in strides])
+
+
+# ---------------------------------------------------------------- fp16 GEMM
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (7, 5, 3), (37, 29, 64), (64, 33, 17)])
+def test_gemm_exact_integers_vs_numpy(M, N, K):
+    rng = np.random.default_rng(M * 1000 + N * 10 + K)
+    a = rng.integers(-4, 5, (M, K))
+    b = rng.integers(-4, 5, (N, K))
+    c = rng.integers(-100, 101, (M, N))
+    d, ref, absum = G.gemm(f16(a), f16(b), f16(c))
+    want = a.astype(np.float64) @ b.T.astype(np.float64) + c
+    assert np.array_equal(ref[0], want)
+    assert np.array_equal(d[0], f16(want))
+    assert np.array_equal(absum[0], np.abs(a).astype(np.float64) @ np.abs(b).T.astype(np.float64))
+
+
+@pytest.mark.parametrize("a_major,b_major", [("row", "row"), ("col", "row"), ("row", "col"), ("col", "col")])
+def test_gemm_strided_batched_views(a_major, b_major):
+    """Transposed (stride-swapped) and batched views, addressed only through
+    their strides, agree with numpy on the same logical matrices."""
+    rng = np.random.default_rng(7)
+    nb, M, N, K = 3, 19, 23, 40
+    A = rng.integers(-4, 5, (nb, M, K))
+    B = rng.integers(-4, 5, (nb, N, K))
+    if a_major == "row":
+        a = strided(f16(A).ravel(), (nb, M, K), (M * K, K, 1))
+    else:  # store (nb, K, M), view as (nb, M, K) with strides (M*K, 1, M)
+        a = strided(f16(A.transpose(0, 2, 1)).ravel().copy(), (nb, M, K), (M * K, 1, M))
+    if b_major == "row":
+        b = strided(f16(B).ravel(), (nb, N, K), (N * K, K, 1))
+    else:
+        b = strided(f16(B.transpose(0, 2, 1)).ravel().copy(), (nb, N, K), (N * K, 1, N))
+    d, ref, _ = G.gemm(a, b)
+    want = np.einsum("bmk,bnk->bmn", A.astype(np.float64), B.astype(np.float64))
+    assert np.array_equal(ref, want)
+
+
+def test_gemm_broadcast_batch_stride_zero():
+    rng = np.random.default_rng(8)
+    nb, M, N, K = 4, 9, 11, 16
+    A = rng.integers(-4, 5, (nb, M, K))
+    B = rng.integers(-4, 5, (N, K))
+    b = strided(f16(B).ravel(), (nb, N, K), (0, K, 1))  # one B for every batch
+    d, ref, _ = G.gemm(f16(A), b)
+    want = np.einsum("bmk,nk->bmn", A.astype(np.float64), B.astype(np.float64))
+    assert np.array_equal(ref, want)
+
+
+def test_gemm_real_values_vs_numpy():
+    rng = np.random.default_rng(9)
+    M, N, K = 33, 47, 130
+    A = dec(f16(rng.standard_normal((M, K))))
+    B = dec(f16(rng.standard_normal((N, K))))
+    C = dec(f16(rng.standard_normal((M, N))))
+    _, ref, absum = G.gemm(f16(A), f16(B), f16(C))
+    want = A @ B.T + C
+    S = np.abs(A) @ np.abs(B).T
+    assert np.all(np.abs(ref[0] - want) <= 1e-13 * (S + np.abs(C)))
+    np.testing.assert_allclose(absum[0], np.abs(A) @ np.abs(B).T, rtol=1e-13)
+
+
+def test_gemm_closed_forms():
+    rng = np.random.default_rng(10)
+    M = K = 24
+    N = 20
+    B = dec(f16(rng.standard_normal((N, K))))
+    C = dec(f16(rng.standard_normal((M, N)))) + 0.0
+    # A = 0: D = C bit for bit
+    d, _, absum = G.gemm(f16(np.zeros((M, K))), f16(B), f16(C))
+    assert np.array_equal(dec(d[0]), C) and not absum.any()
+    # A = I: D = fp16(B^T + C)
+    d, ref, _ = G.gemm(f16(np.eye(M)), f16(B), f16(C))
+    assert np.array_equal(ref[0], B.T + C)
+    assert np.array_equal(d[0], f16(B.T + C))
+    # one-hot A and B meeting at k0: a single 1 at (m0, n0)
+    A1 = np.zeros((M, K)); A1[5, 17] = 1
+    B1 = np.zeros((N, K)); B1[13, 17] = 1; B1[2, 16] = 1
+    _, ref, _ = G.gemm(f16(A1), f16(B1))
+    want = np.zeros((M, N)); want[5, 13] = 1
+    assert np.array_equal(ref[0], want)
+
+
+def test_gemm_points_equal_full():
+    rng = np.random.default_rng(11)
+    nb, M, N, K = 2, 13, 17, 50
+    A = f16(rng.standard_normal((nb, M, K)))
+    B = f16(rng.standard_normal((nb, N, K)))
+    C = f16(rng.standard_normal((nb, M, N)))
+    d, ref, absum = G.gemm(A, B, C)
+    pts = np.stack([rng.integers(0, nb, 40), rng.integers(0, M, 40), rng.integers(0, N, 40)], 1)
+    dp, rp, sp = G.gemm_points(A, B, C, points=pts)
+    assert np.array_equal(dp, d[pts[:, 0], pts[:, 1], pts[:, 2]])
+    assert np.array_equal(rp, ref[pts[:, 0], pts[:, 1], pts[:, 2]])
+    assert np.array_equal(sp, absum[pts[:, 0], pts[:, 1], pts[:, 2]])
+
+
+# ---------------------------------------------------------------- MX GEMM
+
+def e4m3(x):
+    return torch.from_numpy(np.clip(np.asarray(x, np.float32), -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_mx_unit_scales_equal_fp16_gemm_of_decoded_values():
+    rng = np.random.default_rng(12)
+    M, N, K = 21, 18, 96
+    a8 = e4m3(rng.standard_normal((M, K)))
+    b8 = e4m3(rng.standard_normal((N, K)))
+    sfa = np.full((M, K // 32), 127, np.uint8)
+    sfb = np.full((N, K // 32), 127, np.uint8)
+    _, ref_mx, _ = G.gemm(a8, b8, sfa=sfa, sfb=sfb)
+    # every E4M3 value is exactly an fp16 value
+    _, ref_16, _ = G.gemm(f16(e4m3_values(a8)), f16(e4m3_values(b8)))
+    assert np.array_equal(ref_mx, ref_16)
+
+
+def test_mx_scales_vs_numpy():
+    rng = np.random.default_rng(13)
+    M, N, K = 17, 19, 160  # K = 5 blocks
+    a8 = e4m3(rng.standard_normal((M, K)))
+    b8 = e4m3(rng.standard_normal((N, K)))
+    sfa = (rng.integers(-4, 5, (M, K // 32)) + 127).astype(np.uint8)
+    sfb = (rng.integers(-4, 5, (N, K // 32)) + 127).astype(np.uint8)
+    _, ref, _ = G.gemm(a8, b8, sfa=sfa, sfb=sfb)
+    sa = torch.from_numpy(sfa).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    sb = torch.from_numpy(sfb).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    A = e4m3_values(a8) * np.repeat(sa, 32, axis=1)
+    B = e4m3_values(b8) * np.repeat(sb, 32, axis=1)
+    # E4M3 x 2^e values have few significant bits: every product and partial
+    # sum here is exact in fp64, so the comparison is exact
+    assert np.array_equal(ref[0], A @ B.T)
+
+
+def test_mx_one_scale_step_doubles_one_block():
+    rng = np.random.default_rng(14)
+    M, N, K = 8, 6, 128
+    a8 = e4m3(rng.standard_normal((M, K)))
+    b8 = e4m3(rng.standard_normal((N, K)))
+    sfa = (rng.integers(-4, 5, (M, 4)) + 127).astype(np.uint8)
+    sfb = (rng.integers(-4, 5, (N, 4)) + 127).astype(np.uint8)
+    _, base, _ = G.gemm(a8, b8, sfa=sfa, sfb=sfb)
+    m0, kb = 3, 2
+    sfa2 = sfa.copy(); sfa2[m0, kb] += 1
+    _, bumped, _ = G.gemm(a8, b8, sfa=sfa2, sfb=sfb)
+    # the block's own contribution, from the block alone
+    a_blk = np.zeros_like(a8); a_blk[:, 32 * kb:32 * kb + 32] = a8[:, 32 * kb:32 * kb + 32]
+    _, part, _ = G.gemm(a_blk, b8, sfa=sfa, sfb=sfb)
+    diff = bumped[0] - base[0]
+    assert np.array_equal(diff[m0], part[0, m0])
+    assert not np.delete(diff, m0, axis=0).any()
+
+
+# ---------------------------------------------------------------- acceptance
+
+def test_check_bound():
+    one = int(f16(1.0))
+    up1, up2 = one + 1, one + 2         # 1 + 2^-10, 1 + 2^-9
+    d_ref = np.array([one, one, one, one], np.uint16)
+    absum = np.zeros(4)
+    assert G.check(np.array([one, up1, one, one], np.uint16), d_ref, absum)[0] == 0
+    bad, wi, _ = G.check(np.array([one, up2, one, one], np.uint16), d_ref, absum)
+    assert bad == 1 and wi == 1
+    # the S term admits a larger error
+    absum2 = np.array([0, 2.0 ** 4, 0, 0])
+    assert G.check(np.array([one, up2, one, one], np.uint16), d_ref, absum2)[0] == 0
+    # NaN never passes
+    assert G.check(np.array([0x7e00], np.uint16), np.array([0x7e00], np.uint16), np.zeros(1))[0] == 1
