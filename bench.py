@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the strided-layout GEMM on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one call of sl_gemm over the workload's operands, already resident
+in HBM.  W untimed steps, then K steps timed between two device
+synchronisations; HIP events on the launch stream give the kernel's
+average duration for the roofline object.  Prints one JSON line.
+
+Default workload: fp16 TN GEMM M = N = K = 8192 with C (normal(0,1) inputs,
+seed 1) -- the large square case the fp16 throughput target is stated on.
+Other workloads (for measurement only): fp16_4096 (the same recipe at 4096),
+ragged (4000x3000x2056), skinny (8192x128x8192), batched_nn / batched_nt
+(64 x 512^3, A M-contiguous), mxfp8 (8192^3 MXFP8).
+
+The CPU baseline is the oracle (plain fp64 triple loop, all host cores) on a
+bounded sample of output points of the same workload, scaled to TFLOP/s.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and % of dense MFMA peak, fp16 TN GEMM 4096^3/8192^3 on 1 MI355X"
+PEAK_F16 = 2516.6   # TFLOP/s: 256 CUs x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
+PEAK_F8 = 5033.2    # TFLOP/s: 256 CUs x 2.4 GHz x 8192 dense MX-fp8 FLOP/clk/CU
+PEAK_HBM = 8000.0   # GB/s
+
+
+def workloads():
+    from stride_layouts_lds_amd import inputs as I
+    return {
+        "fp16_8192": ("fp16 TN GEMM M=N=K=8192, A/B/C normal(0,1) fp16, seed 1", lambda: I.config2(8192)),
+        "fp16_4096": ("fp16 TN GEMM M=N=K=4096, A/B/C normal(0,1) fp16, seed 1", lambda: I.config2(4096)),
+        "ragged": ("fp16 TN GEMM 4000x3000x2056, uniform[-1,1], C=0, seed 2", lambda: I.config3()[0]),
+        "skinny": ("fp16 TN GEMM 8192x128x8192, uniform[-1,1], C=0, seed 2", lambda: I.config3()[1]),
+        "batched_nn": ("fp16 batched 64x512^3, A M-contiguous, B K-contiguous, seed 3", lambda: I.config4("NN")),
+        "batched_nt": ("fp16 batched 64x512^3, A M-contiguous, B N-contiguous, seed 3", lambda: I.config4("NT")),
+        "mxfp8": ("MXFP8 GEMM M=N=K=8192, E4M3 data, E8M0 scale per 32 K, C=0, seed 4", lambda: I.config5(8192)),
+    }
+
+
+def algorithmic_bytes(w) -> int:
+    """A, B (and scales) read once, C read once if present, D written once."""
+    es = 1 if w.mx else 2
+    b = w.batch * (w.M * w.K + w.N * w.K) * es + w.batch * w.M * w.N * 2
+    if w.c is not None:
+        b += w.batch * w.M * w.N * 2
+    if w.mx:
+        b += w.sfa.storage.size + w.sfb.storage.size
+    return b
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "stride_layouts_lds_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float = 12.0):
+    """The oracle, as it stands, on a bounded sample of output points."""
+    import numpy as np
+    from oracle import gemm as OG
+    threads = max(1, len(os.sched_getaffinity(0)))
+    rng = np.random.default_rng(123)
+
+    def run(n):
+        pts = np.stack([rng.integers(0, w.batch, n), rng.integers(0, w.M, n), rng.integers(0, w.N, n)], 1)
+        t0 = time.perf_counter()
+        OG.gemm_points(w.a.view, w.b.view, w.c.view if w.c else None, w.sfa.view if w.sfa else None,
+                       w.sfb.view if w.sfb else None, points=pts, block_k=w.block_k, nthreads=threads)
+        return time.perf_counter() - t0
+
+    n = max(threads * 4, 64)
+    dt = run(n)
+    while dt < 0.5:
+        n *= 4
+        dt = run(n)
+    n = max(n, int(n * target_s / dt))
+    dt = run(n)
+    flop = 2.0 * w.K * n
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} output elements of the same workload (each a {w.K}-term fp64 dot product), "
+                      f"{dt:.1f} s on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fp16_8192")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        sys.exit(1)
+    from stride_layouts_lds_amd import api
+    api.lib()
+
+    desc, make = workloads()[args.workload]
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    w = make()
+    from stride_layouts_lds_amd.inputs import to_device
+    a, b, c = to_device(w.a), to_device(w.b), to_device(w.c)
+    sfa, sfb = to_device(w.sfa), to_device(w.sfb)
+    out = torch.empty(w.d_shape, dtype=torch.float16, device="cuda")
+    margs = api.make_args(a, b, c, out, sfa, sfb, w.block_k)
+    plan = api.sl_gemm_plan(margs)
+    stream = torch.cuda.current_stream()
+    sid = stream.cuda_stream
+
+    print(f"[bench] plan {plan}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        api.sl_gemm(margs, sid)
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        api.sl_gemm(margs, sid)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] {args.steps} steps in {wall:.4f} s; {kern_ms * 1e3:.1f} us per launch (events)",
+          file=sys.stderr, flush=True)
+
+    flop = w.flops
+    value = flop * args.steps / wall / 1e12
+    mfma_bound = args.workload not in ("skinny", "batched_nn", "batched_nt")
+    peak = PEAK_F8 if w.mx else PEAK_F16
+    if mfma_bound:
+        achieved = flop / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        achieved = algorithmic_bytes(w) / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM, 4)}
+    roof["traffic"] = measured_traffic(args.workload)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f8e4m3" if w.mx else "f16",
+        "data": "synthetic",
+        "config": {"workload": desc, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
+                   "tile": f"{plan['tile_m']}x{plan['tile_n']}x{plan['tile_k']}",
+                   "workgroups": plan["workgroups"], "peak_frac": round(value / peak, 4)},
+        "roofline": roof,
+    }
+    if rank == 0 and not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w)
+    if rank == 0:
+        print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * sl.h -- C ABI of libstride_layouts_lds.so, a strided-layout GEMM for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The one operation:  D = A * B^T + C   (optionally block-scaled).
+ *
+ *  - "CuTe 中 A、B 如何加载到 MMA 寄存器", section 1: the matrix-core
+ *    instruction computes D = A x B + C with A indexed (M,K) and B indexed
+ *    (N,K); D may reuse C's storage.
+ *  - "数据布局及其记号", section "Shape-Stride 模型": a tensor is flat storage
+ *    plus a layout S[(shape):(strides)]; the element at index (i,j,...) is at
+ *    the dot product of the index with the strides, counted in ELEMENTS (not
+ *    bytes).  A transpose is a stride swap; no data moves.
+ *  - same page, section "Replication 与 Offset": the block-scaled product
+ *    A_real[m,k] = A_low[m,k] * SFA[m, k/K_blk], B_real[n,k] = B_low[n,k] *
+ *    SFB[n, k/K_blk], D = C + A_real x B_real^T.  MXFP8: FP8 E4M3 data, one
+ *    E8M0 scale per 32 consecutive K elements (K_blk = 32).
+ *
+ * Every operand is passed as a device pointer plus such a layout, so
+ * row-major, column-major, transposed and batched strided views all go
+ * through the one entry point sl_gemm().
+ *
+ * Conventions
+ *  - All shapes and strides are int64 counts of ELEMENTS.  Strides must be
+ *    >= 0.  A rank-2 layout is (rows, cols); a rank-3 layout is
+ *    (batch, rows, cols).  A rank-2 input is the same matrix for every batch.
+ *  - A: (batch?, M, K); B: (batch?, N, K); C and D: (batch?, M, N);
+ *    SFA: (batch?, M, ceil(K/block_k)); SFB: (batch?, N, ceil(K/block_k)).
+ *  - Batch counts of rank-3 operands must equal D's batch count; an input
+ *    may broadcast along the batch with batch stride 0.  A zero stride
+ *    inside the matrix dimensions of an input is also accepted (every index
+ *    along it reads the same element).  D must not broadcast: its strides
+ *    must map distinct (batch, m, n) to distinct addresses.
+ *  - C may be absent (data == NULL: C = 0) or be exactly D (same pointer and
+ *    same layout: the update is done in place).  Any other overlap of D's
+ *    address range with A, B, C or the scales returns SL_ERR_ALIAS.
+ *  - M == 0 or N == 0 (or batch == 0) is a no-op returning SL_OK.  K == 0
+ *    gives D = C (or D = 0).
+ *  - Ownership: the caller owns every buffer; sl_gemm() neither allocates,
+ *    frees nor retains device memory, and keeps no pointer after it returns.
+ *  - Execution: validation runs on the host before any HIP call; a failure
+ *    returns a negative sl_status and sets the thread-local message.  On
+ *    success the kernel is launched asynchronously on `stream` (a
+ *    hipStream_t; NULL is the default stream) and the call returns without
+ *    waiting.  Errors reported by the launch return SL_ERR_LAUNCH.
+ *  - Numerics: fp16 products are accumulated in fp32; the result (plus C,
+ *    added in fp32) is rounded to fp16 to nearest-even, overflow to +-inf.
+ */
+#ifndef STRIDE_LAYOUTS_LDS_SL_H
+#define STRIDE_LAYOUTS_LDS_SL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SL_ABI_VERSION 1
+
+typedef enum {
+  SL_F16 = 1,     /* IEEE binary16 */
+  SL_F32 = 2,     /* IEEE binary32 (accepted for nothing but reported) */
+  SL_F8_E4M3 = 3, /* OCP MX E4M3 (bias 7, max 448, S.1111.111 = NaN) */
+  SL_E8M0 = 4     /* OCP MX E8M0 scale: 2^(b-127), 255 = NaN */
+} sl_dtype;
+
+typedef enum {
+  SL_OK = 0,
+  SL_ERR_NULL = -1,   /* required pointer is NULL */
+  SL_ERR_DTYPE = -2,  /* unsupported dtype or dtype combination */
+  SL_ERR_SHAPE = -3,  /* shapes disagree, negative sizes, or size limits */
+  SL_ERR_LAYOUT = -4, /* rank, negative stride, or a broadcasting D */
+  SL_ERR_ALIGN = -5,  /* a pointer not aligned to its element size */
+  SL_ERR_ALIAS = -6,  /* D overlaps an input (other than C == D exactly) */
+  SL_ERR_ARCH = -7,   /* the current device is not gfx950 */
+  SL_ERR_LAUNCH = -8, /* the HIP runtime reported an error */
+  SL_ERR_ARG = -9     /* an invalid enum or query argument */
+} sl_status;
+
+/* A shape:stride layout S[(shape):(stride)], counted in elements. */
+typedef struct {
+  int32_t rank;      /* 2: (rows, cols)   3: (batch, rows, cols) */
+  int64_t shape[3];
+  int64_t stride[3];
+} sl_layout;
+
+/* Device pointer + dtype + layout.  data == NULL marks an absent operand. */
+typedef struct {
+  void* data;
+  int32_t dtype; /* sl_dtype */
+  sl_layout layout;
+} sl_tensor;
+
+typedef struct {
+  sl_tensor a;     /* (batch?, M, K)  f16, or f8_e4m3 with scales          */
+  sl_tensor b;     /* (batch?, N, K)  same dtype as a                      */
+  sl_tensor c;     /* (batch?, M, N)  f16; data == NULL means C = 0        */
+  sl_tensor d;     /* (batch?, M, N)  f16 output                           */
+  sl_tensor sfa;   /* (batch?, M, ceil(K/block_k)) e8m0; f8 operands only */
+  sl_tensor sfb;   /* (batch?, N, ceil(K/block_k)) e8m0                    */
+  int32_t block_k; /* 32 for MXFP8; ignored for f16                        */
+} sl_gemm_args;
+
+/* What sl_gemm would launch for these arguments (host only, no HIP call). */
+typedef struct {
+  int32_t kernel;     /* kernel family: 1 fp16 fast, 2 fp16 generic, 3 mxfp8 */
+  int32_t a_load;     /* 0 K-contiguous vector, 1 M-contiguous vector, 2 generic */
+  int32_t b_load;     /* same, for B */
+  int32_t tile_m, tile_n, tile_k;
+  int32_t threads;    /* per workgroup */
+  int32_t split_k;    /* K partitions (1: none) */
+  int64_t workgroups; /* total workgroups launched */
+  int32_t lds_bytes;  /* LDS per workgroup */
+  int64_t batch, m, n, k;
+} sl_plan;
+
+/*
+ * D = A * B^T + C over the strided descriptors above (f16 x f16 -> f16 with
+ * fp32 accumulation), or the MXFP8 block-scaled form when a and b are
+ * SL_F8_E4M3 and sfa/sfb are SL_E8M0 with block_k == 32.
+ * `stream` is a hipStream_t.  Asynchronous; see Conventions.
+ */
+sl_status sl_gemm(const sl_gemm_args* args, void* stream);
+
+/* Validation and kernel selection only: fills *plan, launches nothing and
+ * makes no HIP call.  Same status codes as sl_gemm. */
+sl_status sl_gemm_plan(const sl_gemm_args* args, sl_plan* plan);
+
+/* Static text for a status code (never NULL). */
+const char* sl_status_string(int32_t status);
+
+/* Thread-local text of the last failure in this thread ("" if none); valid
+ * until the next call into the library from the same thread. */
+const char* sl_last_error_message(void);
+
+int32_t sl_abi_version(void);
+
+/*
+ * Matrix-core operand maps used by the kernels, dumped from the same
+ * constexpr tables the kernels are compiled from.  Each entry is one
+ * (lane, slot) -> (row, col) of the operand tile.
+ *   instr:   0 v_mfma_f32_16x16x32_f16      1 v_mfma_f32_32x32x16_f16
+ *            2 v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)
+ *            3 v_mfma_scale_f32_32x32x64_f8f6f4  (E4M3)
+ *   operand: 0 A (row = m, col = k)   1 B (row = n, col = k)
+ *            2 D accumulator (row = m, col = n)
+ *            3 scale (row = operand row, col = K block of 32; slot 0 only)
+ * Arrays receive up to `capacity` entries; *count gets the number of
+ * entries of the map.  Host only; no HIP call.
+ */
+sl_status sl_query_fragment_map(int32_t instr, int32_t operand, int32_t* lane, int32_t* slot,
+                                int32_t* row, int32_t* col, int64_t capacity, int64_t* count);
+
+/*
+ * LDS tile layout of a kernel variant: for each logical element (row, k) of
+ * one operand's tile, its byte offset inside the tile's LDS buffer.
+ * `variant` is the sl_plan.kernel id, `operand` 0 = A, 1 = B.  Writes
+ * rows*cols offsets row-major (index row*cols + k) into `offsets` (up to
+ * `capacity`), and the tile's rows, cols and element bytes into the three
+ * outputs.  Host only.
+ */
+sl_status sl_query_lds_map(int32_t variant, int32_t operand, int64_t* offsets, int64_t capacity,
+                           int32_t* rows, int32_t* cols, int32_t* elem_bytes);
+
+/*
+ * The LDS byte address each (lane, slot) of a fragment load reads for
+ * MFMA tile 0, k-slice 0 of wave 0, i.e. the composition of the LDS tile
+ * layout with the instruction's operand map.  `variant`/`operand` as in
+ * sl_query_lds_map.  `addr` receives lanes*slots entries (lane-major).
+ */
+sl_status sl_query_fragment_addresses(int32_t variant, int32_t operand, int64_t* addr,
+                                      int64_t capacity, int64_t* count);
+
+/*
+ * Device probe of one matrix-core instruction's operand maps: launches one
+ * wave per case on `stream` and writes every accumulator register.
+ *   mode 0: case c = (lane, slot) of A (c = lane*slots + slot) holds 1.0,
+ *           every other A slot 0; B slot (l, s) holds l*slots + s + 1
+ *           (f16; for E4M3 instructions see below).
+ *   mode 1: the same with the roles of A and B swapped.
+ *   For instr 2/3 (E4M3) mode 0/1 use B (resp. A) code (l % 16) + 1 in
+ *   mode 0/1 and 1.0 scales; mode 2 puts 1.0 at the one-hot A (lane, slot),
+ *   B = 1.0 everywhere, and A scale byte of lane l = 127 + l - 32 (B's 127).
+ * `out` (device, fp32) receives cases * 64 * regs values laid out
+ * [case][lane][reg].  Returns the case count through *cases.
+ */
+sl_status sl_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t capacity,
+                        int64_t* cases, void* stream);
+
+/*
+ * Device probe of the LDS data paths: each of 64 lanes of one wave writes
+ * through the path under test and every byte of a 4096-byte LDS buffer is
+ * copied to `out` (device, 4096 bytes), or for mode 2 the registers read.
+ *   mode 0: LDS is first filled with the byte 0xA5; then one direct-to-LDS
+ *           16-byte buffer load per lane: lane l loads the 16 bytes at
+ *           src + 16*(perm[l] & 63), or, when perm[l] < 0, an out-of-range
+ *           offset (src: 1024 device bytes, perm: device int32[64]).
+ *   mode 1: as mode 0 with the global (non-buffer) direct-to-LDS load
+ *           (perm[l] & 63 always).
+ *   mode 2: ds_read_b64_tr_b16: LDS is filled with src (4096 bytes), lane l
+ *           reads at byte address perm[l]; out receives 64 lanes x 8 bytes.
+ */
+sl_status sl_probe_lds(int32_t mode, const void* src, const int32_t* perm, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STRIDE_LAYOUTS_LDS_SL_H */

@@ -1,0 +1,503 @@
+// api.cpp -- the C ABI of include/sl.h: descriptor validation and
+// classification (host only), kernel selection, launch, and the map
+// queries / device probes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/sl.h"
+#include "sl_kernels.hpp"
+#include "sl_maps.hpp"
+
+namespace {
+
+thread_local std::string g_msg;
+
+sl_status fail(sl_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sl_status fail(sl_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_msg = buf;
+  return s;
+}
+
+int elem_size(int32_t dt) {
+  switch (dt) {
+    case SL_F16: return 2;
+    case SL_F32: return 4;
+    case SL_F8_E4M3: return 1;
+    case SL_E8M0: return 1;
+    default: return 0;
+  }
+}
+
+// A matrix view (batch stride, row stride, column stride) of a descriptor.
+struct View {
+  const sl_tensor* t;
+  int64_t batch;  // 1 for rank 2
+  int64_t rows, cols;
+  int64_t bs, rs, cs;
+  bool present;
+};
+
+sl_status make_view(const char* name, const sl_tensor& t, View* v) {
+  v->t = &t;
+  v->present = true;
+  const sl_layout& L = t.layout;
+  if (L.rank != 2 && L.rank != 3) return fail(SL_ERR_LAYOUT, "%s: rank %d (expected 2 or 3)", name, L.rank);
+  for (int i = 0; i < L.rank; ++i) {
+    if (L.shape[i] < 0) return fail(SL_ERR_SHAPE, "%s: negative size %lld", name, (long long)L.shape[i]);
+    if (L.stride[i] < 0) return fail(SL_ERR_LAYOUT, "%s: negative stride %lld", name, (long long)L.stride[i]);
+  }
+  if (L.rank == 3) {
+    v->batch = L.shape[0];
+    v->rows = L.shape[1];
+    v->cols = L.shape[2];
+    v->bs = L.stride[0];
+    v->rs = L.stride[1];
+    v->cs = L.stride[2];
+  } else {
+    v->batch = 1;
+    v->rows = L.shape[0];
+    v->cols = L.shape[1];
+    v->bs = 0;
+    v->rs = L.stride[0];
+    v->cs = L.stride[1];
+  }
+  return SL_OK;
+}
+
+// [lo, hi) byte range a view can touch, for `batch` batches.
+void byte_range(const View& v, int64_t batch, uintptr_t* lo, uintptr_t* hi) {
+  const int es = elem_size(v.t->dtype);
+  const int64_t nb = v.t->layout.rank == 3 ? batch : 1;
+  int64_t last = 0;
+  if (nb > 0 && v.rows > 0 && v.cols > 0) last = (nb - 1) * v.bs + (v.rows - 1) * v.rs + (v.cols - 1) * v.cs;
+  *lo = (uintptr_t)v.t->data;
+  *hi = (uintptr_t)v.t->data + (uintptr_t)((last + 1) * es);
+}
+
+// Distinct (batch, row, col) must map to distinct addresses.
+bool injective(const View& v, int64_t batch) {
+  struct Dim {
+    int64_t n, s;
+  } d[3] = {{batch, v.bs}, {v.rows, v.rs}, {v.cols, v.cs}};
+  Dim live[3];
+  int k = 0;
+  for (auto& x : d)
+    if (x.n > 1) live[k++] = x;
+  std::sort(live, live + k, [](const Dim& a, const Dim& b) { return a.s < b.s; });
+  int64_t span = 0;  // largest offset reached by the faster dims
+  for (int i = 0; i < k; ++i) {
+    if (live[i].s <= span) return false;
+    span += live[i].s * (live[i].n - 1);
+  }
+  return true;
+}
+
+bool same_layout(const sl_tensor& x, const sl_tensor& y) {
+  if (x.layout.rank != y.layout.rank) return false;
+  for (int i = 0; i < x.layout.rank; ++i)
+    if (x.layout.shape[i] != y.layout.shape[i] || x.layout.stride[i] != y.layout.stride[i]) return false;
+  return true;
+}
+
+struct Plan {
+  sl_plan pub;
+  sl::GemmParams p;
+  int32_t tile;
+  int32_t shift;
+  bool mx;
+  bool empty;
+};
+
+int32_t env_int(const char* name, int32_t dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  return (int32_t)strtol(s, nullptr, 10);
+}
+
+// Loader for one operand: rows x K with strides (rs along rows, ks along K).
+int32_t choose_load(const View& v, int64_t K, int64_t tile_rows, int es) {
+  const uintptr_t addr = (uintptr_t)v.t->data;
+  const int64_t vec = 16 / es;  // elements per 16 bytes
+  const bool base16 = addr % 16 == 0 && (v.t->layout.rank == 2 || v.bs % vec == 0);
+  const int64_t limit = (int64_t)1 << 31;
+  if (v.cs == 1 && base16 && v.rs % vec == 0 && K % vec == 0 &&
+      ((tile_rows - 1) * v.rs + K) * es < limit)
+    return sl::LOAD_KVEC;
+  if (es == 2 && v.rs == 1 && base16 && v.cs % vec == 0 && v.rows % 8 == 0 &&
+      ((K > 0 ? K - 1 : 0) * v.cs + tile_rows) * es < limit)
+    return sl::LOAD_MNVEC;
+  return sl::LOAD_GENERIC;
+}
+
+// Estimated relative cost of one tile shape: the number of workgroup waves
+// over the 256 CUs times the time of one wave, where `per_cu` co-resident
+// workgroups share a CU, with an efficiency factor that favours big tiles
+// (fewer LDS bytes per MFMA).
+double tile_cost(const sl::TileShape& t, int64_t batch, int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = batch * ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+  const int64_t per_cu = (t.bm * t.bn <= 128 * 128) ? 2 : 1;
+  const int64_t slots = 256 * per_cu;
+  const int64_t waves = (tiles + slots - 1) / slots;
+  const double eff = (t.bm == 256 && t.bn == 256) ? 1.0 : (t.bm * t.bn == 256 * 128) ? 0.92 : 0.80;
+  return (double)waves * (double)t.bm * (double)t.bn * (double)std::max<int64_t>(K, 64) * per_cu / eff;
+}
+
+sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
+  g_msg.clear();
+  if (!args) return fail(SL_ERR_NULL, "args is NULL");
+  const bool mx = args->a.dtype == SL_F8_E4M3;
+  // dtypes
+  if (mx) {
+    if (args->b.dtype != SL_F8_E4M3) return fail(SL_ERR_DTYPE, "b must be f8_e4m3 when a is");
+    if (args->sfa.dtype != SL_E8M0 || args->sfb.dtype != SL_E8M0)
+      return fail(SL_ERR_DTYPE, "MX operands need e8m0 sfa and sfb");
+    if (args->block_k != 32) return fail(SL_ERR_SHAPE, "block_k must be 32 for MXFP8 (got %d)", args->block_k);
+  } else {
+    if (args->a.dtype != SL_F16 || args->b.dtype != SL_F16)
+      return fail(SL_ERR_DTYPE, "a and b must both be f16, or both f8_e4m3 with scales");
+    if (args->sfa.data || args->sfb.data) return fail(SL_ERR_DTYPE, "scales given for f16 operands");
+  }
+  if (args->d.dtype != SL_F16) return fail(SL_ERR_DTYPE, "d must be f16");
+  const bool has_c = args->c.data != nullptr;
+  if (has_c && args->c.dtype != SL_F16) return fail(SL_ERR_DTYPE, "c must be f16");
+
+  View A, B, C{}, D, SA{}, SB{};
+  sl_status s;
+  if ((s = make_view("a", args->a, &A)) != SL_OK) return s;
+  if ((s = make_view("b", args->b, &B)) != SL_OK) return s;
+  if ((s = make_view("d", args->d, &D)) != SL_OK) return s;
+  if (has_c && (s = make_view("c", args->c, &C)) != SL_OK) return s;
+  if (mx) {
+    if ((s = make_view("sfa", args->sfa, &SA)) != SL_OK) return s;
+    if ((s = make_view("sfb", args->sfb, &SB)) != SL_OK) return s;
+  }
+
+  const int64_t batch = D.batch;
+  const int64_t M = A.rows, K = A.cols, N = B.rows;
+  if (B.cols != K) return fail(SL_ERR_SHAPE, "b is (%lld,%lld) but a has K=%lld", (long long)B.rows,
+                               (long long)B.cols, (long long)K);
+  if (D.rows != M || D.cols != N)
+    return fail(SL_ERR_SHAPE, "d is (%lld,%lld), expected (%lld,%lld)", (long long)D.rows, (long long)D.cols,
+                (long long)M, (long long)N);
+  if (has_c && (C.rows != M || C.cols != N))
+    return fail(SL_ERR_SHAPE, "c is (%lld,%lld), expected (%lld,%lld)", (long long)C.rows, (long long)C.cols,
+                (long long)M, (long long)N);
+  const View* ins[5] = {&A, &B, has_c ? &C : nullptr, mx ? &SA : nullptr, mx ? &SB : nullptr};
+  const char* names[5] = {"a", "b", "c", "sfa", "sfb"};
+  for (int i = 0; i < 5; ++i)
+    if (ins[i] && ins[i]->t->layout.rank == 3 && ins[i]->batch != batch)
+      return fail(SL_ERR_SHAPE, "%s has batch %lld, d has %lld", names[i], (long long)ins[i]->batch,
+                  (long long)batch);
+  const int64_t kb = mx ? (K + 31) / 32 : 0;
+  if (mx) {
+    if (SA.rows != M || SA.cols != kb)
+      return fail(SL_ERR_SHAPE, "sfa is (%lld,%lld), expected (%lld,%lld)", (long long)SA.rows,
+                  (long long)SA.cols, (long long)M, (long long)kb);
+    if (SB.rows != N || SB.cols != kb)
+      return fail(SL_ERR_SHAPE, "sfb is (%lld,%lld), expected (%lld,%lld)", (long long)SB.rows,
+                  (long long)SB.cols, (long long)N, (long long)kb);
+  }
+  const int64_t lim = (int64_t)1 << 31;
+  if (M >= lim || N >= lim || K >= lim || batch >= lim) return fail(SL_ERR_SHAPE, "a dimension exceeds 2^31-1");
+
+  Plan& P = *out;
+  memset(&P, 0, sizeof P);
+  P.mx = mx;
+  P.pub.batch = batch;
+  P.pub.m = M;
+  P.pub.n = N;
+  P.pub.k = K;
+  P.empty = batch == 0 || M == 0 || N == 0;
+  if (P.empty) {
+    P.pub.kernel = mx ? sl::K_MX : sl::K_F16;
+    return SL_OK;
+  }
+
+  // pointers and alignment
+  const View* all[6] = {&A, &B, has_c ? &C : nullptr, &D, mx ? &SA : nullptr, mx ? &SB : nullptr};
+  const char* all_names[6] = {"a", "b", "c", "d", "sfa", "sfb"};
+  for (int i = 0; i < 6; ++i) {
+    if (!all[i]) continue;
+    const bool needs_data = !(i == 0 || i == 1 || i == 4 || i == 5) || K > 0;
+    if (!all[i]->t->data) {
+      if (needs_data) return fail(SL_ERR_NULL, "%s.data is NULL", all_names[i]);
+      continue;
+    }
+    const int es = elem_size(all[i]->t->dtype);
+    if ((uintptr_t)all[i]->t->data % es != 0)
+      return fail(SL_ERR_ALIGN, "%s.data is not aligned to its %d-byte element", all_names[i], es);
+  }
+  // D must not broadcast; D must not overlap an input except C == D exactly
+  if (!injective(D, batch)) return fail(SL_ERR_LAYOUT, "d's strides map distinct elements to one address");
+  uintptr_t dlo, dhi;
+  byte_range(D, batch, &dlo, &dhi);
+  for (int i = 0; i < 6; ++i) {
+    if (!all[i] || i == 3 || !all[i]->t->data) continue;
+    if (i == 2 && args->c.data == args->d.data && same_layout(args->c, args->d)) continue;
+    if (i <= 1 && K == 0) continue;
+    uintptr_t lo, hi;
+    byte_range(*all[i], batch, &lo, &hi);
+    if (lo < dhi && dlo < hi) return fail(SL_ERR_ALIAS, "d overlaps %s", all_names[i]);
+  }
+
+  // kernel selection
+  sl::GemmParams& p = P.p;
+  p.a = args->a.data;
+  p.b = args->b.data;
+  p.c = has_c ? args->c.data : nullptr;
+  p.d = args->d.data;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.a_rs = A.rs, p.a_ks = A.cs, p.a_bs = A.t->layout.rank == 3 ? A.bs : 0;
+  p.b_rs = B.rs, p.b_ks = B.cs, p.b_bs = B.t->layout.rank == 3 ? B.bs : 0;
+  if (has_c) p.c_rs = C.rs, p.c_cs = C.cs, p.c_bs = C.t->layout.rank == 3 ? C.bs : 0;
+  p.d_rs = D.rs, p.d_cs = D.cs, p.d_bs = D.t->layout.rank == 3 ? D.bs : 0;
+  p.batch = (int32_t)batch;
+  p.flags = has_c ? sl::F_HAS_C : 0;
+  if (D.cs == 1 && D.rs % 4 == 0 && (uintptr_t)D.t->data % 8 == 0 && (batch == 1 || p.d_bs % 4 == 0))
+    p.flags |= sl::F_D_VEC;
+  if (has_c && C.cs == 1 && C.rs % 4 == 0 && (uintptr_t)C.t->data % 8 == 0 && (batch == 1 || p.c_bs % 4 == 0))
+    p.flags |= sl::F_C_VEC;
+  P.shift = env_int("SL_SWZ", 0) ? 1 : 0;
+  p.group_m = std::max(1, env_int("SL_GROUP_M", 4));
+
+  int32_t tile = env_int("SL_TILE", -1);
+  if (mx) {
+    p.sfa = (const uint8_t*)args->sfa.data;
+    p.sfb = (const uint8_t*)args->sfb.data;
+    p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
+    p.sb_rs = SB.rs, p.sb_ks = SB.cs, p.sb_bs = SB.t->layout.rank == 3 ? SB.bs : 0;
+    const int32_t la = choose_load(A, K, 256, 1), lb = choose_load(B, K, 256, 1);
+    if (la != sl::LOAD_KVEC || lb != sl::LOAD_KVEC)
+      return fail(SL_ERR_LAYOUT,
+                  "MXFP8 operands must be K-contiguous with 16-byte aligned rows and K %% 16 == 0");
+    if ((M - 1) * SA.rs + (kb - 1) * SA.cs >= lim || (N - 1) * SB.rs + (kb - 1) * SB.cs >= lim)
+      return fail(SL_ERR_SHAPE, "scale tensors span more than 2^31 bytes");
+    if (tile < 0 || tile >= sl::T_COUNT) {
+      tile = sl::T256x128_W2x2;
+      double best = 1e300;
+      for (int t : {sl::T256x128_W2x2, sl::T128x256_W2x2, sl::T128x128_W2x2}) {
+        const double c = tile_cost(sl::kTiles[t], batch, M, N, K);
+        if (c < best) best = c, tile = t;
+      }
+    }
+    P.pub.kernel = sl::K_MX;
+    P.pub.a_load = P.pub.b_load = sl::LOAD_KVEC;
+    P.pub.tile_k = 128;
+    p.k_tiles = (int32_t)((K + 127) / 128);
+  } else {
+    const int32_t la = choose_load(A, K, 256, 2), lb = choose_load(B, K, 256, 2);
+    const bool generic = la == sl::LOAD_GENERIC || lb == sl::LOAD_GENERIC;
+    if (generic) {
+      // one 128x128 configuration, instantiated for every pair that has a
+      // generic side: (G,G) (G,K) (K,G) (G,MN) (MN,G)
+      tile = sl::T128x128_W2x2;
+      P.pub.kernel = sl::K_F16_GENERIC;
+    } else {
+      if (tile < 0 || tile >= sl::T_COUNT) {
+        tile = sl::T256x256_W2x2;
+        double best = 1e300;
+        for (int t = 0; t < sl::T_COUNT; ++t) {
+          const double c = tile_cost(sl::kTiles[t], batch, M, N, K);
+          if (c < best) best = c, tile = t;
+        }
+      }
+      P.pub.kernel = sl::K_F16;
+    }
+    P.pub.a_load = la;
+    P.pub.b_load = lb;
+    P.pub.tile_k = 64;
+    p.k_tiles = (int32_t)((K + 63) / 64);
+  }
+  const sl::TileShape& ts = sl::kTiles[tile];
+  P.tile = tile;
+  p.tiles_m = (int32_t)((M + ts.bm - 1) / ts.bm);
+  p.tiles_n = (int32_t)((N + ts.bn - 1) / ts.bn);
+  const int64_t total = batch * p.tiles_m * p.tiles_n;
+  if (total >= lim) return fail(SL_ERR_SHAPE, "too many output tiles (%lld)", (long long)total);
+  P.pub.tile_m = ts.bm;
+  P.pub.tile_n = ts.bn;
+  P.pub.threads = ts.wm * ts.wn * 64;
+  P.pub.split_k = 1;
+  P.pub.workgroups = total;
+  P.pub.lds_bytes = 2 * (ts.bm + ts.bn) * sl::kRowBytes;
+  return SL_OK;
+}
+
+// gfx950 check, cached per device
+sl_status check_arch() {
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 ok, -1 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SL_ERR_LAUNCH, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(SL_ERR_ARCH, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> g(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(SL_ERR_LAUNCH, "hipGetDeviceProperties failed");
+    known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  if (known[dev] < 0) return fail(SL_ERR_ARCH, "device %d is not gfx950", dev);
+  return SL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sl_abi_version(void) { return SL_ABI_VERSION; }
+
+const char* sl_last_error_message(void) { return g_msg.c_str(); }
+
+const char* sl_status_string(int32_t s) {
+  switch (s) {
+    case SL_OK: return "ok";
+    case SL_ERR_NULL: return "null pointer";
+    case SL_ERR_DTYPE: return "unsupported dtype";
+    case SL_ERR_SHAPE: return "shape mismatch or size limit";
+    case SL_ERR_LAYOUT: return "unsupported layout";
+    case SL_ERR_ALIGN: return "misaligned pointer";
+    case SL_ERR_ALIAS: return "output overlaps an input";
+    case SL_ERR_ARCH: return "device is not gfx950";
+    case SL_ERR_LAUNCH: return "HIP launch error";
+    case SL_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+sl_status sl_gemm_plan(const sl_gemm_args* args, sl_plan* plan) {
+  Plan P;
+  const sl_status s = plan_gemm(args, &P);
+  if (s != SL_OK) return s;
+  if (plan) *plan = P.pub;
+  return SL_OK;
+}
+
+sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
+  Plan P;
+  sl_status s = plan_gemm(args, &P);
+  if (s != SL_OK) return s;
+  if (P.empty) return SL_OK;
+  if ((s = check_arch()) != SL_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (P.mx)
+    e = sl::launch_gemm_mx(P.p, P.tile, P.shift, st);
+  else
+    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, P.shift, st);
+  if (e != hipSuccess) return fail(SL_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return SL_OK;
+}
+
+sl_status sl_query_fragment_map(int32_t instr, int32_t operand, int32_t* lane, int32_t* slot, int32_t* row,
+                                int32_t* col, int64_t capacity, int64_t* count) {
+  g_msg.clear();
+  if (instr < 0 || instr > 3) return fail(SL_ERR_ARG, "instr %d", instr);
+  if (operand < 0 || operand > 3) return fail(SL_ERR_ARG, "operand %d", operand);
+  if ((operand == sl::OP_SCALE) && instr < 2) return fail(SL_ERR_ARG, "instr %d has no scale operand", instr);
+  const int32_t slots = operand == sl::OP_D ? sl::instr_acc_regs(instr) : operand == sl::OP_SCALE ? 1
+                                                                                                  : sl::instr_in_slots(instr);
+  int64_t n = 0;
+  for (int32_t l = 0; l < 64; ++l)
+    for (int32_t v = 0; v < slots; ++v, ++n) {
+      if (n >= capacity) continue;
+      sl::Coord c = operand == sl::OP_D       ? sl::acc_map(instr, l, v)
+                    : operand == sl::OP_SCALE ? sl::scale_map(instr, l)
+                                              : sl::operand_map(instr, l, v);
+      if (lane) lane[n] = l;
+      if (slot) slot[n] = v;
+      if (row) row[n] = c.row;
+      if (col) col[n] = c.col;
+    }
+  if (count) *count = n;
+  return SL_OK;
+}
+
+static int32_t current_shift() { return env_int("SL_SWZ", 0) ? 1 : 0; }
+
+sl_status sl_query_lds_map(int32_t variant, int32_t operand, int64_t* offsets, int64_t capacity, int32_t* rows,
+                           int32_t* cols, int32_t* elem_bytes) {
+  g_msg.clear();
+  if (variant < sl::K_F16 || variant > sl::K_MX) return fail(SL_ERR_ARG, "variant %d", variant);
+  if (operand < 0 || operand > 1) return fail(SL_ERR_ARG, "operand %d", operand);
+  const int32_t R = variant == sl::K_F16_GENERIC ? 128 : 256;
+  const int32_t es = variant == sl::K_MX ? 1 : 2;
+  const int32_t Cn = sl::kRowBytes / es;
+  const int32_t sh = current_shift();
+  int64_t n = 0;
+  for (int32_t r = 0; r < R; ++r)
+    for (int32_t k = 0; k < Cn; ++k, ++n)
+      if (offsets && n < capacity) offsets[n] = sl::lds_offset(r, k * es, sh);
+  if (rows) *rows = R;
+  if (cols) *cols = Cn;
+  if (elem_bytes) *elem_bytes = es;
+  return SL_OK;
+}
+
+sl_status sl_query_fragment_addresses(int32_t variant, int32_t operand, int64_t* addr, int64_t capacity,
+                                      int64_t* count) {
+  g_msg.clear();
+  if (variant < sl::K_F16 || variant > sl::K_MX) return fail(SL_ERR_ARG, "variant %d", variant);
+  if (operand < 0 || operand > 1) return fail(SL_ERR_ARG, "operand %d", operand);
+  const int32_t instr = variant == sl::K_MX ? sl::MFMA16_F8 : sl::MFMA16_F16;
+  const int32_t slots = sl::instr_in_slots(instr);
+  const int32_t es = variant == sl::K_MX ? 1 : 2;
+  const int32_t sh = current_shift();
+  int64_t n = 0;
+  for (int32_t l = 0; l < 64; ++l)
+    for (int32_t v = 0; v < slots; ++v, ++n) {
+      if (!addr || n >= capacity) continue;
+      // the kernels read 16-byte pieces at fragment_lds_offset; slot v sits
+      // (v % (16/es)) elements into piece v / (16/es)
+      const int32_t per = 16 / es;
+      addr[n] = sl::fragment_lds_offset(instr, l, v / per, 0, 0, sh) + (v % per) * es;
+    }
+  if (count) *count = n;
+  return SL_OK;
+}
+
+sl_status sl_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t capacity, int64_t* cases,
+                        void* stream) {
+  g_msg.clear();
+  if (instr < 0 || instr > 3) return fail(SL_ERR_ARG, "instr %d", instr);
+  const bool f8 = instr >= 2;
+  if (mode < 0 || mode > (f8 ? 5 : 1)) return fail(SL_ERR_ARG, "mode %d", mode);
+  const int64_t nc = 64 * (int64_t)sl::instr_in_slots(instr);
+  const int64_t need = nc * 64 * sl::instr_acc_regs(instr);
+  if (cases) *cases = nc;
+  if (!out) return fail(SL_ERR_NULL, "out is NULL");
+  if (capacity < need) return fail(SL_ERR_SHAPE, "out holds %lld floats, needs %lld", (long long)capacity,
+                                   (long long)need);
+  sl_status s = check_arch();
+  if (s != SL_OK) return s;
+  const hipError_t e = sl::launch_probe_mfma(instr, mode, out, nc, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SL_ERR_LAUNCH, "probe launch failed: %s", hipGetErrorString(e));
+  return SL_OK;
+}
+
+sl_status sl_probe_lds(int32_t mode, const void* src, const int32_t* perm, void* out, void* stream) {
+  g_msg.clear();
+  if (mode < 0 || mode > 2) return fail(SL_ERR_ARG, "mode %d", mode);
+  if (!src || !perm || !out) return fail(SL_ERR_NULL, "src, perm and out are required");
+  if ((uintptr_t)src % 16 || (uintptr_t)out % 16) return fail(SL_ERR_ALIGN, "src and out must be 16-byte aligned");
+  sl_status s = check_arch();
+  if (s != SL_OK) return s;
+  const hipError_t e = sl::launch_probe_lds(mode, src, perm, out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SL_ERR_LAUNCH, "probe launch failed: %s", hipGetErrorString(e));
+  return SL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,249 @@
+// sl_device.hpp -- device-side building blocks of the GEMM kernels: vector
+// types, buffer resources, the XCD-aware tile order, and the three
+// HBM -> LDS tile loaders.  gfx950 only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sl_kernels.hpp"
+#include "sl_maps.hpp"
+
+namespace sl {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+using lds_void_t = __attribute__((address_space(3))) void;
+
+// A buffer load whose offset is at or beyond the resource's byte count
+// returns zero; every masked lane uses this offset.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts.
+constexpr int32_t kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Wait until every vector-memory operation of this wave (including
+// direct-to-LDS loads) has completed.  s_waitcnt vmcnt(0), other counters
+// left at their maximum.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---------------------------------------------------------------------------
+// Tile order.  Workgroup IDs are handed to the 8 XCDs round-robin; remap so
+// that each XCD owns a contiguous range of the logical order, then walk the
+// output tiles in groups of `group_m` tile-rows so that the workgroups
+// resident on one XCD share A rows and B columns in that XCD's L2.
+// ---------------------------------------------------------------------------
+struct TileCoord {
+  int32_t batch, tm, tn;
+};
+
+__device__ __forceinline__ TileCoord map_tile(int32_t bid, int32_t total, int32_t tiles_m, int32_t tiles_n,
+                                              int32_t group_m) {
+  const int32_t x = bid & 7, local = bid >> 3;
+  const int32_t q = total >> 3, r = total & 7;
+  const int32_t id = x * q + (x < r ? x : r) + local;
+  const int32_t per_batch = tiles_m * tiles_n;
+  const int32_t b = id / per_batch;
+  const int32_t t = id - b * per_batch;
+  const int32_t span = group_m * tiles_n;
+  const int32_t g = t / span;
+  const int32_t first_m = g * group_m;
+  const int32_t left = tiles_m - first_m;
+  const int32_t gsz = left < group_m ? left : group_m;
+  const int32_t in = t - g * span;
+  return TileCoord{b, first_m + in % gsz, in / gsz};
+}
+
+// ---------------------------------------------------------------------------
+// HBM -> LDS tile loaders.  A tile is ROWS rows (of A's m or B's n) by 128
+// bytes of K (64 fp16 or 128 fp8 values), stored in LDS through
+// lds_offset(row, byte, SHIFT).  Each loader exposes
+//   issue(t, lds)  : start bringing K-tile t (direct loaders write LDS here)
+//   commit(lds)    : finish writing K-tile t into LDS (staged loaders)
+// Out-of-range rows and K positions read as zero (both operands must be
+// zero past K: 0 * stale NaN would poison the sum).
+// ---------------------------------------------------------------------------
+
+// K-contiguous rows, 16-B aligned: each lane's 16-B chunk is fetched by a
+// direct HBM->LDS buffer load.  One wave instruction fills 1 KiB of LDS,
+// i.e. 8 consecutive rows, lane l landing at byte 16*l of that block.  The
+// swizzle is therefore realised on the global side: the lane that lands in
+// physical chunk p of row r fetches logical chunk p ^ swz(r).
+template <int ROWS, int NT, int SHIFT, int ELEM>
+struct LoaderKVec {
+  static constexpr int WAVES = NT / 64;
+  static constexpr int ITERS = ROWS * 8 / NT;
+  static constexpr int KT = 128 / ELEM;      // K elements per tile
+  static constexpr int CE = 16 / ELEM;       // K elements per 16-B chunk
+  static_assert(ITERS >= 1 && ROWS * 8 % NT == 0, "tile too small for the workgroup");
+  static_assert(SHIFT == 0 || SHIFT == 1, "swizzle shift");
+
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off0;      // byte offset of this lane's chunk in instruction 0, tile 0
+  uint32_t row_step;  // bytes between the row blocks of consecutive instructions
+  int32_t kc0, kc1;   // first K element of the chunk for even / odd row blocks
+  int32_t K;
+  int32_t wave;
+
+  __device__ __forceinline__ LoaderKVec(const void* base, int32_t rows_valid, int64_t rs, int64_t /*ks*/,
+                                        int64_t K_, int32_t wave_, int32_t lane) {
+    K = (int32_t)K_;
+    wave = wave_;
+    const uint32_t bytes =
+        rows_valid > 0 ? (uint32_t)(((int64_t)(rows_valid - 1) * rs + K_) * ELEM) : 0u;
+    rsrc = make_rsrc(base, bytes);
+    // instruction j covers rows (j*WAVES + wave)*8 + 0..7; lane l lands in
+    // row +l/8, physical chunk l%8, and fetches logical chunk l%8 ^ swz(row)
+    const int32_t row = wave * 8 + (lane >> 3);
+    const int32_t c0 = (lane & 7) ^ swz(row, SHIFT);
+    const int32_t c1 = (lane & 7) ^ swz(row + WAVES * 8, SHIFT);
+    kc0 = c0 * CE;
+    kc1 = c1 * CE;
+    off0 = (uint32_t)(row * rs * ELEM) + (uint32_t)(c0 * 16);
+    row_step = (uint32_t)(WAVES * 8 * rs * ELEM);
+  }
+
+  __device__ __forceinline__ void issue(int32_t t, char* lds) const {
+#pragma unroll
+    for (int j = 0; j < ITERS; ++j) {
+      // rows advance by j*WAVES*8: swz(row, 0) never changes, swz(row, 1)
+      // flips bit 2 when j*WAVES is odd
+      const bool odd = SHIFT == 1 && ((j * WAVES) & 1);
+      const int32_t kc = odd ? kc1 : kc0;
+      const uint32_t o = odd ? off0 + (uint32_t)((kc1 - kc0) / CE * 16) : off0;
+      const uint32_t a = o + (uint32_t)j * row_step + (uint32_t)(t * 128);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16,
+                                               (t * KT + kc < K) ? a : kOutOfRange, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void commit(char*) const {}
+};
+
+// M- (or N-) contiguous fp16 rows, 16-B aligned: the tile is stored in HBM
+// as K rows of ROWS contiguous values.  A thread fetches KB consecutive K
+// rows of one 8-value block (8 x KB halves), transposes them in registers
+// and writes 8 K-contiguous pieces of KB halves into the LDS tile.
+template <int ROWS, int NT, int SHIFT>
+struct LoaderMNVec {
+  static constexpr int MB = ROWS / 8;        // 8-row blocks
+  static constexpr int KB = 64 * MB / NT;    // K rows per thread
+  static_assert(KB == 8 || KB == 4, "unsupported tile for the transposing loader");
+
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off0;
+  uint32_t kstep;  // bytes between consecutive K rows
+  int32_t mb, kbase, K;
+  bool row_ok;
+  u32x4 stage[KB];
+
+  __device__ __forceinline__ LoaderMNVec(const void* base, int32_t rows_valid, int64_t /*rs*/, int64_t ks,
+                                         int64_t K_, int32_t /*wave*/, int32_t /*lane*/) {
+    K = (int32_t)K_;
+    const int32_t tid = threadIdx.x;
+    mb = tid % MB;
+    kbase = (tid / MB) * KB;
+    row_ok = mb * 8 < rows_valid;
+    const uint32_t bytes =
+        (rows_valid > 0 && K_ > 0) ? (uint32_t)(((K_ - 1) * ks + rows_valid) * 2) : 0u;
+    rsrc = make_rsrc(base, bytes);
+    kstep = (uint32_t)(ks * 2);
+    off0 = (uint32_t)(mb * 16) + (uint32_t)kbase * kstep;
+  }
+
+  __device__ __forceinline__ void issue(int32_t t, char*) {
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int32_t k = t * 64 + kbase + j;
+      const uint32_t o = (row_ok && k < K) ? off0 + (uint32_t)(t * 64 + j) * kstep : kOutOfRange;
+      stage[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, o, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void commit(char* lds) const {
+    // stage[j] holds values (m = 8*mb + e, k = kbase + j), e = 0..7, two per
+    // 32-bit word.  Row e of the output needs (m = 8*mb + e, k = kbase + j)
+    // for j = 0..KB-1.
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int32_t row = mb * 8 + e;
+      const int32_t byte = kbase * 2;
+      uint32_t w[KB / 2];
+#pragma unroll
+      for (int j = 0; j < KB; j += 2) {
+        const uint32_t lo = stage[j][e >> 1], hi = stage[j + 1][e >> 1];
+        // select the 16-bit half e&1 of each, pack (k = j) low, (k = j+1) high
+        w[j / 2] = (e & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                           : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      }
+      char* dst = lds + lds_offset(row, byte, SHIFT);
+      if constexpr (KB == 8) {
+        *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
+      } else {
+        *(u32x2*)dst = u32x2{w[0], w[1]};
+      }
+    }
+  }
+};
+
+// Any strides: every element is fetched on its own (64-bit addressing).
+template <int ROWS, int NT, int SHIFT>
+struct LoaderGeneric {
+  static constexpr int PER = ROWS * 64 / NT;
+  const uint16_t* base;
+  int64_t rs, ks;
+  int32_t rows_valid, K;
+  uint16_t stage[PER];
+
+  __device__ __forceinline__ LoaderGeneric(const void* base_, int32_t rows_valid_, int64_t rs_, int64_t ks_,
+                                           int64_t K_, int32_t, int32_t) {
+    base = (const uint16_t*)base_;
+    rs = rs_;
+    ks = ks_;
+    rows_valid = rows_valid_;
+    K = (int32_t)K_;
+  }
+
+  __device__ __forceinline__ void issue(int32_t t, char*) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = j * NT + (int32_t)threadIdx.x;
+      const int32_t r = e >> 6, k = t * 64 + (e & 63);
+      stage[j] = (r < rows_valid && k < K) ? base[(int64_t)r * rs + (int64_t)k * ks] : (uint16_t)0;
+    }
+  }
+
+  __device__ __forceinline__ void commit(char* lds) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int32_t e = j * NT + (int32_t)threadIdx.x;
+      *(uint16_t*)(lds + lds_offset(e >> 6, (e & 63) * 2, SHIFT)) = stage[j];
+    }
+  }
+};
+
+template <int KIND, int ROWS, int NT, int SHIFT>
+struct LoaderSel;
+template <int ROWS, int NT, int SHIFT>
+struct LoaderSel<LOAD_KVEC, ROWS, NT, SHIFT> {
+  using type = LoaderKVec<ROWS, NT, SHIFT, 2>;
+};
+template <int ROWS, int NT, int SHIFT>
+struct LoaderSel<LOAD_MNVEC, ROWS, NT, SHIFT> {
+  using type = LoaderMNVec<ROWS, NT, SHIFT>;
+};
+template <int ROWS, int NT, int SHIFT>
+struct LoaderSel<LOAD_GENERIC, ROWS, NT, SHIFT> {
+  using type = LoaderGeneric<ROWS, NT, SHIFT>;
+};
+
+}  // namespace sl

@@ -1,0 +1,71 @@
+// sl_kernels.hpp -- parameters and launchers shared between the host
+// dispatcher (api.cpp) and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sl {
+
+// How one operand tile is brought from HBM into its K-contiguous LDS tile.
+enum LoadKind : int32_t {
+  LOAD_KVEC = 0,    // K contiguous, 16-B aligned: direct HBM->LDS 16-B buffer loads
+  LOAD_MNVEC = 1,   // M (or N) contiguous, 16-B aligned: 16-B loads, 8x8 register transpose
+  LOAD_GENERIC = 2  // any strides: element loads
+};
+
+// Kernel families (sl_plan.kernel).
+enum KernelKind : int32_t { K_F16 = 1, K_F16_GENERIC = 2, K_MX = 3 };
+
+// Tile configurations the dispatcher can choose (rows of A, rows of B,
+// waves along M, waves along N).
+enum TileCfg : int32_t {
+  T256x256_W2x2 = 0,  // 4 waves, each 128x128
+  T256x128_W2x2 = 1,  // 4 waves, each 128x64
+  T128x256_W2x2 = 2,  // 4 waves, each 64x128
+  T128x128_W2x2 = 3,  // 4 waves, each 64x64
+  T_COUNT = 4
+};
+
+struct TileShape {
+  int32_t bm, bn, wm, wn;
+};
+
+constexpr TileShape kTiles[T_COUNT] = {
+    {256, 256, 2, 2}, {256, 128, 2, 2}, {128, 256, 2, 2}, {128, 128, 2, 2}};
+
+struct GemmParams {
+  const void* a;  // element (b, m, k) at a + b*a_bs + m*a_rs + k*a_ks
+  const void* b;  // element (b, n, k) at b + b*b_bs + n*b_rs + k*b_ks
+  const void* c;  // may be NULL
+  void* d;
+  const uint8_t* sfa;  // MX scales (NULL for fp16)
+  const uint8_t* sfb;
+  int64_t M, N, K;
+  int64_t a_rs, a_ks, a_bs;
+  int64_t b_rs, b_ks, b_bs;
+  int64_t c_rs, c_cs, c_bs;
+  int64_t d_rs, d_cs, d_bs;
+  int64_t sa_rs, sa_ks, sa_bs;  // scale strides (elements = bytes)
+  int64_t sb_rs, sb_ks, sb_bs;
+  int32_t batch;
+  int32_t tiles_m, tiles_n;
+  int32_t group_m;
+  int32_t k_tiles;
+  int32_t flags;
+};
+
+// GemmParams.flags
+constexpr int32_t F_HAS_C = 1;
+constexpr int32_t F_D_VEC = 2;  // D rows contiguous and 8-B aligned: 4-half stores
+constexpr int32_t F_C_VEC = 4;  // C rows contiguous and 8-B aligned: 4-half loads
+
+// Launchers (each returns the launch's hipError_t).
+hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load,
+                           int32_t swz_shift, hipStream_t stream);
+hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, int32_t swz_shift, hipStream_t stream);
+
+hipError_t launch_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t cases, hipStream_t stream);
+hipError_t launch_probe_lds(int32_t mode, const void* src, const int32_t* perm, void* out,
+                            hipStream_t stream);
+
+}  // namespace sl

@@ -1,0 +1,104 @@
+// sl_maps.hpp -- the layouts every stage of the GEMM uses, as constexpr
+// functions callable from host and device.  The kernels compute their LDS
+// and fragment addresses with these functions, and the host query entry
+// points dump them, so what is exported is what runs.
+//
+// Notation follows "数据布局及其记号" (shape:stride layouts, section
+// "Shape-Stride 模型"; XOR swizzle, section "Swizzle Layout") and the TV
+// (thread, value) maps of "CuTe 中 A、B 如何加载到 MMA 寄存器", section 2:
+// a lane index l and a value (slot) index v are unflattened first-mode-
+// fastest and the map returns the operand tile coordinate.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define SL_HD __host__ __device__ __forceinline__
+#else
+#define SL_HD inline
+#endif
+
+namespace sl {
+
+// ---------------------------------------------------------------------------
+// Matrix-core operand maps (CDNA4 / gfx950).
+//
+// v_mfma_f32_16x16x32_f16: lane l = l0 + 16*l1 (l0 < 16, l1 < 4), slot v < 8
+//   A (16 x 32):  m = l0, k = 8*l1 + v        TV ((16,4),8):((1,128),16), q = m + 16k
+//   B (16 x 32):  n = l0, k = 8*l1 + v        (same form)
+//   D (16 x 16):  n = l0, m = 4*l1 + v (v<4)   TV ((16,4),4):((16,4),1),  q = m + 16n
+// v_mfma_f32_32x32x16_f16: lane l = l0 + 32*l1 (l0 < 32, l1 < 2)
+//   A (32 x 16):  m = l0, k = 8*l1 + v
+//   D (32 x 32):  n = l0, m = 8*(v/4) + 4*l1 + v%4  (v < 16)
+// v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3): slot v < 32 (bytes)
+//   A (16 x 128): m = l0, k = 32*l1 + v; scale lane l -> (m = l0, block l1)
+// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3):
+//   A (32 x 64):  m = l0, k = 32*l1 + v; scale lane l -> (m = l0, block l1)
+// ---------------------------------------------------------------------------
+
+enum Instr : int32_t { MFMA16_F16 = 0, MFMA32_F16 = 1, MFMA16_F8 = 2, MFMA32_F8 = 3 };
+enum Operand : int32_t { OP_A = 0, OP_B = 1, OP_D = 2, OP_SCALE = 3 };
+
+struct Coord {
+  int32_t row, col;
+};
+
+SL_HD constexpr int32_t instr_rows(int32_t instr) { return (instr == MFMA16_F16 || instr == MFMA16_F8) ? 16 : 32; }
+SL_HD constexpr int32_t instr_k(int32_t instr) {
+  return instr == MFMA16_F16 ? 32 : instr == MFMA32_F16 ? 16 : instr == MFMA16_F8 ? 128 : 64;
+}
+// input slots per lane (elements) for A/B
+SL_HD constexpr int32_t instr_in_slots(int32_t instr) { return (instr == MFMA16_F16 || instr == MFMA32_F16) ? 8 : 32; }
+// accumulator registers per lane
+SL_HD constexpr int32_t instr_acc_regs(int32_t instr) { return instr_rows(instr) == 16 ? 4 : 16; }
+
+// (lane, slot) -> (row, col) of operand A or B: row = l0, col = slots*l1 + v.
+SL_HD constexpr Coord operand_map(int32_t instr, int32_t lane, int32_t slot) {
+  const int32_t R = instr_rows(instr);
+  return Coord{lane % R, instr_in_slots(instr) * (lane / R) + slot};
+}
+
+// (lane, reg) -> (m, n) of the accumulator.
+SL_HD constexpr Coord acc_map(int32_t instr, int32_t lane, int32_t reg) {
+  return instr_rows(instr) == 16 ? Coord{4 * (lane / 16) + reg, lane % 16}
+                                 : Coord{8 * (reg / 4) + 4 * (lane / 32) + reg % 4, lane % 32};
+}
+
+// scale lane -> (row, K block of 32) for the scaled f8 instructions
+SL_HD constexpr Coord scale_map(int32_t instr, int32_t lane) {
+  const int32_t R = instr_rows(instr);
+  return Coord{lane % R, lane / R};
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile layout: a K-contiguous tile of `rows` x 128 bytes.  Logical byte
+// (row, b) lives in 16-byte chunk c = b/16 of its row; the chunk index is
+// XOR-swizzled with bits of the row so that the lanes of one ds_read_b128
+// pass land on distinct banks:
+//   offset(row, b) = row*128 + 16*(c ^ swz(row)) + b%16
+// with swz(row) = (row >> shift) & 7.  shift = 0 is the page's SWIZZLE_128B
+// rule (row-in-8 XOR the chunk), shift = 1 pairs rows for a 64-bank LDS.
+// The rule is a bijection on every 8*2^shift-row block, and writer and
+// reader both call this one function.
+// ---------------------------------------------------------------------------
+
+constexpr int32_t kRowBytes = 128;
+
+SL_HD constexpr int32_t swz(int32_t row, int32_t shift) { return (row >> shift) & 7; }
+
+SL_HD constexpr int32_t lds_offset(int32_t row, int32_t byte_in_row, int32_t shift) {
+  return row * kRowBytes + 16 * (((byte_in_row >> 4) ^ swz(row, shift)) & 7) + (byte_in_row & 15);
+}
+
+// Byte offset in the LDS tile that lane `lane` reads, for its 16-byte
+// fragment piece `piece` (f16: 1 piece of 8 halves; f8: 2 pieces of 16
+// bytes), of the MFMA tile whose first row is `row0`, at k-slice `ks` (in
+// units of the instruction's K), for an operand with `elem_bytes` bytes.
+SL_HD constexpr int32_t fragment_lds_offset(int32_t instr, int32_t lane, int32_t piece, int32_t row0,
+                                            int32_t ks, int32_t shift) {
+  const Coord c = operand_map(instr, lane, piece * 16 / (instr_in_slots(instr) == 8 ? 2 : 1));
+  const int32_t elem_bytes = instr_in_slots(instr) == 8 ? 2 : 1;
+  const int32_t byte = (ks * instr_k(instr) + c.col) * elem_bytes;
+  return lds_offset(row0 + c.row, byte, shift);
+}
+
+}  // namespace sl

@@ -138,6 +138,17 @@ def gemm_workload(name: str, M: int, N: int, K: int, *, seed: int, dist: str = "
     return Workload(name, M, N, K, batch or 1, a, b, c, sfa, sfb, block_k, d_shape, d_strides)
 
 
+def to_device(op: Optional[HostOperand]):
+    """The same storage bytes on the current GPU, viewed with the same
+    strides (a torch tensor); None stays None."""
+    import torch
+    if op is None:
+        return None
+    st = torch.from_numpy(np.ascontiguousarray(op.storage))
+    st = st.view({"f16": torch.float16, "e4m3": torch.float8_e4m3fn, "e8m0": torch.float8_e8m0fnu}[op.kind])
+    return st.to("cuda").as_strided(op.shape, op.strides)
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads
 # ---------------------------------------------------------------------------

@@ -1,0 +1,84 @@
+"""Shared helpers of the GPU tests: move seeded host operands to the device
+with their strides, run the library, and judge its output against the
+oracle (full or at sampled points)."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+from oracle import gemm as OG
+from stride_layouts_lds_amd.inputs import HostOperand, Workload, to_device  # noqa: F401
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_library(w: Workload, out=None, stream=None):
+    """D from the HIP library for workload w (D row-major, allocated by torch)."""
+    import torch
+    from stride_layouts_lds_amd import api
+    a, b, c = to_device(w.a), to_device(w.b), to_device(w.c)
+    sfa, sfb = to_device(w.sfa), to_device(w.sfb)
+    if out is None:
+        out = torch.empty(w.d_shape, dtype=torch.float16, device="cuda")
+    api.gemm(a, b, c, out=out, sfa=sfa, sfb=sfb, block_k=w.block_k, stream=stream)
+    torch.cuda.synchronize()
+    return out
+
+
+def d_codes(d) -> np.ndarray:
+    import torch
+    return d.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def oracle_full(w: Workload):
+    return OG.gemm(w.a.view, w.b.view, w.c.view if w.c else None,
+                   w.sfa.view if w.sfa else None, w.sfb.view if w.sfb else None, block_k=w.block_k)
+
+
+def oracle_points(w: Workload, pts: np.ndarray):
+    return OG.gemm_points(w.a.view, w.b.view, w.c.view if w.c else None,
+                          w.sfa.view if w.sfa else None, w.sfb.view if w.sfb else None, points=pts,
+                          block_k=w.block_k)
+
+
+def sample_points(w: Workload, n: int, seed: int = 0) -> np.ndarray:
+    """Random output points plus every corner and the last row / column
+    (ragged edges), as (batch, m, n)."""
+    rng = np.random.default_rng(seed)
+    B, M, N = w.batch, w.M, w.N
+    pts = [np.stack([rng.integers(0, B, n), rng.integers(0, M, n), rng.integers(0, N, n)], 1)]
+    edge = []
+    for b in {0, B - 1}:
+        for m in {0, M - 1}:
+            for nn in {0, N - 1}:
+                edge.append((b, m, nn))
+        for nn in rng.integers(0, N, 64):
+            edge.append((b, M - 1, int(nn)))
+        for m in rng.integers(0, M, 64):
+            edge.append((b, int(m), N - 1))
+    pts.append(np.array(edge, np.int64))
+    return np.concatenate(pts).astype(np.int64)
+
+
+def assert_within_bound(d: np.ndarray, d_ref: np.ndarray, absum: np.ndarray, what: str) -> None:
+    bad, wi, wr = OG.check(d, d_ref, absum)
+    if bad:
+        dd = d.ravel()[wi].view(np.float16)
+        rr = d_ref.ravel()[wi].view(np.float16)
+        raise AssertionError(f"{what}: {bad} of {d.size} elements outside |D-Dref| <= 2^-10|Dref| + 2^-13 S; "
+                             f"worst index {wi}: D={float(dd)} Dref={float(rr)} S={absum.ravel()[wi]} "
+                             f"(error/bound {wr:.3g})")
+
+
+def dump(name: str, arr) -> None:
+    """Save an array under gpurun_out/ for offline reading (debug aid)."""
+    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+    if os.environ.get("SL_DUMP"):
+        os.makedirs(d, exist_ok=True)
+        np.save(os.path.join(d, name + ".npy"), np.asarray(arr))

@@ -1,0 +1,213 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every symbol
+include/sl.h declares, validates descriptors before any HIP call, selects
+loaders and tiles, and its exported layout maps equal the oracle's
+bit for bit.  No compute call is made here."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import layout as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def api():
+    from stride_layouts_lds_amd import api as A
+    if not os.path.exists(A.LIB_PATH):
+        from stride_layouts_lds_amd import build
+        build.build(verbose=False)
+    A.lib()
+    return A
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "sl.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[\w\s\*]*?\b(sl_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(api):
+    declared = header_functions()
+    assert "sl_gemm" in declared and len(declared) >= 10
+    assert sorted(api.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(api.lib(), name), name
+
+
+def test_abi_version_and_strings(api):
+    text = open(os.path.join(ROOT, "include", "sl.h")).read()
+    assert api.abi_version() == int(re.search(r"#define SL_ABI_VERSION (\d+)", text).group(1))
+    for code in api.STATUS:
+        assert api.status_string(code) and api.status_string(code) != "unknown status"
+    assert api.status_string(12345) == "unknown status"
+
+
+# ------------------------------------------------------------------ validation
+
+F16 = 1
+BASE_A, BASE_B, BASE_C, BASE_D = 0x100000000, 0x200000000, 0x300000000, 0x400000000
+
+
+def rowmajor(ptr, shape, dtype=F16):
+    st = [0] * len(shape)
+    acc = 1
+    for i in reversed(range(len(shape))):
+        st[i] = acc
+        acc *= shape[i]
+    return ptr, dtype, shape, st
+
+
+def plan(api, a, b, c=None, d=None, sfa=None, sfb=None, block_k=32):
+    D = lambda x: api.desc(*x) if x is not None else None
+    return api.sl_gemm_plan(api.make_args(D(a), D(b), D(c), D(d), D(sfa), D(sfb), block_k))
+
+
+def err(api, *args, **kw):
+    with pytest.raises(api.SLError) as e:
+        plan(api, *args, **kw)
+    return e.value.name
+
+
+def test_plan_tn_square(api):
+    p = plan(api, rowmajor(BASE_A, (8192, 8192)), rowmajor(BASE_B, (8192, 8192)), None,
+             rowmajor(BASE_D, (8192, 8192)))
+    assert p["kernel"] == api.K_F16 and p["a_load"] == 0 and p["b_load"] == 0
+    assert (p["tile_m"], p["tile_n"], p["tile_k"]) == (256, 256, 64)
+    assert p["workgroups"] == 32 * 32
+
+
+def test_plan_transposed_views_select_loaders(api):
+    nb, M, N, K = 64, 512, 512, 512
+    a_mn = (BASE_A, F16, (nb, M, K), (M * K, 1, M))          # M contiguous (stride-swapped view)
+    b_k = (BASE_B, F16, (nb, N, K), (N * K, K, 1))           # K contiguous
+    b_n = (BASE_B, F16, (nb, N, K), (N * K, 1, N))           # N contiguous
+    d = (BASE_D, F16, (nb, M, N), (M * N, N, 1))
+    p = plan(api, a_mn, b_k, None, d)
+    assert (p["a_load"], p["b_load"]) == (1, 0) and p["batch"] == nb
+    p = plan(api, a_mn, b_n, None, d)
+    assert (p["a_load"], p["b_load"]) == (1, 1)
+    # an odd stride or a misaligned base goes to the element loader
+    odd = (BASE_A, F16, (M, K), (K + 1, 1))
+    p = plan(api, odd, rowmajor(BASE_B, (N, K)), None, rowmajor(BASE_D, (M, N)))
+    assert p["kernel"] == api.K_F16_GENERIC and p["a_load"] == 2
+    mis = (BASE_A + 2, F16, (M, K), (K, 1))
+    p = plan(api, mis, rowmajor(BASE_B, (N, K)), None, rowmajor(BASE_D, (M, N)))
+    assert p["a_load"] == 2
+
+
+def test_validation_errors(api):
+    A = rowmajor(BASE_A, (64, 32))
+    B = rowmajor(BASE_B, (48, 32))
+    Dd = rowmajor(BASE_D, (64, 48))
+    assert err(api, (BASE_A, 2, (64, 32), (32, 1)), B, None, Dd) == "SL_ERR_DTYPE"
+    assert err(api, A, rowmajor(BASE_B, (48, 31)), None, Dd) == "SL_ERR_SHAPE"
+    assert err(api, A, B, None, rowmajor(BASE_D, (64, 47))) == "SL_ERR_SHAPE"
+    assert err(api, A, B, rowmajor(BASE_C, (63, 48)), Dd) == "SL_ERR_SHAPE"
+    assert err(api, (BASE_A, F16, (64, 32), (-32, 1)), B, None, Dd) == "SL_ERR_LAYOUT"
+    assert err(api, (BASE_A, F16, (64, 32), (32, 1)), B, None, (BASE_D, F16, (64, 48), (0, 1))) == "SL_ERR_LAYOUT"
+    assert err(api, (BASE_A + 1, F16, (64, 32), (32, 1)), B, None, Dd) == "SL_ERR_ALIGN"
+    assert err(api, (0, F16, (64, 32), (32, 1)), B, None, Dd) == "SL_ERR_NULL"
+    # D overlapping an input
+    assert err(api, A, B, None, (BASE_A + 64, F16, (64, 48), (48, 1))) == "SL_ERR_ALIAS"
+    # C == D in place is allowed; C overlapping D otherwise is not
+    plan(api, A, B, Dd, Dd)
+    assert err(api, A, B, (BASE_D + 2, F16, (64, 48), (48, 1)), Dd) == "SL_ERR_ALIAS"
+    # batch mismatch
+    assert err(api, rowmajor(BASE_A, (3, 64, 32)), B, None, rowmajor(BASE_D, (2, 64, 48))) == "SL_ERR_SHAPE"
+    # rank
+    with pytest.raises(api.SLError):
+        api.sl_gemm_plan(api.make_args(api.desc(BASE_A, F16, (1, 1, 64, 32)[:3], (1, 32, 1)),
+                                       api.desc(*B), None, api.desc(*Dd)))
+
+
+def test_degenerate_sizes_are_noops(api):
+    p = plan(api, rowmajor(BASE_A, (0, 32)), rowmajor(BASE_B, (48, 32)), None, rowmajor(BASE_D, (0, 48)))
+    assert p["m"] == 0 and p["workgroups"] == 0
+    # K = 0: D = C, still a launch (A and B may be NULL)
+    p = plan(api, (0, F16, (64, 0), (0, 1)), (0, F16, (48, 0), (0, 1)), rowmajor(BASE_C, (64, 48)),
+             rowmajor(BASE_D, (64, 48)))
+    assert p["k"] == 0 and p["workgroups"] > 0
+
+
+def test_broadcast_inputs_allowed(api):
+    # one B for every batch (batch stride 0), and a zero row stride on A
+    p = plan(api, rowmajor(BASE_A, (4, 64, 32)), (BASE_B, F16, (4, 48, 32), (0, 32, 1)), None,
+             rowmajor(BASE_D, (4, 64, 48)))
+    assert p["batch"] == 4
+    plan(api, (BASE_A, F16, (64, 32), (0, 1)), rowmajor(BASE_B, (48, 32)), None, rowmajor(BASE_D, (64, 48)))
+
+
+def test_mx_validation(api):
+    E4, E8 = 3, 4
+    M = N = K = 256
+    a = (BASE_A, E4, (M, K), (K, 1))
+    b = (BASE_B, E4, (N, K), (K, 1))
+    sa = (BASE_C, E8, (M, K // 32), (K // 32, 1))
+    sb = (BASE_C + 0x10000, E8, (N, K // 32), (K // 32, 1))
+    d = rowmajor(BASE_D, (M, N))
+    p = plan(api, a, b, None, d, sa, sb)
+    assert p["kernel"] == api.K_MX and p["tile_k"] == 128
+    assert err(api, a, b, None, d, sa, sb, block_k=16) == "SL_ERR_SHAPE"
+    assert err(api, a, b, None, d, sa, (BASE_C + 0x10000, E8, (N, 7), (7, 1))) == "SL_ERR_SHAPE"
+    assert err(api, a, b, None, d, None, None) == "SL_ERR_DTYPE"
+    assert err(api, (BASE_A, E4, (M, K), (1, M)), b, None, d, sa, sb) == "SL_ERR_LAYOUT"
+
+
+# ------------------------------------------------------------------ maps
+
+@pytest.mark.parametrize("instr", [0, 1, 2, 3])
+@pytest.mark.parametrize("operand", [0, 1, 2])
+def test_fragment_maps_equal_oracle(api, instr, operand):
+    got = api.query_fragment_map(instr, operand)
+    tv = L.INSTR_MAPS[instr][operand]
+    want = np.array(tv.table(), np.int32)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("instr", [2, 3])
+def test_scale_map_equal_oracle(api, instr):
+    got = api.query_fragment_map(instr, 3)
+    rows = 16 if instr == 2 else 32
+    want = np.array([(l, 0) + L.mfma_scale_owner(rows, l) for l in range(64)], np.int32)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_lds_map_is_the_xor_swizzle(api, variant):
+    offs, es = api.query_lds_map(variant, 0)
+    rows, cols = offs.shape
+    assert rows * cols * es == rows * 128
+    # a bijection onto the tile's bytes (element granularity)
+    assert sorted((offs // es).ravel().tolist()) == list(range(rows * cols))
+    # equal to Swizzle<3, 4, 3 + shift> of the row-major byte offset, the
+    # byte form of the pages' Swizzle<3,3,3> on fp16 elements
+    shift = int(os.environ.get("SL_SWZ", "0") or 0) and 1
+    for r in range(rows):
+        for k in range(cols):
+            assert offs[r, k] == L.swizzle_bms(r * 128 + k * es, 3, 4, 3 + shift)
+
+
+@pytest.mark.parametrize("variant,instr", [(1, 0), (3, 2)])
+def test_fragment_addresses_compose_maps(api, variant, instr):
+    got = api.query_fragment_addresses(variant, 0)
+    tv = L.INSTR_MAPS[instr][0]
+    es = 2 if instr < 2 else 1
+    shift = int(os.environ.get("SL_SWZ", "0") or 0) and 1
+    want = [L.swizzle_bms(r * 128 + c * es, 3, 4, 3 + shift) for _, _, r, c in tv.table()]
+    assert got.tolist() == want
+
+
+def test_fragment_reads_conflict_free_under_the_page_bank_model(api):
+    """Under the data-layout page's bank model (32 banks x 4 B, 16-byte
+    accesses served 8 lanes per pass) every ds_read_b128 of a fragment load
+    takes the minimum 8 passes with the default swizzle, and 8x that
+    without it.  The gfx950 verdict is the hardware counter."""
+    addrs = api.query_fragment_addresses(1, 0).reshape(64, 8)[:, 0]
+    assert L.bank_conflict_passes(addrs.tolist(), 16, 32, 4, 8) == 8
+    plain = [r * 128 + c * 2 for _, v, r, c in L.MFMA16_F16_A.table() if v == 0]
+    assert L.bank_conflict_passes(plain, 16, 32, 4, 8) == 64

@@ -1,0 +1,222 @@
+"""Parity of the HIP GEMM with the oracle, through the C ABI.
+
+* exact: small-integer inputs make every product, partial sum and fp32
+  accumulation exact, so the library's fp16 output must equal the oracle's
+  bit for bit, over ragged multi-tile shapes, every majorness combination,
+  batches, broadcasts, in-place C, K = 0 and the element-loader path;
+* bounded: real-valued seeded inputs, every element within
+  |D - D_ref| <= 2^-10 |D_ref| + 2^-13 sum_k |A B| (full oracle on small
+  shapes; sampled points, corners and ragged edges at the full workload
+  sizes, plus a finiteness check of every element).
+"""
+
+import numpy as np
+import pytest
+
+from stride_layouts_lds_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from stride_layouts_lds_amd import api as A
+    A.lib()
+    return A
+
+
+def H():
+    import gpu_helpers
+    return gpu_helpers
+
+
+# ------------------------------------------------------------------ exact
+
+EXACT = [
+    # M, N, K, batch, a_major, b_major, with_c
+    (256, 256, 64, None, "row", "row", False),
+    (300, 520, 200, None, "row", "row", True),
+    (1, 1, 8, None, "row", "row", False),
+    (17, 33, 8, None, "row", "row", True),
+    (513, 257, 1000, None, "row", "row", True),
+    (520, 264, 136, 2, "col", "row", False),
+    (96, 80, 64, 3, "col", "col", True),
+    (96, 80, 72, 3, "row", "col", False),
+    (264, 136, 200, None, "col", "col", False),
+    (100, 60, 40, None, "col", "row", False),   # M % 8 != 0: element loader for A
+    (70, 90, 37, None, "row", "row", True),     # K % 8 != 0: element loaders
+]
+
+
+@pytest.mark.parametrize("case", EXACT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_{c[4]}{c[5]}_c{int(c[6])}")
+def test_exact_integer_parity(api, case):
+    h = H()
+    M, N, K, batch, am, bm, with_c = case
+    w = I.gemm_workload("exact", M, N, K, seed=M + N + K, dist="int4", batch=batch, a_major=am, b_major=bm,
+                        with_c=with_c)
+    h.log(f"exact {case} plan={_plan(api, w)}")
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
+def _plan(api, w):
+    import torch
+    h = H()
+    out = torch.empty(w.d_shape, dtype=torch.float16, device="cuda")
+    args = api.make_args(h.to_device(w.a), h.to_device(w.b), h.to_device(w.c), out, h.to_device(w.sfa),
+                         h.to_device(w.sfb), w.block_k)
+    p = api.sl_gemm_plan(args)
+    return {k: p[k] for k in ("kernel", "a_load", "b_load", "tile_m", "tile_n", "workgroups")}
+
+
+def test_odd_strides_take_the_element_loader(api):
+    """Row stride K+3 and a column-strided view (every other K element)."""
+    import torch
+    h = H()
+    rng = np.random.default_rng(21)
+    M, N, K = 150, 130, 96
+    a_st = rng.integers(-4, 5, (M, K + 3)).astype(np.float16)
+    b_st = rng.integers(-4, 5, (N, 2 * K)).astype(np.float16)
+    a = torch.from_numpy(a_st).cuda()[:, :K]
+    b = torch.from_numpy(b_st).cuda()[:, ::2]
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    p = api.sl_gemm_plan(api.make_args(a, b, None, out))
+    assert p["kernel"] == api.K_F16_GENERIC
+    api.gemm(a, b, out=out)
+    torch.cuda.synchronize()
+    from oracle import gemm as OG
+    d_ref, _, _ = OG.gemm(a_st.view(np.uint16)[:, :K], b_st.view(np.uint16)[:, ::2])
+    assert np.array_equal(h.d_codes(out), d_ref[0])
+
+
+def test_in_place_c_equals_d(api):
+    import torch
+    h = H()
+    w = I.gemm_workload("inplace", 200, 136, 128, seed=5, dist="int4", with_c=True)
+    d_ref, _, _ = h.oracle_full(w)
+    c = h.to_device(w.c).contiguous()
+    api.gemm(h.to_device(w.a), h.to_device(w.b), c, out=c)
+    torch.cuda.synchronize()
+    assert np.array_equal(h.d_codes(c), d_ref[0])
+
+
+def test_k_zero_gives_c(api):
+    import torch
+    h = H()
+    M, N = 70, 40
+    c = torch.randn(M, N).half().cuda()
+    a = torch.empty((M, 0), dtype=torch.float16, device="cuda")
+    b = torch.empty((N, 0), dtype=torch.float16, device="cuda")
+    out = torch.full((M, N), 7.0, dtype=torch.float16, device="cuda")
+    api.gemm(a, b, c, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), c.cpu())
+    api.gemm(a, b, None, out=out)
+    torch.cuda.synchronize()
+    assert not out.cpu().any()
+
+
+def test_empty_is_a_noop(api):
+    import torch
+    a = torch.zeros((0, 64), dtype=torch.float16, device="cuda")
+    b = torch.zeros((32, 64), dtype=torch.float16, device="cuda")
+    out = torch.zeros((0, 32), dtype=torch.float16, device="cuda")
+    api.gemm(a, b, out=out)
+    torch.cuda.synchronize()
+
+
+def test_broadcast_b_across_batch(api):
+    import torch
+    h = H()
+    rng = np.random.default_rng(22)
+    nb, M, N, K = 4, 136, 72, 64
+    A = rng.integers(-4, 5, (nb, M, K)).astype(np.float16)
+    B = rng.integers(-4, 5, (N, K)).astype(np.float16)
+    a = torch.from_numpy(A).cuda()
+    b = torch.from_numpy(B).cuda().unsqueeze(0).expand(nb, N, K)  # batch stride 0
+    out = api.gemm(a, b)
+    torch.cuda.synchronize()
+    from oracle import gemm as OG
+    bv = np.lib.stride_tricks.as_strided(B.view(np.uint16), (nb, N, K), (0, 2 * K, 2))
+    d_ref, _, _ = OG.gemm(A.view(np.uint16), bv)
+    assert np.array_equal(h.d_codes(out), d_ref)
+
+
+def test_mx_exact_parity(api):
+    """E4M3 integers and scale exponents in [-2, 2]: every product is a
+    multiple of 2^-4 below 2^8 and every partial sum stays exact in fp32."""
+    h = H()
+    for (M, N, K) in [(256, 256, 128), (300, 200, 384), (64, 520, 256)]:
+        w = I.gemm_workload("mx_exact", M, N, K, seed=K, dist="int4", mx=True, scale_range=(-2, 2))
+        h.log(f"mx exact {M}x{N}x{K}")
+        d = h.d_codes(h.run_library(w))
+        d_ref, _, _ = h.oracle_full(w)
+        assert np.array_equal(d.reshape(d_ref.shape), d_ref), (M, N, K)
+
+
+# ------------------------------------------------------------------ bounded
+
+SMALL = [
+    ("normal_c", dict(M=520, N=264, K=320, dist="normal", with_c=True)),
+    ("uniform_ragged", dict(M=333, N=251, K=264, dist="uniform")),
+    ("batched_nn", dict(M=136, N=128, K=200, dist="normal", batch=3, a_major="col", b_major="row")),
+    ("batched_nt", dict(M=128, N=136, K=96, dist="normal", batch=2, a_major="col", b_major="col")),
+    ("mx", dict(M=300, N=264, K=512, dist="normal", mx=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_bounded_small(api, name, kw):
+    h = H()
+    M, N, K = kw.pop("M"), kw.pop("N"), kw.pop("K")
+    w = I.gemm_workload(name, M, N, K, seed=31, **kw)
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, absum = h.oracle_full(w)
+    h.assert_within_bound(d.reshape(d_ref.shape), d_ref, absum, name)
+
+
+def test_config1_full(api):
+    h = H()
+    w = I.config1()
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, absum = h.oracle_full(w)
+    h.assert_within_bound(d.reshape(d_ref.shape), d_ref, absum, w.name)
+
+
+def _sampled(api, w, n=3000):
+    import torch
+    h = H()
+    h.log(f"{w.name}: plan {_plan(api, w)}")
+    out = h.run_library(w)
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+    d = h.d_codes(out).reshape(w.batch, w.M, w.N)
+    pts = h.sample_points(w, n)
+    d_ref, _, absum = h.oracle_points(w, pts)
+    h.assert_within_bound(d[pts[:, 0], pts[:, 1], pts[:, 2]], d_ref, absum, w.name)
+
+
+def test_config2_4096_with_c(api):
+    _sampled(api, I.config2(4096))
+
+
+def test_config2_8192_with_c(api):
+    _sampled(api, I.config2(8192), n=1500)
+
+
+def test_config3_ragged_and_skinny(api):
+    for w in I.config3():
+        _sampled(api, w)
+
+
+@pytest.mark.parametrize("case", ["NN", "NT", "TN", "TT"])
+def test_config4_batched_strided(api, case):
+    _sampled(api, I.config4(case))
+
+
+def test_config5_mxfp8_8192(api):
+    _sampled(api, I.config5(8192), n=1500)

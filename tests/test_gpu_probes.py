@@ -1,0 +1,119 @@
+"""Device probes: the operand maps of the matrix-core instructions and the
+LDS data paths, observed on the hardware, against the maps written in the
+oracle's TV algebra.  These maps are hardware facts the pages do not fix
+(parity unpinned by the pages); the probes pin them."""
+
+import numpy as np
+import pytest
+
+from oracle import gemm as OG
+from oracle import layout as L
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from stride_layouts_lds_amd import api as A
+    A.lib()
+    return A
+
+
+def _expected_f16(instr, mode):
+    code = lambda l, s: l * 8 + s + 1
+    f = L.probe_expected_onehot_A if mode == 0 else L.probe_expected_onehot_B
+    return np.array([f(instr, c // 8, c % 8, code) for c in range(512)], np.float32)
+
+
+@pytest.mark.parametrize("instr", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_probe_f16_maps(api, instr, mode):
+    from gpu_helpers import dump, log
+    log(f"probe f16 instr={instr} mode={mode}")
+    got = api.probe_mfma(instr, mode).cpu().numpy()
+    dump(f"probe_f16_{instr}_{mode}", got)
+    want = _expected_f16(instr, mode)
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} registers differ"
+
+
+E4M3_BASE = 0x20
+
+
+def _expected_f8(instr, mode):
+    amap, bmap, dmap = L.INSTR_MAPS[instr]
+    R = 16 if instr == 2 else 32
+    dec = np.array([OG.e4m3_decode(E4M3_BASE + x) for x in range(64)], np.float32)
+    dm = np.array([[dmap(l, i)[0] for i in range(dmap.values)] for l in range(64)])
+    dn = np.array([[dmap(l, i)[1] for i in range(dmap.values)] for l in range(64)])
+    binv, ainv = bmap.inverse(), amap.inverse()
+    owner = {L.mfma_scale_owner(R, s): s for s in range(64)}
+    out = np.zeros((64 * 32, 64, dmap.values), np.float32)
+    for c in range(64 * 32):
+        hl, hs = c // 32, c % 32
+        if mode in (0, 1, 4):
+            m0, k0 = amap(hl, hs)
+            mask = dm == m0
+            if mode == 4:
+                out[c][mask] = 2.0 ** (owner[(m0, k0 // 32)] - 32)
+            else:
+                ls = np.array([binv[(n, k0)] for n in range(R)])  # (lane, slot) of B(n, k0)
+                out[c][mask] = dec[ls[dn[mask], 0 if mode == 0 else 1]]
+        else:
+            n0, k0 = bmap(hl, hs)
+            mask = dn == n0
+            if mode == 5:
+                out[c][mask] = 2.0 ** (owner[(n0, k0 // 32)] - 32)
+            else:
+                ls = np.array([ainv[(m, k0)] for m in range(R)])
+                out[c][mask] = dec[ls[dm[mask], 0 if mode == 2 else 1]]
+    return out
+
+
+@pytest.mark.parametrize("instr", [2, 3])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4, 5])
+def test_probe_f8_maps(api, instr, mode):
+    from gpu_helpers import dump, log
+    log(f"probe f8 instr={instr} mode={mode}")
+    got = api.probe_mfma(instr, mode).cpu().numpy()
+    dump(f"probe_f8_{instr}_{mode}", got)
+    want = _expected_f8(instr, mode)
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} registers differ"
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_probe_direct_to_lds(api, mode):
+    """A 16-byte direct HBM->LDS load of one wave writes lane l's bytes at
+    LDS base + 16*l, whatever global address the lane fetched."""
+    import torch
+    from gpu_helpers import dump, log
+    log(f"probe lds dma mode={mode}")
+    rng = np.random.default_rng(5)
+    src = (np.arange(1024) * 37 + 11).astype(np.uint8)
+    perm = rng.permutation(64).astype(np.int32)
+    if mode == 0:
+        perm[[3, 17, 40]] = -1  # out-of-range lanes: must land as zeros
+    got = api.probe_lds(mode, torch.from_numpy(src).cuda(), torch.from_numpy(perm).cuda()).cpu().numpy()
+    dump(f"probe_lds_{mode}", got)
+    want = np.full(4096, 0xA5, np.uint8)
+    for l in range(64):
+        want[16 * l:16 * l + 16] = 0 if perm[l] < 0 else src[16 * perm[l]:16 * perm[l] + 16]
+    assert np.array_equal(got, want)
+
+
+def test_probe_ds_read_tr16(api):
+    import torch
+    from gpu_helpers import dump, log
+    log("probe ds_read_b64_tr_b16")
+    halves = np.arange(2048, dtype=np.uint16)
+    # lane l of group g: 64-bit block at row (4g + i//4), columns 4*(i%4).. of
+    # a matrix with 32 halves per row
+    addr = np.array([((4 * (l // 16) + (l % 16) // 4) * 32 + 4 * (l % 4)) * 2 for l in range(64)], np.int32)
+    got = api.probe_lds(2, torch.from_numpy(halves.view(np.uint8).copy()).cuda(),
+                        torch.from_numpy(addr).cuda()).cpu().numpy()
+    got = got[:512].view(np.uint16).reshape(64, 4)
+    dump("probe_tr16", got)
+    want = np.array(L.ds_read_tr16_b64_expected(addr.tolist(), halves.tolist()), np.uint16)
+    assert np.array_equal(got, want)
