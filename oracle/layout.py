@@ -414,17 +414,25 @@ MFMA32_F16_B = TV(shape=((32, 2), 8), stride=((1, 256), 32), rows=32, cols=16)
 # D (32 x 32): n = l0, m = 8*(i//4) + 4*l1 + i%4
 MFMA32_D = TV(shape=((32, 2), (4, 4)), stride=((32, 4), (1, 8)), rows=32, cols=32)
 
-# v_mfma_scale_f32_16x16x128_f8f6f4 with E4M3 data, A (16 x 128): m = l0, k = 32*l1 + v
-MFMA16_F8_A = TV(shape=((16, 4), 32), stride=((1, 512), 16), rows=16, cols=128)
-MFMA16_F8_B = TV(shape=((16, 4), 32), stride=((1, 512), 16), rows=16, cols=128)
-# v_mfma_scale_f32_32x32x64_f8f6f4, A (32 x 64): m = l0, k = 32*l1 + v
-MFMA32_F8_A = TV(shape=((32, 2), 32), stride=((1, 1024), 32), rows=32, cols=64)
-MFMA32_F8_B = TV(shape=((32, 2), 32), stride=((1, 1024), 32), rows=32, cols=64)
+# The scaled f8 instructions take 32 bytes per lane in two 16-byte halves,
+# v = v0 + 16*v1.  Which bytes share one E8M0 scale fixes the absolute k
+# order: the block-scaled product of the data-layout page ("Replication 与
+# Offset": sfk = k // K_blk) gives one scale to 32 CONSECUTIVE k, and the
+# bytes that share a scale lane are v0 < 16 of lanes l1 = 2b, 2b+1 (16x16x128)
+# or l1 = 0, 1 (32x32x64) in half v1.  The k order consistent with both is:
+# v_mfma_scale_f32_16x16x128_f8f6f4 with E4M3 data, A (16 x 128):
+#   m = l0, k = 16*l1 + v0 + 64*v1
+MFMA16_F8_A = TV(shape=((16, 4), (16, 2)), stride=((1, 256), (16, 1024)), rows=16, cols=128)
+MFMA16_F8_B = TV(shape=((16, 4), (16, 2)), stride=((1, 256), (16, 1024)), rows=16, cols=128)
+# v_mfma_scale_f32_32x32x64_f8f6f4, A (32 x 64): m = l0, k = 16*l1 + v0 + 32*v1
+MFMA32_F8_A = TV(shape=((32, 2), (16, 2)), stride=((1, 512), (32, 1024)), rows=32, cols=64)
+MFMA32_F8_B = TV(shape=((32, 2), (16, 2)), stride=((1, 512), (32, 1024)), rows=32, cols=64)
 
 
 def mfma_scale_owner(rows: int, lane: int) -> Tuple[int, int]:
     """(row, k-block of 32) whose E8M0 scale lane ``lane`` supplies for the
-    scaled f8 instructions: row = lane % rows, block = lane // rows."""
+    scaled f8 instructions: row = lane % rows, block = lane // rows (blocks
+    counted in the k order above)."""
     return lane % rows, lane // rows
 
 

@@ -29,10 +29,11 @@ namespace sl {
 // v_mfma_f32_32x32x16_f16: lane l = l0 + 32*l1 (l0 < 32, l1 < 2)
 //   A (32 x 16):  m = l0, k = 8*l1 + v
 //   D (32 x 32):  n = l0, m = 8*(v/4) + 4*l1 + v%4  (v < 16)
-// v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3): slot v < 32 (bytes)
-//   A (16 x 128): m = l0, k = 32*l1 + v; scale lane l -> (m = l0, block l1)
+// v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3): slot v = v0 + 16*v1 < 32 (bytes)
+//   A (16 x 128): m = l0, k = 16*l1 + v0 + 64*v1; scale lane l -> (m = l0, block l1)
 // v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3):
-//   A (32 x 64):  m = l0, k = 32*l1 + v; scale lane l -> (m = l0, block l1)
+//   A (32 x 64):  m = l0, k = 16*l1 + v0 + 32*v1; scale lane l -> (m = l0, block l1)
+// (the blocks of 32 consecutive k are the ones whose bytes share a scale lane)
 // ---------------------------------------------------------------------------
 
 enum Instr : int32_t { MFMA16_F16 = 0, MFMA32_F16 = 1, MFMA16_F8 = 2, MFMA32_F8 = 3 };
@@ -51,10 +52,13 @@ SL_HD constexpr int32_t instr_in_slots(int32_t instr) { return (instr == MFMA16_
 // accumulator registers per lane
 SL_HD constexpr int32_t instr_acc_regs(int32_t instr) { return instr_rows(instr) == 16 ? 4 : 16; }
 
-// (lane, slot) -> (row, col) of operand A or B: row = l0, col = slots*l1 + v.
+// (lane, slot) -> (row, col) of operand A or B.
+//   f16:  row = l0, col = 8*l1 + v
+//   f8:   row = l0, col = 16*l1 + v%16 + (K/2)*(v/16)
 SL_HD constexpr Coord operand_map(int32_t instr, int32_t lane, int32_t slot) {
   const int32_t R = instr_rows(instr);
-  return Coord{lane % R, instr_in_slots(instr) * (lane / R) + slot};
+  if (instr_in_slots(instr) == 8) return Coord{lane % R, 8 * (lane / R) + slot};
+  return Coord{lane % R, 16 * (lane / R) + slot % 16 + (instr_k(instr) / 2) * (slot / 16)};
 }
 
 // (lane, reg) -> (m, n) of the accumulator.
