@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp16_8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (3 times), the known-size "
+                         "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -128,6 +131,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = 1 << 30
+        x = torch.empty(n // 2, dtype=torch.float16, device="cuda").normal_()
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
     from stride_layouts_lds_amd import api
     api.lib()
 

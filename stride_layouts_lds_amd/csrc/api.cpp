@@ -271,8 +271,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     p.flags |= sl::F_D_VEC;
   if (has_c && C.cs == 1 && C.rs % 4 == 0 && (uintptr_t)C.t->data % 8 == 0 && (batch == 1 || p.c_bs % 4 == 0))
     p.flags |= sl::F_C_VEC;
-  P.shift = env_int("SL_SWZ", 0) ? 1 : 0;
-  p.group_m = std::max(1, env_int("SL_GROUP_M", 4));
+  P.shift = std::min(2, std::max(0, env_int("SL_SWZ", 0)));
+  p.group_m = std::max(1, env_int("SL_GROUP_M", 8));
 
   int32_t tile = env_int("SL_TILE", -1);
   if (mx) {
@@ -286,8 +286,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
                   "MXFP8 operands must be K-contiguous with 16-byte aligned rows and K %% 16 == 0");
     if ((M - 1) * SA.rs + (kb - 1) * SA.cs >= lim || (N - 1) * SB.rs + (kb - 1) * SB.cs >= lim)
       return fail(SL_ERR_SHAPE, "scale tensors span more than 2^31 bytes");
-    if (tile < 0 || tile >= sl::T_COUNT) {
-      tile = sl::T256x128_W2x2;
+    if (tile < 0 || tile > sl::T128x128_W2x2) {
+      tile = sl::T256x128_W2x2;  // MX kernels exist for the first four tiles
       double best = 1e300;
       for (int t : {sl::T256x128_W2x2, sl::T128x256_W2x2, sl::T128x128_W2x2}) {
         const double c = tile_cost(sl::kTiles[t], batch, M, N, K);
@@ -307,10 +307,15 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       tile = sl::T128x128_W2x2;
       P.pub.kernel = sl::K_F16_GENERIC;
     } else {
-      if (tile < 0 || tile >= sl::T_COUNT) {
-        tile = sl::T256x256_W2x2;
+      // the 8-wave, multi-stage and ping-pong variants exist for
+      // K-contiguous operands only; among the automatic choices the 8-wave
+      // 256x256 kernel replaces the 4-wave one for them
+      const bool kk = la == sl::LOAD_KVEC && lb == sl::LOAD_KVEC;
+      if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T128x128_W2x2)) {
+        const int32_t big = kk ? sl::T256x256_W2x4 : sl::T256x256_W2x2;
+        tile = big;
         double best = 1e300;
-        for (int t = 0; t < sl::T_COUNT; ++t) {
+        for (int t : {big, (int32_t)sl::T256x128_W2x2, (int32_t)sl::T128x256_W2x2, (int32_t)sl::T128x128_W2x2}) {
           const double c = tile_cost(sl::kTiles[t], batch, M, N, K);
           if (c < best) best = c, tile = t;
         }
@@ -319,8 +324,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     }
     P.pub.a_load = la;
     P.pub.b_load = lb;
-    P.pub.tile_k = 64;
-    p.k_tiles = (int32_t)((K + 63) / 64);
+    P.pub.tile_k = sl::kTiles[tile].bk;
+    p.k_tiles = (int32_t)((K + P.pub.tile_k - 1) / P.pub.tile_k);
   }
   const sl::TileShape& ts = sl::kTiles[tile];
   P.tile = tile;
@@ -333,7 +338,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.pub.threads = ts.wm * ts.wn * 64;
   P.pub.split_k = 1;
   P.pub.workgroups = total;
-  P.pub.lds_bytes = 2 * (ts.bm + ts.bn) * sl::kRowBytes;
+  P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * P.pub.tile_k * (mx ? 1 : 2);
   return SL_OK;
 }
 

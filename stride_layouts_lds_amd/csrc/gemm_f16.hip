@@ -17,95 +17,24 @@
 namespace sl {
 namespace {
 
-template <int BM, int BN, int WM, int WN, int ALOAD, int BLOAD, int SHIFT>
-__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_f16_kernel(const GemmParams p) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
-  constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 instruction tiles per wave
-  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
-  constexpr int STAGE = ABYTES + BBYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
-
-  const int32_t lane = threadIdx.x & 63;
-  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int32_t wm = wave % WM, wn = wave / WM;
-
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
-  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
-  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
-  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
-  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
-  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
-
-  typename LoaderSel<ALOAD, BM, NT, SHIFT>::type la(A, rows_a, p.a_rs, p.a_ks, p.K, wave, lane);
-  typename LoaderSel<BLOAD, BN, NT, SHIFT>::type lb(B, rows_b, p.b_rs, p.b_ks, p.K, wave, lane);
-
-  floatx4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // Per-lane fragment offsets inside one stage, k-slice 0 of tile 0 of this
-  // wave; the others differ by compile-time constants.
-  const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
-
-  const int32_t T = p.k_tiles;
-  if (T > 0) {
-    la.issue(0, smem);
-    lb.issue(0, smem + ABYTES);
-    la.commit(smem);
-    lb.commit(smem + ABYTES);
-    wait_vmem();
-    __syncthreads();
-  }
-
-  for (int32_t t = 0; t < T; ++t) {
-    char* cur = smem + (t & 1) * STAGE;
-    char* nxt = smem + ((t + 1) & 1) * STAGE;
-    const bool more = t + 1 < T;
-    if (more) {
-      la.issue(t + 1, nxt);
-      lb.issue(t + 1, nxt + ABYTES);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      half8 af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *(const half8*)(cur + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, ks, SHIFT));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bf[j] = *(const half8*)(cur + ABYTES +
-                                fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, ks, SHIFT));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      la.commit(nxt);
-      lb.commit(nxt + ABYTES);
-    }
-    wait_vmem();
-    __syncthreads();
-  }
-
-  // Epilogue.  acc[i][j][r] is output (m, n) with
-  //   m = m0 + a_row0 + 16 i + lane % 16,  n = n0 + b_row0 + 16 j + 4 (lane / 16) + r
+// Epilogue: acc[i][j][r] is output (m, n) with
+//   m = m_base + 16 i + lane % 16,  n = n_base + 16 j + 4 (lane / 16) + r
+// D = fp16_rne(acc + C), stores predicated on m < M, n < N.
+template <int FM, int FN>
+__device__ __forceinline__ void epilogue(const floatx4 (&acc)[FM][FN], const GemmParams& p, int32_t batch,
+                                         int64_t m_base, int64_t n_base, int32_t lane) {
   const bool has_c = p.flags & F_HAS_C;
   const bool d_vec = p.flags & F_D_VEC;
   const bool c_vec = p.flags & F_C_VEC;
-  uint16_t* D = (uint16_t*)p.d + tc.batch * p.d_bs;
-  const uint16_t* C = has_c ? (const uint16_t*)p.c + tc.batch * p.c_bs : nullptr;
+  uint16_t* D = (uint16_t*)p.d + batch * p.d_bs;
+  const uint16_t* C = has_c ? (const uint16_t*)p.c + batch * p.c_bs : nullptr;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int64_t m = m0 + a_row0 + 16 * i + (lane & 15);
+    const int64_t m = m_base + 16 * i + (lane & 15);
     if (m >= p.M) continue;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int64_t n = n0 + b_row0 + 16 * j + 4 * (lane >> 4);
+      const int64_t n = n_base + 16 * j + 4 * (lane >> 4);
       if (n >= p.N) continue;
       floatx4 v = acc[i][j];
       const bool full = n + 3 < p.N;
@@ -135,24 +64,407 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_f16_kernel(const GemmPara
   }
 }
 
-template <int BM, int BN, int WM, int WN, int AL, int BL>
+// PIPE 0: per k-slice, read the fragments then issue the MFMAs (latency is
+// covered by the other wave on the SIMD when WM*WN = 8).  PIPE 1: two
+// fragment sets, the next slice is read while the current one computes.
+template <int BM, int BN, int WM, int WN, int ALOAD, int BLOAD, int SHIFT, int PIPE>
+__global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kernel(const GemmParams p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 instruction tiles per wave
+  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
+  constexpr int STAGE = ABYTES + BBYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t wm = wave % WM, wn = wave / WM;
+
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
+
+  typename LoaderSel<ALOAD, BM, NT, SHIFT>::type la(A, rows_a, p.a_rs, p.a_ks, p.K, wave, lane);
+  typename LoaderSel<BLOAD, BN, NT, SHIFT>::type lb(B, rows_b, p.b_rs, p.b_ks, p.K, wave, lane);
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
+  // operand fragments of one k-slice (32 of the tile's 64 K), two sets:
+  // one feeds the MFMAs while the other is being read from LDS
+  half8 fa0[FM], fb0[FN];
+  [[maybe_unused]] half8 fa1[FM], fb1[FN];
+  auto read_slice = [&](const char* buf, int ks, half8(&fa)[FM], half8(&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = *(const half8*)(buf + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, ks, SHIFT));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[j] = *(const half8*)(buf + ABYTES + fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, ks, SHIFT));
+  };
+  // instruction A = our B fragment, instruction B = our A fragment
+  auto mfma_slice = [&](const half8(&fa)[FM], const half8(&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+  constexpr int NREAD = FM + FN;          // ds_read_b128 per slice
+  constexpr int NMFMA = FM * FN;          // MFMAs per slice
+  constexpr int PER = NMFMA / NREAD;      // MFMAs between two reads
+
+  const int32_t T = p.k_tiles;
+  if (T > 0) {
+    la.issue(0, smem);
+    lb.issue(0, smem + ABYTES);
+    la.commit(smem);
+    lb.commit(smem + ABYTES);
+    wait_vmem();
+    __syncthreads();
+    if constexpr (PIPE == 1) read_slice(smem, 0, fa0, fb0);
+  }
+
+  // Loop body without branches: past the last tile the loads are fully
+  // out of range (they write zeros into the idle buffer) and the reads of
+  // the idle buffer are never consumed.
+  for (int32_t t = 0; t < T; ++t) {
+    char* cur = smem + (t & 1) * STAGE;
+    char* nxt = smem + ((t + 1) & 1) * STAGE;
+    la.issue(t + 1, nxt);
+    lb.issue(t + 1, nxt + ABYTES);
+    if constexpr (PIPE == 0) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        read_slice(cur, ks, fa0, fb0);
+        mfma_slice(fa0, fb0);
+      }
+      la.commit(nxt);
+      lb.commit(nxt + ABYTES);
+      wait_vmem();
+      __syncthreads();
+    } else {
+      // first half: read slice 1 of tile t, compute slice 0
+      read_slice(cur, 1, fa1, fb1);
+      mfma_slice(fa0, fb0);
+#pragma unroll
+      for (int g = 0; g < NREAD; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one ds_read
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // PER MFMAs
+      }
+      la.commit(nxt);
+      lb.commit(nxt + ABYTES);
+      // tile t+1 is in LDS and every wave is done reading tile t's slice 0
+      wait_vmem();
+      __syncthreads();
+      // second half: read slice 0 of tile t+1, compute slice 1 of tile t
+      read_slice(nxt, 0, fa0, fb0);
+      mfma_slice(fa1, fb1);
+#pragma unroll
+      for (int g = 0; g < NREAD; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+      }
+    }
+  }
+
+  epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+}
+
+// Multi-stage variant for K-contiguous operands: K-tiles of 32 (LDS rows of
+// 64 bytes), STAGES LDS buffers, loads for tile t+STAGES-1 issued while
+// tile t computes, so each tile's HBM->LDS copy has STAGES-1 tiles of
+// compute to land.  One barrier per tile makes the landed tile visible to
+// every wave and retires the buffer the next issue overwrites.
+template <int BM, int BN, int WM, int WN, int STAGES, int SHIFT>
+__global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_kernel(const GemmParams p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int RB = 64;  // 32 fp16 of K per LDS row
+  constexpr int ABYTES = BM * RB, BBYTES = BN * RB;
+  constexpr int STAGE = ABYTES + BBYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  using LA = LoaderKVec<BM, NT, SHIFT, 2, RB>;
+  using LB = LoaderKVec<BN, NT, SHIFT, 2, RB>;
+  constexpr int LOADS = LA::ITERS + LB::ITERS;  // vector-memory ops per tile per thread
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t wm = wave % WM, wn = wave / WM;
+
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
+  LA la(A, rows_a, p.a_rs, 1, p.K, wave, lane);
+  LB lb(B, rows_b, p.b_rs, 1, p.K, wave, lane);
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
+
+  const int32_t T = (int32_t)((p.K + 31) / 32);
+  // prologue: tiles 0 .. STAGES-2 in flight, wait for tile 0
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    la.issue(s, smem + s * STAGE);
+    lb.issue(s, smem + s * STAGE + ABYTES);
+  }
+  wait_vmem_n<(STAGES - 2) * LOADS>();
+  __syncthreads();
+
+  for (int32_t t = 0; t < T; ++t) {
+    const char* cur = smem + (t % STAGES) * STAGE;
+    char* fut = smem + ((t + STAGES - 1) % STAGES) * STAGE;
+    // the buffer of tile t-1 is retired (barrier at the end of t-1): refill
+    // it with tile t+STAGES-1 (fully out of range past the last tile)
+    la.issue(t + STAGES - 1, fut);
+    lb.issue(t + STAGES - 1, fut + ABYTES);
+    half8 fa[FM], fb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = *(const half8*)(cur + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, 0, SHIFT, RB));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[j] = *(const half8*)(cur + ABYTES + fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, 0, SHIFT, RB));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    // tile t+1 landed (this wave's part); the barrier publishes every
+    // wave's part and retires tile t's buffer
+    wait_vmem_n<(STAGES - 2) * LOADS>();
+    __syncthreads();
+  }
+  epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+}
+
+// Ping-pong variant for K-contiguous operands, 256x256 tile, 8 waves.
+// The waves form two groups of four, one wave of each group per SIMD, each
+// wave owning a 128x64 block of the tile.  Every K-tile is two phases per
+// wave: a memory phase M(t) (group 0 also issues the HBM->LDS copy of tile
+// t+1; every wave reads all its fragments of tile t) and a compute phase
+// C(t) (64 MFMAs back to back on registers).  Group 1 runs one phase behind
+// group 0, so on every SIMD one wave computes while the other moves data;
+// the phases are separated by phase barriers.
+//   group 0:  b0 M(0) b1 C(0) b2 M(1) b3 C(1) ...  C(T-1) b2T  [epilogue] b2T+1
+//   group 1:  b0 ---- b1 M(0) b2 C(0) b3 M(1) ...  M(T-1) b2T  C(T-1) b2T+1 [epilogue]
+// Both groups pass 2T+2 barriers.  Tile t+1 is copied into the buffer of
+// tile t-1 during M(t) of group 0; its last readers (M(t-1) of both groups)
+// finished before barrier b2t.  Group 0 waits for the copy at the end of
+// C(t), before barrier b2t+2, ahead of the first read in M(t+1).
+template <int SHIFT>
+__global__ __launch_bounds__(512, 2) void gemm_f16_pp_kernel(const GemmParams p) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int TM = 128, TN = 64;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
+  constexpr int STAGE = ABYTES + BBYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t grp = wave >> 2;
+  const int32_t wm = wave & 1, wn = wave >> 1;  // group 0: wn 0,1; group 1: wn 2,3
+
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
+  // the copy is done by the four group-0 waves
+  LoaderKVec<BM, 256, SHIFT, 2> la(A, rows_a, p.a_rs, 1, p.K, wave & 3, lane);
+  LoaderKVec<BN, 256, SHIFT, 2> lb(B, rows_b, p.b_rs, 1, p.K, wave & 3, lane);
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
+  half8 fa[2][FM], fb[2][FN];
+
+  const int32_t T = p.k_tiles;
+  if (grp == 0) {
+    la.issue(0, smem);
+    lb.issue(0, smem + ABYTES);
+    wait_vmem();
+  }
+  phase_barrier();                 // b0: tile 0 in LDS
+  if (grp == 1) phase_barrier();   // b1 for group 1: start one phase behind
+
+  for (int32_t t = 0; t < T; ++t) {
+    const char* cur = smem + (t & 1) * STAGE;
+    char* nxt = smem + ((t + 1) & 1) * STAGE;
+    // ---- M(t)
+    if (grp == 0) {
+      la.issue(t + 1, nxt);       // fully out of range past the last tile
+      lb.issue(t + 1, nxt + ABYTES);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[ks][i] = *(const half8*)(cur + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, ks, SHIFT));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[ks][j] =
+            *(const half8*)(cur + ABYTES + fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, ks, SHIFT));
+    }
+    phase_barrier();
+    // ---- C(t)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+    if (grp == 0) wait_vmem();   // tile t+1 landed before b2t+2
+    phase_barrier();
+  }
+  if (grp == 0) {
+    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+    phase_barrier();               // b2T+1: matches group 1's last barrier
+  } else {
+    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  }
+}
+
+// Ping-pong with deep prefetch: the ping-pong schedule above on K-tiles of
+// 32 (LDS rows of 64 bytes) held in STAGES buffers.  Group 0 issues the copy
+// of tile t+STAGES-1 during M(t) into the buffer of tile t-1 (its last
+// readers, M(t-1) of both groups, finished before barrier b2t), and at the
+// end of C(t) waits only until tile t+1 has landed (the copies of tiles
+// t+2 .. t+STAGES-1 stay in flight), so every copy has STAGES-1 tiles of
+// compute to complete.
+template <int STAGES, int SHIFT>
+__global__ __launch_bounds__(512, 2) void gemm_f16_pps_kernel(const GemmParams p) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int TM = 128, TN = 64;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int RB = 64;
+  constexpr int ABYTES = BM * RB, BBYTES = BN * RB;
+  constexpr int STAGE = ABYTES + BBYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  using LA = LoaderKVec<BM, 256, SHIFT, 2, RB>;
+  using LB = LoaderKVec<BN, 256, SHIFT, 2, RB>;
+  constexpr int LOADS = LA::ITERS + LB::ITERS;  // copy instructions per tile per group-0 wave
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t grp = wave >> 2;
+  const int32_t wm = wave & 1, wn = wave >> 1;
+
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
+  LA la(A, rows_a, p.a_rs, 1, p.K, wave & 3, lane);
+  LB lb(B, rows_b, p.b_rs, 1, p.K, wave & 3, lane);
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
+  half8 fa[FM], fb[FN];
+
+  const int32_t T = (int32_t)((p.K + 31) / 32);
+  if (grp == 0) {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+      la.issue(s, smem + s * STAGE);
+      lb.issue(s, smem + s * STAGE + ABYTES);
+    }
+    wait_vmem_n<(STAGES - 2) * LOADS>();  // tile 0 landed
+  }
+  phase_barrier();               // b0
+  if (grp == 1) phase_barrier(); // group 1 starts one phase behind
+
+  for (int32_t t = 0; t < T; ++t) {
+    const char* cur = smem + (t % STAGES) * STAGE;
+    char* fut = smem + ((t + STAGES - 1) % STAGES) * STAGE;
+    // ---- M(t)
+    if (grp == 0) {
+      la.issue(t + STAGES - 1, fut);  // fully out of range past the last tile
+      lb.issue(t + STAGES - 1, fut + ABYTES);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = *(const half8*)(cur + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, 0, SHIFT, RB));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[j] = *(const half8*)(cur + ABYTES + fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, 0, SHIFT, RB));
+    phase_barrier();
+    // ---- C(t)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    if (grp == 0) wait_vmem_n<(STAGES - 2) * LOADS>();  // tile t+1 landed
+    phase_barrier();
+  }
+  if (grp == 0) {
+    wait_vmem();  // the out-of-range copies past the last tile
+    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+    phase_barrier();
+  } else {
+    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int AL, int BL, int PIPE>
 hipError_t launch_cfg(const GemmParams& p, int32_t shift, hipStream_t s) {
   const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
   dim3 grid((uint32_t)total), block(WM * WN * 64);
   if (shift == 0)
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, AL, BL, 0>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, AL, BL, 0, PIPE>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, AL, BL, 1>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, AL, BL, 1, PIPE>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+hipError_t launch_ms(const GemmParams& p, int32_t shift, hipStream_t s) {
+  const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
+  dim3 grid((uint32_t)total), block(WM * WN * 64);
+  switch (shift) {
+    case 0: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 0>), grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 1>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 2>), grid, block, 0, s, p); break;
+  }
   return hipGetLastError();
 }
 
 template <int AL, int BL>
 hipError_t launch_tile(const GemmParams& p, int32_t tile, int32_t shift, hipStream_t s) {
   switch (tile) {
-    case T256x256_W2x2: return launch_cfg<256, 256, 2, 2, AL, BL>(p, shift, s);
-    case T256x128_W2x2: return launch_cfg<256, 128, 2, 2, AL, BL>(p, shift, s);
-    case T128x256_W2x2: return launch_cfg<128, 256, 2, 2, AL, BL>(p, shift, s);
-    case T128x128_W2x2: return launch_cfg<128, 128, 2, 2, AL, BL>(p, shift, s);
+    case T256x256_W2x2: return launch_cfg<256, 256, 2, 2, AL, BL, 0>(p, shift, s);
+    case T256x128_W2x2: return launch_cfg<256, 128, 2, 2, AL, BL, 0>(p, shift, s);
+    case T128x256_W2x2: return launch_cfg<128, 256, 2, 2, AL, BL, 0>(p, shift, s);
+    case T128x128_W2x2: return launch_cfg<128, 128, 2, 2, AL, BL, 0>(p, shift, s);
+    case T256x256_W2x4: return launch_cfg<256, 256, 2, 4, AL, BL, 0>(p, shift, s);
+    case T256x256_W2x4_P: return launch_cfg<256, 256, 2, 4, AL, BL, 1>(p, shift, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -165,18 +477,49 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
     // one configuration for every stride pattern
     if (tile != T128x128_W2x2) return hipErrorInvalidValue;
     if (a_load == LOAD_GENERIC && b_load == LOAD_GENERIC)
-      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_GENERIC>(p, shift, s);
+      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_GENERIC, 0>(p, shift, s);
     if (a_load == LOAD_GENERIC && b_load == LOAD_KVEC)
-      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_KVEC>(p, shift, s);
+      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_KVEC, 0>(p, shift, s);
     if (a_load == LOAD_KVEC && b_load == LOAD_GENERIC)
-      return launch_cfg<128, 128, 2, 2, LOAD_KVEC, LOAD_GENERIC>(p, shift, s);
+      return launch_cfg<128, 128, 2, 2, LOAD_KVEC, LOAD_GENERIC, 0>(p, shift, s);
     if (a_load == LOAD_GENERIC && b_load == LOAD_MNVEC)
-      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_MNVEC>(p, shift, s);
+      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_MNVEC, 0>(p, shift, s);
     if (a_load == LOAD_MNVEC && b_load == LOAD_GENERIC)
-      return launch_cfg<128, 128, 2, 2, LOAD_MNVEC, LOAD_GENERIC>(p, shift, s);
+      return launch_cfg<128, 128, 2, 2, LOAD_MNVEC, LOAD_GENERIC, 0>(p, shift, s);
     return hipErrorInvalidValue;
   }
-  if (a_load == LOAD_KVEC && b_load == LOAD_KVEC) return launch_tile<LOAD_KVEC, LOAD_KVEC>(p, tile, shift, s);
+  if (a_load == LOAD_KVEC && b_load == LOAD_KVEC) {
+    switch (tile) {
+      case T256x256_W2x4_S3: return launch_ms<256, 256, 2, 4, 3>(p, shift, s);
+      case T256x256_W2x4_S4: return launch_ms<256, 256, 2, 4, 4>(p, shift, s);
+      case T256x256_W2x4_S5: return launch_ms<256, 256, 2, 4, 5>(p, shift, s);
+      case T256x256_PPS4:
+      case T256x256_PPS5: {
+        const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
+        const dim3 g((uint32_t)total), b(512);
+        if (tile == T256x256_PPS4) {
+          if (shift == 0) hipLaunchKernelGGL((gemm_f16_pps_kernel<4, 0>), g, b, 0, s, p);
+          else if (shift == 1) hipLaunchKernelGGL((gemm_f16_pps_kernel<4, 1>), g, b, 0, s, p);
+          else hipLaunchKernelGGL((gemm_f16_pps_kernel<4, 2>), g, b, 0, s, p);
+        } else {
+          if (shift == 0) hipLaunchKernelGGL((gemm_f16_pps_kernel<5, 0>), g, b, 0, s, p);
+          else if (shift == 1) hipLaunchKernelGGL((gemm_f16_pps_kernel<5, 1>), g, b, 0, s, p);
+          else hipLaunchKernelGGL((gemm_f16_pps_kernel<5, 2>), g, b, 0, s, p);
+        }
+        return hipGetLastError();
+      }
+      case T256x256_PP: {
+        const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
+        if (shift == 0)
+          hipLaunchKernelGGL(gemm_f16_pp_kernel<0>, dim3((uint32_t)total), dim3(512), 0, s, p);
+        else
+          hipLaunchKernelGGL(gemm_f16_pp_kernel<1>, dim3((uint32_t)total), dim3(512), 0, s, p);
+        return hipGetLastError();
+      }
+      default: return launch_tile<LOAD_KVEC, LOAD_KVEC>(p, tile, shift, s);
+    }
+  }
+  if (tile > T128x128_W2x2) return hipErrorInvalidValue;
   if (a_load == LOAD_MNVEC && b_load == LOAD_KVEC) return launch_tile<LOAD_MNVEC, LOAD_KVEC>(p, tile, shift, s);
   if (a_load == LOAD_KVEC && b_load == LOAD_MNVEC) return launch_tile<LOAD_KVEC, LOAD_MNVEC>(p, tile, shift, s);
   if (a_load == LOAD_MNVEC && b_load == LOAD_MNVEC)

@@ -37,6 +37,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // left at their maximum.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Phase barrier of the ping-pong schedule: this wave's LDS reads are
+// complete (lgkmcnt(0)), then s_barrier.  Direct HBM->LDS copies stay in
+// flight across it (a fence would wait for them: the hardware counts them
+// with the vector-memory counter).  The memory clobber keeps the compiler
+// from moving memory operations across it, the scheduling barriers keep it
+// from moving anything else (MFMAs included), so the phases stay separate.
+// A copy is made visible by the issuing wave's wait_vmem() before a later
+// phase barrier.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still
+// outstanding (they complete in issue order).  vmcnt is split over bits
+// [3:0] and [15:14]; expcnt (bits [6:4]) and lgkmcnt ([11:8]) at maximum.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // ---------------------------------------------------------------------------
 // Tile order.  Workgroup IDs are handed to the 8 XCDs round-robin; remap so
 // that each XCD owns a contiguous range of the logical order, then walk the
@@ -76,54 +99,49 @@ __device__ __forceinline__ TileCoord map_tile(int32_t bid, int32_t total, int32_
 
 // K-contiguous rows, 16-B aligned: each lane's 16-B chunk is fetched by a
 // direct HBM->LDS buffer load.  One wave instruction fills 1 KiB of LDS,
-// i.e. 8 consecutive rows, lane l landing at byte 16*l of that block.  The
-// swizzle is therefore realised on the global side: the lane that lands in
-// physical chunk p of row r fetches logical chunk p ^ swz(r).
-template <int ROWS, int NT, int SHIFT, int ELEM>
+// i.e. 1024/RB consecutive rows, lane l landing at byte 16*l of that block.
+// The swizzle is therefore realised on the global side: the lane that
+// lands in physical chunk p of row r fetches logical chunk p ^ swz(r).
+template <int ROWS, int NT, int SHIFT, int ELEM, int RB = kRowBytes>
 struct LoaderKVec {
   static constexpr int WAVES = NT / 64;
-  static constexpr int ITERS = ROWS * 8 / NT;
-  static constexpr int KT = 128 / ELEM;      // K elements per tile
-  static constexpr int CE = 16 / ELEM;       // K elements per 16-B chunk
-  static_assert(ITERS >= 1 && ROWS * 8 % NT == 0, "tile too small for the workgroup");
-  static_assert(SHIFT == 0 || SHIFT == 1, "swizzle shift");
+  static constexpr int CPR = RB / 16;          // chunks per row
+  static constexpr int RPI = 1024 / RB;        // rows per wave instruction
+  static constexpr int ITERS = ROWS * RB / (NT * 16);
+  static constexpr int KT = RB / ELEM;         // K elements per tile
+  static constexpr int CE = 16 / ELEM;         // K elements per 16-B chunk
+  static_assert(ITERS >= 1 && ROWS * RB % (NT * 16) == 0, "tile too small for the workgroup");
 
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off0;      // byte offset of this lane's chunk in instruction 0, tile 0
+  uint32_t row_off;   // byte offset of this lane's row in instruction 0
   uint32_t row_step;  // bytes between the row blocks of consecutive instructions
-  int32_t kc0, kc1;   // first K element of the chunk for even / odd row blocks
+  int32_t row0;       // this lane's tile row in instruction 0
   int32_t K;
   int32_t wave;
+  int32_t lane;
 
   __device__ __forceinline__ LoaderKVec(const void* base, int32_t rows_valid, int64_t rs, int64_t /*ks*/,
-                                        int64_t K_, int32_t wave_, int32_t lane) {
+                                        int64_t K_, int32_t wave_, int32_t lane_) {
     K = (int32_t)K_;
     wave = wave_;
+    lane = lane_;
     const uint32_t bytes =
         rows_valid > 0 ? (uint32_t)(((int64_t)(rows_valid - 1) * rs + K_) * ELEM) : 0u;
     rsrc = make_rsrc(base, bytes);
-    // instruction j covers rows (j*WAVES + wave)*8 + 0..7; lane l lands in
-    // row +l/8, physical chunk l%8, and fetches logical chunk l%8 ^ swz(row)
-    const int32_t row = wave * 8 + (lane >> 3);
-    const int32_t c0 = (lane & 7) ^ swz(row, SHIFT);
-    const int32_t c1 = (lane & 7) ^ swz(row + WAVES * 8, SHIFT);
-    kc0 = c0 * CE;
-    kc1 = c1 * CE;
-    off0 = (uint32_t)(row * rs * ELEM) + (uint32_t)(c0 * 16);
-    row_step = (uint32_t)(WAVES * 8 * rs * ELEM);
+    row0 = wave * RPI + lane / CPR;
+    row_off = (uint32_t)(row0 * rs * ELEM);
+    row_step = (uint32_t)(WAVES * RPI * rs * ELEM);
   }
 
   __device__ __forceinline__ void issue(int32_t t, char* lds) const {
 #pragma unroll
     for (int j = 0; j < ITERS; ++j) {
-      // rows advance by j*WAVES*8: swz(row, 0) never changes, swz(row, 1)
-      // flips bit 2 when j*WAVES is odd
-      const bool odd = SHIFT == 1 && ((j * WAVES) & 1);
-      const int32_t kc = odd ? kc1 : kc0;
-      const uint32_t o = odd ? off0 + (uint32_t)((kc1 - kc0) / CE * 16) : off0;
-      const uint32_t a = o + (uint32_t)j * row_step + (uint32_t)(t * 128);
+      // instruction j covers rows (j*WAVES + wave)*RPI + 0..RPI-1
+      const int32_t row = row0 + j * WAVES * RPI;
+      const int32_t c = (lane % CPR) ^ swz(row, SHIFT, RB);
+      const uint32_t a = row_off + (uint32_t)j * row_step + (uint32_t)(c * 16) + (uint32_t)(t * RB);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16,
-                                               (t * KT + kc < K) ? a : kOutOfRange, 0, 0, 0);
+                                               (t * KT + c * CE < K) ? a : kOutOfRange, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void commit(char*) const {}

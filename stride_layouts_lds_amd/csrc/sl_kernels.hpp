@@ -16,22 +16,34 @@ enum LoadKind : int32_t {
 // Kernel families (sl_plan.kernel).
 enum KernelKind : int32_t { K_F16 = 1, K_F16_GENERIC = 2, K_MX = 3 };
 
-// Tile configurations the dispatcher can choose (rows of A, rows of B,
-// waves along M, waves along N).
+// Tile configurations the dispatcher can choose: rows of A, rows of B,
+// waves along M, waves along N, and whether the fragments are double-
+// buffered in registers (pipe).
 enum TileCfg : int32_t {
-  T256x256_W2x2 = 0,  // 4 waves, each 128x128
-  T256x128_W2x2 = 1,  // 4 waves, each 128x64
-  T128x256_W2x2 = 2,  // 4 waves, each 64x128
-  T128x128_W2x2 = 3,  // 4 waves, each 64x64
-  T_COUNT = 4
+  T256x256_W2x2 = 0,    // 4 waves, each 128x128
+  T256x128_W2x2 = 1,    // 4 waves, each 128x64
+  T128x256_W2x2 = 2,    // 4 waves, each 64x128
+  T128x128_W2x2 = 3,    // 4 waves, each 64x64
+  T256x256_W2x4 = 4,    // 8 waves (2 per SIMD), each 128x64
+  T256x256_W2x4_P = 5,  // 8 waves, double-buffered fragments
+  T256x256_W2x4_S3 = 6, // 8 waves, K-tiles of 32, 3 LDS stages
+  T256x256_W2x4_S4 = 7, // 8 waves, K-tiles of 32, 4 LDS stages
+  T256x256_W2x4_S5 = 8, // 8 waves, K-tiles of 32, 5 LDS stages
+  T256x256_PP = 9,      // 8 waves in two ping-pong groups, each wave 128x64
+  T256x256_PPS4 = 10,   // ping-pong, K-tiles of 32, 4 LDS stages
+  T256x256_PPS5 = 11,   // ping-pong, K-tiles of 32, 5 LDS stages
+  T_COUNT = 12
 };
 
 struct TileShape {
-  int32_t bm, bn, wm, wn;
+  int32_t bm, bn, wm, wn, bk, stages;
 };
 
 constexpr TileShape kTiles[T_COUNT] = {
-    {256, 256, 2, 2}, {256, 128, 2, 2}, {128, 256, 2, 2}, {128, 128, 2, 2}};
+    {256, 256, 2, 2, 64, 2}, {256, 128, 2, 2, 64, 2}, {128, 256, 2, 2, 64, 2},
+    {128, 128, 2, 2, 64, 2}, {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 64, 2},
+    {256, 256, 2, 4, 32, 3}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
+    {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5}};
 
 struct GemmParams {
   const void* a;  // element (b, m, k) at a + b*a_bs + m*a_rs + k*a_ks

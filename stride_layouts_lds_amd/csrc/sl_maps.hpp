@@ -74,35 +74,40 @@ SL_HD constexpr Coord scale_map(int32_t instr, int32_t lane) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile layout: a K-contiguous tile of `rows` x 128 bytes.  Logical byte
+// LDS tile layout: a K-contiguous tile of `rows` x RB bytes (RB = 128: one
+// 64-wide fp16 K-tile per row; RB = 64: a 32-wide one).  Logical byte
 // (row, b) lives in 16-byte chunk c = b/16 of its row; the chunk index is
 // XOR-swizzled with bits of the row so that the lanes of one ds_read_b128
 // pass land on distinct banks:
-//   offset(row, b) = row*128 + 16*(c ^ swz(row)) + b%16
-// with swz(row) = (row >> shift) & 7.  shift = 0 is the page's SWIZZLE_128B
-// rule (row-in-8 XOR the chunk), shift = 1 pairs rows for a 64-bank LDS.
-// The rule is a bijection on every 8*2^shift-row block, and writer and
-// reader both call this one function.
+//   offset(row, b) = row*RB + 16*(c ^ swz(row)) + b%16
+// with swz(row) = (row >> shift) & (RB/16 - 1).  For RB = 128 and shift 0
+// this is the pages' SWIZZLE_128B rule (row-in-8 XOR the 16-byte chunk).
+// The rule is a bijection on every block of (RB/16) << shift rows, and the
+// writer (loader) and the reader (fragment load) call this one function.
 // ---------------------------------------------------------------------------
 
 constexpr int32_t kRowBytes = 128;
 
-SL_HD constexpr int32_t swz(int32_t row, int32_t shift) { return (row >> shift) & 7; }
+SL_HD constexpr int32_t swz(int32_t row, int32_t shift, int32_t row_bytes = kRowBytes) {
+  return (row >> shift) & (row_bytes / 16 - 1);
+}
 
-SL_HD constexpr int32_t lds_offset(int32_t row, int32_t byte_in_row, int32_t shift) {
-  return row * kRowBytes + 16 * (((byte_in_row >> 4) ^ swz(row, shift)) & 7) + (byte_in_row & 15);
+SL_HD constexpr int32_t lds_offset(int32_t row, int32_t byte_in_row, int32_t shift,
+                                   int32_t row_bytes = kRowBytes) {
+  return row * row_bytes + 16 * (((byte_in_row >> 4) ^ swz(row, shift, row_bytes)) & (row_bytes / 16 - 1)) +
+         (byte_in_row & 15);
 }
 
 // Byte offset in the LDS tile that lane `lane` reads, for its 16-byte
 // fragment piece `piece` (f16: 1 piece of 8 halves; f8: 2 pieces of 16
 // bytes), of the MFMA tile whose first row is `row0`, at k-slice `ks` (in
-// units of the instruction's K), for an operand with `elem_bytes` bytes.
+// units of the instruction's K).
 SL_HD constexpr int32_t fragment_lds_offset(int32_t instr, int32_t lane, int32_t piece, int32_t row0,
-                                            int32_t ks, int32_t shift) {
+                                            int32_t ks, int32_t shift, int32_t row_bytes = kRowBytes) {
   const Coord c = operand_map(instr, lane, piece * 16 / (instr_in_slots(instr) == 8 ? 2 : 1));
   const int32_t elem_bytes = instr_in_slots(instr) == 8 ? 2 : 1;
   const int32_t byte = (ks * instr_k(instr) + c.col) * elem_bytes;
-  return lds_offset(row0 + c.row, byte, shift);
+  return lds_offset(row0 + c.row, byte, shift, row_bytes);
 }
 
 }  // namespace sl
