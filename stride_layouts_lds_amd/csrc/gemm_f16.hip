@@ -433,6 +433,207 @@ __global__ __launch_bounds__(512, 2) void gemm_f16_pps_kernel(const GemmParams p
   }
 }
 
+// Ping-pong with deep prefetch and a spread copy: as above, but every wave
+// copies an eighth of each tile, and issues its copy instructions one per 8
+// MFMAs inside its own compute phase (copy of tile t+STAGES-1 during C(t),
+// into the buffer of tile t-1 whose last readers finished before b2t).  The
+// memory phases hold only fragment reads, so both phases of every SIMD are
+// balanced.  Before barrier b2t+2 both groups have their part of tile t+1
+// landed: group 0 (at the end of C(t), copies issued up to tile t+S-1) allows
+// S-2 tiles in flight, group 1 (at the end of M(t), copies up to tile
+// t+S-2) allows S-3.
+template <int STAGES, int SHIFT>
+__global__ __launch_bounds__(512, 2) void gemm_f16_pps2_kernel(const GemmParams p) {
+  static_assert(STAGES >= 3, "group 1 waits for S-3 tiles");
+  constexpr int BM = 256, BN = 256;
+  constexpr int TM = 128, TN = 64;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int RB = 64;
+  constexpr int ABYTES = BM * RB, BBYTES = BN * RB;
+  constexpr int STAGE = ABYTES + BBYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  using LA = LoaderKVec<BM, 512, SHIFT, 2, RB>;
+  using LB = LoaderKVec<BN, 512, SHIFT, 2, RB>;
+  constexpr int LOADS = LA::ITERS + LB::ITERS;  // copy instructions per tile per wave
+  static_assert(LA::ITERS == 2 && LB::ITERS == 2, "copy layout");
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t grp = wave >> 2;
+  const int32_t wm = wave & 1, wn = wave >> 1;
+
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
+  LA la(A, rows_a, p.a_rs, 1, p.K, wave, lane);
+  LB lb(B, rows_b, p.b_rs, 1, p.K, wave, lane);
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
+  half8 fa[FM], fb[FN];
+
+  const int32_t T = (int32_t)((p.K + 31) / 32);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    la.issue(s, smem + s * STAGE);
+    lb.issue(s, smem + s * STAGE + ABYTES);
+  }
+  wait_vmem_n<(STAGES - 2) * LOADS>();  // this wave's part of tile 0 landed
+  phase_barrier();                       // b0
+  if (grp == 1) phase_barrier();
+
+  for (int32_t t = 0; t < T; ++t) {
+    const char* cur = smem + (t % STAGES) * STAGE;
+    char* fut = smem + ((t + STAGES - 1) % STAGES) * STAGE;
+    // ---- M(t)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = *(const half8*)(cur + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, 0, SHIFT, RB));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[j] = *(const half8*)(cur + ABYTES + fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, 0, SHIFT, RB));
+    if (grp == 1) wait_vmem_n<(STAGES - 3) * LOADS>();  // group 1's part of tile t+1
+    phase_barrier();
+    // ---- C(t): 32 MFMAs with the 4 copy instructions of tile t+S-1 spread in
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      if (i % 2 == 1) {
+        const int c = i / 2;  // 0..3
+        if (c < 2)
+          la.issue_one(t + STAGES - 1, fut, c);
+        else
+          lb.issue_one(t + STAGES - 1, fut + ABYTES, c - 2);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy instruction
+    }
+    if (grp == 0) wait_vmem_n<(STAGES - 2) * LOADS>();  // group 0's part of tile t+1
+    phase_barrier();
+  }
+  wait_vmem();  // the out-of-range copies past the last tile
+  if (grp == 0) {
+    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+    phase_barrier();
+  } else {
+    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  }
+}
+
+// Ping-pong on 64-wide K-tiles (two LDS stages) where group 1 alone copies,
+// spreading the copy instructions of tile t+2 over its compute phase C(t),
+// one per 4 MFMAs; the memory phases hold only fragment reads.
+//   group 0:  b0 M(0) b1 C(0) b2 M(1) b3 ...      C(T-1) b2T  [epilogue] b2T+1
+//   group 1:  b0 copy(1) b1 M(0) b2 C(0)+copy(2) b3 M(1) b4 ... C(T-1) b2T+1
+// Tile t+2 goes into the buffer of tile t during C(t) of group 1, i.e. after
+// b2t+2, when M(t) of both groups (the buffer's last readers) is over.  Group
+// 1 waits for the copy of tile t+1 at the end of its M(t), before b2t+2,
+// ahead of the first read of tile t+1 (M(t+1) of group 0).  Tile 0 is copied
+// by all waves before b0; tile 1 by group 1 in its first phase.
+template <int SHIFT>
+__global__ __launch_bounds__(512, 2) void gemm_f16_ppg_kernel(const GemmParams p) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int TM = 128, TN = 64;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
+  constexpr int STAGE = ABYTES + BBYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  using LA = LoaderKVec<BM, 256, SHIFT, 2>;
+  using LB = LoaderKVec<BN, 256, SHIFT, 2>;
+  static_assert(LA::ITERS == 8 && LB::ITERS == 8, "copy layout");
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t grp = wave >> 2;
+  const int32_t wm = wave & 1, wn = wave >> 1;
+
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
+  // each group's four waves can copy a whole tile
+  LA la(A, rows_a, p.a_rs, 1, p.K, wave & 3, lane);
+  LB lb(B, rows_b, p.b_rs, 1, p.K, wave & 3, lane);
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
+  half8 fa[2][FM], fb[2][FN];
+
+  const int32_t T = p.k_tiles;
+  if (grp == 0) {
+    la.issue(0, smem);
+    lb.issue(0, smem + ABYTES);
+    wait_vmem();
+  }
+  phase_barrier();  // b0: tile 0 in LDS
+  if (grp == 1) {
+    la.issue(1, smem + STAGE);  // out of range if there is no tile 1
+    lb.issue(1, smem + STAGE + ABYTES);
+    phase_barrier();  // b1
+  }
+
+  for (int32_t t = 0; t < T; ++t) {
+    const char* cur = smem + (t & 1) * STAGE;
+    char* cpy = smem + (t & 1) * STAGE;  // tile t+2 reuses tile t's buffer
+    // ---- M(t)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[ks][i] = *(const half8*)(cur + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, ks, SHIFT));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[ks][j] =
+            *(const half8*)(cur + ABYTES + fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, ks, SHIFT));
+    }
+    if (grp == 1) wait_vmem();  // the copy of tile t+1 landed (before b2t+2)
+    phase_barrier();
+    // ---- C(t): one MFMA sequence; group 1 issues a copy instruction of
+    // tile t+2 after every 4 MFMAs (a wave-uniform branch)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+        if (grp == 1) {
+          const int c = ks * FM + i;  // 0..15: eight A then eight B row blocks
+          if (c < 8)
+            la.issue_one(t + 2, cpy, c);
+          else
+            lb.issue_one(t + 2, cpy + ABYTES, c - 8);
+        }
+      }
+    phase_barrier();
+  }
+  if (grp == 0) {
+    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+    phase_barrier();  // b2T+1
+  } else {
+    wait_vmem();  // the out-of-range copies past the last tile
+    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int AL, int BL, int PIPE>
 hipError_t launch_cfg(const GemmParams& p, int32_t shift, hipStream_t s) {
   const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
@@ -493,6 +694,29 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
       case T256x256_W2x4_S3: return launch_ms<256, 256, 2, 4, 3>(p, shift, s);
       case T256x256_W2x4_S4: return launch_ms<256, 256, 2, 4, 4>(p, shift, s);
       case T256x256_W2x4_S5: return launch_ms<256, 256, 2, 4, 5>(p, shift, s);
+      case T256x256_PPG: {
+        const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
+        if (shift == 0)
+          hipLaunchKernelGGL(gemm_f16_ppg_kernel<0>, dim3((uint32_t)total), dim3(512), 0, s, p);
+        else
+          hipLaunchKernelGGL(gemm_f16_ppg_kernel<1>, dim3((uint32_t)total), dim3(512), 0, s, p);
+        return hipGetLastError();
+      }
+      case T256x256_PPC4:
+      case T256x256_PPC5: {
+        const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
+        const dim3 g((uint32_t)total), b(512);
+        if (tile == T256x256_PPC4) {
+          if (shift == 0) hipLaunchKernelGGL((gemm_f16_pps2_kernel<4, 0>), g, b, 0, s, p);
+          else if (shift == 1) hipLaunchKernelGGL((gemm_f16_pps2_kernel<4, 1>), g, b, 0, s, p);
+          else hipLaunchKernelGGL((gemm_f16_pps2_kernel<4, 2>), g, b, 0, s, p);
+        } else {
+          if (shift == 0) hipLaunchKernelGGL((gemm_f16_pps2_kernel<5, 0>), g, b, 0, s, p);
+          else if (shift == 1) hipLaunchKernelGGL((gemm_f16_pps2_kernel<5, 1>), g, b, 0, s, p);
+          else hipLaunchKernelGGL((gemm_f16_pps2_kernel<5, 2>), g, b, 0, s, p);
+        }
+        return hipGetLastError();
+      }
       case T256x256_PPS4:
       case T256x256_PPS5: {
         const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;

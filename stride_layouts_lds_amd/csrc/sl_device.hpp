@@ -133,16 +133,19 @@ struct LoaderKVec {
     row_step = (uint32_t)(WAVES * RPI * rs * ELEM);
   }
 
+  // one copy instruction: j-th row block of K-tile t
+  __device__ __forceinline__ void issue_one(int32_t t, char* lds, int j) const {
+    // instruction j covers rows (j*WAVES + wave)*RPI + 0..RPI-1
+    const int32_t row = row0 + j * WAVES * RPI;
+    const int32_t c = (lane % CPR) ^ swz(row, SHIFT, RB);
+    const uint32_t a = row_off + (uint32_t)j * row_step + (uint32_t)(c * 16) + (uint32_t)(t * RB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16,
+                                             (t * KT + c * CE < K) ? a : kOutOfRange, 0, 0, 0);
+  }
+
   __device__ __forceinline__ void issue(int32_t t, char* lds) const {
 #pragma unroll
-    for (int j = 0; j < ITERS; ++j) {
-      // instruction j covers rows (j*WAVES + wave)*RPI + 0..RPI-1
-      const int32_t row = row0 + j * WAVES * RPI;
-      const int32_t c = (lane % CPR) ^ swz(row, SHIFT, RB);
-      const uint32_t a = row_off + (uint32_t)j * row_step + (uint32_t)(c * 16) + (uint32_t)(t * RB);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16,
-                                               (t * KT + c * CE < K) ? a : kOutOfRange, 0, 0, 0);
-    }
+    for (int j = 0; j < ITERS; ++j) issue_one(t, lds, j);
   }
   __device__ __forceinline__ void commit(char*) const {}
 };

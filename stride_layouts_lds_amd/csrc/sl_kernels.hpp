@@ -32,7 +32,10 @@ enum TileCfg : int32_t {
   T256x256_PP = 9,      // 8 waves in two ping-pong groups, each wave 128x64
   T256x256_PPS4 = 10,   // ping-pong, K-tiles of 32, 4 LDS stages
   T256x256_PPS5 = 11,   // ping-pong, K-tiles of 32, 5 LDS stages
-  T_COUNT = 12
+  T256x256_PPC4 = 12,   // ping-pong, 4 stages, copy spread over all waves' compute phases
+  T256x256_PPC5 = 13,   // same with 5 stages
+  T256x256_PPG = 14,    // ping-pong, 2 stages of 64-wide K-tiles, group 1 copies inside its compute phase
+  T_COUNT = 15
 };
 
 struct TileShape {
@@ -43,7 +46,8 @@ constexpr TileShape kTiles[T_COUNT] = {
     {256, 256, 2, 2, 64, 2}, {256, 128, 2, 2, 64, 2}, {128, 256, 2, 2, 64, 2},
     {128, 128, 2, 2, 64, 2}, {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 64, 2},
     {256, 256, 2, 4, 32, 3}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
-    {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5}};
+    {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
+    {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5}, {256, 256, 2, 4, 64, 2}};
 
 struct GemmParams {
   const void* a;  // element (b, m, k) at a + b*a_bs + m*a_rs + k*a_ks
