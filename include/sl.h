@@ -103,7 +103,9 @@ typedef struct {
 
 /* What sl_gemm would launch for these arguments (host only, no HIP call). */
 typedef struct {
-  int32_t kernel;     /* kernel family: 1 fp16 fast, 2 fp16 generic, 3 mxfp8 */
+  int32_t kernel;     /* kernel family: 1 fp16 fast, 2 fp16 generic, 3 mxfp8
+                         (4 waves, 16x16x128 instruction), 4 mxfp8 (8 waves,
+                         32x32x64 instruction, scales staged in LDS) */
   int32_t a_load;     /* 0 K-contiguous vector, 1 M-contiguous vector, 2 generic */
   int32_t b_load;     /* same, for B */
   int32_t tile_m, tile_n, tile_k;
@@ -199,6 +201,8 @@ sl_status sl_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t capacit
  *           (perm[l] & 63 always).
  *   mode 2: ds_read_b64_tr_b16: LDS is filled with src (4096 bytes), lane l
  *           reads at byte address perm[l]; out receives 64 lanes x 8 bytes.
+ *   mode 3: as mode 0 with a 4-byte direct-to-LDS buffer load: lane l loads
+ *           the 4 bytes at src + 4*(perm[l] & 255).
  */
 sl_status sl_probe_lds(int32_t mode, const void* src, const int32_t* perm, void* out, void* stream);
 

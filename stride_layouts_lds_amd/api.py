@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libstride_layouts_lds.so")
 
 SL_F16, SL_F32, SL_F8_E4M3, SL_E8M0 = 1, 2, 3, 4
-K_F16, K_F16_GENERIC, K_MX = 1, 2, 3
+K_F16, K_F16_GENERIC, K_MX, K_MX_W8 = 1, 2, 3, 4
 STATUS = {0: "SL_OK", -1: "SL_ERR_NULL", -2: "SL_ERR_DTYPE", -3: "SL_ERR_SHAPE", -4: "SL_ERR_LAYOUT",
           -5: "SL_ERR_ALIGN", -6: "SL_ERR_ALIAS", -7: "SL_ERR_ARCH", -8: "SL_ERR_LAUNCH", -9: "SL_ERR_ARG"}
 

@@ -286,15 +286,25 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
                   "MXFP8 operands must be K-contiguous with 16-byte aligned rows and K %% 16 == 0");
     if ((M - 1) * SA.rs + (kb - 1) * SA.cs >= lim || (N - 1) * SB.rs + (kb - 1) * SB.cs >= lim)
       return fail(SL_ERR_SHAPE, "scale tensors span more than 2^31 bytes");
-    if (tile < 0 || tile > sl::T128x128_W2x2) {
-      tile = sl::T256x128_W2x2;  // MX kernels exist for the first four tiles
+    // The 8-wave kernel copies one dword of scales per row and K-tile: the
+    // scale rows must be K-contiguous, 4-byte aligned, and hold a multiple
+    // of four blocks.
+    auto dword_rows = [&](const View& S) {
+      return S.cs == 1 && S.rs % 4 == 0 && (uintptr_t)S.t->data % 4 == 0 &&
+             (S.t->layout.rank == 2 || S.bs % 4 == 0);
+    };
+    const bool wide_ok = kb % 4 == 0 && dword_rows(SA) && dword_rows(SB);
+    const bool valid = tile == sl::T256x256_W2x4 ? wide_ok : tile >= 0 && tile <= sl::T128x128_W2x2;
+    if (!valid) {
+      tile = sl::T256x128_W2x2;
       double best = 1e300;
-      for (int t : {sl::T256x128_W2x2, sl::T128x256_W2x2, sl::T128x128_W2x2}) {
+      for (int t : {sl::T256x256_W2x4, sl::T256x128_W2x2, sl::T128x256_W2x2, sl::T128x128_W2x2}) {
+        if (t == sl::T256x256_W2x4 && !wide_ok) continue;
         const double c = tile_cost(sl::kTiles[t], batch, M, N, K);
         if (c < best) best = c, tile = t;
       }
     }
-    P.pub.kernel = sl::K_MX;
+    P.pub.kernel = tile == sl::T256x256_W2x4 ? sl::K_MX_W8 : sl::K_MX;
     P.pub.a_load = P.pub.b_load = sl::LOAD_KVEC;
     P.pub.tile_k = 128;
     p.k_tiles = (int32_t)((K + 127) / 128);
@@ -339,6 +349,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.pub.split_k = 1;
   P.pub.workgroups = total;
   P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * P.pub.tile_k * (mx ? 1 : 2);
+  if (P.pub.kernel == sl::K_MX_W8) P.pub.lds_bytes += ts.stages * (ts.bm + ts.bn) * 4;
   return SL_OK;
 }
 
@@ -436,10 +447,10 @@ static int32_t current_shift() { return env_int("SL_SWZ", 0) ? 1 : 0; }
 sl_status sl_query_lds_map(int32_t variant, int32_t operand, int64_t* offsets, int64_t capacity, int32_t* rows,
                            int32_t* cols, int32_t* elem_bytes) {
   g_msg.clear();
-  if (variant < sl::K_F16 || variant > sl::K_MX) return fail(SL_ERR_ARG, "variant %d", variant);
+  if (variant < sl::K_F16 || variant > sl::K_MX_W8) return fail(SL_ERR_ARG, "variant %d", variant);
   if (operand < 0 || operand > 1) return fail(SL_ERR_ARG, "operand %d", operand);
   const int32_t R = variant == sl::K_F16_GENERIC ? 128 : 256;
-  const int32_t es = variant == sl::K_MX ? 1 : 2;
+  const int32_t es = variant >= sl::K_MX ? 1 : 2;
   const int32_t Cn = sl::kRowBytes / es;
   const int32_t sh = current_shift();
   int64_t n = 0;
@@ -455,11 +466,11 @@ sl_status sl_query_lds_map(int32_t variant, int32_t operand, int64_t* offsets, i
 sl_status sl_query_fragment_addresses(int32_t variant, int32_t operand, int64_t* addr, int64_t capacity,
                                       int64_t* count) {
   g_msg.clear();
-  if (variant < sl::K_F16 || variant > sl::K_MX) return fail(SL_ERR_ARG, "variant %d", variant);
+  if (variant < sl::K_F16 || variant > sl::K_MX_W8) return fail(SL_ERR_ARG, "variant %d", variant);
   if (operand < 0 || operand > 1) return fail(SL_ERR_ARG, "operand %d", operand);
-  const int32_t instr = variant == sl::K_MX ? sl::MFMA16_F8 : sl::MFMA16_F16;
+  const int32_t instr = variant == sl::K_MX_W8 ? sl::MFMA32_F8 : variant == sl::K_MX ? sl::MFMA16_F8 : sl::MFMA16_F16;
   const int32_t slots = sl::instr_in_slots(instr);
-  const int32_t es = variant == sl::K_MX ? 1 : 2;
+  const int32_t es = variant >= sl::K_MX ? 1 : 2;
   const int32_t sh = current_shift();
   int64_t n = 0;
   for (int32_t l = 0; l < 64; ++l)
@@ -495,7 +506,7 @@ sl_status sl_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t capacit
 
 sl_status sl_probe_lds(int32_t mode, const void* src, const int32_t* perm, void* out, void* stream) {
   g_msg.clear();
-  if (mode < 0 || mode > 2) return fail(SL_ERR_ARG, "mode %d", mode);
+  if (mode < 0 || mode > 3) return fail(SL_ERR_ARG, "mode %d", mode);
   if (!src || !perm || !out) return fail(SL_ERR_NULL, "src, perm and out are required");
   if ((uintptr_t)src % 16 || (uintptr_t)out % 16) return fail(SL_ERR_ALIGN, "src and out must be 16-byte aligned");
   sl_status s = check_arch();

@@ -23,45 +23,13 @@ namespace {
 template <int FM, int FN>
 __device__ __forceinline__ void epilogue(const floatx4 (&acc)[FM][FN], const GemmParams& p, int32_t batch,
                                          int64_t m_base, int64_t n_base, int32_t lane) {
-  const bool has_c = p.flags & F_HAS_C;
-  const bool d_vec = p.flags & F_D_VEC;
-  const bool c_vec = p.flags & F_C_VEC;
   uint16_t* D = (uint16_t*)p.d + batch * p.d_bs;
-  const uint16_t* C = has_c ? (const uint16_t*)p.c + batch * p.c_bs : nullptr;
+  const uint16_t* C = (p.flags & F_HAS_C) ? (const uint16_t*)p.c + batch * p.c_bs : nullptr;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int64_t m = m_base + 16 * i + (lane & 15);
-    if (m >= p.M) continue;
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = n_base + 16 * j + 4 * (lane >> 4);
-      if (n >= p.N) continue;
-      floatx4 v = acc[i][j];
-      const bool full = n + 3 < p.N;
-      if (has_c) {
-        const uint16_t* cp = C + m * p.c_rs + n * p.c_cs;
-        if (full && c_vec) {
-          const half4 cv = *(const half4*)cp;
-          v[0] += (float)cv[0];
-          v[1] += (float)cv[1];
-          v[2] += (float)cv[2];
-          v[3] += (float)cv[3];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < p.N) v[r] += (float)__builtin_bit_cast(_Float16, cp[r * p.c_cs]);
-        }
-      }
-      uint16_t* dp = D + m * p.d_rs + n * p.d_cs;
-      if (full && d_vec) {
-        *(half4*)dp = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < p.N) dp[r * p.d_cs] = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
-      }
-    }
-  }
+    for (int j = 0; j < FN; ++j)
+      store_quad(p, C, D, m_base + 16 * i + (lane & 15), n_base + 16 * j + 4 * (lane >> 4), acc[i][j]);
 }
 
 // PIPE 0: per k-slice, read the fragments then issue the MFMAs (latency is

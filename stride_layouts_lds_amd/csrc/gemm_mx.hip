@@ -5,11 +5,11 @@
 // "Replication 与 Offset", with B stored (N, K) and K_blk = 32.
 //
 // Same data flow as the fp16 kernel: a K-tile is 128 bytes = 128 E4M3
-// values per row, loaded straight into the XOR-swizzled LDS tile; the
-// instruction v_mfma_scale_f32_16x16x128_f8f6f4 consumes 32 bytes per lane
-// (two ds_read_b128) and one scale byte per lane.  Its scale lane l covers
-// (row l % 16, K block l / 16) of its operand, so lane l fetches the byte
-// SF[row0 + l % 16][4 t + l / 16] for K-tile t.
+// values per row, loaded straight into the XOR-swizzled LDS tile.  Two
+// kernels: a 4-wave one on v_mfma_scale_f32_16x16x128_f8f6f4 that takes
+// any scale strides (scale lane l covers (row l % 16, K block l / 16) of
+// its operand, so lane l fetches the byte SF[row0 + l % 16][4 t + l / 16]
+// for K-tile t), and the 8-wave one below for dword-aligned scale rows.
 #include "sl_device.hpp"
 
 namespace sl {
@@ -113,44 +113,145 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_mx_kernel(const GemmParam
     __syncthreads();
   }
 
-  const bool has_c = p.flags & F_HAS_C;
-  const bool d_vec = p.flags & F_D_VEC;
-  const bool c_vec = p.flags & F_C_VEC;
   uint16_t* D = (uint16_t*)p.d + tc.batch * p.d_bs;
-  const uint16_t* C = has_c ? (const uint16_t*)p.c + tc.batch * p.c_bs : nullptr;
+  const uint16_t* C = (p.flags & F_HAS_C) ? (const uint16_t*)p.c + tc.batch * p.c_bs : nullptr;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      store_quad(p, C, D, m0 + a_row0 + 16 * i + (lane & 15), n0 + b_row0 + 16 * j + 4 * (lane >> 4), acc[i][j]);
+}
+
+// 8 waves (2 along M x 4 along N) on a 256 x 256 output tile, each wave a
+// 128 x 64 block as 4 x 2 tiles of v_mfma_scale_f32_32x32x64_f8f6f4; one
+// 128-byte K-tile is two 64-wide k-slices.  The wider instruction halves the
+// fragment registers of a slice (6 x 8 VGPRs) against the 16x16x128 form.
+//
+// Scales go through LDS with the data: per K-tile a row of A or B owns one
+// dword of SF (its four E8M0 bytes for k-blocks 4t..4t+3), copied straight
+// into LDS by one 4-byte buffer load per row (waves 0-3: A rows, 4-7: B
+// rows).  This needs the scale rows K-contiguous, dword aligned and a whole
+// number of dwords long; the planner checks it.  In slice s, scale lane l
+// of an instruction tile wants block 2s + l / 32 of row l % 32: the lane
+// reads its row's dword, shifts it right by 8 (l / 32) once per K-tile, and
+// passes byte 2s of the result.
+template <int SHIFT>
+__global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) {
+  constexpr int BM = 256, BN = 256, WM = 2, NT = 512;
+  constexpr int TM = 128, TN = 64;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
+  constexpr int SOFF = ABYTES + BBYTES;  // A scale dwords, then B scale dwords
+  constexpr int STAGE = SOFF + (BM + BN) * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t wm = wave % WM, wn = wave / WM;
+
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  const char* A = (const char*)p.a + (tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + (tc.batch * p.b_bs + n0 * p.b_rs);
+
+  LoaderKVec<BM, NT, SHIFT, 1> la(A, rows_a, p.a_rs, 1, p.K, wave, lane);
+  LoaderKVec<BN, NT, SHIFT, 1> lb(B, rows_b, p.b_rs, 1, p.K, wave, lane);
+
+  // scale copy of this wave: operand (wave / 4), rows 64 (wave % 4) + lane
+  const int32_t kdw = (int32_t)((p.K + 127) / 128);  // scale dwords per row
+  const bool s_is_b = wave >= 4;
+  const uint8_t* S = s_is_b ? p.sfb + tc.batch * p.sb_bs + n0 * p.sb_rs : p.sfa + tc.batch * p.sa_bs + m0 * p.sa_rs;
+  const int64_t s_rs = s_is_b ? p.sb_rs : p.sa_rs;
+  const int32_t s_rows = s_is_b ? rows_b : rows_a;
+  const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(S, s_rows > 0 ? (uint32_t)((s_rows - 1) * s_rs + 4 * kdw) : 0u);
+  const int32_t s_row = 64 * (wave & 3) + lane;
+  const uint32_t s_off = s_row < s_rows ? (uint32_t)(s_row * s_rs) : kOutOfRange;
+  const int32_t s_lds = SOFF + (s_is_b ? BM * 4 : 0) + 256 * (wave & 3);
+  auto issue_scales = [&](int32_t t, char* stage) {
+    const uint32_t off = (s_off != kOutOfRange && t < kdw) ? s_off + 4u * (uint32_t)t : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void_t*)(stage + s_lds), 4, off, 0, 0, 0);
+  };
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
+
+  const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
+  const int32_t half_sel = 8 * (lane >> 5);
+
+  const int32_t T = p.k_tiles;
+  if (T > 0) {
+    la.issue(0, smem);
+    lb.issue(0, smem + ABYTES);
+    issue_scales(0, smem);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // Loop body without branches, as in the fp16 kernel: past the last tile
+  // the copies are fully out of range and fill the idle stage with zeros.
+  for (int32_t t = 0; t < T; ++t) {
+    char* cur = smem + (t & 1) * STAGE;
+    char* nxt = smem + ((t + 1) & 1) * STAGE;
+    la.issue(t + 1, nxt);
+    lb.issue(t + 1, nxt + ABYTES);
+    issue_scales(t + 1, nxt);
+    uint32_t sa[FM], sb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      sa[i] = *(const uint32_t*)(cur + SOFF + 4 * (a_row0 + 32 * i + (lane & 31))) >> half_sel;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      sb[j] = *(const uint32_t*)(cur + SOFF + BM * 4 + 4 * (b_row0 + 32 * j + (lane & 31))) >> half_sel;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x8 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const u32x4 lo = *(const u32x4*)(cur + fragment_lds_offset(MFMA32_F8, lane, 0, a_row0 + 32 * i, ks, SHIFT));
+        const u32x4 hi = *(const u32x4*)(cur + fragment_lds_offset(MFMA32_F8, lane, 1, a_row0 + 32 * i, ks, SHIFT));
+        af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const u32x4 lo =
+            *(const u32x4*)(cur + ABYTES + fragment_lds_offset(MFMA32_F8, lane, 0, b_row0 + 32 * j, ks, SHIFT));
+        const u32x4 hi =
+            *(const u32x4*)(cur + ABYTES + fragment_lds_offset(MFMA32_F8, lane, 1, b_row0 + 32 * j, ks, SHIFT));
+        bf[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      // instruction A = our B tile (its scales: sb), instruction B = our A tile
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              bf[j], af[i], acc[i][j], kFmtE4M3, kFmtE4M3, 0, (int)((sb[j] >> (16 * ks)) & 0xFFu), 0,
+              (int)((sa[i] >> (16 * ks)) & 0xFFu));
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // accumulator register r of tile (i, j): instruction row (our n)
+  // 8 (r / 4) + 4 (lane / 32) + r % 4, instruction column (our m) lane % 32
+  uint16_t* D = (uint16_t*)p.d + tc.batch * p.d_bs;
+  const uint16_t* C = (p.flags & F_HAS_C) ? (const uint16_t*)p.c + tc.batch * p.c_bs : nullptr;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int64_t m = m0 + a_row0 + 16 * i + (lane & 15);
-    if (m >= p.M) continue;
+    const int64_t m = m0 + a_row0 + 32 * i + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = n0 + b_row0 + 16 * j + 4 * (lane >> 4);
-      if (n >= p.N) continue;
-      floatx4 v = acc[i][j];
-      const bool full = n + 3 < p.N;
-      if (has_c) {
-        const uint16_t* cp = C + m * p.c_rs + n * p.c_cs;
-        if (full && c_vec) {
-          const half4 cv = *(const half4*)cp;
-          v[0] += (float)cv[0];
-          v[1] += (float)cv[1];
-          v[2] += (float)cv[2];
-          v[3] += (float)cv[3];
-        } else {
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < p.N) v[r] += (float)__builtin_bit_cast(_Float16, cp[r * p.c_cs]);
-        }
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + b_row0 + 32 * j + 8 * g + 4 * (lane >> 5);
+        const floatx16& a = acc[i][j];
+        store_quad(p, C, D, m, n, floatx4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]});
       }
-      uint16_t* dp = D + m * p.d_rs + n * p.d_cs;
-      if (full && d_vec) {
-        *(half4*)dp = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < p.N) dp[r * p.d_cs] = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
-      }
-    }
   }
 }
 
@@ -173,6 +274,14 @@ hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, int32_t shift, hipS
     case T256x128_W2x2: return launch_cfg<256, 128, 2, 2>(p, shift, s);
     case T128x256_W2x2: return launch_cfg<128, 256, 2, 2>(p, shift, s);
     case T128x128_W2x2: return launch_cfg<128, 128, 2, 2>(p, shift, s);
+    case T256x256_W2x4: {
+      dim3 grid((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), block(512);
+      if (shift == 0)
+        hipLaunchKernelGGL(gemm_mx_w8_kernel<0>, grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL(gemm_mx_w8_kernel<1>, grid, block, 0, s, p);
+      return hipGetLastError();
+    }
     default: return hipErrorInvalidValue;
   }
 }

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64) void probe_lds(int32_t mode, const uint8_t* src
                                                 uint8_t* out) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[4096];
   const int32_t lane = threadIdx.x;
-  if (mode == 0 || mode == 1) {
+  if (mode == 0 || mode == 1 || mode == 3) {
 #pragma unroll
     for (int i = 0; i < 4096 / 64 / 4; ++i) ((uint32_t*)lds)[i * 64 + lane] = 0xA5A5A5A5u;
     __syncthreads();
@@ -110,6 +110,10 @@ __global__ __launch_bounds__(64) void probe_lds(int32_t mode, const uint8_t* src
       const __amdgpu_buffer_rsrc_t r = make_rsrc(src, 1024u);
       const uint32_t off = perm[lane] < 0 ? kOutOfRange : (uint32_t)(16 * p);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, off, 0, 0, 0);
+    } else if (mode == 3) {
+      // 4-byte direct-to-LDS buffer load: lane l fetches src + 4*perm[l]
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(src, 1024u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, (uint32_t)(4 * (perm[lane] & 255)), 0, 0, 0);
     } else {
       __builtin_amdgcn_global_load_lds((const void*)(src + 16 * p), (lds_void_t*)lds, 16, 0, 0);
     }

@@ -88,6 +88,40 @@ __device__ __forceinline__ TileCoord map_tile(int32_t bid, int32_t total, int32_
 }
 
 // ---------------------------------------------------------------------------
+// Epilogue store of four consecutive outputs (m, n..n+3) of one lane:
+// D = fp16_rne(v + C), predicated on m < M and n + r < N.  8-byte accesses
+// when the row is contiguous and aligned (F_D_VEC / F_C_VEC) and all four
+// columns are in range.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_quad(const GemmParams& p, const uint16_t* C, uint16_t* D, int64_t m,
+                                           int64_t n, floatx4 v) {
+  if (m >= p.M || n >= p.N) return;
+  const bool full = n + 3 < p.N;
+  if (p.flags & F_HAS_C) {
+    const uint16_t* cp = C + m * p.c_rs + n * p.c_cs;
+    if (full && (p.flags & F_C_VEC)) {
+      const half4 cv = *(const half4*)cp;
+      v[0] += (float)cv[0];
+      v[1] += (float)cv[1];
+      v[2] += (float)cv[2];
+      v[3] += (float)cv[3];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < p.N) v[r] += (float)__builtin_bit_cast(_Float16, cp[r * p.c_cs]);
+    }
+  }
+  uint16_t* dp = D + m * p.d_rs + n * p.d_cs;
+  if (full && (p.flags & F_D_VEC)) {
+    *(half4*)dp = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < p.N) dp[r * p.d_cs] = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // HBM -> LDS tile loaders.  A tile is ROWS rows (of A's m or B's n) by 128
 // bytes of K (64 fp16 or 128 fp8 values), stored in LDS through
 // lds_offset(row, byte, SHIFT).  Each loader exposes

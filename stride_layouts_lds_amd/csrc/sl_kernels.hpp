@@ -14,7 +14,12 @@ enum LoadKind : int32_t {
 };
 
 // Kernel families (sl_plan.kernel).
-enum KernelKind : int32_t { K_F16 = 1, K_F16_GENERIC = 2, K_MX = 3 };
+enum KernelKind : int32_t {
+  K_F16 = 1,          // fp16, vector loaders
+  K_F16_GENERIC = 2,  // fp16 with an element-wise loader on one side
+  K_MX = 3,           // MXFP8, 4 waves, v_mfma_scale 16x16x128, scales by byte loads
+  K_MX_W8 = 4         // MXFP8, 8 waves, v_mfma_scale 32x32x64, scales staged in LDS
+};
 
 // Tile configurations the dispatcher can choose: rows of A, rows of B,
 // waves along M, waves along N, and whether the fragments are double-

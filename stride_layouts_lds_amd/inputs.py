@@ -105,19 +105,25 @@ def matrix(rng, dist: str, batch: Optional[int], rows: int, cols: int, major: st
     return HostOperand(codes, (batch, rows, cols), st, kind)
 
 
-def scales(rng, batch: Optional[int], rows: int, kblocks: int, lo: int = -4, hi: int = 4) -> HostOperand:
-    e = rng.integers(lo, hi + 1, (batch or 1) * rows * kblocks)
+def scales(rng, batch: Optional[int], rows: int, kblocks: int, lo: int = -4, hi: int = 4,
+           pad: int = 0) -> HostOperand:
+    """E8M0 scale codes 127 + e, e uniform in [lo, hi]; rows are kblocks + pad
+    bytes apart (the pad bytes hold NaN codes, 0xFF, and are never read)."""
+    rs = kblocks + pad
+    e = rng.integers(lo, hi + 1, (batch or 1) * rows * rs)
     codes = (e + 127).astype(np.uint8)
+    if pad:
+        codes.reshape(-1, rs)[:, kblocks:] = 0xFF
     if batch is None:
-        return HostOperand(codes, (rows, kblocks), (kblocks, 1), "e8m0")
-    return HostOperand(codes, (batch, rows, kblocks), (rows * kblocks, kblocks, 1), "e8m0")
+        return HostOperand(codes, (rows, kblocks), (rs, 1), "e8m0")
+    return HostOperand(codes, (batch, rows, kblocks), (rows * rs, rs, 1), "e8m0")
 
 
 def gemm_workload(name: str, M: int, N: int, K: int, *, seed: int, dist: str = "normal",
                   batch: Optional[int] = None, a_major: str = "row", b_major: str = "row",
                   with_c: bool = False, c_dist: Optional[str] = None, mx: bool = False,
                   block_k: int = 32, rng: Optional[np.random.Generator] = None,
-                  scale_range: Tuple[int, int] = (-4, 4)) -> Workload:
+                  scale_range: Tuple[int, int] = (-4, 4), scale_pad: int = 0) -> Workload:
     """A generic seeded GEMM problem.  ``a_major``/``b_major`` say which of
     the two matrix dimensions is contiguous: 'row' = K-contiguous (TN
     convention), 'col' = M- (or N-) contiguous."""
@@ -129,8 +135,8 @@ def gemm_workload(name: str, M: int, N: int, K: int, *, seed: int, dist: str = "
     sfa = sfb = None
     if mx:
         kb = -(-K // block_k)
-        sfa = scales(rng, batch, M, kb, *scale_range)
-        sfb = scales(rng, batch, N, kb, *scale_range)
+        sfa = scales(rng, batch, M, kb, *scale_range, pad=scale_pad)
+        sfb = scales(rng, batch, N, kb, *scale_range, pad=scale_pad)
     if batch is None:
         d_shape, d_strides = (M, N), (N, 1)
     else:

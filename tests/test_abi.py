@@ -150,7 +150,22 @@ def test_mx_validation(api):
     sb = (BASE_C + 0x10000, E8, (N, K // 32), (K // 32, 1))
     d = rowmajor(BASE_D, (M, N))
     p = plan(api, a, b, None, d, sa, sb)
-    assert p["kernel"] == api.K_MX and p["tile_k"] == 128
+    assert p["kernel"] in (api.K_MX, api.K_MX_W8) and p["tile_k"] == 128
+    # a full-chip problem takes the 8-wave kernel when the scale rows are
+    # whole dwords, the 4-wave byte-load kernel otherwise
+    M4 = N4 = 4096
+    a4, b4 = (BASE_A, E4, (M4, K), (K, 1)), (BASE_B, E4, (N4, K), (K, 1))
+    s4a, s4b = (BASE_C, E8, (M4, K // 32), (K // 32, 1)), (BASE_C + 0x100000, E8, (N4, K // 32), (K // 32, 1))
+    d4 = rowmajor(BASE_D, (M4, N4))
+    p = plan(api, a4, b4, None, d4, s4a, s4b)
+    assert p["kernel"] == api.K_MX_W8 and p["threads"] == 512 and p["tile_m"] == p["tile_n"] == 256
+    assert p["lds_bytes"] == 2 * (256 + 256) * (128 + 4)
+    s9 = (BASE_C, E8, (M4, K // 32), (9, 1))
+    assert plan(api, a4, b4, None, d4, s9, s4b)["kernel"] == api.K_MX
+    K2 = 208  # 7 scale blocks per row
+    a2, b2 = (BASE_A, E4, (M4, K2), (224, 1)), (BASE_B, E4, (N4, K2), (224, 1))
+    s2a, s2b = (BASE_C, E8, (M4, 8), (8, 1)), (BASE_C + 0x100000, E8, (N4, 8), (8, 1))
+    assert plan(api, a2, b2, None, d4, s2a[:2] + ((M4, 7), (8, 1)), s2b[:2] + ((N4, 7), (8, 1)))["kernel"] == api.K_MX
     assert err(api, a, b, None, d, sa, sb, block_k=16) == "SL_ERR_SHAPE"
     assert err(api, a, b, None, d, sa, (BASE_C + 0x10000, E8, (N, 7), (7, 1))) == "SL_ERR_SHAPE"
     assert err(api, a, b, None, d, None, None) == "SL_ERR_DTYPE"
@@ -177,7 +192,7 @@ def test_scale_map_equal_oracle(api, instr):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
 def test_lds_map_is_the_xor_swizzle(api, variant):
     offs, es = api.query_lds_map(variant, 0)
     rows, cols = offs.shape
@@ -192,7 +207,7 @@ def test_lds_map_is_the_xor_swizzle(api, variant):
             assert offs[r, k] == L.swizzle_bms(r * 128 + k * es, 3, 4, 3 + shift)
 
 
-@pytest.mark.parametrize("variant,instr", [(1, 0), (3, 2)])
+@pytest.mark.parametrize("variant,instr", [(1, 0), (3, 2), (4, 3)])
 def test_fragment_addresses_compose_maps(api, variant, instr):
     got = api.query_fragment_addresses(variant, 0)
     tv = L.INSTR_MAPS[instr][0]

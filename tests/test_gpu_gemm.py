@@ -147,16 +147,52 @@ def test_broadcast_b_across_batch(api):
     assert np.array_equal(h.d_codes(out), d_ref)
 
 
-def test_mx_exact_parity(api):
+MX_EXACT = [
+    # M, N, K, batch, scale row padding, kernel the planner must pick when
+    # asked for the 8-wave tile
+    (256, 256, 128, None, 0, 4),
+    (300, 200, 384, None, 0, 4),
+    (64, 520, 256, None, 0, 4),
+    (130, 260, 112, None, 0, 4),   # last scale block covers 16 of its 32 K
+    (136, 128, 256, 2, 0, 4),      # batched scales
+    (256, 264, 256, None, 4, 4),   # padded scale rows, still dword aligned
+    (256, 264, 256, None, 1, 3),   # scale rows 9 bytes apart: byte-load kernel
+    (300, 200, 208, None, 0, 3),   # 7 scale blocks per row: byte-load kernel
+    (72, 96, 96, 3, 0, 3),
+]
+
+
+@pytest.mark.parametrize("case", MX_EXACT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_p{c[4]}_k{c[5]}")
+def test_mx_exact_parity(api, case, monkeypatch):
     """E4M3 integers and scale exponents in [-2, 2]: every product is a
     multiple of 2^-4 below 2^8 and every partial sum stays exact in fp32."""
     h = H()
-    for (M, N, K) in [(256, 256, 128), (300, 200, 384), (64, 520, 256)]:
-        w = I.gemm_workload("mx_exact", M, N, K, seed=K, dist="int4", mx=True, scale_range=(-2, 2))
-        h.log(f"mx exact {M}x{N}x{K}")
-        d = h.d_codes(h.run_library(w))
-        d_ref, _, _ = h.oracle_full(w)
-        assert np.array_equal(d.reshape(d_ref.shape), d_ref), (M, N, K)
+    monkeypatch.setenv("SL_TILE", "4")
+    M, N, K, batch, pad, kernel = case
+    w = I.gemm_workload("mx_exact", M, N, K, seed=K + M, dist="int4", batch=batch, mx=True,
+                        scale_range=(-2, 2), scale_pad=pad)
+    plan = _plan(api, w)
+    h.log(f"mx exact {case} plan={plan}")
+    assert plan["kernel"] == kernel
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
+@pytest.mark.parametrize("tile", [1, 3, 4])
+def test_mx_kernels_agree_on_one_input(api, tile, monkeypatch):
+    """The same normal-valued MXFP8 problem through each MX kernel (tile
+    forced), every element within the bound."""
+    h = H()
+    monkeypatch.setenv("SL_TILE", str(tile))
+    w = I.gemm_workload("mx_tiles", 300, 264, 512, seed=77, dist="normal", mx=True, with_c=True)
+    plan = _plan(api, w)
+    h.log(f"mx tile {tile} plan={plan}")
+    assert plan["kernel"] == (api.K_MX_W8 if tile == 4 else api.K_MX)
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, absum = h.oracle_full(w)
+    h.assert_within_bound(d.reshape(d_ref.shape), d_ref, absum, f"mx tile {tile}")
 
 
 # ------------------------------------------------------------------ bounded

@@ -103,6 +103,22 @@ def test_probe_direct_to_lds(api, mode):
     assert np.array_equal(got, want)
 
 
+def test_probe_direct_to_lds_dword(api):
+    """A 4-byte direct HBM->LDS load of one wave writes lane l's bytes at
+    LDS base + 4*l."""
+    import torch
+    from gpu_helpers import log
+    log("probe lds dma dword")
+    rng = np.random.default_rng(6)
+    src = (np.arange(1024) * 29 + 5).astype(np.uint8)
+    perm = rng.permutation(256)[:64].astype(np.int32)
+    got = api.probe_lds(3, torch.from_numpy(src).cuda(), torch.from_numpy(perm).cuda()).cpu().numpy()
+    want = np.full(4096, 0xA5, np.uint8)
+    for l in range(64):
+        want[4 * l:4 * l + 4] = src[4 * perm[l]:4 * perm[l] + 4]
+    assert np.array_equal(got, want)
+
+
 def test_probe_ds_read_tr16(api):
     import torch
     from gpu_helpers import dump, log
