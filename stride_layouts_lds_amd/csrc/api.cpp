@@ -147,10 +147,16 @@ int32_t choose_load(const View& v, int64_t K, int64_t tile_rows, int es) {
 // (fewer LDS bytes per MFMA).
 double tile_cost(const sl::TileShape& t, int64_t batch, int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = batch * ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
-  const int64_t per_cu = (t.bm * t.bn <= 128 * 128) ? 2 : 1;
+  const int64_t lds = (int64_t)t.stages * (t.bm + t.bn) * t.bk * 2;
+  const int64_t per_cu = lds <= 80 * 1024 ? 2 : 1;
   const int64_t slots = 256 * per_cu;
   const int64_t waves = (tiles + slots - 1) / slots;
-  const double eff = (t.bm == 256 && t.bn == 256) ? 1.0 : (t.bm * t.bn == 256 * 128) ? 0.92 : 0.80;
+  // the streaming tile moves 5x the L2 bytes per MFMA of a 256x256 tile:
+  // worth it only where the big tiles leave most of the chip idle
+  const double eff = (t.bm == 256 && t.bn == 256) ? 1.0
+                     : (t.bm * t.bn == 256 * 128) ? 0.92
+                     : (t.bm * t.bn == 128 * 128) ? 0.80
+                                                  : 0.50;
   return (double)waves * (double)t.bm * (double)t.bn * (double)std::max<int64_t>(K, 64) * per_cu / eff;
 }
 
@@ -325,7 +331,9 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
         const int32_t big = kk ? sl::T256x256_W2x4 : sl::T256x256_W2x2;
         tile = big;
         double best = 1e300;
-        for (int t : {big, (int32_t)sl::T256x128_W2x2, (int32_t)sl::T128x256_W2x2, (int32_t)sl::T128x128_W2x2}) {
+        for (int t : {big, (int32_t)sl::T256x128_W2x2, (int32_t)sl::T128x256_W2x2, (int32_t)sl::T128x128_W2x2,
+                      (int32_t)sl::T32x128_STREAM}) {
+          if (t == sl::T32x128_STREAM && !kk) continue;
           const double c = tile_cost(sl::kTiles[t], batch, M, N, K);
           if (c < best) best = c, tile = t;
         }

@@ -146,23 +146,32 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
   epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
 }
 
-// Multi-stage variant for K-contiguous operands: K-tiles of 32 (LDS rows of
-// 64 bytes), STAGES LDS buffers, loads for tile t+STAGES-1 issued while
-// tile t computes, so each tile's HBM->LDS copy has STAGES-1 tiles of
-// compute to land.  One barrier per tile makes the landed tile visible to
-// every wave and retires the buffer the next issue overwrites.
-template <int BM, int BN, int WM, int WN, int STAGES, int SHIFT>
+// Multi-stage variant for K-contiguous operands: K-tiles of RB/2 fp16 (LDS
+// rows of RB bytes), STAGES LDS buffers in a ring, the copy of tile
+// t+STAGES-1 issued while tile t computes, so each tile's HBM->LDS copy has
+// STAGES-1 tiles of compute to land.  One phase barrier per tile makes the
+// landed tile visible to every wave and retires the buffer the next issue
+// overwrites.  (A __syncthreads() here would wait for every copy in flight:
+// its fence counts the direct-to-LDS copies as outstanding LDS writes.)
+//
+// With BM = 32, BN = 128 and 64-wide K-tiles this is the streaming kernel
+// for outputs too small to fill the chip with big tiles (skinny N): one
+// 32-row panel of A per workgroup, read once from HBM, against all of B,
+// which every workgroup shares through L2.
+template <int BM, int BN, int WM, int WN, int STAGES, int SHIFT, int RB = 64>
 __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_kernel(const GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int RB = 64;  // 32 fp16 of K per LDS row
+  constexpr int KT = RB / 2;   // fp16 of K per tile
+  constexpr int KS = KT / 32;  // k-slices of the instruction per tile
   constexpr int ABYTES = BM * RB, BBYTES = BN * RB;
   constexpr int STAGE = ABYTES + BBYTES;
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
   using LA = LoaderKVec<BM, NT, SHIFT, 2, RB>;
   using LB = LoaderKVec<BN, NT, SHIFT, 2, RB>;
   constexpr int LOADS = LA::ITERS + LB::ITERS;  // vector-memory ops per tile per thread
+  static_assert((STAGES - 2) * LOADS < 64, "vmcnt range");
 
   const int32_t lane = threadIdx.x & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
 
-  const int32_t T = (int32_t)((p.K + 31) / 32);
+  const int32_t T = (int32_t)((p.K + KT - 1) / KT);
   // prologue: tiles 0 .. STAGES-2 in flight, wait for tile 0
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
     lb.issue(s, smem + s * STAGE + ABYTES);
   }
   wait_vmem_n<(STAGES - 2) * LOADS>();
-  __syncthreads();
+  phase_barrier();
 
   for (int32_t t = 0; t < T; ++t) {
     const char* cur = smem + (t % STAGES) * STAGE;
@@ -201,23 +210,30 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
     // it with tile t+STAGES-1 (fully out of range past the last tile)
     la.issue(t + STAGES - 1, fut);
     lb.issue(t + STAGES - 1, fut + ABYTES);
-    half8 fa[FM], fb[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[i] = *(const half8*)(cur + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, 0, SHIFT, RB));
+    for (int ks = 0; ks < KS; ++ks) {
+      half8 fa[FM], fb[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[j] = *(const half8*)(cur + ABYTES + fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, 0, SHIFT, RB));
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
+        fa[i] = *(const half8*)(cur + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, ks, SHIFT, RB));
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        fb[j] = *(const half8*)(cur + ABYTES + fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, ks, SHIFT, RB));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
     // tile t+1 landed (this wave's part); the barrier publishes every
-    // wave's part and retires tile t's buffer
+    // wave's part and, with this wave's LDS reads complete, retires tile t's
+    // buffer
     wait_vmem_n<(STAGES - 2) * LOADS>();
-    __syncthreads();
+    phase_barrier();
   }
+  // the out-of-range copies past the last tile still target this
+  // workgroup's LDS: let them land before the workgroup can end
+  wait_vmem();
   epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
 }
 
@@ -613,14 +629,14 @@ hipError_t launch_cfg(const GemmParams& p, int32_t shift, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, int RB = 64>
 hipError_t launch_ms(const GemmParams& p, int32_t shift, hipStream_t s) {
   const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
   dim3 grid((uint32_t)total), block(WM * WN * 64);
   switch (shift) {
-    case 0: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 0>), grid, block, 0, s, p); break;
-    case 1: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 1>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 2>), grid, block, 0, s, p); break;
+    case 0: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 0, RB>), grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 1, RB>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 2, RB>), grid, block, 0, s, p); break;
   }
   return hipGetLastError();
 }
@@ -662,6 +678,7 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
       case T256x256_W2x4_S3: return launch_ms<256, 256, 2, 4, 3>(p, shift, s);
       case T256x256_W2x4_S4: return launch_ms<256, 256, 2, 4, 4>(p, shift, s);
       case T256x256_W2x4_S5: return launch_ms<256, 256, 2, 4, 5>(p, shift, s);
+      case T32x128_STREAM: return launch_ms<32, 128, 1, 4, 6, 128>(p, shift, s);
       case T256x256_PPG: {
         const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
         if (shift == 0)

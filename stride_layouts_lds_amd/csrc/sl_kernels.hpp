@@ -40,7 +40,8 @@ enum TileCfg : int32_t {
   T256x256_PPC4 = 12,   // ping-pong, 4 stages, copy spread over all waves' compute phases
   T256x256_PPC5 = 13,   // same with 5 stages
   T256x256_PPG = 14,    // ping-pong, 2 stages of 64-wide K-tiles, group 1 copies inside its compute phase
-  T_COUNT = 15
+  T32x128_STREAM = 15,  // 4 waves along N, each 32x32; 6 stages of 64-wide K-tiles (skinny outputs)
+  T_COUNT = 16
 };
 
 struct TileShape {
@@ -52,7 +53,8 @@ constexpr TileShape kTiles[T_COUNT] = {
     {128, 128, 2, 2, 64, 2}, {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 64, 2},
     {256, 256, 2, 4, 32, 3}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
     {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
-    {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5}, {256, 256, 2, 4, 64, 2}};
+    {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5}, {256, 256, 2, 4, 64, 2},
+    {32, 128, 1, 4, 64, 6}};
 
 struct GemmParams {
   const void* a;  // element (b, m, k) at a + b*a_bs + m*a_rs + k*a_ks

@@ -80,16 +80,24 @@ SL_HD constexpr Coord scale_map(int32_t instr, int32_t lane) {
 // XOR-swizzled with bits of the row so that the lanes of one ds_read_b128
 // pass land on distinct banks:
 //   offset(row, b) = row*RB + 16*(c ^ swz(row)) + b%16
-// with swz(row) = (row >> shift) & (RB/16 - 1).  For RB = 128 and shift 0
-// this is the pages' SWIZZLE_128B rule (row-in-8 XOR the 16-byte chunk).
-// The rule is a bijection on every block of (RB/16) << shift rows, and the
-// writer (loader) and the reader (fragment load) call this one function.
+// with swz(row) = ((row >> shift) ^ ((row >> (shift + 4)) & 1)) & (RB/16 - 1).
+// For RB = 128 and shift 0 the first term is the pages' SWIZZLE_128B rule
+// (row-in-8 XOR the 16-byte chunk, Swizzle<3,4,3> on byte offsets); the
+// second flips chunk bit 0 on rows 16-31 of every 32 (Swizzle<1,4,7>
+// composed on top).  gfx950 serves a ds_read_b128 in passes that pair
+// lanes 0-7 with 16-23 (and 8-15 with 24-31, ...) over 64 banks of 4 bytes;
+// the 32-row instructions put rows r and r + 16 of one chunk into one pass,
+// which SWIZZLE_128B alone sends to the same banks (a 2-way conflict on
+// every fragment read, seen in the LDS conflict counter).  The extra flip
+// separates them and leaves the 16-row patterns conflict-free.  Any per-row
+// XOR is a bijection on the row's chunks, and the writer (loader) and the
+// reader (fragment load) call this one function.
 // ---------------------------------------------------------------------------
 
 constexpr int32_t kRowBytes = 128;
 
 SL_HD constexpr int32_t swz(int32_t row, int32_t shift, int32_t row_bytes = kRowBytes) {
-  return (row >> shift) & (row_bytes / 16 - 1);
+  return ((row >> shift) ^ ((row >> (shift + 4)) & 1)) & (row_bytes / 16 - 1);
 }
 
 SL_HD constexpr int32_t lds_offset(int32_t row, int32_t byte_in_row, int32_t shift,

@@ -64,6 +64,25 @@ def test_exact_integer_parity(api, case):
     assert mism == 0, f"{mism} elements differ"
 
 
+# every fp16 tile configuration the planner can be told to use (SL_TILE),
+# on K-contiguous operands, over several output tiles with ragged edges
+F16_TILES = list(range(16))
+
+
+@pytest.mark.parametrize("tile", F16_TILES)
+def test_exact_parity_every_fp16_tile(api, tile, monkeypatch):
+    h = H()
+    monkeypatch.setenv("SL_TILE", str(tile))
+    w = I.gemm_workload("tiles", 520, 300, 328, seed=tile, dist="int4", with_c=True)
+    plan = _plan(api, w)
+    h.log(f"tile {tile} plan={plan}")
+    assert plan["kernel"] == api.K_F16
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
 def _plan(api, w):
     import torch
     h = H()
