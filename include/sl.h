@@ -36,15 +36,24 @@
  *    address range with A, B, C or the scales returns SL_ERR_ALIAS.
  *  - M == 0 or N == 0 (or batch == 0) is a no-op returning SL_OK.  K == 0
  *    gives D = C (or D = 0).
- *  - Ownership: the caller owns every buffer; sl_gemm() neither allocates,
- *    frees nor retains device memory, and keeps no pointer after it returns.
+ *  - Ownership: the caller owns every buffer and sl_gemm() keeps no pointer
+ *    after it returns.  The one allocation the library makes is the fp32
+ *    workspace of a split-K plan (sl_plan.split_k > 1): it comes from a
+ *    library-private stream-ordered pool on the current device and is
+ *    allocated and freed on `stream` around the two kernels (so calls on
+ *    different streams never share one); the pool keeps freed memory for
+ *    reuse until the process ends.  Its failure returns SL_ERR_NOMEM.
  *  - Execution: validation runs on the host before any HIP call; a failure
  *    returns a negative sl_status and sets the thread-local message.  On
  *    success the kernel is launched asynchronously on `stream` (a
  *    hipStream_t; NULL is the default stream) and the call returns without
- *    waiting.  Errors reported by the launch return SL_ERR_LAUNCH.
+ *    waiting.  Errors reported by the launch return SL_ERR_LAUNCH.  A
+ *    split-K plan launches two kernels (partial sums, then D = C + their
+ *    sum) on the same stream.
  *  - Numerics: fp16 products are accumulated in fp32; the result (plus C,
  *    added in fp32) is rounded to fp16 to nearest-even, overflow to +-inf.
+ *    A split-K plan sums each K-split in fp32 and then adds the splits in
+ *    fp32 (a different summation order, same precision).
  */
 #ifndef STRIDE_LAYOUTS_LDS_SL_H
 #define STRIDE_LAYOUTS_LDS_SL_H
@@ -74,7 +83,8 @@ typedef enum {
   SL_ERR_ALIAS = -6,  /* D overlaps an input (other than C == D exactly) */
   SL_ERR_ARCH = -7,   /* the current device is not gfx950 */
   SL_ERR_LAUNCH = -8, /* the HIP runtime reported an error */
-  SL_ERR_ARG = -9     /* an invalid enum or query argument */
+  SL_ERR_ARG = -9,    /* an invalid enum or query argument */
+  SL_ERR_NOMEM = -10  /* the split-K workspace could not be allocated */
 } sl_status;
 
 /* A shape:stride layout S[(shape):(stride)], counted in elements. */
@@ -110,7 +120,8 @@ typedef struct {
   int32_t b_load;     /* same, for B */
   int32_t tile_m, tile_n, tile_k;
   int32_t threads;    /* per workgroup */
-  int32_t split_k;    /* K partitions (1: none) */
+  int32_t split_k;    /* K partitions (1: none); > 1 adds a workspace of
+                         split_k * batch * m * n fp32 and a reduction kernel */
   int64_t workgroups; /* total workgroups launched */
   int32_t lds_bytes;  /* LDS per workgroup */
   int64_t batch, m, n, k;

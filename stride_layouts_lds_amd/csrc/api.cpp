@@ -118,6 +118,7 @@ struct Plan {
   int32_t shift;
   bool mx;
   bool empty;
+  size_t ws_bytes;  // split-K partial sums (0: none)
 };
 
 int32_t env_int(const char* name, int32_t dflt) {
@@ -277,6 +278,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     p.flags |= sl::F_D_VEC;
   if (has_c && C.cs == 1 && C.rs % 4 == 0 && (uintptr_t)C.t->data % 8 == 0 && (batch == 1 || p.c_bs % 4 == 0))
     p.flags |= sl::F_C_VEC;
+  p.splits = 1;
+  p.split_tiles = 0;
   P.shift = std::min(2, std::max(0, env_int("SL_SWZ", 0)));
   p.group_m = std::max(1, env_int("SL_GROUP_M", 8));
 
@@ -327,6 +330,21 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       // K-contiguous operands only; among the automatic choices the 8-wave
       // 256x256 kernel replaces the 4-wave one for them
       const bool kk = la == sl::LOAD_KVEC && lb == sl::LOAD_KVEC;
+      // Split-K for outputs that leave most of the chip idle even in
+      // 128x128 tiles (a skinny N, a small M x N with a long K): up to 8
+      // K-splits, each at least 4 K-tiles of 64, towards 256 workgroups.
+      const int64_t T_all = (K + 63) / 64;
+      const int64_t t128 = batch * ((M + 127) / 128) * ((N + 127) / 128);
+      const int64_t auto_splits =
+          std::max<int64_t>(1, std::min<int64_t>({8, 256 / std::max<int64_t>(1, t128), T_all / 4}));
+      if (kk && tile < 0 && t128 < 128 && auto_splits >= 2) tile = sl::T128x128_SPLITK;
+      if (tile == sl::T128x128_SPLITK && kk) {
+        int64_t splits = env_int("SL_SPLITK", 0) > 0 ? env_int("SL_SPLITK", 0) : auto_splits;
+        splits = std::max<int64_t>(1, std::min<int64_t>(splits, std::max<int64_t>(T_all, 1)));
+        const int64_t per = (std::max<int64_t>(T_all, 1) + splits - 1) / splits;
+        p.split_tiles = (int32_t)per;
+        p.splits = (int32_t)((std::max<int64_t>(T_all, 1) + per - 1) / per);
+      }
       if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T128x128_W2x2)) {
         const int32_t big = kk ? sl::T256x256_W2x4 : sl::T256x256_W2x2;
         tile = big;
@@ -349,15 +367,45 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.tile = tile;
   p.tiles_m = (int32_t)((M + ts.bm - 1) / ts.bm);
   p.tiles_n = (int32_t)((N + ts.bn - 1) / ts.bn);
-  const int64_t total = batch * p.tiles_m * p.tiles_n;
+  const int64_t total = batch * p.tiles_m * p.tiles_n * p.splits;
   if (total >= lim) return fail(SL_ERR_SHAPE, "too many output tiles (%lld)", (long long)total);
   P.pub.tile_m = ts.bm;
   P.pub.tile_n = ts.bn;
   P.pub.threads = ts.wm * ts.wn * 64;
-  P.pub.split_k = 1;
+  P.pub.split_k = p.splits;
   P.pub.workgroups = total;
+  P.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)M * (size_t)N * sizeof(float) : 0;
   P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * P.pub.tile_k * (mx ? 1 : 2);
   if (P.pub.kernel == sl::K_MX_W8) P.pub.lds_bytes += ts.stages * (ts.bm + ts.bn) * 4;
+  return SL_OK;
+}
+
+// The library's stream-ordered memory pool on the current device (split-K
+// workspaces come from it and go back to it on the launch stream, so calls
+// on different streams never share one).  It keeps freed memory for reuse
+// until the process ends.
+sl_status workspace_pool(hipMemPool_t* out) {
+  static std::mutex mu;
+  static hipMemPool_t pools[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SL_ERR_LAUNCH, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(SL_ERR_ARCH, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> g(mu);
+  if (!pools[dev]) {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof props);
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool;
+    hipError_t e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return fail(SL_ERR_NOMEM, "hipMemPoolCreate: %s", hipGetErrorString(e));
+    uint64_t keep = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) return fail(SL_ERR_NOMEM, "hipMemPoolSetAttribute: %s", hipGetErrorString(e));
+    pools[dev] = pool;
+  }
+  *out = pools[dev];
   return SL_OK;
 }
 
@@ -398,6 +446,7 @@ const char* sl_status_string(int32_t s) {
     case SL_ERR_ARCH: return "device is not gfx950";
     case SL_ERR_LAUNCH: return "HIP launch error";
     case SL_ERR_ARG: return "invalid argument";
+    case SL_ERR_NOMEM: return "device memory for a workspace could not be obtained";
     default: return "unknown status";
   }
 }
@@ -418,10 +467,23 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
   if ((s = check_arch()) != SL_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (P.mx)
+  if (P.mx) {
     e = sl::launch_gemm_mx(P.p, P.tile, P.shift, st);
-  else
+  } else if (P.ws_bytes) {
+    hipMemPool_t pool;
+    if ((s = workspace_pool(&pool)) != SL_OK) return s;
+    void* ws = nullptr;
+    e = hipMallocFromPoolAsync(&ws, P.ws_bytes, pool, st);
+    if (e != hipSuccess)
+      return fail(SL_ERR_NOMEM, "split-K workspace of %zu bytes: %s", P.ws_bytes, hipGetErrorString(e));
+    P.p.ws = (float*)ws;
     e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, P.shift, st);
+    if (e == hipSuccess) e = sl::launch_splitk_reduce(P.p, st);
+    const hipError_t ef = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = ef;
+  } else {
+    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, P.shift, st);
+  }
   if (e != hipSuccess) return fail(SL_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return SL_OK;
 }

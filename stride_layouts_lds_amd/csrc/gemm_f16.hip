@@ -32,6 +32,31 @@ __device__ __forceinline__ void epilogue(const floatx4 (&acc)[FM][FN], const Gem
       store_quad(p, C, D, m_base + 16 * i + (lane & 15), n_base + 16 * j + 4 * (lane >> 4), acc[i][j]);
 }
 
+// Split-K partial: acc[i][j] (same layout as the epilogue's) goes to
+// ws[split][batch][m][n] in fp32, 16-byte stores where the row allows.
+template <int FM, int FN>
+__device__ __forceinline__ void store_partial(const floatx4 (&acc)[FM][FN], const GemmParams& p, int32_t split,
+                                              int32_t batch, int64_t m_base, int64_t n_base, int32_t lane) {
+  float* W = p.ws + ((int64_t)split * p.batch + batch) * p.M * p.N;
+  const bool vec = (p.N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t m = m_base + 16 * i + (lane & 15);
+      const int64_t n = n_base + 16 * j + 4 * (lane >> 4);
+      if (m >= p.M || n >= p.N) continue;
+      float* w = W + m * p.N + n;
+      if (vec) {
+        *(floatx4*)w = acc[i][j];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < p.N) w[r] = acc[i][j][r];
+      }
+    }
+}
+
 // PIPE 0: per k-slice, read the fragments then issue the MFMAs (latency is
 // covered by the other wave on the SIMD when WM*WN = 8).  PIPE 1: two
 // fragment sets, the next slice is read while the current one computes.
@@ -48,7 +73,7 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t wm = wave % WM, wn = wave / WM;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
@@ -177,7 +202,7 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t wm = wave % WM, wn = wave / WM;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
@@ -193,12 +218,17 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int32_t a_row0 = wm * TM, b_row0 = wn * TN;
 
-  const int32_t T = (int32_t)((p.K + KT - 1) / KT);
+  // K-tiles [t0, t0 + T) of this workgroup: all of K, or one split's share
+  const int32_t T_all = (int32_t)((p.K + KT - 1) / KT);
+  const int32_t t0 = tc.split * p.split_tiles;
+  const int32_t T = p.splits > 1 ? (T_all - t0 < p.split_tiles ? T_all - t0 : p.split_tiles) : T_all;
+  // the u-th tile of the range; past its end, a tile fully out of range
+  auto ktile = [&](int32_t u) { return u < T ? t0 + u : T_all; };
   // prologue: tiles 0 .. STAGES-2 in flight, wait for tile 0
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
-    la.issue(s, smem + s * STAGE);
-    lb.issue(s, smem + s * STAGE + ABYTES);
+    la.issue(ktile(s), smem + s * STAGE);
+    lb.issue(ktile(s), smem + s * STAGE + ABYTES);
   }
   wait_vmem_n<(STAGES - 2) * LOADS>();
   phase_barrier();
@@ -208,8 +238,8 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
     char* fut = smem + ((t + STAGES - 1) % STAGES) * STAGE;
     // the buffer of tile t-1 is retired (barrier at the end of t-1): refill
     // it with tile t+STAGES-1 (fully out of range past the last tile)
-    la.issue(t + STAGES - 1, fut);
-    lb.issue(t + STAGES - 1, fut + ABYTES);
+    la.issue(ktile(t + STAGES - 1), fut);
+    lb.issue(ktile(t + STAGES - 1), fut + ABYTES);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       half8 fa[FM], fb[FN];
@@ -234,7 +264,39 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
   // the out-of-range copies past the last tile still target this
   // workgroup's LDS: let them land before the workgroup can end
   wait_vmem();
-  epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  if (p.splits > 1)
+    store_partial<FM, FN>(acc, p, tc.split, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  else
+    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+}
+
+// D = fp16(C + sum_s ws[s]) over every output, four consecutive n per
+// thread (grid-stride).  The partial planes are [batch][M][N] fp32,
+// contiguous.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
+  const int64_t nq = (p.N + 3) / 4;
+  const int64_t total = (int64_t)p.batch * p.M * nq;
+  const int64_t plane = (int64_t)p.batch * p.M * p.N;
+  const bool vec = (p.N & 3) == 0;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
+    const int64_t n = (q % nq) * 4;
+    const int64_t bm = q / nq;
+    const int64_t m = bm % p.M;
+    const int32_t b = (int32_t)(bm / p.M);
+    const float* w = p.ws + (b * p.M + m) * p.N + n;
+    floatx4 v = {0.f, 0.f, 0.f, 0.f};
+    if (vec) {
+      for (int32_t sp = 0; sp < p.splits; ++sp) v += *(const floatx4*)(w + sp * plane);
+    } else {
+      for (int32_t sp = 0; sp < p.splits; ++sp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < p.N) v[r] += w[sp * plane + r];
+    }
+    uint16_t* D = (uint16_t*)p.d + b * p.d_bs;
+    const uint16_t* C = (p.flags & F_HAS_C) ? (const uint16_t*)p.c + b * p.c_bs : nullptr;
+    store_quad(p, C, D, m, n, v);
+  }
 }
 
 // Ping-pong variant for K-contiguous operands, 256x256 tile, 8 waves.
@@ -265,7 +327,7 @@ __global__ __launch_bounds__(512, 2) void gemm_f16_pp_kernel(const GemmParams p)
   const int32_t grp = wave >> 2;
   const int32_t wm = wave & 1, wn = wave >> 1;  // group 0: wn 0,1; group 1: wn 2,3
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
@@ -355,7 +417,7 @@ __global__ __launch_bounds__(512, 2) void gemm_f16_pps_kernel(const GemmParams p
   const int32_t grp = wave >> 2;
   const int32_t wm = wave & 1, wn = wave >> 1;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
@@ -446,7 +508,7 @@ __global__ __launch_bounds__(512, 2) void gemm_f16_pps2_kernel(const GemmParams 
   const int32_t grp = wave >> 2;
   const int32_t wm = wave & 1, wn = wave >> 1;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
@@ -543,7 +605,7 @@ __global__ __launch_bounds__(512, 2) void gemm_f16_ppg_kernel(const GemmParams p
   const int32_t grp = wave >> 2;
   const int32_t wm = wave & 1, wn = wave >> 1;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
@@ -631,7 +693,7 @@ hipError_t launch_cfg(const GemmParams& p, int32_t shift, hipStream_t s) {
 
 template <int BM, int BN, int WM, int WN, int STAGES, int RB = 64>
 hipError_t launch_ms(const GemmParams& p, int32_t shift, hipStream_t s) {
-  const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
+  const int64_t total = (int64_t)p.splits * p.batch * p.tiles_m * p.tiles_n;
   dim3 grid((uint32_t)total), block(WM * WN * 64);
   switch (shift) {
     case 0: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 0, RB>), grid, block, 0, s, p); break;
@@ -656,6 +718,13 @@ hipError_t launch_tile(const GemmParams& p, int32_t tile, int32_t shift, hipStre
 
 }  // namespace
 
+hipError_t launch_splitk_reduce(const GemmParams& p, hipStream_t s) {
+  const int64_t total = (int64_t)p.batch * p.M * ((p.N + 3) / 4);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load,
                            int32_t shift, hipStream_t s) {
   if (a_load == LOAD_GENERIC || b_load == LOAD_GENERIC) {
@@ -679,6 +748,7 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
       case T256x256_W2x4_S4: return launch_ms<256, 256, 2, 4, 4>(p, shift, s);
       case T256x256_W2x4_S5: return launch_ms<256, 256, 2, 4, 5>(p, shift, s);
       case T32x128_STREAM: return launch_ms<32, 128, 1, 4, 6, 128>(p, shift, s);
+      case T128x128_SPLITK: return launch_ms<128, 128, 2, 2, 4, 128>(p, shift, s);
       case T256x256_PPG: {
         const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
         if (shift == 0)

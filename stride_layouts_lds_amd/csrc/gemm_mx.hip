@@ -30,7 +30,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_mx_kernel(const GemmParam
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t wm = wave % WM, wn = wave / WM;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t wm = wave % WM, wn = wave / WM;
 
-  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m);
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);

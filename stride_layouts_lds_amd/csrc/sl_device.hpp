@@ -67,15 +67,21 @@ __device__ __forceinline__ void wait_vmem_n() {
 // resident on one XCD share A rows and B columns in that XCD's L2.
 // ---------------------------------------------------------------------------
 struct TileCoord {
-  int32_t batch, tm, tn;
+  int32_t batch, tm, tn, split;
 };
 
+// `total` workgroups hold `total / (batch * tiles_m * tiles_n)` K-splits of
+// the output tiles; the splits are the slowest-varying index, so the
+// workgroups of one split (which read the same K range of a shared
+// operand) sit on neighbouring XCD ranges.
 __device__ __forceinline__ TileCoord map_tile(int32_t bid, int32_t total, int32_t tiles_m, int32_t tiles_n,
-                                              int32_t group_m) {
+                                              int32_t group_m, int32_t batch) {
   const int32_t x = bid & 7, local = bid >> 3;
   const int32_t q = total >> 3, r = total & 7;
-  const int32_t id = x * q + (x < r ? x : r) + local;
+  int32_t id = x * q + (x < r ? x : r) + local;
   const int32_t per_batch = tiles_m * tiles_n;
+  const int32_t split = id / (batch * per_batch);
+  id -= split * batch * per_batch;
   const int32_t b = id / per_batch;
   const int32_t t = id - b * per_batch;
   const int32_t span = group_m * tiles_n;
@@ -84,7 +90,7 @@ __device__ __forceinline__ TileCoord map_tile(int32_t bid, int32_t total, int32_
   const int32_t left = tiles_m - first_m;
   const int32_t gsz = left < group_m ? left : group_m;
   const int32_t in = t - g * span;
-  return TileCoord{b, first_m + in % gsz, in / gsz};
+  return TileCoord{b, first_m + in % gsz, in / gsz, split};
 }
 
 // ---------------------------------------------------------------------------

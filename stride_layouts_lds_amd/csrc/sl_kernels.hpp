@@ -41,7 +41,8 @@ enum TileCfg : int32_t {
   T256x256_PPC5 = 13,   // same with 5 stages
   T256x256_PPG = 14,    // ping-pong, 2 stages of 64-wide K-tiles, group 1 copies inside its compute phase
   T32x128_STREAM = 15,  // 4 waves along N, each 32x32; 6 stages of 64-wide K-tiles (skinny outputs)
-  T_COUNT = 16
+  T128x128_SPLITK = 16, // 4 waves, each 64x64; 4 stages of 64-wide K-tiles; K split over workgroups
+  T_COUNT = 17
 };
 
 struct TileShape {
@@ -54,7 +55,7 @@ constexpr TileShape kTiles[T_COUNT] = {
     {256, 256, 2, 4, 32, 3}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
     {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
     {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5}, {256, 256, 2, 4, 64, 2},
-    {32, 128, 1, 4, 64, 6}};
+    {32, 128, 1, 4, 64, 6}, {128, 128, 2, 2, 64, 4}};
 
 struct GemmParams {
   const void* a;  // element (b, m, k) at a + b*a_bs + m*a_rs + k*a_ks
@@ -75,6 +76,12 @@ struct GemmParams {
   int32_t group_m;
   int32_t k_tiles;
   int32_t flags;
+  // split-K: the grid holds `splits` copies of the output tiles, copy s
+  // covering K-tiles [s*split_tiles, (s+1)*split_tiles); each writes fp32
+  // partial sums to ws[s][batch][M][N] and a second kernel reduces them
+  int32_t splits;       // 1: no split
+  int32_t split_tiles;  // K-tiles per split
+  float* ws;
 };
 
 // GemmParams.flags
@@ -85,6 +92,8 @@ constexpr int32_t F_C_VEC = 4;  // C rows contiguous and 8-B aligned: 4-half loa
 // Launchers (each returns the launch's hipError_t).
 hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load,
                            int32_t swz_shift, hipStream_t stream);
+// D = C + sum over splits of ws (the second kernel of a split-K GEMM).
+hipError_t launch_splitk_reduce(const GemmParams& p, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, int32_t swz_shift, hipStream_t stream);
 
 hipError_t launch_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t cases, hipStream_t stream);

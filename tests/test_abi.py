@@ -263,3 +263,15 @@ def test_fragment_reads_conflict_free_on_gfx950(api, variant, slots_per_piece):
     # the plain rule on the 32-row f8 instruction: rows r and r + 16 collide
     plain = [L.swizzle_bms(r * 128 + c, 3, 4, 3) for _, v, r, c in L.MFMA32_F8_A.table() if v == 0]
     assert _gfx950_b128_passes(plain) == 8
+
+
+def test_plan_split_k_for_skinny_outputs(api):
+    """An 8192 x 128 x 8192 output fills 64 tiles of 128 x 128: the planner
+    splits K four ways (256 workgroups); a square 4096^3 is not split."""
+    p = plan(api, rowmajor(BASE_A, (8192, 8192)), rowmajor(BASE_B, (128, 8192)), None, rowmajor(BASE_D, (8192, 128)))
+    assert (p["split_k"], p["tile_m"], p["tile_n"], p["workgroups"]) == (4, 128, 128, 256)
+    p = plan(api, rowmajor(BASE_A, (4096, 4096)), rowmajor(BASE_B, (4096, 4096)), None, rowmajor(BASE_D, (4096, 4096)))
+    assert p["split_k"] == 1
+    # short K: no split (fewer than 4 K-tiles of 64 per split)
+    p = plan(api, rowmajor(BASE_A, (256, 256)), rowmajor(BASE_B, (256, 256)), None, rowmajor(BASE_D, (256, 256)))
+    assert p["split_k"] == 1

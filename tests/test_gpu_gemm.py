@@ -83,6 +83,60 @@ def test_exact_parity_every_fp16_tile(api, tile, monkeypatch):
     assert mism == 0, f"{mism} elements differ"
 
 
+SPLITK = [
+    # M, N, K, batch, with_c, forced split count (0: the planner's), expected splits
+    (300, 72, 2056, None, True, 0, 7),    # 33 K-tiles: 7 splits of 5 (the last of 3)
+    (130, 120, 1032, 2, False, 3, 3),
+    (200, 70, 1000, None, True, 5, 4),    # N % 4 != 0: scalar partial stores; 16 K-tiles in 4 splits of 4
+    (64, 64, 4096, None, False, 0, 8),
+    (520, 136, 776, None, True, 2, 2),    # ragged last split (13 K-tiles: 7 + 6)
+]
+
+
+@pytest.mark.parametrize("case", SPLITK, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_s{c[6]}")
+def test_splitk_exact_parity(api, case, monkeypatch):
+    h = H()
+    M, N, K, batch, with_c, force, want = case
+    monkeypatch.setenv("SL_TILE", "16")
+    if force:
+        monkeypatch.setenv("SL_SPLITK", str(force))
+    w = I.gemm_workload("splitk", M, N, K, seed=M + K, dist="int4", batch=batch, with_c=with_c)
+    import torch
+    out = torch.empty(w.d_shape, dtype=torch.float16, device="cuda")
+    args = api.make_args(h.to_device(w.a), h.to_device(w.b), h.to_device(w.c), out, None, None, 32)
+    plan = api.sl_gemm_plan(args)
+    h.log(f"splitk {case} plan={plan}")
+    assert plan["split_k"] == want and plan["tile_m"] == plan["tile_n"] == 128
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
+def test_splitk_in_place_and_repeated_calls(api, monkeypatch):
+    """C == D in place through a split-K plan, then the same call again on
+    another stream: each call gets its own workspace from the pool."""
+    import torch
+    h = H()
+    monkeypatch.setenv("SL_TILE", "16")
+    monkeypatch.setenv("SL_SPLITK", "4")
+    w = I.gemm_workload("splitk_inplace", 264, 96, 1024, seed=9, dist="int4", with_c=True)
+    a, b = h.to_device(w.a), h.to_device(w.b)
+    d = h.to_device(w.c).contiguous().clone()
+    api.gemm(a, b, d, out=d)
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        d2 = torch.zeros_like(d)
+        api.gemm(a, b, None, out=d2, stream=s2.cuda_stream)
+    torch.cuda.synchronize()
+    d_ref, _, _ = h.oracle_full(w)
+    assert np.array_equal(h.d_codes(d), d_ref[0])
+    w0 = I.gemm_workload("splitk_inplace", 264, 96, 1024, seed=9, dist="int4", with_c=True)
+    w0.c = None
+    d0_ref, _, _ = h.oracle_full(w0)
+    assert np.array_equal(h.d_codes(d2), d0_ref[0])
+
+
 def _plan(api, w):
     import torch
     h = H()
