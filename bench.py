@@ -12,7 +12,8 @@ Default workload: fp16 TN GEMM M = N = K = 8192 with C (normal(0,1) inputs,
 seed 1) -- the large square case the fp16 throughput target is stated on.
 Other workloads (for measurement only): fp16_4096 (the same recipe at 4096),
 ragged (4000x3000x2056), skinny (8192x128x8192), batched_nn / batched_nt
-(64 x 512^3, A M-contiguous), mxfp8 (8192^3 MXFP8).
+(64 x 512^3, A M-contiguous), batched_tn / batched_tt (A K-contiguous),
+mxfp8 (8192^3 MXFP8).
 
 The CPU baseline is the oracle (plain fp64 triple loop, all host cores) on a
 bounded sample of output points of the same workload, scaled to TFLOP/s.
@@ -45,6 +46,8 @@ def workloads():
         "skinny": ("fp16 TN GEMM 8192x128x8192, uniform[-1,1], C=0, seed 2", lambda: I.config3()[1]),
         "batched_nn": ("fp16 batched 64x512^3, A M-contiguous, B K-contiguous, seed 3", lambda: I.config4("NN")),
         "batched_nt": ("fp16 batched 64x512^3, A M-contiguous, B N-contiguous, seed 3", lambda: I.config4("NT")),
+        "batched_tn": ("fp16 batched 64x512^3, A and B K-contiguous, seed 3", lambda: I.config4("TN")),
+        "batched_tt": ("fp16 batched 64x512^3, A K-contiguous, B N-contiguous, seed 3", lambda: I.config4("TT")),
         "mxfp8": ("MXFP8 GEMM M=N=K=8192, E4M3 data, E8M0 scale per 32 K, C=0, seed 4", lambda: I.config5(8192)),
     }
 

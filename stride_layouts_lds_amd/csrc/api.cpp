@@ -326,9 +326,10 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       tile = sl::T128x128_W2x2;
       P.pub.kernel = sl::K_F16_GENERIC;
     } else {
-      // the 8-wave, multi-stage and ping-pong variants exist for
-      // K-contiguous operands only; among the automatic choices the 8-wave
-      // 256x256 kernel replaces the 4-wave one for them
+      // the multi-stage, ping-pong, streaming and split-K variants exist
+      // for K-contiguous operands only; the 8-wave 256x256 kernel also for
+      // M- (N-) contiguous ones, and among the automatic choices it
+      // replaces the 4-wave 256x256 one
       const bool kk = la == sl::LOAD_KVEC && lb == sl::LOAD_KVEC;
       // Split-K for outputs that leave most of the chip idle even in
       // 128x128 tiles (a skinny N, a small M x N with a long K): up to 8
@@ -345,8 +346,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
         p.split_tiles = (int32_t)per;
         p.splits = (int32_t)((std::max<int64_t>(T_all, 1) + per - 1) / per);
       }
-      if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T128x128_W2x2)) {
-        const int32_t big = kk ? sl::T256x256_W2x4 : sl::T256x256_W2x2;
+      if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T256x256_W2x4_P)) {
+        const int32_t big = sl::T256x256_W2x4;
         tile = big;
         double best = 1e300;
         for (int t : {big, (int32_t)sl::T256x128_W2x2, (int32_t)sl::T128x256_W2x2, (int32_t)sl::T128x128_W2x2,

@@ -748,7 +748,7 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
       case T256x256_W2x4_S4: return launch_ms<256, 256, 2, 4, 4>(p, shift, s);
       case T256x256_W2x4_S5: return launch_ms<256, 256, 2, 4, 5>(p, shift, s);
       case T32x128_STREAM: return launch_ms<32, 128, 1, 4, 6, 128>(p, shift, s);
-      case T128x128_SPLITK: return launch_ms<128, 128, 2, 2, 4, 128>(p, shift, s);
+      case T128x128_SPLITK: return launch_ms<128, 128, 2, 4, 3, 128>(p, shift, s);
       case T256x256_PPG: {
         const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
         if (shift == 0)
@@ -798,7 +798,7 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
       default: return launch_tile<LOAD_KVEC, LOAD_KVEC>(p, tile, shift, s);
     }
   }
-  if (tile > T128x128_W2x2) return hipErrorInvalidValue;
+  if (tile > T256x256_W2x4_P) return hipErrorInvalidValue;
   if (a_load == LOAD_MNVEC && b_load == LOAD_KVEC) return launch_tile<LOAD_MNVEC, LOAD_KVEC>(p, tile, shift, s);
   if (a_load == LOAD_KVEC && b_load == LOAD_MNVEC) return launch_tile<LOAD_KVEC, LOAD_MNVEC>(p, tile, shift, s);
   if (a_load == LOAD_MNVEC && b_load == LOAD_MNVEC)
