@@ -155,6 +155,7 @@ double tile_cost(const sl::TileShape& t, int64_t batch, int64_t M, int64_t N, in
   // the streaming tile moves 5x the L2 bytes per MFMA of a 256x256 tile:
   // worth it only where the big tiles leave most of the chip idle
   const double eff = (t.bm == 256 && t.bn == 256) ? 1.0
+                     : (t.bm == 256 && t.bn == 192) ? 0.96
                      : (t.bm * t.bn == 256 * 128) ? 0.92
                      : (t.bm * t.bn == 128 * 128) ? 0.80
                                                   : 0.50;
@@ -350,9 +351,9 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
         const int32_t big = sl::T256x256_W2x4;
         tile = big;
         double best = 1e300;
-        for (int t : {big, (int32_t)sl::T256x128_W2x2, (int32_t)sl::T128x256_W2x2, (int32_t)sl::T128x128_W2x2,
-                      (int32_t)sl::T32x128_STREAM}) {
-          if (t == sl::T32x128_STREAM && !kk) continue;
+        for (int t : {big, (int32_t)sl::T256x192_W2x4, (int32_t)sl::T256x128_W2x2, (int32_t)sl::T128x256_W2x2,
+                      (int32_t)sl::T128x128_W2x2, (int32_t)sl::T32x128_STREAM}) {
+          if ((t == sl::T32x128_STREAM || t == sl::T256x192_W2x4) && !kk) continue;
           const double c = tile_cost(sl::kTiles[t], batch, M, N, K);
           if (c < best) best = c, tile = t;
         }

@@ -749,6 +749,7 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
       case T256x256_W2x4_S5: return launch_ms<256, 256, 2, 4, 5>(p, shift, s);
       case T32x128_STREAM: return launch_ms<32, 128, 1, 4, 6, 128>(p, shift, s);
       case T128x128_SPLITK: return launch_ms<128, 128, 2, 4, 3, 128>(p, shift, s);
+      case T256x192_W2x4: return launch_cfg<256, 192, 2, 4, LOAD_KVEC, LOAD_KVEC, 0>(p, shift, s);
       case T256x256_PPG: {
         const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
         if (shift == 0)

@@ -42,7 +42,8 @@ enum TileCfg : int32_t {
   T256x256_PPG = 14,    // ping-pong, 2 stages of 64-wide K-tiles, group 1 copies inside its compute phase
   T32x128_STREAM = 15,  // 4 waves along N, each 32x32; 6 stages of 64-wide K-tiles (skinny outputs)
   T128x128_SPLITK = 16, // 8 waves, each 64x32; 3 stages of 64-wide K-tiles; K split over workgroups
-  T_COUNT = 17
+  T256x192_W2x4 = 17,   // 8 waves, each 128x48 (fills the chip on ~4000 x 3000 outputs)
+  T_COUNT = 18
 };
 
 struct TileShape {
@@ -55,7 +56,7 @@ constexpr TileShape kTiles[T_COUNT] = {
     {256, 256, 2, 4, 32, 3}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
     {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
     {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5}, {256, 256, 2, 4, 64, 2},
-    {32, 128, 1, 4, 64, 6}, {128, 128, 2, 4, 64, 3}};
+    {32, 128, 1, 4, 64, 6}, {128, 128, 2, 4, 64, 3}, {256, 192, 2, 4, 64, 2}};
 
 struct GemmParams {
   const void* a;  // element (b, m, k) at a + b*a_bs + m*a_rs + k*a_ks

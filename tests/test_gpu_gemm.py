@@ -66,7 +66,7 @@ def test_exact_integer_parity(api, case):
 
 # every fp16 tile configuration the planner can be told to use (SL_TILE),
 # on K-contiguous operands, over several output tiles with ragged edges
-F16_TILES = list(range(17))
+F16_TILES = list(range(18))
 
 
 @pytest.mark.parametrize("tile", F16_TILES)
