@@ -116,7 +116,9 @@ typedef struct {
   int32_t kernel;     /* kernel family: 1 fp16 fast, 2 fp16 generic, 3 mxfp8
                          (4 waves, 16x16x128 instruction), 4 mxfp8 (8 waves,
                          32x32x64 instruction, scales staged in LDS) */
-  int32_t a_load;     /* 0 K-contiguous vector, 1 M-contiguous vector, 2 generic */
+  int32_t a_load;     /* 0 K-contiguous vector, 1 M-contiguous vector (register
+                         transpose), 2 generic, 3 M-contiguous direct copy into
+                         an M-major LDS tile read by transposing reads */
   int32_t b_load;     /* same, for B */
   int32_t tile_m, tile_n, tile_k;
   int32_t threads;    /* per workgroup */
@@ -167,7 +169,9 @@ sl_status sl_query_fragment_map(int32_t instr, int32_t operand, int32_t* lane, i
 /*
  * LDS tile layout of a kernel variant: for each logical element (row, k) of
  * one operand's tile, its byte offset inside the tile's LDS buffer.
- * `variant` is the sl_plan.kernel id, `operand` 0 = A, 1 = B.  Writes
+ * `variant` is the sl_plan.kernel id, or 5 for the M-major tile that an
+ * operand with a_load / b_load == 3 uses (256 rows, one 64-wide K-tile,
+ * M contiguous); `operand` 0 = A, 1 = B.  Writes
  * rows*cols offsets row-major (index row*cols + k) into `offsets` (up to
  * `capacity`), and the tile's rows, cols and element bytes into the three
  * outputs.  Host only.
@@ -180,6 +184,8 @@ sl_status sl_query_lds_map(int32_t variant, int32_t operand, int64_t* offsets, i
  * MFMA tile 0, k-slice 0 of wave 0, i.e. the composition of the LDS tile
  * layout with the instruction's operand map.  `variant`/`operand` as in
  * sl_query_lds_map.  `addr` receives lanes*slots entries (lane-major).
+ * For variant 5 it receives, per lane, the two addresses the lane supplies
+ * to the fragment's two ds_read_b64_tr_b16 reads (lane-major, 128 entries).
  */
 sl_status sl_query_fragment_addresses(int32_t variant, int32_t operand, int64_t* addr,
                                       int64_t capacity, int64_t* count);

@@ -319,7 +319,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     P.pub.tile_k = 128;
     p.k_tiles = (int32_t)((K + 127) / 128);
   } else {
-    const int32_t la = choose_load(A, K, 256, 2), lb = choose_load(B, K, 256, 2);
+    int32_t la = choose_load(A, K, 256, 2), lb = choose_load(B, K, 256, 2);
     const bool generic = la == sl::LOAD_GENERIC || lb == sl::LOAD_GENERIC;
     if (generic) {
       // one 128x128 configuration, instantiated for every pair that has a
@@ -359,6 +359,13 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
         }
       }
       P.pub.kernel = sl::K_F16;
+    }
+    // M- (N-) contiguous operands of the 8-wave 256x256 kernel are copied
+    // straight into an M-major LDS tile (SL_MN_LOADER=1 keeps the register-
+    // transposing loader)
+    if (tile == sl::T256x256_W2x4 && env_int("SL_MN_LOADER", 3) == 3) {
+      if (la == sl::LOAD_MNVEC) la = sl::LOAD_MNDMA;
+      if (lb == sl::LOAD_MNVEC) lb = sl::LOAD_MNDMA;
     }
     P.pub.a_load = la;
     P.pub.b_load = lb;
@@ -514,13 +521,27 @@ sl_status sl_query_fragment_map(int32_t instr, int32_t operand, int32_t* lane, i
   return SL_OK;
 }
 
+// query id of the M-major LDS tile (LOAD_MNDMA operands), next to the
+// kernel family ids
+constexpr int32_t kMnTile = 5;
+
 static int32_t current_shift() { return env_int("SL_SWZ", 0) ? 1 : 0; }
 
 sl_status sl_query_lds_map(int32_t variant, int32_t operand, int64_t* offsets, int64_t capacity, int32_t* rows,
                            int32_t* cols, int32_t* elem_bytes) {
   g_msg.clear();
-  if (variant < sl::K_F16 || variant > sl::K_MX_W8) return fail(SL_ERR_ARG, "variant %d", variant);
+  if (variant < sl::K_F16 || variant > kMnTile) return fail(SL_ERR_ARG, "variant %d", variant);
   if (operand < 0 || operand > 1) return fail(SL_ERR_ARG, "operand %d", operand);
+  if (variant == kMnTile) {
+    int64_t n = 0;
+    for (int32_t r = 0; r < 256; ++r)
+      for (int32_t k = 0; k < 64; ++k, ++n)
+        if (offsets && n < capacity) offsets[n] = sl::mn_lds_offset(k, r, 256);
+    if (rows) *rows = 256;
+    if (cols) *cols = 64;
+    if (elem_bytes) *elem_bytes = 2;
+    return SL_OK;
+  }
   const int32_t R = variant == sl::K_F16_GENERIC ? 128 : 256;
   const int32_t es = variant >= sl::K_MX ? 1 : 2;
   const int32_t Cn = sl::kRowBytes / es;
@@ -538,8 +559,17 @@ sl_status sl_query_lds_map(int32_t variant, int32_t operand, int64_t* offsets, i
 sl_status sl_query_fragment_addresses(int32_t variant, int32_t operand, int64_t* addr, int64_t capacity,
                                       int64_t* count) {
   g_msg.clear();
-  if (variant < sl::K_F16 || variant > sl::K_MX_W8) return fail(SL_ERR_ARG, "variant %d", variant);
+  if (variant < sl::K_F16 || variant > kMnTile) return fail(SL_ERR_ARG, "variant %d", variant);
   if (operand < 0 || operand > 1) return fail(SL_ERR_ARG, "operand %d", operand);
+  if (variant == kMnTile) {
+    // the address each lane supplies to the two transposing reads
+    int64_t n = 0;
+    for (int32_t l = 0; l < 64; ++l)
+      for (int32_t r = 0; r < 2; ++r, ++n)
+        if (addr && n < capacity) addr[n] = sl::tr_read_offset(l, r, 0, 0, 256);
+    if (count) *count = n;
+    return SL_OK;
+  }
   const int32_t instr = variant == sl::K_MX_W8 ? sl::MFMA32_F8 : variant == sl::K_MX ? sl::MFMA16_F8 : sl::MFMA16_F16;
   const int32_t slots = sl::instr_in_slots(instr);
   const int32_t es = variant >= sl::K_MX ? 1 : 2;

@@ -96,11 +96,9 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
   [[maybe_unused]] half8 fa1[FM], fb1[FN];
   auto read_slice = [&](const char* buf, int ks, half8(&fa)[FM], half8(&fb)[FN]) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[i] = *(const half8*)(buf + fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * i, ks, SHIFT));
+    for (int i = 0; i < FM; ++i) fa[i] = read_frag<ALOAD, BM, SHIFT>(buf, lane, a_row0 + 16 * i, ks);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[j] = *(const half8*)(buf + ABYTES + fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * j, ks, SHIFT));
+    for (int j = 0; j < FN; ++j) fb[j] = read_frag<BLOAD, BN, SHIFT>(buf + ABYTES, lane, b_row0 + 16 * j, ks);
   };
   // instruction A = our B fragment, instruction B = our A fragment
   auto mfma_slice = [&](const half8(&fa)[FM], const half8(&fb)[FN]) {
@@ -798,6 +796,17 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
       }
       default: return launch_tile<LOAD_KVEC, LOAD_KVEC>(p, tile, shift, s);
     }
+  }
+  if (a_load == LOAD_MNDMA || b_load == LOAD_MNDMA) {
+    // the M-major direct-copy tiles exist for the 8-wave 256x256 kernel
+    if (tile != T256x256_W2x4) return hipErrorInvalidValue;
+    if (a_load == LOAD_MNDMA && b_load == LOAD_KVEC)
+      return launch_cfg<256, 256, 2, 4, LOAD_MNDMA, LOAD_KVEC, 0>(p, shift, s);
+    if (a_load == LOAD_KVEC && b_load == LOAD_MNDMA)
+      return launch_cfg<256, 256, 2, 4, LOAD_KVEC, LOAD_MNDMA, 0>(p, shift, s);
+    if (a_load == LOAD_MNDMA && b_load == LOAD_MNDMA)
+      return launch_cfg<256, 256, 2, 4, LOAD_MNDMA, LOAD_MNDMA, 0>(p, shift, s);
+    return hipErrorInvalidValue;
   }
   if (tile > T256x256_W2x4_P) return hipErrorInvalidValue;
   if (a_load == LOAD_MNVEC && b_load == LOAD_KVEC) return launch_tile<LOAD_MNVEC, LOAD_KVEC>(p, tile, shift, s);

@@ -256,6 +256,69 @@ struct LoaderMNVec {
   }
 };
 
+// M- (N-) contiguous fp16 rows, 16-B aligned, copied straight into the
+// M-major LDS tile (mn_lds_offset): K-row k of the tile is ROWS contiguous
+// values at base + k*ks.  One wave instruction fills 1 KiB of LDS, i.e.
+// RPI = 1024 / (2 ROWS) consecutive K-rows, lane l landing at byte 16 l of
+// that block; the lane that lands in physical chunk p of K-row k fetches
+// logical chunk p ^ mn_swz(k).
+template <int ROWS, int NT>
+struct LoaderMNDma {
+  static constexpr int WAVES = NT / 64;
+  static constexpr int CPR = ROWS / 8;             // 16-byte chunks per K-row
+  static constexpr int RPI = 1024 / (2 * ROWS);    // K-rows per wave instruction
+  static constexpr int ITERS = 64 * ROWS * 2 / (NT * 16);
+  static_assert(ROWS >= 128 && RPI >= 1 && ITERS >= 1 && 64 * ROWS * 2 % (NT * 16) == 0, "unsupported tile");
+
+  __amdgpu_buffer_rsrc_t rsrc;
+  int32_t K, wave, lane, rows_valid;
+  int64_t ks;
+
+  __device__ __forceinline__ LoaderMNDma(const void* base, int32_t rows_valid_, int64_t /*rs*/, int64_t ks_,
+                                         int64_t K_, int32_t wave_, int32_t lane_) {
+    K = (int32_t)K_;
+    wave = wave_;
+    lane = lane_;
+    rows_valid = rows_valid_;
+    ks = ks_;
+    const uint32_t bytes =
+        (rows_valid_ > 0 && K_ > 0) ? (uint32_t)(((K_ - 1) * ks_ + rows_valid_) * 2) : 0u;
+    rsrc = make_rsrc(base, bytes);
+  }
+
+  __device__ __forceinline__ void issue(int32_t t, char* lds) const {
+#pragma unroll
+    for (int j = 0; j < ITERS; ++j) {
+      const int32_t blk = j * WAVES + wave;             // 1 KiB block of the tile
+      const int32_t kr = blk * RPI + lane / CPR;        // K-row inside the tile
+      const int32_t c = (lane % CPR) ^ mn_swz(kr);      // logical chunk this lane fetches
+      const int32_t k = t * 64 + kr;
+      const bool ok = k < K && c * 8 < rows_valid;
+      const uint32_t off = (uint32_t)(((int64_t)k * ks + c * 8) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + blk * 1024), 16, ok ? off : kOutOfRange,
+                                               0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void commit(char*) const {}
+};
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// One fp16 MFMA fragment (8 halves of one lane) of the 16-row tile at row0,
+// k-slice ks, from an LDS tile of layout KIND: K-major (every loader but
+// LOAD_MNDMA) by one ds_read_b128, M-major by two transposing reads.
+template <int KIND, int ROWS, int SHIFT>
+__device__ __forceinline__ half8 read_frag(const char* buf, int32_t lane, int32_t row0, int32_t ks) {
+  if constexpr (KIND == LOAD_MNDMA) {
+    typedef __attribute__((address_space(3))) short4_t lds_s4;
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(buf + tr_read_offset(lane, 0, row0, ks, ROWS)));
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(buf + tr_read_offset(lane, 1, row0, ks, ROWS)));
+    return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    return *(const half8*)(buf + fragment_lds_offset(MFMA16_F16, lane, 0, row0, ks, SHIFT));
+  }
+}
+
 // Any strides: every element is fetched on its own (64-bit addressing).
 template <int ROWS, int NT, int SHIFT>
 struct LoaderGeneric {
@@ -305,6 +368,10 @@ struct LoaderSel<LOAD_MNVEC, ROWS, NT, SHIFT> {
 template <int ROWS, int NT, int SHIFT>
 struct LoaderSel<LOAD_GENERIC, ROWS, NT, SHIFT> {
   using type = LoaderGeneric<ROWS, NT, SHIFT>;
+};
+template <int ROWS, int NT, int SHIFT>
+struct LoaderSel<LOAD_MNDMA, ROWS, NT, SHIFT> {
+  using type = LoaderMNDma<ROWS, NT>;
 };
 
 }  // namespace sl

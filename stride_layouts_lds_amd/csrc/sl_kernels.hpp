@@ -10,7 +10,9 @@ namespace sl {
 enum LoadKind : int32_t {
   LOAD_KVEC = 0,    // K contiguous, 16-B aligned: direct HBM->LDS 16-B buffer loads
   LOAD_MNVEC = 1,   // M (or N) contiguous, 16-B aligned: 16-B loads, 8x8 register transpose
-  LOAD_GENERIC = 2  // any strides: element loads
+  LOAD_GENERIC = 2, // any strides: element loads
+  LOAD_MNDMA = 3    // M (or N) contiguous, 16-B aligned: direct HBM->LDS into an M-major tile,
+                    // fragments by transposing LDS reads (8-wave 256x256 kernel)
 };
 
 // Kernel families (sl_plan.kernel).

@@ -118,4 +118,36 @@ SL_HD constexpr int32_t fragment_lds_offset(int32_t instr, int32_t lane, int32_t
   return lds_offset(row0 + c.row, byte, shift, row_bytes);
 }
 
+// ---------------------------------------------------------------------------
+// M- (N-) major LDS tile, for operands stored with M (or N) contiguous: the
+// tile keeps the global orientation, 64 K-rows of `rows` fp16 each, so the
+// HBM -> LDS copy moves whole 16-byte chunks along M with no register
+// transpose.  16-byte chunk c of K-row k sits at physical chunk
+//   c ^ mn_swz(k),  mn_swz(k) = 2 * ((k & 3) | ((k >> 3) & 1) << 2)
+// (an XOR on chunk bits 1-3; rows >= 128 keeps it inside the row).
+//
+// The MFMA fragment (lane l = l0 + 16 l1 wants element (row l0, k 8 l1 + v))
+// is read with two ds_read_b64_tr_b16: in such a read the 16 lanes of group
+// l1 each supply the address of one 8-byte block (4 consecutive rows at one
+// k), the group's 16 blocks form a 4 x 16 matrix (row j = blocks of lanes
+// 4j .. 4j+3) and lane i receives its column i.  Lane p of group l1 in read
+// r therefore supplies the block of rows row0 + 4 (p % 4) .. + 3 at
+// k = 32 ks + 8 l1 + 4 r + p / 4, and lane i receives rows row0 + i at
+// k = 32 ks + 8 l1 + 4 r + j, j = 0..3: slots 4 r .. 4 r + 3 of its
+// fragment.  With the swizzle above the 8 K-rows that one 32-lane half of
+// the read touches land on 16 distinct 16-byte bank groups.
+// ---------------------------------------------------------------------------
+
+SL_HD constexpr int32_t mn_swz(int32_t k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+
+SL_HD constexpr int32_t mn_lds_offset(int32_t k, int32_t row, int32_t rows) {
+  return k * rows * 2 + 16 * ((row >> 3) ^ mn_swz(k)) + (row & 7) * 2;
+}
+
+// byte address lane `lane` supplies to transposing read r (0, 1) of the
+// fragment of the 16-row MFMA tile at `row0`, k-slice `ks` (32 wide)
+SL_HD constexpr int32_t tr_read_offset(int32_t lane, int32_t r, int32_t row0, int32_t ks, int32_t rows) {
+  return mn_lds_offset(32 * ks + 8 * (lane / 16) + 4 * r + (lane % 16) / 4, row0 + 4 * (lane % 4), rows);
+}
+
 }  // namespace sl

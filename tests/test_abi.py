@@ -86,9 +86,18 @@ def test_plan_transposed_views_select_loaders(api):
     b_k = (BASE_B, F16, (nb, N, K), (N * K, K, 1))           # K contiguous
     b_n = (BASE_B, F16, (nb, N, K), (N * K, 1, N))           # N contiguous
     d = (BASE_D, F16, (nb, M, N), (M * N, N, 1))
+    # the 8-wave 256x256 tile copies M- (N-) contiguous operands straight
+    # into an M-major LDS tile (loader 3)
     p = plan(api, a_mn, b_k, None, d)
-    assert (p["a_load"], p["b_load"]) == (1, 0) and p["batch"] == nb
+    assert (p["a_load"], p["b_load"]) == (3, 0) and p["batch"] == nb and p["tile_m"] == 256
     p = plan(api, a_mn, b_n, None, d)
+    assert (p["a_load"], p["b_load"]) == (3, 3)
+    # other tiles keep the register-transposing loader (loader 1)
+    os.environ["SL_TILE"] = "0"
+    try:
+        p = plan(api, a_mn, b_n, None, d)
+    finally:
+        del os.environ["SL_TILE"]
     assert (p["a_load"], p["b_load"]) == (1, 1)
     # an odd stride or a misaligned base goes to the element loader
     odd = (BASE_A, F16, (M, K), (K + 1, 1))
@@ -275,3 +284,38 @@ def test_plan_split_k_for_skinny_outputs(api):
     # short K: no split (fewer than 4 K-tiles of 64 per split)
     p = plan(api, rowmajor(BASE_A, (256, 256)), rowmajor(BASE_B, (256, 256)), None, rowmajor(BASE_D, (256, 256)))
     assert p["split_k"] == 1
+
+
+def test_m_major_tile_is_a_chunk_swizzle(api):
+    """The M-major LDS tile (operands copied with M contiguous): a bijection
+    onto 256 x 64 halves in which every 16-byte chunk holds 8 consecutive
+    rows of one K-row (what one 16-byte direct copy moves)."""
+    offs, es = api.query_lds_map(5, 0)
+    assert offs.shape == (256, 64) and es == 2
+    assert sorted((offs // 2).ravel().tolist()) == list(range(256 * 64))
+    for k in range(64):
+        for c in range(32):
+            col = offs[8 * c:8 * c + 8, k]
+            assert col[0] % 16 == 0 and np.array_equal(col - col[0], np.arange(8) * 2)
+            assert col[0] // 512 == k  # K-row k occupies bytes [512 k, 512 k + 512)
+
+
+def test_m_major_fragment_by_transposing_reads(api):
+    """Fill an LDS image through the M-major tile map, apply the transposing
+    read (its lane semantics as pinned on the device) to the addresses each
+    lane supplies, and check that every lane receives exactly its MFMA
+    16x16x32 fragment: (row l % 16, k 8 (l / 16) + v)."""
+    offs, _ = api.query_lds_map(5, 0)
+    code = lambda r, k: (r * 64 + k) & 0xFFFF
+    lds = np.zeros(256 * 64, np.int64)
+    for r in range(256):
+        for k in range(64):
+            lds[offs[r, k] // 2] = code(r, k)
+    addr = api.query_fragment_addresses(5, 0).reshape(64, 2)
+    got = [[], []]
+    for rd in range(2):
+        got[rd] = L.ds_read_tr16_b64_expected(addr[:, rd].tolist(), lds.tolist())
+    want = {(l, v): code(r, c) for l, v, r, c in L.MFMA16_F16_A.table()}
+    for l in range(64):
+        frag = got[0][l] + got[1][l]
+        assert frag == [want[(l, v)] for v in range(8)], l

@@ -83,6 +83,34 @@ def test_exact_parity_every_fp16_tile(api, tile, monkeypatch):
     assert mism == 0, f"{mism} elements differ"
 
 
+MN_DIRECT = [
+    # M, N, K, batch, a_major, b_major, with_c: M- / N-contiguous operands
+    # through the 8-wave kernel's direct M-major copy and transposing reads
+    (520, 264, 136, 2, "col", "row", False),
+    (256, 256, 64, None, "col", "col", True),
+    (264, 520, 200, None, "row", "col", True),
+    (512, 512, 512, 3, "col", "col", False),
+    (136, 72, 1000, None, "col", "row", True),   # K-tiles past the ragged end of K
+]
+
+
+@pytest.mark.parametrize("case", MN_DIRECT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_{c[4]}{c[5]}")
+def test_exact_parity_m_major_direct_copy(api, case, monkeypatch):
+    h = H()
+    monkeypatch.setenv("SL_TILE", "4")
+    M, N, K, batch, am, bm, with_c = case
+    w = I.gemm_workload("mn_direct", M, N, K, seed=M + 2 * N + K, dist="int4", batch=batch, a_major=am,
+                        b_major=bm, with_c=with_c)
+    plan = _plan(api, w)
+    h.log(f"mn direct {case} plan={plan}")
+    assert plan["tile_m"] == 256 and plan["a_load"] == (3 if am == "col" else 0)
+    assert plan["b_load"] == (3 if bm == "col" else 0)
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
 SPLITK = [
     # M, N, K, batch, with_c, forced split count (0: the planner's), expected splits
     (300, 72, 2056, None, True, 0, 7),    # 33 K-tiles: 7 splits of 5 (the last of 3)
