@@ -304,6 +304,11 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
              (S.t->layout.rank == 2 || S.bs % 4 == 0);
     };
     const bool wide_ok = kb % 4 == 0 && dword_rows(SA) && dword_rows(SB);
+    auto chunk_rows = [&](const View& S) {
+      return S.cs == 1 && S.rs % 16 == 0 && (uintptr_t)S.t->data % 16 == 0 &&
+             (S.t->layout.rank == 2 || S.bs % 16 == 0);
+    };
+    if (kb % 16 == 0 && chunk_rows(SA) && chunk_rows(SB) && env_int("SL_SCALE16", 1)) p.flags |= sl::F_SCALE16;
     const bool valid = tile == sl::T256x256_W2x4 ? wide_ok : tile >= 0 && tile <= sl::T128x128_W2x2;
     if (!valid) {
       tile = sl::T256x128_W2x2;
@@ -385,7 +390,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.pub.workgroups = total;
   P.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)M * (size_t)N * sizeof(float) : 0;
   P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * P.pub.tile_k * (mx ? 1 : 2);
-  if (P.pub.kernel == sl::K_MX_W8) P.pub.lds_bytes += ts.stages * (ts.bm + ts.bn) * 4;
+  if (P.pub.kernel == sl::K_MX_W8)
+    P.pub.lds_bytes += (p.flags & sl::F_SCALE16) ? 2 * (ts.bm + ts.bn) * 16 : ts.stages * (ts.bm + ts.bn) * 4;
   return SL_OK;
 }
 

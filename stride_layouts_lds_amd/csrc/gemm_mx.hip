@@ -127,23 +127,32 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_mx_kernel(const GemmParam
 // 128-byte K-tile is two 64-wide k-slices.  The wider instruction halves the
 // fragment registers of a slice (6 x 8 VGPRs) against the 16x16x128 form.
 //
-// Scales go through LDS with the data: per K-tile a row of A or B owns one
-// dword of SF (its four E8M0 bytes for k-blocks 4t..4t+3), copied straight
-// into LDS by one 4-byte buffer load per row (waves 0-3: A rows, 4-7: B
-// rows).  This needs the scale rows K-contiguous, dword aligned and a whole
-// number of dwords long; the planner checks it.  In slice s, scale lane l
-// of an instruction tile wants block 2s + l / 32 of row l % 32: the lane
-// reads its row's dword, shifts it right by 8 (l / 32) once per K-tile, and
+// Scales go through LDS with the data: for K-tile t a row of A or B owns
+// the dword of SF holding its four E8M0 bytes for k-blocks 4t..4t+3.
+//   SV = 1: that dword is copied per K-tile into the tile's stage by one
+//           4-byte direct-to-LDS load per row (waves 0-3: A rows, 4-7: B).
+//   SV = 4: every fourth K-tile, one 16-byte copy per row brings the dwords
+//           of the next four K-tiles into one of two scale buffers.  A row's
+//           scales are then one line request per four K-tiles instead of
+//           one per K-tile, which matters because a CU's line requests in
+//           flight bound its copy bandwidth.  Needs rows of a multiple of 16
+//           blocks on 16-byte boundaries.
+// Both need the scale rows K-contiguous, dword aligned and a whole number
+// of dwords long; the planner checks it.  In slice s, scale lane l of an
+// instruction tile wants block 2s + l / 32 of row l % 32: the lane reads
+// its row's dword, shifts it right by 8 (l / 32) once per K-tile, and
 // passes byte 2s of the result.
-template <int SHIFT>
+template <int SHIFT, int SV>
 __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) {
   constexpr int BM = 256, BN = 256, WM = 2, NT = 512;
   constexpr int TM = 128, TN = 64;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
-  constexpr int SOFF = ABYTES + BBYTES;  // A scale dwords, then B scale dwords
-  constexpr int STAGE = SOFF + (BM + BN) * 4;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int SOFF = ABYTES + BBYTES;  // SV 1: A scale dwords, then B scale dwords
+  constexpr int STAGE = SV == 1 ? SOFF + (BM + BN) * 4 : SOFF;
+  constexpr int SBUF = SV == 1 ? 0 : (BM + BN) * 16;  // SV 4: one of the two scale buffers
+  static_assert(SV == 1 || SV == 4, "scale copy width");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 2 * SBUF];
 
   const int32_t lane = threadIdx.x & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -168,10 +177,26 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
   const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(S, s_rows > 0 ? (uint32_t)((s_rows - 1) * s_rs + 4 * kdw) : 0u);
   const int32_t s_row = 64 * (wave & 3) + lane;
   const uint32_t s_off = s_row < s_rows ? (uint32_t)(s_row * s_rs) : kOutOfRange;
-  const int32_t s_lds = SOFF + (s_is_b ? BM * 4 : 0) + 256 * (wave & 3);
+  // SV 1: dword of K-tile t into the stage; SV 4: 16 bytes (K-tiles 4q..4q+3)
+  // into scale buffer q & 1
   auto issue_scales = [&](int32_t t, char* stage) {
-    const uint32_t off = (s_off != kOutOfRange && t < kdw) ? s_off + 4u * (uint32_t)t : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void_t*)(stage + s_lds), 4, off, 0, 0, 0);
+    if constexpr (SV == 1) {
+      const uint32_t off = (s_off != kOutOfRange && t < kdw) ? s_off + 4u * (uint32_t)t : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void_t*)(stage + SOFF + (s_is_b ? BM * 4 : 0) + 256 * (wave & 3)),
+                                               4, off, 0, 0, 0);
+    } else {
+      const int32_t q = t;  // chunk index
+      const uint32_t off = (s_off != kOutOfRange && 4 * q < kdw) ? s_off + 16u * (uint32_t)q : kOutOfRange;
+      char* buf = smem + 2 * STAGE + (q & 1) * SBUF + (s_is_b ? BM * 16 : 0) + 1024 * (wave & 3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void_t*)buf, 16, off, 0, 0, 0);
+    }
+  };
+  // the scale dword of K-tile t for row `row` of operand `op` (0 A, 1 B)
+  auto scale_word = [&](const char* cur, int32_t t, int32_t op, int32_t row) -> uint32_t {
+    if constexpr (SV == 1)
+      return *(const uint32_t*)(cur + SOFF + op * BM * 4 + 4 * row);
+    else
+      return *(const uint32_t*)(smem + 2 * STAGE + ((t >> 2) & 1) * SBUF + op * BM * 16 + 16 * row + 4 * (t & 3));
   };
 
   floatx16 acc[FM][FN];
@@ -199,14 +224,18 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
     char* nxt = smem + ((t + 1) & 1) * STAGE;
     la.issue(t + 1, nxt);
     lb.issue(t + 1, nxt + ABYTES);
-    issue_scales(t + 1, nxt);
+    if constexpr (SV == 1) {
+      issue_scales(t + 1, nxt);
+    } else {
+      // chunk t/4 + 1 into the buffer chunk t/4 - 1 used (retired by the
+      // barrier that ended K-tile t - 1); it lands by K-tile t + 4
+      if ((t & 3) == 0) issue_scales((t >> 2) + 1, nullptr);
+    }
     uint32_t sa[FM], sb[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      sa[i] = *(const uint32_t*)(cur + SOFF + 4 * (a_row0 + 32 * i + (lane & 31))) >> half_sel;
+    for (int i = 0; i < FM; ++i) sa[i] = scale_word(cur, t, 0, a_row0 + 32 * i + (lane & 31)) >> half_sel;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      sb[j] = *(const uint32_t*)(cur + SOFF + BM * 4 + 4 * (b_row0 + 32 * j + (lane & 31))) >> half_sel;
+    for (int j = 0; j < FN; ++j) sb[j] = scale_word(cur, t, 1, b_row0 + 32 * j + (lane & 31)) >> half_sel;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       i32x8 af[FM], bf[FN];
@@ -276,10 +305,14 @@ hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, int32_t shift, hipS
     case T128x128_W2x2: return launch_cfg<128, 128, 2, 2>(p, shift, s);
     case T256x256_W2x4: {
       dim3 grid((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), block(512);
-      if (shift == 0)
-        hipLaunchKernelGGL(gemm_mx_w8_kernel<0>, grid, block, 0, s, p);
-      else
-        hipLaunchKernelGGL(gemm_mx_w8_kernel<1>, grid, block, 0, s, p);
+      const bool s16 = p.flags & F_SCALE16;
+      if (shift == 0) {
+        if (s16) hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 1>), grid, block, 0, s, p);
+      } else {
+        if (s16) hipLaunchKernelGGL((gemm_mx_w8_kernel<1, 4>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((gemm_mx_w8_kernel<1, 1>), grid, block, 0, s, p);
+      }
       return hipGetLastError();
     }
     default: return hipErrorInvalidValue;

@@ -91,6 +91,7 @@ struct GemmParams {
 constexpr int32_t F_HAS_C = 1;
 constexpr int32_t F_D_VEC = 2;  // D rows contiguous and 8-B aligned: 4-half stores
 constexpr int32_t F_C_VEC = 4;  // C rows contiguous and 8-B aligned: 4-half loads
+constexpr int32_t F_SCALE16 = 8;  // MX scale rows 16-B aligned, a multiple of 16 blocks long
 
 // Launchers (each returns the launch's hipError_t).
 hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load,

@@ -172,7 +172,7 @@ def _plan(api, w):
     args = api.make_args(h.to_device(w.a), h.to_device(w.b), h.to_device(w.c), out, h.to_device(w.sfa),
                          h.to_device(w.sfb), w.block_k)
     p = api.sl_gemm_plan(args)
-    return {k: p[k] for k in ("kernel", "a_load", "b_load", "tile_m", "tile_n", "workgroups")}
+    return {k: p[k] for k in ("kernel", "a_load", "b_load", "tile_m", "tile_n", "workgroups", "lds_bytes", "split_k")}
 
 
 def test_odd_strides_take_the_element_loader(api):
@@ -258,6 +258,10 @@ MX_EXACT = [
     (136, 128, 256, 2, 0, 4),      # batched scales
     (256, 264, 256, None, 4, 4),   # padded scale rows, still dword aligned
     (256, 264, 256, None, 1, 3),   # scale rows 9 bytes apart: byte-load kernel
+    (300, 264, 512, None, 0, 4),   # 16 blocks per row: 16-byte scale copies every 4 K-tiles
+    (256, 200, 1536, 2, 0, 4),     # batched, 48 blocks per row
+    (264, 136, 1024, None, 16, 4),  # padded rows 48 bytes apart: 16-byte copies
+    (264, 136, 512, None, 4, 4),   # rows 20 bytes apart: dword copies
     (300, 200, 208, None, 0, 3),   # 7 scale blocks per row: byte-load kernel
     (72, 96, 96, 3, 0, 3),
 ]
@@ -275,6 +279,10 @@ def test_mx_exact_parity(api, case, monkeypatch):
     plan = _plan(api, w)
     h.log(f"mx exact {case} plan={plan}")
     assert plan["kernel"] == kernel
+    if kernel == 4:  # 16-byte scale copies (two 8 KiB buffers) iff rows allow them
+        kb = -(-K // 32)
+        s16 = kb % 16 == 0 and (kb + pad) % 16 == 0
+        assert plan["lds_bytes"] == 2 * 512 * 128 + (2 * 512 * 16 if s16 else 2 * 512 * 4)
     d = h.d_codes(h.run_library(w))
     d_ref, _, _ = h.oracle_full(w)
     mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
