@@ -191,13 +191,21 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void_t*)buf, 16, off, 0, 0, 0);
     }
   };
-  // the scale dword of K-tile t for row `row` of operand `op` (0 A, 1 B)
-  auto scale_word = [&](const char* cur, int32_t t, int32_t op, int32_t row) -> uint32_t {
-    if constexpr (SV == 1)
-      return *(const uint32_t*)(cur + SOFF + op * BM * 4 + 4 * row);
-    else
-      return *(const uint32_t*)(smem + 2 * STAGE + ((t >> 2) & 1) * SBUF + op * BM * 16 + 16 * row + 4 * (t & 3));
+  // SV 1: the scale dword of K-tile t for row `row` of operand `op` (0 A,
+  // 1 B) in the tile's stage.  SV 4: the 16 bytes of K-tiles 4q..4q+3 of
+  // that row, read into registers once per four K-tiles (one ds_read_b128
+  // of 32 consecutive rows is free of bank conflicts; per-tile dword reads
+  // 16 bytes apart are not).
+  auto scale_word = [&](const char* cur, int32_t op, int32_t row) -> uint32_t {
+    return *(const uint32_t*)(cur + SOFF + op * BM * 4 + 4 * row);
   };
+  auto scale_chunk = [&](int32_t q, int32_t op, int32_t row) -> u32x4 {
+    return *(const u32x4*)(smem + 2 * STAGE + (q & 1) * SBUF + op * BM * 16 + 16 * row);
+  };
+  auto pick = [](const u32x4& v, int32_t s) -> uint32_t {
+    return s == 0 ? v[0] : s == 1 ? v[1] : s == 2 ? v[2] : v[3];
+  };
+  [[maybe_unused]] u32x4 sa4[FM], sb4[FN];
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -232,10 +240,23 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
       if ((t & 3) == 0) issue_scales((t >> 2) + 1, nullptr);
     }
     uint32_t sa[FM], sb[FN];
+    if constexpr (SV == 1) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) sa[i] = scale_word(cur, t, 0, a_row0 + 32 * i + (lane & 31)) >> half_sel;
+      for (int i = 0; i < FM; ++i) sa[i] = scale_word(cur, 0, a_row0 + 32 * i + (lane & 31)) >> half_sel;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) sb[j] = scale_word(cur, t, 1, b_row0 + 32 * j + (lane & 31)) >> half_sel;
+      for (int j = 0; j < FN; ++j) sb[j] = scale_word(cur, 1, b_row0 + 32 * j + (lane & 31)) >> half_sel;
+    } else {
+      if ((t & 3) == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) sa4[i] = scale_chunk(t >> 2, 0, a_row0 + 32 * i + (lane & 31));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sb4[j] = scale_chunk(t >> 2, 1, b_row0 + 32 * j + (lane & 31));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa[i] = pick(sa4[i], t & 3) >> half_sel;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sb[j] = pick(sb4[j], t & 3) >> half_sel;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       i32x8 af[FM], bf[FN];
