@@ -178,8 +178,11 @@ def main():
 
     flop = w.flops
     value = flop * args.steps / wall / 1e12
-    mfma_bound = args.workload not in ("skinny", "batched_nn", "batched_nt")
     peak = PEAK_F8 if w.mx else PEAK_F16
+    # the roofline that bounds the workload: MFMA when its arithmetic
+    # intensity (algorithmic FLOP per algorithmic byte) is above the ridge
+    # point peak / HBM bandwidth, HBM below it
+    mfma_bound = flop / algorithmic_bytes(w) >= peak * 1e12 / (PEAK_HBM * 1e9)
     if mfma_bound:
         achieved = flop / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
