@@ -27,7 +27,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gemm_ref.c")
 LIB = os.path.join(HERE, "libgemm_oracle.so")
 
-F16, F32, E4M3, E8M0 = 1, 2, 3, 4
+F16, F32, E4M3, E8M0, BF16 = 1, 2, 3, 4, 5
 
 
 class _Tensor(ctypes.Structure):
@@ -64,20 +64,25 @@ def lib():
         L.go_f16_decode.argtypes = [ctypes.c_uint16]
         L.go_f16_encode.restype = ctypes.c_uint16
         L.go_f16_encode.argtypes = [ctypes.c_double]
+        L.go_bf16_decode.restype = ctypes.c_double
+        L.go_bf16_decode.argtypes = [ctypes.c_uint16]
+        L.go_bf16_encode.restype = ctypes.c_uint16
+        L.go_bf16_encode.argtypes = [ctypes.c_double]
         L.go_e4m3_decode.restype = ctypes.c_double
         L.go_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.go_e8m0_decode.restype = ctypes.c_double
         L.go_e8m0_decode.argtypes = [ctypes.c_uint8]
         L.go_gemm.restype = ctypes.c_int
         L.go_gemm.argtypes = [P(_Tensor)] * 5 + [ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
-                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                                 ctypes.c_int32]
         L.go_gemm_points.restype = ctypes.c_int
         L.go_gemm_points.argtypes = [P(_Tensor)] * 5 + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                                        ctypes.c_int32]
+                                                        ctypes.c_int32, ctypes.c_int32]
         L.go_check.restype = ctypes.c_int64
         L.go_check.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                               P(ctypes.c_int64), P(ctypes.c_double)]
+                               P(ctypes.c_int64), P(ctypes.c_double), ctypes.c_int32]
         _lib = L
     return _lib
 
@@ -105,10 +110,13 @@ def _tensor(arr: Optional[np.ndarray], dtype: Optional[int] = None) -> _Tensor:
     return t
 
 
-def _args(a, b, c, sfa, sfb, mx: bool):
+def _args(a, b, c, sfa, sfb, mx: bool, bf16: bool = False):
     if mx:
         return (_tensor(a, E4M3), _tensor(b, E4M3), _tensor(c),
                 _tensor(sfa, E8M0), _tensor(sfb, E8M0))
+    if bf16:
+        return (_tensor(a, BF16), _tensor(b, BF16), _tensor(c, BF16 if c is not None else None),
+                _tensor(None), _tensor(None))
     return _tensor(a), _tensor(b), _tensor(c), _tensor(None), _tensor(None)
 
 
@@ -120,30 +128,31 @@ def _threads(nthreads: Optional[int]) -> int:
 
 def gemm(a: np.ndarray, b: np.ndarray, c: Optional[np.ndarray] = None,
          sfa: Optional[np.ndarray] = None, sfb: Optional[np.ndarray] = None,
-         block_k: int = 32, nthreads: Optional[int] = None
+         block_k: int = 32, nthreads: Optional[int] = None, bf16: bool = False
          ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Every element of D = A B^T + C.  ``a``: (batch?, M, K), ``b``:
     (batch?, N, K), ``c``: (batch?, M, N) or None.  With ``sfa``/``sfb`` the
-    operands are E4M3 codes scaled per ``block_k`` K elements.  Returns
-    (D fp16 codes as uint16 (batch, M, N), fp64 value before rounding,
-    sum_k |A B| in fp64)."""
+    operands are E4M3 codes scaled per ``block_k`` K elements.  With
+    ``bf16`` the uint16 codes of a, b and c are bf16 and D is rounded to
+    bf16.  Returns (D codes as uint16 (batch, M, N), fp64 value before
+    rounding, sum_k |A B| in fp64)."""
     mx = sfa is not None
     batch = max(x.shape[0] if x is not None and x.ndim == 3 else 1 for x in (a, b, c))
     M, N = a.shape[-2], b.shape[-2]
     d = np.empty((batch, M, N), np.uint16)
     ref = np.empty((batch, M, N), np.float64)
     absum = np.empty((batch, M, N), np.float64)
-    ta, tb, tc, tsa, tsb = _args(a, b, c, sfa, sfb, mx)
+    ta, tb, tc, tsa, tsb = _args(a, b, c, sfa, sfb, mx, bf16)
     rc = lib().go_gemm(ctypes.byref(ta), ctypes.byref(tb), ctypes.byref(tc), ctypes.byref(tsa),
                        ctypes.byref(tsb), block_k, batch, d.ctypes.data, ref.ctypes.data,
-                       absum.ctypes.data, _threads(nthreads))
+                       absum.ctypes.data, _threads(nthreads), BF16 if bf16 else F16)
     if rc:
         raise ValueError(f"oracle gemm rejected the operands (code {rc})")
     return d, ref, absum
 
 
 def gemm_points(a, b, c=None, sfa=None, sfb=None, points: np.ndarray = None,
-                block_k: int = 32, nthreads: Optional[int] = None):
+                block_k: int = 32, nthreads: Optional[int] = None, bf16: bool = False):
     """As ``gemm`` but only at ``points`` (an int64 (count, 3) array of
     (batch, m, n)).  Returns (d codes, ref, absum), each of length count."""
     mx = sfa is not None
@@ -153,19 +162,19 @@ def gemm_points(a, b, c=None, sfa=None, sfb=None, points: np.ndarray = None,
     d = np.empty(n, np.uint16)
     ref = np.empty(n, np.float64)
     absum = np.empty(n, np.float64)
-    ta, tb, tc, tsa, tsb = _args(a, b, c, sfa, sfb, mx)
+    ta, tb, tc, tsa, tsb = _args(a, b, c, sfa, sfb, mx, bf16)
     rc = lib().go_gemm_points(ctypes.byref(ta), ctypes.byref(tb), ctypes.byref(tc), ctypes.byref(tsa),
                               ctypes.byref(tsb), block_k, pts.ctypes.data, n, d.ctypes.data,
-                              ref.ctypes.data, absum.ctypes.data, _threads(nthreads))
+                              ref.ctypes.data, absum.ctypes.data, _threads(nthreads), BF16 if bf16 else F16)
     if rc:
         raise ValueError(f"oracle gemm rejected the operands (code {rc})")
     return d, ref, absum
 
 
-def check(d: np.ndarray, d_ref: np.ndarray, absum: np.ndarray) -> Tuple[int, int, float]:
-    """The acceptance bound |D - D_ref| <= 2^-10 |D_ref| + 2^-13 S, per
-    element.  Returns (violations, index of the worst element, its
-    |D - D_ref| / bound)."""
+def check(d: np.ndarray, d_ref: np.ndarray, absum: np.ndarray, bf16: bool = False) -> Tuple[int, int, float]:
+    """The acceptance bound |D - D_ref| <= 2^-10 |D_ref| + 2^-13 S (2^-7 in
+    place of 2^-10 for bf16 codes), per element.  Returns (violations,
+    index of the worst element, its |D - D_ref| / bound)."""
     d = np.ascontiguousarray(d, dtype=np.uint16).ravel()
     d_ref = np.ascontiguousarray(d_ref, dtype=np.uint16).ravel()
     absum = np.ascontiguousarray(absum, dtype=np.float64).ravel()
@@ -173,7 +182,7 @@ def check(d: np.ndarray, d_ref: np.ndarray, absum: np.ndarray) -> Tuple[int, int
     wi = ctypes.c_int64(-1)
     wr = ctypes.c_double(0.0)
     bad = lib().go_check(d.ctypes.data, d_ref.ctypes.data, absum.ctypes.data, d.size,
-                         ctypes.byref(wi), ctypes.byref(wr))
+                         ctypes.byref(wi), ctypes.byref(wr), BF16 if bf16 else F16)
     return int(bad), int(wi.value), float(wr.value)
 
 
@@ -183,6 +192,14 @@ def f16_decode(code: int) -> float:
 
 def f16_encode(x: float) -> int:
     return lib().go_f16_encode(x)
+
+
+def bf16_decode(code: int) -> float:
+    return lib().go_bf16_decode(code)
+
+
+def bf16_encode(x: float) -> int:
+    return lib().go_bf16_encode(x)
 
 
 def e4m3_decode(code: int) -> float:

@@ -21,10 +21,14 @@
  *    S.1111.111 is NaN, max 448; E8M0: 2^(b-127), 255 is NaN).
  *  - fp16 is IEEE 754 binary16 (bias 15, subnormals, inf/NaN); encoding
  *    rounds to nearest, ties to even, overflow to infinity.
+ *  - bf16 (the same product in the other 16-bit format; the pages name only
+ *    fp16) is the upper half of IEEE binary32: bias 127, 7 stored
+ *    significand bits, subnormals, inf/NaN; encoded the same way.
  *
  * Summation: fp64, k ascending, one output element at a time.  Alongside the
  * exact-ish value it returns S = sum_k |A(m,k) B(n,k)| (fp64), which the
- * acceptance bound |D - D_ref| <= 2^-10 |D_ref| + 2^-13 S needs.
+ * acceptance bound |D - D_ref| <= 2^-10 |D_ref| + 2^-13 S needs (2^-7 in
+ * place of 2^-10 for a bf16 result: twice the format's unit roundoff).
  *
  * Parallelism: pthreads over output rows only; the inner loop stays plain.
  */
@@ -34,7 +38,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { GO_F16 = 1, GO_F32 = 2, GO_E4M3 = 3, GO_E8M0 = 4 };
+enum { GO_F16 = 1, GO_F32 = 2, GO_E4M3 = 3, GO_E8M0 = 4, GO_BF16 = 5 };
 
 typedef struct {
   const void* data; /* NULL: absent (C = 0, or no scales) */
@@ -96,14 +100,53 @@ double go_e8m0_decode(uint8_t b) {
   return ldexp(1.0, (int)b - 127);
 }
 
+/* bf16: sign, 8-bit exponent (bias 127), 7-bit fraction */
+double go_bf16_decode(uint16_t h) {
+  int sgn = h >> 15, e = (h >> 7) & 0xFF, f = h & 0x7F;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -133);                /* subnormal: f * 2^-133 */
+  else if (e == 255)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(0x80 | f), e - 134);    /* (1 + f/128) * 2^(e-127) */
+  return sgn ? -v : v;
+}
+
+uint16_t go_bf16_encode(double x) {
+  if (isnan(x)) return 0x7FC0;
+  uint16_t sgn = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (a < ldexp(1.0, -126)) {
+    /* subnormal range, step 2^-133; q == 128 is the smallest normal */
+    int q = (int)rint(ldexp(a, 133));
+    return sgn | (uint16_t)q;
+  }
+  int E;
+  frexp(a, &E);                                /* a in [2^(E-1), 2^E) */
+  if (E - 1 > 127) return sgn | 0x7F80;
+  int q = (int)rint(ldexp(a, 8 - E));          /* significand in [128, 256] */
+  int e = E - 1;
+  if (q == 256) {
+    q = 128;
+    e += 1;
+  }
+  if (e > 127) return sgn | 0x7F80;            /* rounded past the largest finite */
+  return sgn | (uint16_t)((e + 127) << 7) | (uint16_t)(q - 128);
+}
+
 /* decoding tables, filled once from the functions above */
 static double g_f16_tab[65536];
+static double g_bf16_tab[65536];
 static double g_e4m3_tab[256];
 static double g_e8m0_tab[256];
 static pthread_once_t g_tab_once = PTHREAD_ONCE_INIT;
 
 static void fill_tables(void) {
-  for (int i = 0; i < 65536; ++i) g_f16_tab[i] = go_f16_decode((uint16_t)i);
+  for (int i = 0; i < 65536; ++i) {
+    g_f16_tab[i] = go_f16_decode((uint16_t)i);
+    g_bf16_tab[i] = go_bf16_decode((uint16_t)i);
+  }
   for (int i = 0; i < 256; ++i) {
     g_e4m3_tab[i] = go_e4m3_decode((uint8_t)i);
     g_e8m0_tab[i] = go_e8m0_decode((uint8_t)i);
@@ -124,6 +167,7 @@ static double element(const go_tensor* t, int64_t b, int64_t i, int64_t j) {
   int64_t o = offset_of(t, b, i, j);
   switch (t->dtype) {
     case GO_F16: return g_f16_tab[((const uint16_t*)t->data)[o]];
+    case GO_BF16: return g_bf16_tab[((const uint16_t*)t->data)[o]];
     case GO_F32: return (double)((const float*)t->data)[o];
     case GO_E4M3: return g_e4m3_tab[((const uint8_t*)t->data)[o]];
     case GO_E8M0: return g_e8m0_tab[((const uint8_t*)t->data)[o]];
@@ -138,7 +182,12 @@ typedef struct {
   const go_tensor *a, *b, *c, *sfa, *sfb;
   int32_t block_k;
   int64_t K;
+  int32_t out_dtype; /* GO_F16 or GO_BF16: the format D is rounded to */
 } problem;
+
+static uint16_t encode_out(const problem* p, double v) {
+  return p->out_dtype == GO_BF16 ? go_bf16_encode(v) : go_f16_encode(v);
+}
 
 /* one output element: fp64 sum over k ascending, plus sum of |products| */
 static void one_point(const problem* p, int64_t bi, int64_t m, int64_t n,
@@ -162,7 +211,9 @@ static void one_point(const problem* p, int64_t bi, int64_t m, int64_t n,
 }
 
 static int setup(problem* p, const go_tensor* a, const go_tensor* b, const go_tensor* c,
-                 const go_tensor* sfa, const go_tensor* sfb, int32_t block_k) {
+                 const go_tensor* sfa, const go_tensor* sfb, int32_t block_k, int32_t out_dtype) {
+  if (out_dtype != GO_F16 && out_dtype != GO_BF16) return -2;
+  p->out_dtype = out_dtype;
   pthread_once(&g_tab_once, fill_tables);
   if (!a || !b || !a->data || !b->data) return -1;
   if (a->rank < 2 || a->rank > 3 || b->rank < 2 || b->rank > 3) return -3;
@@ -195,7 +246,7 @@ static void* point_worker(void* arg) {
   for (int64_t i = j->lo; i < j->hi; ++i) {
     double v, s;
     one_point(j->p, j->pts[3 * i], j->pts[3 * i + 1], j->pts[3 * i + 2], &v, &s);
-    if (j->d) j->d[i] = go_f16_encode(v);
+    if (j->d) j->d[i] = encode_out(j->p, v);
     if (j->ref) j->ref[i] = v;
     if (j->absum) j->absum[i] = s;
   }
@@ -224,14 +275,15 @@ static int run_points(const problem* p, const int64_t* pts, int64_t count, uint1
   return 0;
 }
 
-/* Values at the listed (batch, m, n) points only: d (fp16 codes of the
- * rounded result), ref (fp64 before rounding) and absum may each be NULL. */
+/* Values at the listed (batch, m, n) points only: d (codes of the result
+ * rounded to out_dtype), ref (fp64 before rounding) and absum may each be
+ * NULL. */
 int go_gemm_points(const go_tensor* a, const go_tensor* b, const go_tensor* c,
                    const go_tensor* sfa, const go_tensor* sfb, int32_t block_k,
                    const int64_t* pts, int64_t count, uint16_t* d, double* ref,
-                   double* absum, int32_t nthreads) {
+                   double* absum, int32_t nthreads, int32_t out_dtype) {
   problem p;
-  int rc = setup(&p, a, b, c, sfa, sfb, block_k);
+  int rc = setup(&p, a, b, c, sfa, sfb, block_k, out_dtype);
   if (rc) return rc;
   return run_points(&p, pts, count, d, ref, absum, nthreads);
 }
@@ -255,7 +307,7 @@ static void* row_worker(void* arg) {
       double v, s;
       one_point(j->p, bi, m, n, &v, &s);
       int64_t o = r * j->N + n;
-      if (j->d) j->d[o] = go_f16_encode(v);
+      if (j->d) j->d[o] = encode_out(j->p, v);
       if (j->ref) j->ref[o] = v;
       if (j->absum) j->absum[o] = s;
     }
@@ -266,9 +318,9 @@ static void* row_worker(void* arg) {
 /* Every output element, written densely as (batch, M, N) row-major. */
 int go_gemm(const go_tensor* a, const go_tensor* b, const go_tensor* c, const go_tensor* sfa,
             const go_tensor* sfb, int32_t block_k, int64_t batch, uint16_t* d, double* ref,
-            double* absum, int32_t nthreads) {
+            double* absum, int32_t nthreads, int32_t out_dtype) {
   problem p;
-  int rc = setup(&p, a, b, c, sfa, sfb, block_k);
+  int rc = setup(&p, a, b, c, sfa, sfb, block_k, out_dtype);
   if (rc) return rc;
   int64_t M = rows_of(a), N = rows_of(b), rows = batch * M;
   if (nthreads < 1) nthreads = 1;
@@ -295,19 +347,23 @@ int go_gemm(const go_tensor* a, const go_tensor* b, const go_tensor* c, const go
 
 /* ----------------------------------------------------------- acceptance */
 
-/* Per element: |D - D_ref| <= 2^-10 |D_ref| + 2^-13 S, where D_ref is the
- * fp64 value rounded to fp16 and both D and D_ref are decoded from fp16.
+/* Per element: |D - D_ref| <= 2^-r |D_ref| + 2^-13 S, where D_ref is the
+ * fp64 value rounded to the output format and both D and D_ref are decoded
+ * from it; r = 10 for fp16 and 7 for bf16 (twice the format's unit
+ * roundoff, 2^-11 and 2^-8).
  * A NaN on either side fails.  Returns the number of violations and
  * writes the index of the worst one (largest excess over the bound) and
  * the excess ratio |D - D_ref| / bound. */
 int64_t go_check(const uint16_t* d, const uint16_t* d_ref, const double* absum, int64_t count,
-                 int64_t* worst_index, double* worst_ratio) {
+                 int64_t* worst_index, double* worst_ratio, int32_t out_dtype) {
   pthread_once(&g_tab_once, fill_tables);
+  const double* tab = out_dtype == GO_BF16 ? g_bf16_tab : g_f16_tab;
+  const int rel = out_dtype == GO_BF16 ? -7 : -10;
   int64_t bad = 0, wi = -1;
   double wr = 0.0;
   for (int64_t i = 0; i < count; ++i) {
-    double x = g_f16_tab[d[i]], r = g_f16_tab[d_ref[i]];
-    double bound = ldexp(fabs(r), -10) + ldexp(absum[i], -13);
+    double x = tab[d[i]], r = tab[d_ref[i]];
+    double bound = ldexp(fabs(r), rel) + ldexp(absum[i], -13);
     double err = fabs(x - r);
     int ok;
     double ratio;

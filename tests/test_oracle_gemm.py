@@ -259,3 +259,73 @@ def test_check_bound():
     assert G.check(np.array([one, up2, one, one], np.uint16), d_ref, absum2)[0] == 0
     # NaN never passes
     assert G.check(np.array([0x7e00], np.uint16), np.array([0x7e00], np.uint16), np.zeros(1))[0] == 1
+
+
+# ---------------------------------------------------------------- bf16
+
+def _bf16_values():
+    codes = np.arange(65536, dtype=np.uint16)
+    return codes, torch.from_numpy(codes.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_bf16_decode_all_codes():
+    codes, ref = _bf16_values()
+    got = np.array([G.bf16_decode(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_encode_is_nearest_even_by_brute_force():
+    """Every finite code round-trips; and for values between codes (random,
+    exact midpoints, subnormal, near overflow) the encoder returns the
+    nearest finite bf16, ties to the even code, found by search over the
+    decoded table (itself pinned to torch above)."""
+    codes, vals = _bf16_values()
+    pos = [(v, int(c)) for c, v in zip(codes, vals) if np.isfinite(v) and v > 0 and not (int(c) & 0x8000)]
+    pos.sort()
+    pv = np.array([v for v, _ in pos])
+    pc = [c for _, c in pos]
+    for c, v in zip(codes, vals):
+        if np.isfinite(v):
+            assert G.bf16_encode(float(v)) == int(c)
+    rng = np.random.default_rng(5)
+    xs = list(rng.uniform(0, 1, 300) * 2.0 ** rng.integers(-140, 128, 300))
+    xs += [0.5 * (pv[i] + pv[i + 1]) for i in rng.integers(0, len(pv) - 1, 300)]  # exact midpoints
+    xs += [2.0 ** -134, 3 * 2.0 ** -134, 2.0 ** -126 * (1 - 2.0 ** -9)]
+    for x in xs:
+        i = int(np.searchsorted(pv, x))
+        if i == 0:
+            cand = [(0.0, 0)] + [(pv[0], pc[0])]
+        elif i >= len(pv):
+            cand = [(pv[-1], pc[-1])]
+        else:
+            cand = [(pv[i - 1], pc[i - 1]), (pv[i], pc[i])]
+        best = min(cand, key=lambda t: (abs(t[0] - x), t[1] & 1))
+        if x >= pv[-1] + 0.5 * (pv[-1] - pv[-2]):
+            best = (np.inf, 0x7F80)  # at or past the midpoint to 2^128: infinity
+        assert G.bf16_encode(float(x)) == best[1], x
+        assert G.bf16_encode(-float(x)) == best[1] | 0x8000, x
+
+
+def test_bf16_gemm_exact_integers_vs_numpy():
+    rng = np.random.default_rng(8)
+    M, N, K = 33, 20, 48
+    a = rng.integers(-4, 5, (M, K)).astype(np.float64)
+    b = rng.integers(-4, 5, (N, K)).astype(np.float64)
+    c = rng.integers(-4, 5, (M, N)).astype(np.float64)
+    enc = lambda x: np.array([G.bf16_encode(float(v)) for v in x.ravel()], np.uint16).reshape(x.shape)
+    d, ref, absum = G.gemm(enc(a), enc(b).T.copy().T, enc(c), bf16=True)
+    want = a @ b.T + c
+    assert np.array_equal(ref[0], want)
+    assert np.array_equal(d[0], enc(want))
+    assert np.array_equal(absum[0], np.abs(a) @ np.abs(b).T)
+
+
+def test_check_bound_bf16():
+    one = G.bf16_encode(1.0)
+    up1, up2 = one + 1, one + 2         # 1 + 2^-7, 1 + 2^-6
+    d_ref = np.array([one, one], np.uint16)
+    assert G.check(np.array([one, up1], np.uint16), d_ref, np.zeros(2), bf16=True)[0] == 0
+    assert G.check(np.array([one, up2], np.uint16), d_ref, np.zeros(2), bf16=True)[0] == 1
