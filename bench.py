@@ -13,7 +13,7 @@ seed 1) -- the large square case the fp16 throughput target is stated on.
 Other workloads (for measurement only): fp16_4096 (the same recipe at 4096),
 ragged (4000x3000x2056), skinny (8192x128x8192), batched_nn / batched_nt
 (64 x 512^3, A M-contiguous), batched_tn / batched_tt (A K-contiguous),
-mxfp8 (8192^3 MXFP8).
+mxfp8 (8192^3 MXFP8), bf16_8192 (the default recipe in bf16).
 
 The CPU baseline is the oracle (plain fp64 triple loop, all host cores) on a
 bounded sample of output points of the same workload, scaled to TFLOP/s.
@@ -49,6 +49,9 @@ def workloads():
         "batched_tn": ("fp16 batched 64x512^3, A and B K-contiguous, seed 3", lambda: I.config4("TN")),
         "batched_tt": ("fp16 batched 64x512^3, A K-contiguous, B N-contiguous, seed 3", lambda: I.config4("TT")),
         "mxfp8": ("MXFP8 GEMM M=N=K=8192, E4M3 data, E8M0 scale per 32 K, C=0, seed 4", lambda: I.config5(8192)),
+        "bf16_8192": ("bf16 TN GEMM M=N=K=8192, A/B/C normal(0,1) bf16, seed 1",
+                      lambda: I.gemm_workload("bf16_tn_8192_c", 8192, 8192, 8192, seed=1, dist="normal",
+                                              with_c=True, bf16=True)),
     }
 
 
@@ -204,7 +207,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f8e4m3" if w.mx else "f16",
+        "dtype": "f8e4m3" if w.mx else "bf16" if w.bf16 else "f16",
         "data": "synthetic",
         "config": {"workload": desc, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
                    "tile": f"{plan['tile_m']}x{plan['tile_n']}x{plan['tile_k']}",

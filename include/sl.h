@@ -50,8 +50,9 @@
  *    waiting.  Errors reported by the launch return SL_ERR_LAUNCH.  A
  *    split-K plan launches two kernels (partial sums, then D = C + their
  *    sum) on the same stream.
- *  - Numerics: fp16 products are accumulated in fp32; the result (plus C,
- *    added in fp32) is rounded to fp16 to nearest-even, overflow to +-inf.
+ *  - Numerics: fp16 (bf16) products are accumulated in fp32; the result
+ *    (plus C, added in fp32) is rounded to fp16 (bf16) to nearest-even,
+ *    overflow to +-inf.  bf16 inputs take bf16 C and D.
  *    A split-K plan sums each K-split in fp32 and then adds the splits in
  *    fp32 (a different summation order, same precision).
  */
@@ -70,7 +71,8 @@ typedef enum {
   SL_F16 = 1,     /* IEEE binary16 */
   SL_F32 = 2,     /* IEEE binary32 (accepted for nothing but reported) */
   SL_F8_E4M3 = 3, /* OCP MX E4M3 (bias 7, max 448, S.1111.111 = NaN) */
-  SL_E8M0 = 4     /* OCP MX E8M0 scale: 2^(b-127), 255 = NaN */
+  SL_E8M0 = 4,    /* OCP MX E8M0 scale: 2^(b-127), 255 = NaN */
+  SL_BF16 = 5     /* bfloat16: binary32's sign and 8-bit exponent, 7 stored significand bits */
 } sl_dtype;
 
 typedef enum {
@@ -102,10 +104,10 @@ typedef struct {
 } sl_tensor;
 
 typedef struct {
-  sl_tensor a;     /* (batch?, M, K)  f16, or f8_e4m3 with scales          */
+  sl_tensor a;     /* (batch?, M, K)  f16, bf16, or f8_e4m3 with scales    */
   sl_tensor b;     /* (batch?, N, K)  same dtype as a                      */
-  sl_tensor c;     /* (batch?, M, N)  f16; data == NULL means C = 0        */
-  sl_tensor d;     /* (batch?, M, N)  f16 output                           */
+  sl_tensor c;     /* (batch?, M, N)  D's dtype; data == NULL means C = 0  */
+  sl_tensor d;     /* (batch?, M, N)  bf16 for bf16 a/b, else f16 output  */
   sl_tensor sfa;   /* (batch?, M, ceil(K/block_k)) e8m0; f8 operands only */
   sl_tensor sfb;   /* (batch?, N, ceil(K/block_k)) e8m0                    */
   int32_t block_k; /* 32 for MXFP8; ignored for f16                        */
@@ -130,9 +132,13 @@ typedef struct {
 } sl_plan;
 
 /*
- * D = A * B^T + C over the strided descriptors above (f16 x f16 -> f16 with
- * fp32 accumulation), or the MXFP8 block-scaled form when a and b are
- * SL_F8_E4M3 and sfa/sfb are SL_E8M0 with block_k == 32.
+ * D = A * B^T + C over the strided descriptors above (f16 x f16 -> f16 or
+ * bf16 x bf16 -> bf16, with fp32 accumulation), or the MXFP8 block-scaled
+ * form when a and b are SL_F8_E4M3 and sfa/sfb are SL_E8M0 with
+ * block_k == 32 (the matrix product of "CuTe 中 A、B 如何加载到 MMA 寄存器",
+ * section 1, and the block-scaled product of "数据布局及其记号", section
+ * "Replication 与 Offset").  bf16 is the same product in another 16-bit
+ * format; the pages name fp16 only.
  * `stream` is a hipStream_t.  Asynchronous; see Conventions.
  */
 sl_status sl_gemm(const sl_gemm_args* args, void* stream);

@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libstride_layouts_lds.so")
 
-SL_F16, SL_F32, SL_F8_E4M3, SL_E8M0 = 1, 2, 3, 4
+SL_F16, SL_F32, SL_F8_E4M3, SL_E8M0, SL_BF16 = 1, 2, 3, 4, 5
 K_F16, K_F16_GENERIC, K_MX, K_MX_W8 = 1, 2, 3, 4
 STATUS = {0: "SL_OK", -1: "SL_ERR_NULL", -2: "SL_ERR_DTYPE", -3: "SL_ERR_SHAPE", -4: "SL_ERR_LAYOUT",
           -5: "SL_ERR_ALIGN", -6: "SL_ERR_ALIAS", -7: "SL_ERR_ARCH", -8: "SL_ERR_LAUNCH", -9: "SL_ERR_ARG",
@@ -117,7 +117,7 @@ def _torch_dtype_code(x, override: Optional[int]) -> int:
     import torch
     if override is not None:
         return override
-    table = {torch.float16: SL_F16, torch.float32: SL_F32, torch.float8_e4m3fn: SL_F8_E4M3,
+    table = {torch.float16: SL_F16, torch.bfloat16: SL_BF16, torch.float32: SL_F32, torch.float8_e4m3fn: SL_F8_E4M3,
              torch.float8_e8m0fnu: SL_E8M0}
     if x.dtype not in table:
         raise TypeError(f"unsupported dtype {x.dtype}")
@@ -163,14 +163,15 @@ def sl_gemm_plan(args: sl_gemm_args) -> dict:
 
 def gemm(a, b, c=None, out=None, sfa=None, sfb=None, block_k: int = 32, stream: Optional[int] = None):
     """D = A B^T + C on torch tensors (any strides).  ``a``: (batch?, M, K)
-    fp16 or float8_e4m3fn; ``b``: (batch?, N, K); ``c``: (batch?, M, N) fp16
-    or None; ``sfa``/``sfb``: float8_e8m0fnu scales (batch?, rows, K/32) for
+    fp16, bf16 or float8_e4m3fn; ``b``: (batch?, N, K); ``c``: (batch?, M, N)
+    of D's dtype (bf16 for bf16 operands, else fp16) or None; ``sfa``/``sfb``: float8_e8m0fnu scales (batch?, rows, K/32) for
     the MX form.  Returns ``out`` (allocated by torch if None)."""
     import torch
     if out is None:
         batch = max(x.shape[0] if x is not None and x.dim() == 3 else 0 for x in (a, b, c))
         shape = (a.shape[-2], b.shape[-2]) if batch == 0 else (batch, a.shape[-2], b.shape[-2])
-        out = torch.empty(shape, dtype=torch.float16, device=a.device)
+        out = torch.empty(shape, dtype=torch.bfloat16 if a.dtype == torch.bfloat16 else torch.float16,
+                          device=a.device)
     sl_gemm(make_args(a, b, c, out, sfa, sfb, block_k), stream)
     return out
 

@@ -33,6 +33,7 @@ sl_status fail(sl_status s, const char* fmt, ...) {
 int elem_size(int32_t dt) {
   switch (dt) {
     case SL_F16: return 2;
+    case SL_BF16: return 2;
     case SL_F32: return 4;
     case SL_F8_E4M3: return 1;
     case SL_E8M0: return 1;
@@ -115,7 +116,6 @@ struct Plan {
   sl_plan pub;
   sl::GemmParams p;
   int32_t tile;
-  int32_t shift;
   bool mx;
   bool empty;
   size_t ws_bytes;  // split-K partial sums (0: none)
@@ -173,13 +173,16 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       return fail(SL_ERR_DTYPE, "MX operands need e8m0 sfa and sfb");
     if (args->block_k != 32) return fail(SL_ERR_SHAPE, "block_k must be 32 for MXFP8 (got %d)", args->block_k);
   } else {
-    if (args->a.dtype != SL_F16 || args->b.dtype != SL_F16)
-      return fail(SL_ERR_DTYPE, "a and b must both be f16, or both f8_e4m3 with scales");
-    if (args->sfa.data || args->sfb.data) return fail(SL_ERR_DTYPE, "scales given for f16 operands");
+    if (!((args->a.dtype == SL_F16 && args->b.dtype == SL_F16) || (args->a.dtype == SL_BF16 && args->b.dtype == SL_BF16)))
+      return fail(SL_ERR_DTYPE, "a and b must both be f16, both bf16, or both f8_e4m3 with scales");
+    if (args->sfa.data || args->sfb.data) return fail(SL_ERR_DTYPE, "scales given for 16-bit operands");
   }
-  if (args->d.dtype != SL_F16) return fail(SL_ERR_DTYPE, "d must be f16");
+  // D (and C) are bf16 for bf16 operands, f16 otherwise
+  const bool bf16 = args->a.dtype == SL_BF16;
+  const int32_t out_dt = bf16 ? SL_BF16 : SL_F16;
+  if (args->d.dtype != out_dt) return fail(SL_ERR_DTYPE, "d must be %s", bf16 ? "bf16" : "f16");
   const bool has_c = args->c.data != nullptr;
-  if (has_c && args->c.dtype != SL_F16) return fail(SL_ERR_DTYPE, "c must be f16");
+  if (has_c && args->c.dtype != out_dt) return fail(SL_ERR_DTYPE, "c must be %s", bf16 ? "bf16" : "f16");
 
   View A, B, C{}, D, SA{}, SB{};
   sl_status s;
@@ -281,7 +284,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     p.flags |= sl::F_C_VEC;
   p.splits = 1;
   p.split_tiles = 0;
-  P.shift = std::min(2, std::max(0, env_int("SL_SWZ", 0)));
+  if (bf16) p.flags |= sl::F_BF16;
   p.group_m = std::max(1, env_int("SL_GROUP_M", 8));
 
   int32_t tile = env_int("SL_TILE", -1);
@@ -352,7 +355,9 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
         p.split_tiles = (int32_t)per;
         p.splits = (int32_t)((std::max<int64_t>(T_all, 1) + per - 1) / per);
       }
-      if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T256x256_W2x4_P)) {
+      // the ping-pong variants (tiles 9-14) are fp16 only
+      const bool pingpong = tile >= sl::T256x256_PP && tile <= sl::T256x256_PPG;
+      if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T256x256_W2x4_P) || (bf16 && pingpong)) {
         const int32_t big = sl::T256x256_W2x4;
         tile = big;
         double best = 1e300;
@@ -483,7 +488,7 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (P.mx) {
-    e = sl::launch_gemm_mx(P.p, P.tile, P.shift, st);
+    e = sl::launch_gemm_mx(P.p, P.tile, st);
   } else if (P.ws_bytes) {
     hipMemPool_t pool;
     if ((s = workspace_pool(&pool)) != SL_OK) return s;
@@ -492,12 +497,12 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
     if (e != hipSuccess)
       return fail(SL_ERR_NOMEM, "split-K workspace of %zu bytes: %s", P.ws_bytes, hipGetErrorString(e));
     P.p.ws = (float*)ws;
-    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, P.shift, st);
+    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
     if (e == hipSuccess) e = sl::launch_splitk_reduce(P.p, st);
     const hipError_t ef = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = ef;
   } else {
-    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, P.shift, st);
+    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
   }
   if (e != hipSuccess) return fail(SL_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return SL_OK;
@@ -531,7 +536,8 @@ sl_status sl_query_fragment_map(int32_t instr, int32_t operand, int32_t* lane, i
 // kernel family ids
 constexpr int32_t kMnTile = 5;
 
-static int32_t current_shift() { return env_int("SL_SWZ", 0) ? 1 : 0; }
+// the kernels are built with the row-shift 0 swizzle (swz)
+static int32_t current_shift() { return 0; }
 
 sl_status sl_query_lds_map(int32_t variant, int32_t operand, int64_t* offsets, int64_t capacity, int32_t* rows,
                            int32_t* cols, int32_t* elem_bytes) {

@@ -20,7 +20,7 @@ namespace {
 // Epilogue: acc[i][j][r] is output (m, n) with
 //   m = m_base + 16 i + lane % 16,  n = n_base + 16 j + 4 (lane / 16) + r
 // D = fp16_rne(acc + C), stores predicated on m < M, n < N.
-template <int FM, int FN>
+template <int FM, int FN, int DT = DT_F16>
 __device__ __forceinline__ void epilogue(const floatx4 (&acc)[FM][FN], const GemmParams& p, int32_t batch,
                                          int64_t m_base, int64_t n_base, int32_t lane) {
   uint16_t* D = (uint16_t*)p.d + batch * p.d_bs;
@@ -29,7 +29,7 @@ __device__ __forceinline__ void epilogue(const floatx4 (&acc)[FM][FN], const Gem
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      store_quad(p, C, D, m_base + 16 * i + (lane & 15), n_base + 16 * j + 4 * (lane >> 4), acc[i][j]);
+      store_quad<DT>(p, C, D, m_base + 16 * i + (lane & 15), n_base + 16 * j + 4 * (lane >> 4), acc[i][j]);
 }
 
 // Split-K partial: acc[i][j] (same layout as the epilogue's) goes to
@@ -60,7 +60,7 @@ __device__ __forceinline__ void store_partial(const floatx4 (&acc)[FM][FN], cons
 // PIPE 0: per k-slice, read the fragments then issue the MFMAs (latency is
 // covered by the other wave on the SIMD when WM*WN = 8).  PIPE 1: two
 // fragment sets, the next slice is read while the current one computes.
-template <int BM, int BN, int WM, int WN, int ALOAD, int BLOAD, int SHIFT, int PIPE>
+template <int BM, int BN, int WM, int WN, int ALOAD, int BLOAD, int SHIFT, int PIPE, int DT = DT_F16>
 __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kernel(const GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma16<DT>(fb[j], fa[i], acc[i][j]);
   };
   constexpr int NREAD = FM + FN;          // ds_read_b128 per slice
   constexpr int NMFMA = FM * FN;          // MFMAs per slice
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
     }
   }
 
-  epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
 }
 
 // Multi-stage variant for K-contiguous operands: K-tiles of RB/2 fp16 (LDS
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
 // for outputs too small to fill the chip with big tiles (skinny N): one
 // 32-row panel of A per workgroup, read once from HBM, against all of B,
 // which every workgroup shares through L2.
-template <int BM, int BN, int WM, int WN, int STAGES, int SHIFT, int RB = 64>
+template <int BM, int BN, int WM, int WN, int STAGES, int SHIFT, int RB = 64, int DT = DT_F16>
 __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_kernel(const GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma16<DT>(fb[j], fa[i], acc[i][j]);
     }
     // tile t+1 landed (this wave's part); the barrier publishes every
     // wave's part and, with this wave's LDS reads complete, retires tile t's
@@ -265,12 +265,13 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
   if (p.splits > 1)
     store_partial<FM, FN>(acc, p, tc.split, tc.batch, m0 + a_row0, n0 + b_row0, lane);
   else
-    epilogue<FM, FN>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+    epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
 }
 
-// D = fp16(C + sum_s ws[s]) over every output, four consecutive n per
-// thread (grid-stride).  The partial planes are [batch][M][N] fp32,
-// contiguous.
+// D = round(C + sum_s ws[s]) to D's format over every output, four
+// consecutive n per thread (grid-stride).  The partial planes are
+// [batch][M][N] fp32, contiguous.
+template <int DT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
   const int64_t nq = (p.N + 3) / 4;
   const int64_t total = (int64_t)p.batch * p.M * nq;
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) 
     }
     uint16_t* D = (uint16_t*)p.d + b * p.d_bs;
     const uint16_t* C = (p.flags & F_HAS_C) ? (const uint16_t*)p.c + b * p.c_bs : nullptr;
-    store_quad(p, C, D, m, n, v);
+    store_quad<DT>(p, C, D, m, n, v);
   }
 }
 
@@ -678,40 +679,103 @@ __global__ __launch_bounds__(512, 2) void gemm_f16_ppg_kernel(const GemmParams p
   }
 }
 
-template <int BM, int BN, int WM, int WN, int AL, int BL, int PIPE>
-hipError_t launch_cfg(const GemmParams& p, int32_t shift, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, int AL, int BL, int PIPE, int DT>
+hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
   dim3 grid((uint32_t)total), block(WM * WN * 64);
-  if (shift == 0)
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, AL, BL, 0, PIPE>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, AL, BL, 1, PIPE>), grid, block, 0, s, p);
+  hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, AL, BL, 0, PIPE, DT>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int RB = 64>
-hipError_t launch_ms(const GemmParams& p, int32_t shift, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, int STAGES, int RB, int DT>
+hipError_t launch_ms(const GemmParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.splits * p.batch * p.tiles_m * p.tiles_n;
   dim3 grid((uint32_t)total), block(WM * WN * 64);
-  switch (shift) {
-    case 0: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 0, RB>), grid, block, 0, s, p); break;
-    case 1: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 1, RB>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 2, RB>), grid, block, 0, s, p); break;
+  hipLaunchKernelGGL((gemm_f16_ms_kernel<BM, BN, WM, WN, STAGES, 0, RB, DT>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+template <int AL, int BL, int DT>
+hipError_t launch_tile(const GemmParams& p, int32_t tile, hipStream_t s) {
+  switch (tile) {
+    case T256x256_W2x2: return launch_cfg<256, 256, 2, 2, AL, BL, 0, DT>(p, s);
+    case T256x128_W2x2: return launch_cfg<256, 128, 2, 2, AL, BL, 0, DT>(p, s);
+    case T128x256_W2x2: return launch_cfg<128, 256, 2, 2, AL, BL, 0, DT>(p, s);
+    case T128x128_W2x2: return launch_cfg<128, 128, 2, 2, AL, BL, 0, DT>(p, s);
+    case T256x256_W2x4: return launch_cfg<256, 256, 2, 4, AL, BL, 0, DT>(p, s);
+    case T256x256_W2x4_P: return launch_cfg<256, 256, 2, 4, AL, BL, 1, DT>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// the ping-pong variants (fp16 only)
+hipError_t launch_pingpong(const GemmParams& p, int32_t tile, hipStream_t s) {
+  const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
+  const dim3 g((uint32_t)total), b(512);
+  switch (tile) {
+    case T256x256_PP: hipLaunchKernelGGL(gemm_f16_pp_kernel<0>, g, b, 0, s, p); break;
+    case T256x256_PPS4: hipLaunchKernelGGL((gemm_f16_pps_kernel<4, 0>), g, b, 0, s, p); break;
+    case T256x256_PPS5: hipLaunchKernelGGL((gemm_f16_pps_kernel<5, 0>), g, b, 0, s, p); break;
+    case T256x256_PPC4: hipLaunchKernelGGL((gemm_f16_pps2_kernel<4, 0>), g, b, 0, s, p); break;
+    case T256x256_PPC5: hipLaunchKernelGGL((gemm_f16_pps2_kernel<5, 0>), g, b, 0, s, p); break;
+    case T256x256_PPG: hipLaunchKernelGGL(gemm_f16_ppg_kernel<0>, g, b, 0, s, p); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int AL, int BL>
-hipError_t launch_tile(const GemmParams& p, int32_t tile, int32_t shift, hipStream_t s) {
-  switch (tile) {
-    case T256x256_W2x2: return launch_cfg<256, 256, 2, 2, AL, BL, 0>(p, shift, s);
-    case T256x128_W2x2: return launch_cfg<256, 128, 2, 2, AL, BL, 0>(p, shift, s);
-    case T128x256_W2x2: return launch_cfg<128, 256, 2, 2, AL, BL, 0>(p, shift, s);
-    case T128x128_W2x2: return launch_cfg<128, 128, 2, 2, AL, BL, 0>(p, shift, s);
-    case T256x256_W2x4: return launch_cfg<256, 256, 2, 4, AL, BL, 0>(p, shift, s);
-    case T256x256_W2x4_P: return launch_cfg<256, 256, 2, 4, AL, BL, 1>(p, shift, s);
-    default: return hipErrorInvalidValue;
+template <int DT>
+hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load, hipStream_t s) {
+  if (a_load == LOAD_GENERIC || b_load == LOAD_GENERIC) {
+    // one configuration for every stride pattern
+    if (tile != T128x128_W2x2) return hipErrorInvalidValue;
+    if (a_load == LOAD_GENERIC && b_load == LOAD_GENERIC)
+      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_GENERIC, 0, DT>(p, s);
+    if (a_load == LOAD_GENERIC && b_load == LOAD_KVEC)
+      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_KVEC, 0, DT>(p, s);
+    if (a_load == LOAD_KVEC && b_load == LOAD_GENERIC)
+      return launch_cfg<128, 128, 2, 2, LOAD_KVEC, LOAD_GENERIC, 0, DT>(p, s);
+    if (a_load == LOAD_GENERIC && b_load == LOAD_MNVEC)
+      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_MNVEC, 0, DT>(p, s);
+    if (a_load == LOAD_MNVEC && b_load == LOAD_GENERIC)
+      return launch_cfg<128, 128, 2, 2, LOAD_MNVEC, LOAD_GENERIC, 0, DT>(p, s);
+    return hipErrorInvalidValue;
   }
+  if (a_load == LOAD_KVEC && b_load == LOAD_KVEC) {
+    switch (tile) {
+      case T256x256_W2x4_S3: return launch_ms<256, 256, 2, 4, 3, 64, DT>(p, s);
+      case T256x256_W2x4_S4: return launch_ms<256, 256, 2, 4, 4, 64, DT>(p, s);
+      case T256x256_W2x4_S5: return launch_ms<256, 256, 2, 4, 5, 64, DT>(p, s);
+      case T32x128_STREAM: return launch_ms<32, 128, 1, 4, 6, 128, DT>(p, s);
+      case T128x128_SPLITK: return launch_ms<128, 128, 2, 4, 3, 128, DT>(p, s);
+      case T256x192_W2x4: return launch_cfg<256, 192, 2, 4, LOAD_KVEC, LOAD_KVEC, 0, DT>(p, s);
+      case T256x256_PP:
+      case T256x256_PPS4:
+      case T256x256_PPS5:
+      case T256x256_PPC4:
+      case T256x256_PPC5:
+      case T256x256_PPG:
+        if constexpr (DT == DT_F16) return launch_pingpong(p, tile, s);
+        return hipErrorInvalidValue;
+      default: return launch_tile<LOAD_KVEC, LOAD_KVEC, DT>(p, tile, s);
+    }
+  }
+  if (a_load == LOAD_MNDMA || b_load == LOAD_MNDMA) {
+    // the M-major direct-copy tiles exist for the 8-wave 256x256 kernel
+    if (tile != T256x256_W2x4) return hipErrorInvalidValue;
+    if (a_load == LOAD_MNDMA && b_load == LOAD_KVEC)
+      return launch_cfg<256, 256, 2, 4, LOAD_MNDMA, LOAD_KVEC, 0, DT>(p, s);
+    if (a_load == LOAD_KVEC && b_load == LOAD_MNDMA)
+      return launch_cfg<256, 256, 2, 4, LOAD_KVEC, LOAD_MNDMA, 0, DT>(p, s);
+    if (a_load == LOAD_MNDMA && b_load == LOAD_MNDMA)
+      return launch_cfg<256, 256, 2, 4, LOAD_MNDMA, LOAD_MNDMA, 0, DT>(p, s);
+    return hipErrorInvalidValue;
+  }
+  if (tile > T256x256_W2x4_P) return hipErrorInvalidValue;
+  if (a_load == LOAD_MNVEC && b_load == LOAD_KVEC) return launch_tile<LOAD_MNVEC, LOAD_KVEC, DT>(p, tile, s);
+  if (a_load == LOAD_KVEC && b_load == LOAD_MNVEC) return launch_tile<LOAD_KVEC, LOAD_MNVEC, DT>(p, tile, s);
+  if (a_load == LOAD_MNVEC && b_load == LOAD_MNVEC) return launch_tile<LOAD_MNVEC, LOAD_MNVEC, DT>(p, tile, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -719,101 +783,17 @@ hipError_t launch_tile(const GemmParams& p, int32_t tile, int32_t shift, hipStre
 hipError_t launch_splitk_reduce(const GemmParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.batch * p.M * ((p.N + 3) / 4);
   const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p);
+  const dim3 g((uint32_t)(blocks < 4096 ? blocks : 4096)), b(256);
+  if (p.flags & F_BF16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<DT_BF16>, g, b, 0, s, p);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<DT_F16>, g, b, 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load,
-                           int32_t shift, hipStream_t s) {
-  if (a_load == LOAD_GENERIC || b_load == LOAD_GENERIC) {
-    // one configuration for every stride pattern
-    if (tile != T128x128_W2x2) return hipErrorInvalidValue;
-    if (a_load == LOAD_GENERIC && b_load == LOAD_GENERIC)
-      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_GENERIC, 0>(p, shift, s);
-    if (a_load == LOAD_GENERIC && b_load == LOAD_KVEC)
-      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_KVEC, 0>(p, shift, s);
-    if (a_load == LOAD_KVEC && b_load == LOAD_GENERIC)
-      return launch_cfg<128, 128, 2, 2, LOAD_KVEC, LOAD_GENERIC, 0>(p, shift, s);
-    if (a_load == LOAD_GENERIC && b_load == LOAD_MNVEC)
-      return launch_cfg<128, 128, 2, 2, LOAD_GENERIC, LOAD_MNVEC, 0>(p, shift, s);
-    if (a_load == LOAD_MNVEC && b_load == LOAD_GENERIC)
-      return launch_cfg<128, 128, 2, 2, LOAD_MNVEC, LOAD_GENERIC, 0>(p, shift, s);
-    return hipErrorInvalidValue;
-  }
-  if (a_load == LOAD_KVEC && b_load == LOAD_KVEC) {
-    switch (tile) {
-      case T256x256_W2x4_S3: return launch_ms<256, 256, 2, 4, 3>(p, shift, s);
-      case T256x256_W2x4_S4: return launch_ms<256, 256, 2, 4, 4>(p, shift, s);
-      case T256x256_W2x4_S5: return launch_ms<256, 256, 2, 4, 5>(p, shift, s);
-      case T32x128_STREAM: return launch_ms<32, 128, 1, 4, 6, 128>(p, shift, s);
-      case T128x128_SPLITK: return launch_ms<128, 128, 2, 4, 3, 128>(p, shift, s);
-      case T256x192_W2x4: return launch_cfg<256, 192, 2, 4, LOAD_KVEC, LOAD_KVEC, 0>(p, shift, s);
-      case T256x256_PPG: {
-        const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
-        if (shift == 0)
-          hipLaunchKernelGGL(gemm_f16_ppg_kernel<0>, dim3((uint32_t)total), dim3(512), 0, s, p);
-        else
-          hipLaunchKernelGGL(gemm_f16_ppg_kernel<1>, dim3((uint32_t)total), dim3(512), 0, s, p);
-        return hipGetLastError();
-      }
-      case T256x256_PPC4:
-      case T256x256_PPC5: {
-        const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
-        const dim3 g((uint32_t)total), b(512);
-        if (tile == T256x256_PPC4) {
-          if (shift == 0) hipLaunchKernelGGL((gemm_f16_pps2_kernel<4, 0>), g, b, 0, s, p);
-          else if (shift == 1) hipLaunchKernelGGL((gemm_f16_pps2_kernel<4, 1>), g, b, 0, s, p);
-          else hipLaunchKernelGGL((gemm_f16_pps2_kernel<4, 2>), g, b, 0, s, p);
-        } else {
-          if (shift == 0) hipLaunchKernelGGL((gemm_f16_pps2_kernel<5, 0>), g, b, 0, s, p);
-          else if (shift == 1) hipLaunchKernelGGL((gemm_f16_pps2_kernel<5, 1>), g, b, 0, s, p);
-          else hipLaunchKernelGGL((gemm_f16_pps2_kernel<5, 2>), g, b, 0, s, p);
-        }
-        return hipGetLastError();
-      }
-      case T256x256_PPS4:
-      case T256x256_PPS5: {
-        const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
-        const dim3 g((uint32_t)total), b(512);
-        if (tile == T256x256_PPS4) {
-          if (shift == 0) hipLaunchKernelGGL((gemm_f16_pps_kernel<4, 0>), g, b, 0, s, p);
-          else if (shift == 1) hipLaunchKernelGGL((gemm_f16_pps_kernel<4, 1>), g, b, 0, s, p);
-          else hipLaunchKernelGGL((gemm_f16_pps_kernel<4, 2>), g, b, 0, s, p);
-        } else {
-          if (shift == 0) hipLaunchKernelGGL((gemm_f16_pps_kernel<5, 0>), g, b, 0, s, p);
-          else if (shift == 1) hipLaunchKernelGGL((gemm_f16_pps_kernel<5, 1>), g, b, 0, s, p);
-          else hipLaunchKernelGGL((gemm_f16_pps_kernel<5, 2>), g, b, 0, s, p);
-        }
-        return hipGetLastError();
-      }
-      case T256x256_PP: {
-        const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
-        if (shift == 0)
-          hipLaunchKernelGGL(gemm_f16_pp_kernel<0>, dim3((uint32_t)total), dim3(512), 0, s, p);
-        else
-          hipLaunchKernelGGL(gemm_f16_pp_kernel<1>, dim3((uint32_t)total), dim3(512), 0, s, p);
-        return hipGetLastError();
-      }
-      default: return launch_tile<LOAD_KVEC, LOAD_KVEC>(p, tile, shift, s);
-    }
-  }
-  if (a_load == LOAD_MNDMA || b_load == LOAD_MNDMA) {
-    // the M-major direct-copy tiles exist for the 8-wave 256x256 kernel
-    if (tile != T256x256_W2x4) return hipErrorInvalidValue;
-    if (a_load == LOAD_MNDMA && b_load == LOAD_KVEC)
-      return launch_cfg<256, 256, 2, 4, LOAD_MNDMA, LOAD_KVEC, 0>(p, shift, s);
-    if (a_load == LOAD_KVEC && b_load == LOAD_MNDMA)
-      return launch_cfg<256, 256, 2, 4, LOAD_KVEC, LOAD_MNDMA, 0>(p, shift, s);
-    if (a_load == LOAD_MNDMA && b_load == LOAD_MNDMA)
-      return launch_cfg<256, 256, 2, 4, LOAD_MNDMA, LOAD_MNDMA, 0>(p, shift, s);
-    return hipErrorInvalidValue;
-  }
-  if (tile > T256x256_W2x4_P) return hipErrorInvalidValue;
-  if (a_load == LOAD_MNVEC && b_load == LOAD_KVEC) return launch_tile<LOAD_MNVEC, LOAD_KVEC>(p, tile, shift, s);
-  if (a_load == LOAD_KVEC && b_load == LOAD_MNVEC) return launch_tile<LOAD_KVEC, LOAD_MNVEC>(p, tile, shift, s);
-  if (a_load == LOAD_MNVEC && b_load == LOAD_MNVEC)
-    return launch_tile<LOAD_MNVEC, LOAD_MNVEC>(p, tile, shift, s);
-  return hipErrorInvalidValue;
+hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load, hipStream_t s) {
+  if (p.flags & F_BF16) return launch_typed<DT_BF16>(p, tile, a_load, b_load, s);
+  return launch_typed<DT_F16>(p, tile, a_load, b_load, s);
 }
 
 }  // namespace sl

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_mx_kernel(const GemmParam
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      store_quad(p, C, D, m0 + a_row0 + 16 * i + (lane & 15), n0 + b_row0 + 16 * j + 4 * (lane >> 4), acc[i][j]);
+      store_quad<DT_F16>(p, C, D, m0 + a_row0 + 16 * i + (lane & 15), n0 + b_row0 + 16 * j + 4 * (lane >> 4), acc[i][j]);
 }
 
 // 8 waves (2 along M x 4 along N) on a 256 x 256 output tile, each wave a
@@ -300,40 +300,33 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
       for (int g = 0; g < 4; ++g) {
         const int64_t n = n0 + b_row0 + 32 * j + 8 * g + 4 * (lane >> 5);
         const floatx16& a = acc[i][j];
-        store_quad(p, C, D, m, n, floatx4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]});
+        store_quad<DT_F16>(p, C, D, m, n, floatx4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]});
       }
   }
 }
 
 template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const GemmParams& p, int32_t shift, hipStream_t s) {
+hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
   dim3 grid((uint32_t)total), block(WM * WN * 64);
-  if (shift == 0)
-    hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, WM, WN, 0>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, WM, WN, 1>), grid, block, 0, s, p);
+  hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, WM, WN, 0>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, int32_t shift, hipStream_t s) {
+hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, hipStream_t s) {
   switch (tile) {
-    case T256x256_W2x2: return launch_cfg<256, 256, 2, 2>(p, shift, s);
-    case T256x128_W2x2: return launch_cfg<256, 128, 2, 2>(p, shift, s);
-    case T128x256_W2x2: return launch_cfg<128, 256, 2, 2>(p, shift, s);
-    case T128x128_W2x2: return launch_cfg<128, 128, 2, 2>(p, shift, s);
+    case T256x256_W2x2: return launch_cfg<256, 256, 2, 2>(p, s);
+    case T256x128_W2x2: return launch_cfg<256, 128, 2, 2>(p, s);
+    case T128x256_W2x2: return launch_cfg<128, 256, 2, 2>(p, s);
+    case T128x128_W2x2: return launch_cfg<128, 128, 2, 2>(p, s);
     case T256x256_W2x4: {
       dim3 grid((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), block(512);
-      const bool s16 = p.flags & F_SCALE16;
-      if (shift == 0) {
-        if (s16) hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 1>), grid, block, 0, s, p);
-      } else {
-        if (s16) hipLaunchKernelGGL((gemm_mx_w8_kernel<1, 4>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((gemm_mx_w8_kernel<1, 1>), grid, block, 0, s, p);
-      }
+      if (p.flags & F_SCALE16)
+        hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 1>), grid, block, 0, s, p);
       return hipGetLastError();
     }
     default: return hipErrorInvalidValue;

@@ -19,6 +19,37 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// One 16x16x32 MFMA step on 16-bit operands of element type DT (the
+// fragments travel as 16 raw bytes; fp16 and bf16 share the operand and
+// accumulator layouts).
+template <int DT>
+__device__ __forceinline__ floatx4 mfma16(const half8& a, const half8& b, const floatx4& c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+
+// 16-bit element of type DT -> fp32 (exact), and fp32 -> DT rounded to
+// nearest-even (overflow to infinity)
+template <int DT>
+__device__ __forceinline__ float to_f32(uint16_t bits) {
+  if constexpr (DT == DT_F16)
+    return (float)__builtin_bit_cast(_Float16, bits);
+  else
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+}
+template <int DT>
+__device__ __forceinline__ uint16_t from_f32(float v) {
+  if constexpr (DT == DT_F16)
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+  else
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
 
 using lds_void_t = __attribute__((address_space(3))) void;
 
@@ -95,10 +126,12 @@ __device__ __forceinline__ TileCoord map_tile(int32_t bid, int32_t total, int32_
 
 // ---------------------------------------------------------------------------
 // Epilogue store of four consecutive outputs (m, n..n+3) of one lane:
-// D = fp16_rne(v + C), predicated on m < M and n + r < N.  8-byte accesses
+// D = round(v + C) to D's 16-bit type DT (nearest-even), predicated on
+// m < M and n + r < N.  8-byte accesses
 // when the row is contiguous and aligned (F_D_VEC / F_C_VEC) and all four
 // columns are in range.
 // ---------------------------------------------------------------------------
+template <int DT = DT_F16>
 __device__ __forceinline__ void store_quad(const GemmParams& p, const uint16_t* C, uint16_t* D, int64_t m,
                                            int64_t n, floatx4 v) {
   if (m >= p.M || n >= p.N) return;
@@ -106,24 +139,22 @@ __device__ __forceinline__ void store_quad(const GemmParams& p, const uint16_t* 
   if (p.flags & F_HAS_C) {
     const uint16_t* cp = C + m * p.c_rs + n * p.c_cs;
     if (full && (p.flags & F_C_VEC)) {
-      const half4 cv = *(const half4*)cp;
-      v[0] += (float)cv[0];
-      v[1] += (float)cv[1];
-      v[2] += (float)cv[2];
-      v[3] += (float)cv[3];
+      const u16x4 cv = *(const u16x4*)cp;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] += to_f32<DT>(cv[r]);
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (n + r < p.N) v[r] += (float)__builtin_bit_cast(_Float16, cp[r * p.c_cs]);
+        if (n + r < p.N) v[r] += to_f32<DT>(cp[r * p.c_cs]);
     }
   }
   uint16_t* dp = D + m * p.d_rs + n * p.d_cs;
   if (full && (p.flags & F_D_VEC)) {
-    *(half4*)dp = half4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *(u16x4*)dp = u16x4{from_f32<DT>(v[0]), from_f32<DT>(v[1]), from_f32<DT>(v[2]), from_f32<DT>(v[3])};
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (n + r < p.N) dp[r * p.d_cs] = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
+      if (n + r < p.N) dp[r * p.d_cs] = from_f32<DT>(v[r]);
   }
 }
 

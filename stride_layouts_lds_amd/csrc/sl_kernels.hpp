@@ -92,13 +92,19 @@ constexpr int32_t F_HAS_C = 1;
 constexpr int32_t F_D_VEC = 2;  // D rows contiguous and 8-B aligned: 4-half stores
 constexpr int32_t F_C_VEC = 4;  // C rows contiguous and 8-B aligned: 4-half loads
 constexpr int32_t F_SCALE16 = 8;  // MX scale rows 16-B aligned, a multiple of 16 blocks long
+constexpr int32_t F_BF16 = 16;    // A, B, C and D are bf16 (else fp16)
 
-// Launchers (each returns the launch's hipError_t).
+// element type of the 16-bit GEMM kernels (template argument)
+constexpr int DT_F16 = 0;
+constexpr int DT_BF16 = 1;
+
+// Launchers (each returns the launch's hipError_t).  The 16-bit kernels
+// take their element type from GemmParams.flags (F_BF16).
 hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load,
-                           int32_t swz_shift, hipStream_t stream);
+                           hipStream_t stream);
 // D = C + sum over splits of ws (the second kernel of a split-K GEMM).
 hipError_t launch_splitk_reduce(const GemmParams& p, hipStream_t stream);
-hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, int32_t swz_shift, hipStream_t stream);
+hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, hipStream_t stream);
 
 hipError_t launch_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t cases, hipStream_t stream);
 hipError_t launch_probe_lds(int32_t mode, const void* src, const int32_t* perm, void* out,

@@ -28,7 +28,7 @@ class HostOperand:
     storage: np.ndarray
     shape: Tuple[int, ...]
     strides: Tuple[int, ...]
-    kind: str  # 'f16' | 'e4m3' | 'e8m0'
+    kind: str  # 'f16' | 'bf16' | 'e4m3' | 'e8m0'
 
     @property
     def view(self) -> np.ndarray:
@@ -60,6 +60,10 @@ class Workload:
         return self.sfa is not None
 
     @property
+    def bf16(self) -> bool:
+        return self.a.kind == "bf16"
+
+    @property
     def flops(self) -> int:
         return 2 * self.batch * self.M * self.N * self.K
 
@@ -79,6 +83,12 @@ def _f16_codes(x: np.ndarray) -> np.ndarray:
     return x.astype(np.float16).view(np.uint16)
 
 
+def _bf16_codes(x: np.ndarray) -> np.ndarray:
+    import torch  # fp32 first, then torch's nearest-even bfloat16 conversion
+    t = torch.from_numpy(x.astype(np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
 def _e4m3_codes(x: np.ndarray) -> np.ndarray:
     import torch  # the cast rounds to nearest even; clamp first so it saturates
     t = torch.from_numpy(np.clip(x, -448.0, 448.0).astype(np.float32))
@@ -93,7 +103,7 @@ def matrix(rng, dist: str, batch: Optional[int], rows: int, cols: int, major: st
     (cols, rows) matrix."""
     nb = batch or 1
     x = _draw(rng, dist, nb * rows * cols)
-    codes = _e4m3_codes(x) if kind == "e4m3" else _f16_codes(x)
+    codes = _e4m3_codes(x) if kind == "e4m3" else _bf16_codes(x) if kind == "bf16" else _f16_codes(x)
     if major == "row":
         st = (rows * cols, cols, 1)
     elif major == "col":
@@ -123,15 +133,15 @@ def gemm_workload(name: str, M: int, N: int, K: int, *, seed: int, dist: str = "
                   batch: Optional[int] = None, a_major: str = "row", b_major: str = "row",
                   with_c: bool = False, c_dist: Optional[str] = None, mx: bool = False,
                   block_k: int = 32, rng: Optional[np.random.Generator] = None,
-                  scale_range: Tuple[int, int] = (-4, 4), scale_pad: int = 0) -> Workload:
+                  scale_range: Tuple[int, int] = (-4, 4), scale_pad: int = 0, bf16: bool = False) -> Workload:
     """A generic seeded GEMM problem.  ``a_major``/``b_major`` say which of
     the two matrix dimensions is contiguous: 'row' = K-contiguous (TN
     convention), 'col' = M- (or N-) contiguous."""
     rng = rng if rng is not None else np.random.default_rng(seed)
-    kind = "e4m3" if mx else "f16"
+    kind = "e4m3" if mx else "bf16" if bf16 else "f16"
     a = matrix(rng, dist, batch, M, K, a_major, kind)
     b = matrix(rng, dist, batch, N, K, b_major, kind)
-    c = matrix(rng, c_dist or dist, batch, M, N, "row") if with_c else None
+    c = matrix(rng, c_dist or dist, batch, M, N, "row", "bf16" if bf16 else "f16") if with_c else None
     sfa = sfb = None
     if mx:
         kb = -(-K // block_k)
@@ -151,7 +161,8 @@ def to_device(op: Optional[HostOperand]):
     if op is None:
         return None
     st = torch.from_numpy(np.ascontiguousarray(op.storage))
-    st = st.view({"f16": torch.float16, "e4m3": torch.float8_e4m3fn, "e8m0": torch.float8_e8m0fnu}[op.kind])
+    st = st.view({"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn,
+                  "e8m0": torch.float8_e8m0fnu}[op.kind])
     return st.to("cuda").as_strided(op.shape, op.strides)
 
 

@@ -25,7 +25,7 @@ def run_library(w: Workload, out=None, stream=None):
     a, b, c = to_device(w.a), to_device(w.b), to_device(w.c)
     sfa, sfb = to_device(w.sfa), to_device(w.sfb)
     if out is None:
-        out = torch.empty(w.d_shape, dtype=torch.float16, device="cuda")
+        out = torch.empty(w.d_shape, dtype=torch.bfloat16 if w.bf16 else torch.float16, device="cuda")
     api.gemm(a, b, c, out=out, sfa=sfa, sfb=sfb, block_k=w.block_k, stream=stream)
     torch.cuda.synchronize()
     return out
@@ -38,13 +38,14 @@ def d_codes(d) -> np.ndarray:
 
 def oracle_full(w: Workload):
     return OG.gemm(w.a.view, w.b.view, w.c.view if w.c else None,
-                   w.sfa.view if w.sfa else None, w.sfb.view if w.sfb else None, block_k=w.block_k)
+                   w.sfa.view if w.sfa else None, w.sfb.view if w.sfb else None, block_k=w.block_k,
+                   bf16=w.bf16)
 
 
 def oracle_points(w: Workload, pts: np.ndarray):
     return OG.gemm_points(w.a.view, w.b.view, w.c.view if w.c else None,
                           w.sfa.view if w.sfa else None, w.sfb.view if w.sfb else None, points=pts,
-                          block_k=w.block_k)
+                          block_k=w.block_k, bf16=w.bf16)
 
 
 def sample_points(w: Workload, n: int, seed: int = 0) -> np.ndarray:
@@ -66,13 +67,14 @@ def sample_points(w: Workload, n: int, seed: int = 0) -> np.ndarray:
     return np.concatenate(pts).astype(np.int64)
 
 
-def assert_within_bound(d: np.ndarray, d_ref: np.ndarray, absum: np.ndarray, what: str) -> None:
-    bad, wi, wr = OG.check(d, d_ref, absum)
+def assert_within_bound(d: np.ndarray, d_ref: np.ndarray, absum: np.ndarray, what: str, bf16: bool = False) -> None:
+    bad, wi, wr = OG.check(d, d_ref, absum, bf16=bf16)
     if bad:
-        dd = d.ravel()[wi].view(np.float16)
-        rr = d_ref.ravel()[wi].view(np.float16)
-        raise AssertionError(f"{what}: {bad} of {d.size} elements outside |D-Dref| <= 2^-10|Dref| + 2^-13 S; "
-                             f"worst index {wi}: D={float(dd)} Dref={float(rr)} S={absum.ravel()[wi]} "
+        dec = OG.bf16_decode if bf16 else OG.f16_decode
+        dd, rr = dec(int(d.ravel()[wi])), dec(int(d_ref.ravel()[wi]))
+        rel = "2^-7" if bf16 else "2^-10"
+        raise AssertionError(f"{what}: {bad} of {d.size} elements outside |D-Dref| <= {rel}|Dref| + 2^-13 S; "
+                             f"worst index {wi}: D={dd} Dref={rr} S={absum.ravel()[wi]} "
                              f"(error/bound {wr:.3g})")
 
 

@@ -319,3 +319,24 @@ def test_m_major_fragment_by_transposing_reads(api):
     for l in range(64):
         frag = got[0][l] + got[1][l]
         assert frag == [want[(l, v)] for v in range(8)], l
+
+
+def test_bf16_dtypes(api):
+    """bf16 operands take bf16 C and D; mixing 16-bit formats is rejected."""
+    BF = 5
+    A = (BASE_A, BF, (64, 32), (32, 1))
+    B = (BASE_B, BF, (48, 32), (32, 1))
+    Dbf = (BASE_D, BF, (64, 48), (48, 1))
+    p = plan(api, A, B, (BASE_C, BF, (64, 48), (48, 1)), Dbf)
+    assert p["kernel"] == api.K_F16
+    assert err(api, A, B, None, rowmajor(BASE_D, (64, 48))) == "SL_ERR_DTYPE"      # f16 D
+    assert err(api, A, rowmajor(BASE_B, (48, 32)), None, Dbf) == "SL_ERR_DTYPE"    # f16 B
+    assert err(api, A, B, rowmajor(BASE_C, (64, 48)), Dbf) == "SL_ERR_DTYPE"       # f16 C
+    # ping-pong tiles are fp16 only: a bf16 plan asked for one falls back to the planner's choice
+    os.environ["SL_TILE"] = "9"
+    try:
+        p = plan(api, (BASE_A, BF, (4096, 4096), (4096, 1)), (BASE_B, BF, (4096, 4096), (4096, 1)), None,
+                 (BASE_D, BF, (4096, 4096), (4096, 1)))
+    finally:
+        del os.environ["SL_TILE"]
+    assert p["tile_m"] == 256 and p["threads"] == 512

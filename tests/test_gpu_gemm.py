@@ -168,7 +168,7 @@ def test_splitk_in_place_and_repeated_calls(api, monkeypatch):
 def _plan(api, w):
     import torch
     h = H()
-    out = torch.empty(w.d_shape, dtype=torch.float16, device="cuda")
+    out = torch.empty(w.d_shape, dtype=torch.bfloat16 if w.bf16 else torch.float16, device="cuda")
     args = api.make_args(h.to_device(w.a), h.to_device(w.b), h.to_device(w.c), out, h.to_device(w.sfa),
                          h.to_device(w.sfb), w.block_k)
     p = api.sl_gemm_plan(args)
@@ -342,7 +342,7 @@ def _sampled(api, w, n=3000):
     d = h.d_codes(out).reshape(w.batch, w.M, w.N)
     pts = h.sample_points(w, n)
     d_ref, _, absum = h.oracle_points(w, pts)
-    h.assert_within_bound(d[pts[:, 0], pts[:, 1], pts[:, 2]], d_ref, absum, w.name)
+    h.assert_within_bound(d[pts[:, 0], pts[:, 1], pts[:, 2]], d_ref, absum, w.name, bf16=w.bf16)
 
 
 def test_config2_4096_with_c(api):
@@ -365,3 +365,70 @@ def test_config4_batched_strided(api, case):
 
 def test_config5_mxfp8_8192(api):
     _sampled(api, I.config5(8192), n=1500)
+
+
+# ------------------------------------------------------------------ bf16
+
+BF16_EXACT = [
+    # M, N, K, batch, a_major, b_major, with_c, forced tile (None: planner)
+    (300, 520, 200, None, "row", "row", True, None),
+    (520, 264, 136, 2, "col", "row", False, 4),      # M-major direct copy
+    (264, 136, 200, None, "col", "col", True, None),  # register-transposing loader
+    (70, 90, 37, None, "row", "row", True, None),     # element loaders
+    (300, 72, 2056, None, "row", "row", True, 16),    # split-K
+    (520, 300, 328, None, "row", "row", True, 17),
+    (520, 300, 328, None, "row", "row", True, 7),
+    (520, 300, 328, None, "row", "row", True, 15),
+    (520, 300, 328, None, "row", "row", True, 5),
+]
+
+
+@pytest.mark.parametrize("case", BF16_EXACT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_{c[4]}{c[5]}_t{c[7]}")
+def test_bf16_exact_parity(api, case, monkeypatch):
+    h = H()
+    M, N, K, batch, am, bm, with_c, tile = case
+    if tile is not None:
+        monkeypatch.setenv("SL_TILE", str(tile))
+    w = I.gemm_workload("bf16_exact", M, N, K, seed=M + N + K + 1, dist="int4", batch=batch, a_major=am,
+                        b_major=bm, with_c=with_c, bf16=True)
+    h.log(f"bf16 exact {case} plan={_plan(api, w)}")
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
+def test_bf16_bounded_and_sampled(api):
+    h = H()
+    w = I.gemm_workload("bf16_normal", 520, 264, 320, seed=41, dist="normal", with_c=True, bf16=True)
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, absum = h.oracle_full(w)
+    h.assert_within_bound(d.reshape(d_ref.shape), d_ref, absum, w.name, bf16=True)
+    _sampled(api, I.gemm_workload("bf16_tn_4096_c", 4096, 4096, 4096, seed=1, dist="normal", with_c=True,
+                                  bf16=True), n=1500)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f16", "bf16"])
+def test_output_rounding_ties_to_even(api, bf16):
+    """Sums that fall exactly halfway between two representable outputs:
+    D[m][n] = 1 + t_m with t_m = (2j+1) * ulp/2 (and quarter-ulps), so the
+    library's fp32 -> 16-bit conversion must round ties to the even code,
+    bit for bit with the oracle."""
+    import torch
+    h = H()
+    ulp = 2.0 ** -7 if bf16 else 2.0 ** -10
+    ts = [(2 * j + 1) * ulp / 2 for j in range(8)] + [ulp / 4, 3 * ulp / 4, -ulp / 4, -(2 * 3 + 1) * ulp / 4]
+    M, N, K = len(ts), 16, 32
+    a = np.zeros((M, K)); b = np.zeros((N, K))
+    a[:, 0] = 1.0; a[:, 1] = ts
+    b[:, 0] = 1.0; b[:, 1] = 1.0
+    dt = torch.bfloat16 if bf16 else torch.float16
+    at = torch.from_numpy(a).to(dt); bt = torch.from_numpy(b).to(dt)
+    assert torch.equal(at.double(), torch.from_numpy(a)), "inputs must be exact"
+    out = api.gemm(at.cuda(), bt.cuda())
+    torch.cuda.synchronize()
+    from oracle import gemm as OG
+    codes = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    d_ref, ref, _ = OG.gemm(codes(at), codes(bt), bf16=bf16)
+    assert np.array_equal(ref[0][:, 0], 1.0 + np.array(ts))
+    assert np.array_equal(h.d_codes(out), d_ref[0])
