@@ -27,7 +27,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gemm_ref.c")
 LIB = os.path.join(HERE, "libgemm_oracle.so")
 
-F16, F32, E4M3, E8M0, BF16 = 1, 2, 3, 4, 5
+F16, F32, E4M3, E8M0, BF16, E2M1 = 1, 2, 3, 4, 5, 6
 
 
 class _Tensor(ctypes.Structure):
@@ -68,6 +68,8 @@ def lib():
         L.go_bf16_decode.argtypes = [ctypes.c_uint16]
         L.go_bf16_encode.restype = ctypes.c_uint16
         L.go_bf16_encode.argtypes = [ctypes.c_double]
+        L.go_e2m1_decode.restype = ctypes.c_double
+        L.go_e2m1_decode.argtypes = [ctypes.c_uint8]
         L.go_e4m3_decode.restype = ctypes.c_double
         L.go_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.go_e8m0_decode.restype = ctypes.c_double
@@ -90,8 +92,27 @@ def lib():
 _DT = {np.dtype(np.uint16): F16, np.dtype(np.float16): F16, np.dtype(np.float32): F32}
 
 
-def _tensor(arr: Optional[np.ndarray], dtype: Optional[int] = None) -> _Tensor:
+def packed(storage: np.ndarray, shape: Sequence[int], strides: Sequence[int], dtype: int = None):
+    """An operand given as raw storage plus a shape and ELEMENT strides, for
+    formats numpy cannot view (E2M1, two elements per byte)."""
+    return ("packed", np.ascontiguousarray(storage), tuple(shape), tuple(strides), dtype)
+
+
+def _is_packed(x) -> bool:
+    return isinstance(x, tuple) and len(x) == 5 and x[0] == "packed"
+
+
+def _tensor(arr, dtype: Optional[int] = None) -> _Tensor:
     t = _Tensor()
+    if _is_packed(arr):
+        _, storage, shape, strides, code = arr
+        t.data = storage.ctypes.data
+        t.dtype = code if code is not None else dtype
+        t.rank = len(shape)
+        for i in range(len(shape)):
+            t.shape[i] = shape[i]
+            t.stride[i] = strides[i]
+        return t
     if arr is None:
         t.data = None
         t.dtype = 0
@@ -112,6 +133,8 @@ def _tensor(arr: Optional[np.ndarray], dtype: Optional[int] = None) -> _Tensor:
 
 def _args(a, b, c, sfa, sfb, mx: bool, bf16: bool = False):
     if mx:
+        # block-scaled: E4M3 data with E8M0 scales unless the operands say
+        # otherwise (packed E2M1 data, E4M3 scales for NVFP4)
         return (_tensor(a, E4M3), _tensor(b, E4M3), _tensor(c),
                 _tensor(sfa, E8M0), _tensor(sfb, E8M0))
     if bf16:
@@ -137,8 +160,9 @@ def gemm(a: np.ndarray, b: np.ndarray, c: Optional[np.ndarray] = None,
     bf16.  Returns (D codes as uint16 (batch, M, N), fp64 value before
     rounding, sum_k |A B| in fp64)."""
     mx = sfa is not None
-    batch = max(x.shape[0] if x is not None and x.ndim == 3 else 1 for x in (a, b, c))
-    M, N = a.shape[-2], b.shape[-2]
+    dims = lambda x: x[2] if _is_packed(x) else x.shape
+    batch = max(dims(x)[0] if x is not None and len(dims(x)) == 3 else 1 for x in (a, b, c))
+    M, N = dims(a)[-2], dims(b)[-2]
     d = np.empty((batch, M, N), np.uint16)
     ref = np.empty((batch, M, N), np.float64)
     absum = np.empty((batch, M, N), np.float64)
@@ -200,6 +224,10 @@ def bf16_decode(code: int) -> float:
 
 def bf16_encode(x: float) -> int:
     return lib().go_bf16_encode(x)
+
+
+def e2m1_decode(code: int) -> float:
+    return lib().go_e2m1_decode(code)
 
 
 def e4m3_decode(code: int) -> float:

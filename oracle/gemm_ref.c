@@ -21,6 +21,12 @@
  *    S.1111.111 is NaN, max 448; E8M0: 2^(b-127), 255 is NaN).
  *  - fp16 is IEEE 754 binary16 (bias 15, subnormals, inf/NaN); encoding
  *    rounds to nearest, ties to even, overflow to infinity.
+ *  - NVFP4 (same section): A_low, B_low FP4 E2M1 and one E4M3 scale per 16
+ *    consecutive K.  E2M1 follows the OCP MX v1.0 definition (bias 1, one
+ *    significand bit, subnormal 0.5, max 6, no infinities or NaN).  E2M1
+ *    operands are packed two per byte along K: element offset o (in
+ *    elements, from the descriptor's strides) is byte o / 2, low nibble for
+ *    even o, high nibble for odd o.
  *  - bf16 (the same product in the other 16-bit format; the pages name only
  *    fp16) is the upper half of IEEE binary32: bias 127, 7 stored
  *    significand bits, subnormals, inf/NaN; encoded the same way.
@@ -38,7 +44,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { GO_F16 = 1, GO_F32 = 2, GO_E4M3 = 3, GO_E8M0 = 4, GO_BF16 = 5 };
+enum { GO_F16 = 1, GO_F32 = 2, GO_E4M3 = 3, GO_E8M0 = 4, GO_BF16 = 5, GO_E2M1 = 6 };
 
 typedef struct {
   const void* data; /* NULL: absent (C = 0, or no scales) */
@@ -135,11 +141,19 @@ uint16_t go_bf16_encode(double x) {
   return sgn | (uint16_t)((e + 127) << 7) | (uint16_t)(q - 128);
 }
 
+/* E2M1: sign, 2-bit exponent (bias 1), 1-bit fraction */
+double go_e2m1_decode(uint8_t c) {
+  int sgn = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return sgn ? -v : v;
+}
+
 /* decoding tables, filled once from the functions above */
 static double g_f16_tab[65536];
 static double g_bf16_tab[65536];
 static double g_e4m3_tab[256];
 static double g_e8m0_tab[256];
+static double g_e2m1_tab[16];
 static pthread_once_t g_tab_once = PTHREAD_ONCE_INIT;
 
 static void fill_tables(void) {
@@ -151,6 +165,7 @@ static void fill_tables(void) {
     g_e4m3_tab[i] = go_e4m3_decode((uint8_t)i);
     g_e8m0_tab[i] = go_e8m0_decode((uint8_t)i);
   }
+  for (int i = 0; i < 16; ++i) g_e2m1_tab[i] = go_e2m1_decode((uint8_t)i);
 }
 
 /* ------------------------------------------------------- element addressing */
@@ -171,6 +186,10 @@ static double element(const go_tensor* t, int64_t b, int64_t i, int64_t j) {
     case GO_F32: return (double)((const float*)t->data)[o];
     case GO_E4M3: return g_e4m3_tab[((const uint8_t*)t->data)[o]];
     case GO_E8M0: return g_e8m0_tab[((const uint8_t*)t->data)[o]];
+    case GO_E2M1: {
+      const uint8_t byte = ((const uint8_t*)t->data)[o >> 1];
+      return g_e2m1_tab[(o & 1) ? byte >> 4 : byte & 15];
+    }
     default: return NAN;
   }
 }

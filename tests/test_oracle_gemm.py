@@ -329,3 +329,57 @@ def test_check_bound_bf16():
     d_ref = np.array([one, one], np.uint16)
     assert G.check(np.array([one, up1], np.uint16), d_ref, np.zeros(2), bf16=True)[0] == 0
     assert G.check(np.array([one, up2], np.uint16), d_ref, np.zeros(2), bf16=True)[0] == 1
+
+
+# ---------------------------------------------------------------- E2M1 / NVFP4
+
+def test_e2m1_decode_special_values_and_structure():
+    """OCP MX v1.0 E2M1: smallest subnormal 0.5, smallest normal 1.0, largest
+    6.0, sign-magnitude, no infinities or NaN; every value is an E4M3 value
+    (the E4M3 decoder is pinned to torch above)."""
+    v = [G.e2m1_decode(c) for c in range(16)]
+    pos = v[:8]
+    assert pos[0] == 0.0 and pos[1] == 0.5 and pos[2] == 1.0 and pos[7] == 6.0
+    assert all(pos[i] < pos[i + 1] for i in range(7))
+    assert all(v[8 + i] == -pos[i] for i in range(8)) and np.signbit(v[8])
+    assert all(np.isfinite(x) for x in v)
+    e4m3 = {G.e4m3_decode(c) for c in range(256)}
+    assert all(x in e4m3 for x in v)
+    # one significand bit: each binade [2^e, 2^(e+1)) holds exactly {2^e, 1.5 * 2^e}
+    assert pos[2:] == [1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """(rows, K) nibble codes -> (rows, K/2) bytes, element 2i in the low nibble."""
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_nvfp4_gemm_vs_numpy():
+    """Packed E2M1 operands with one E4M3 scale per 16 K: the oracle equals
+    numpy's fp64 matmul of the decoded, block-scaled values (all exact)."""
+    rng = np.random.default_rng(12)
+    M, N, K = 24, 18, 64
+    ca = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    cb = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    # E4M3 scales from a small exact set (powers of two and 1.5 * powers)
+    scale_codes = np.array([c for c in range(256) if G.e4m3_decode(c) in (0.25, 0.5, 0.75, 1.0, 1.5, 2.0, 3.0)],
+                           np.uint8)
+    sa = rng.choice(scale_codes, (M, K // 16)).astype(np.uint8)
+    sb = rng.choice(scale_codes, (N, K // 16)).astype(np.uint8)
+    dec2 = np.vectorize(G.e2m1_decode)
+    dec8 = np.vectorize(G.e4m3_decode)
+    a_real = dec2(ca) * np.repeat(dec8(sa), 16, axis=1)
+    b_real = dec2(cb) * np.repeat(dec8(sb), 16, axis=1)
+    A = G.packed(_pack_e2m1(ca), (M, K), (K, 1), G.E2M1)
+    B = G.packed(_pack_e2m1(cb), (N, K), (K, 1), G.E2M1)
+    SA = G.packed(sa, (M, K // 16), (K // 16, 1), G.E4M3)
+    SB = G.packed(sb, (N, K // 16), (K // 16, 1), G.E4M3)
+    d, ref, absum = G.gemm(A, B, None, SA, SB, block_k=16)
+    assert np.array_equal(ref[0], a_real @ b_real.T)
+    assert np.array_equal(absum[0], np.abs(a_real) @ np.abs(b_real).T)
+    # the same values with the odd elements' nibbles swapped differ: the
+    # packing order is observed
+    swapped = G.packed((_pack_e2m1(ca) >> 4) | (_pack_e2m1(ca) << 4) & 0xF0, (M, K), (K, 1), G.E2M1)
+    _, ref2, _ = G.gemm(swapped, B, None, SA, SB, block_k=16)
+    a_sw = dec2(ca.reshape(M, K // 2, 2)[:, :, ::-1].reshape(M, K)) * np.repeat(dec8(sa), 16, axis=1)
+    assert np.array_equal(ref2[0], a_sw @ b_real.T)
