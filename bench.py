@@ -13,7 +13,8 @@ seed 1) -- the large square case the fp16 throughput target is stated on.
 Other workloads (for measurement only): fp16_4096 (the same recipe at 4096),
 ragged (4000x3000x2056), skinny (8192x128x8192), batched_nn / batched_nt
 (64 x 512^3, A M-contiguous), batched_tn / batched_tt (A K-contiguous),
-mxfp8 (8192^3 MXFP8), bf16_8192 (the default recipe in bf16).
+mxfp8 (8192^3 MXFP8), nvfp4_8192 (8192^3 NVFP4), bf16_8192 (the default
+recipe in bf16).
 
 The CPU baseline is the oracle (plain fp64 triple loop, all host cores) on a
 bounded sample of output points of the same workload, scaled to TFLOP/s.
@@ -49,6 +50,8 @@ def workloads():
         "batched_tn": ("fp16 batched 64x512^3, A and B K-contiguous, seed 3", lambda: I.config4("TN")),
         "batched_tt": ("fp16 batched 64x512^3, A K-contiguous, B N-contiguous, seed 3", lambda: I.config4("TT")),
         "mxfp8": ("MXFP8 GEMM M=N=K=8192, E4M3 data, E8M0 scale per 32 K, C=0, seed 4", lambda: I.config5(8192)),
+        "nvfp4_8192": ("NVFP4 GEMM M=N=K=8192, E2M1 codes uniform, E4M3 scale per 16 K (2^[-4,0] x any mantissa), "
+                       "C=0, seed 6", lambda: I.nvfp4_workload("nvfp4_8192", 8192, 8192, 8192, seed=6)),
         "bf16_8192": ("bf16 TN GEMM M=N=K=8192, A/B/C normal(0,1) bf16, seed 1",
                       lambda: I.gemm_workload("bf16_tn_8192_c", 8192, 8192, 8192, seed=1, dist="normal",
                                               with_c=True, bf16=True)),
@@ -57,8 +60,8 @@ def workloads():
 
 def algorithmic_bytes(w) -> int:
     """A, B (and scales) read once, C read once if present, D written once."""
-    es = 1 if w.mx else 2
-    b = w.batch * (w.M * w.K + w.N * w.K) * es + w.batch * w.M * w.N * 2
+    es = 0.5 if w.nvfp4 else 1 if w.mx else 2
+    b = int(w.batch * (w.M * w.K + w.N * w.K) * es) + w.batch * w.M * w.N * 2
     if w.c is not None:
         b += w.batch * w.M * w.N * 2
     if w.mx:
@@ -95,11 +98,21 @@ def cpu_baseline(w, target_s: float = 12.0):
     threads = max(1, len(os.sched_getaffinity(0)))
     rng = np.random.default_rng(123)
 
+    def ora(op, code=None):
+        if op is None:
+            return None
+        if code is not None:  # raw storage with element strides (packed E2M1, NVFP4 scales)
+            return OG.packed(op.storage, op.shape, op.strides, code)
+        return op.view
+    if w.nvfp4:
+        ops = (ora(w.a, OG.E2M1), ora(w.b, OG.E2M1), ora(w.c), ora(w.sfa, OG.E4M3), ora(w.sfb, OG.E4M3))
+    else:
+        ops = (ora(w.a), ora(w.b), ora(w.c), ora(w.sfa), ora(w.sfb))
+
     def run(n):
         pts = np.stack([rng.integers(0, w.batch, n), rng.integers(0, w.M, n), rng.integers(0, w.N, n)], 1)
         t0 = time.perf_counter()
-        OG.gemm_points(w.a.view, w.b.view, w.c.view if w.c else None, w.sfa.view if w.sfa else None,
-                       w.sfb.view if w.sfb else None, points=pts, block_k=w.block_k, nthreads=threads)
+        OG.gemm_points(*ops, points=pts, block_k=w.block_k, nthreads=threads, bf16=w.bf16)
         return time.perf_counter() - t0
 
     n = max(threads * 4, 64)
@@ -155,7 +168,7 @@ def main():
     from stride_layouts_lds_amd.inputs import to_device
     a, b, c = to_device(w.a), to_device(w.b), to_device(w.c)
     sfa, sfb = to_device(w.sfa), to_device(w.sfb)
-    out = torch.empty(w.d_shape, dtype=torch.float16, device="cuda")
+    out = torch.empty(w.d_shape, dtype=torch.bfloat16 if w.bf16 else torch.float16, device="cuda")
     margs = api.make_args(a, b, c, out, sfa, sfb, w.block_k)
     plan = api.sl_gemm_plan(margs)
     stream = torch.cuda.current_stream()
@@ -181,7 +194,8 @@ def main():
 
     flop = w.flops
     value = flop * args.steps / wall / 1e12
-    peak = PEAK_F8 if w.mx else PEAK_F16
+    # NVFP4 is decoded to fp16 and multiplied on the fp16 matrix cores
+    peak = PEAK_F8 if (w.mx and not w.nvfp4) else PEAK_F16
     # the roofline that bounds the workload: MFMA when its arithmetic
     # intensity (algorithmic FLOP per algorithmic byte) is above the ridge
     # point peak / HBM bandwidth, HBM below it
@@ -207,7 +221,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f8e4m3" if w.mx else "bf16" if w.bf16 else "f16",
+        "dtype": "f4e2m1" if w.nvfp4 else "f8e4m3" if w.mx else "bf16" if w.bf16 else "f16",
         "data": "synthetic",
         "config": {"workload": desc, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
                    "tile": f"{plan['tile_m']}x{plan['tile_n']}x{plan['tile_k']}",

@@ -72,7 +72,9 @@ typedef enum {
   SL_F32 = 2,     /* IEEE binary32 (accepted for nothing but reported) */
   SL_F8_E4M3 = 3, /* OCP MX E4M3 (bias 7, max 448, S.1111.111 = NaN) */
   SL_E8M0 = 4,    /* OCP MX E8M0 scale: 2^(b-127), 255 = NaN */
-  SL_BF16 = 5     /* bfloat16: binary32's sign and 8-bit exponent, 7 stored significand bits */
+  SL_BF16 = 5,    /* bfloat16: binary32's sign and 8-bit exponent, 7 stored significand bits */
+  SL_F4_E2M1 = 6  /* OCP MX E2M1 (bias 1, max 6), packed two per byte along the unit-stride
+                     (K) axis: element offset o is byte o/2, low nibble for even o */
 } sl_dtype;
 
 typedef enum {
@@ -104,20 +106,22 @@ typedef struct {
 } sl_tensor;
 
 typedef struct {
-  sl_tensor a;     /* (batch?, M, K)  f16, bf16, or f8_e4m3 with scales    */
+  sl_tensor a;     /* (batch?, M, K)  f16, bf16, f8_e4m3 or f4_e2m1 (scaled) */
   sl_tensor b;     /* (batch?, N, K)  same dtype as a                      */
   sl_tensor c;     /* (batch?, M, N)  D's dtype; data == NULL means C = 0  */
   sl_tensor d;     /* (batch?, M, N)  bf16 for bf16 a/b, else f16 output  */
-  sl_tensor sfa;   /* (batch?, M, ceil(K/block_k)) e8m0; f8 operands only */
-  sl_tensor sfb;   /* (batch?, N, ceil(K/block_k)) e8m0                    */
-  int32_t block_k; /* 32 for MXFP8; ignored for f16                        */
+  sl_tensor sfa;   /* (batch?, M, ceil(K/block_k)) e8m0 (MXFP8) or f8_e4m3 (NVFP4) */
+  sl_tensor sfb;   /* (batch?, N, ceil(K/block_k)) same dtype as sfa       */
+  int32_t block_k; /* 32 for MXFP8, 16 for NVFP4; ignored for f16 / bf16   */
 } sl_gemm_args;
 
 /* What sl_gemm would launch for these arguments (host only, no HIP call). */
 typedef struct {
-  int32_t kernel;     /* kernel family: 1 fp16 fast, 2 fp16 generic, 3 mxfp8
-                         (4 waves, 16x16x128 instruction), 4 mxfp8 (8 waves,
-                         32x32x64 instruction, scales staged in LDS) */
+  int32_t kernel;     /* kernel family: 1 fp16/bf16 fast, 2 fp16/bf16 with an
+                         element loader, 3 mxfp8 (4 waves, 16x16x128
+                         instruction), 4 mxfp8 (8 waves, 32x32x64 instruction,
+                         scales staged in LDS), 5 nvfp4 (decoded to fp16 in
+                         the loader, fp16 instruction) */
   int32_t a_load;     /* 0 K-contiguous vector, 1 M-contiguous vector (register
                          transpose), 2 generic, 3 M-contiguous direct copy into
                          an M-major LDS tile read by transposing reads */
@@ -137,8 +141,10 @@ typedef struct {
  * form when a and b are SL_F8_E4M3 and sfa/sfb are SL_E8M0 with
  * block_k == 32 (the matrix product of "CuTe 中 A、B 如何加载到 MMA 寄存器",
  * section 1, and the block-scaled product of "数据布局及其记号", section
- * "Replication 与 Offset").  bf16 is the same product in another 16-bit
- * format; the pages name fp16 only.
+ * "Replication 与 Offset"), or its NVFP4 form named on the same page: a and
+ * b SL_F4_E2M1 (packed, K-contiguous, row strides multiples of 32, 16-byte
+ * aligned, K % 32 == 0), sfa/sfb SL_F8_E4M3, block_k == 16, D f16.  bf16
+ * is the same product in another 16-bit format; the pages name fp16 only.
  * `stream` is a hipStream_t.  Asynchronous; see Conventions.
  */
 sl_status sl_gemm(const sl_gemm_args* args, void* stream);

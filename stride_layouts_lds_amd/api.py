@@ -16,8 +16,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libstride_layouts_lds.so")
 
-SL_F16, SL_F32, SL_F8_E4M3, SL_E8M0, SL_BF16 = 1, 2, 3, 4, 5
-K_F16, K_F16_GENERIC, K_MX, K_MX_W8 = 1, 2, 3, 4
+SL_F16, SL_F32, SL_F8_E4M3, SL_E8M0, SL_BF16, SL_F4_E2M1 = 1, 2, 3, 4, 5, 6
+K_F16, K_F16_GENERIC, K_MX, K_MX_W8, K_NVFP4 = 1, 2, 3, 4, 5
 STATUS = {0: "SL_OK", -1: "SL_ERR_NULL", -2: "SL_ERR_DTYPE", -3: "SL_ERR_SHAPE", -4: "SL_ERR_LAYOUT",
           -5: "SL_ERR_ALIGN", -6: "SL_ERR_ALIAS", -7: "SL_ERR_ARCH", -8: "SL_ERR_LAUNCH", -9: "SL_ERR_ARG",
           -10: "SL_ERR_NOMEM"}
@@ -132,6 +132,14 @@ def tensor_desc(x, dtype: Optional[int] = None) -> sl_tensor:
         t.dtype = 0
         t.layout.rank = 2
         return t
+    import torch
+    if x.dtype == torch.float4_e2m1fn_x2:
+        # two E2M1 elements per item, packed along the unit-stride last axis
+        if x.stride(-1) != 1:
+            raise ValueError("packed E2M1 needs a unit stride on the last axis")
+        shape = tuple(x.shape[:-1]) + (2 * x.shape[-1],)
+        strides = tuple(2 * s for s in x.stride()[:-1]) + (1,)
+        return desc(x.data_ptr(), SL_F4_E2M1, shape, strides)
     return desc(x.data_ptr(), _torch_dtype_code(x, dtype), tuple(x.shape), tuple(x.stride()))
 
 

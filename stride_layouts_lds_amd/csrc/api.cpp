@@ -37,6 +37,7 @@ int elem_size(int32_t dt) {
     case SL_F32: return 4;
     case SL_F8_E4M3: return 1;
     case SL_E8M0: return 1;
+    case SL_F4_E2M1: return 1;  // two elements per byte: byte_range halves the span
     default: return 0;
   }
 }
@@ -84,7 +85,10 @@ void byte_range(const View& v, int64_t batch, uintptr_t* lo, uintptr_t* hi) {
   int64_t last = 0;
   if (nb > 0 && v.rows > 0 && v.cols > 0) last = (nb - 1) * v.bs + (v.rows - 1) * v.rs + (v.cols - 1) * v.cs;
   *lo = (uintptr_t)v.t->data;
-  *hi = (uintptr_t)v.t->data + (uintptr_t)((last + 1) * es);
+  if (v.t->dtype == SL_F4_E2M1)
+    *hi = (uintptr_t)v.t->data + (uintptr_t)(last / 2 + 1);
+  else
+    *hi = (uintptr_t)v.t->data + (uintptr_t)((last + 1) * es);
 }
 
 // Distinct (batch, row, col) must map to distinct addresses.
@@ -165,9 +169,14 @@ double tile_cost(const sl::TileShape& t, int64_t batch, int64_t M, int64_t N, in
 sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   g_msg.clear();
   if (!args) return fail(SL_ERR_NULL, "args is NULL");
-  const bool mx = args->a.dtype == SL_F8_E4M3;
+  const bool nvfp4 = args->a.dtype == SL_F4_E2M1;
+  const bool mx = args->a.dtype == SL_F8_E4M3 || nvfp4;
   // dtypes
-  if (mx) {
+  if (nvfp4) {
+    if (args->b.dtype != SL_F4_E2M1) return fail(SL_ERR_DTYPE, "b must be f4_e2m1 when a is");
+    if (args->sfa.dtype != SL_F8_E4M3 || args->sfb.dtype != SL_F8_E4M3 || args->block_k != 16)
+      return fail(SL_ERR_DTYPE, "f4_e2m1 operands are NVFP4: f8_e4m3 sfa and sfb with block_k 16");
+  } else if (mx) {
     if (args->b.dtype != SL_F8_E4M3) return fail(SL_ERR_DTYPE, "b must be f8_e4m3 when a is");
     if (args->sfa.dtype != SL_E8M0 || args->sfb.dtype != SL_E8M0)
       return fail(SL_ERR_DTYPE, "MX operands need e8m0 sfa and sfb");
@@ -211,7 +220,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     if (ins[i] && ins[i]->t->layout.rank == 3 && ins[i]->batch != batch)
       return fail(SL_ERR_SHAPE, "%s has batch %lld, d has %lld", names[i], (long long)ins[i]->batch,
                   (long long)batch);
-  const int64_t kb = mx ? (K + 31) / 32 : 0;
+  const int64_t kb = nvfp4 ? (K + 15) / 16 : mx ? (K + 31) / 32 : 0;
   if (mx) {
     if (SA.rows != M || SA.cols != kb)
       return fail(SL_ERR_SHAPE, "sfa is (%lld,%lld), expected (%lld,%lld)", (long long)SA.rows,
@@ -232,7 +241,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.pub.k = K;
   P.empty = batch == 0 || M == 0 || N == 0;
   if (P.empty) {
-    P.pub.kernel = mx ? sl::K_MX : sl::K_F16;
+    P.pub.kernel = nvfp4 ? sl::K_NVFP4 : mx ? sl::K_MX : sl::K_F16;
     return SL_OK;
   }
 
@@ -288,7 +297,30 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   p.group_m = std::max(1, env_int("SL_GROUP_M", 8));
 
   int32_t tile = env_int("SL_TILE", -1);
-  if (mx) {
+  if (nvfp4) {
+    // packed along K: each row of a K-tile is 32 bytes at a 16-byte aligned
+    // address; K a multiple of 32 so every 16-byte piece is whole
+    auto packed_ok = [&](const View& X) {
+      return X.cs == 1 && X.rs % 32 == 0 && (uintptr_t)X.t->data % 16 == 0 &&
+             (X.t->layout.rank == 2 || X.bs % 32 == 0);
+    };
+    if (!packed_ok(A) || !packed_ok(B) || K % 32 != 0)
+      return fail(SL_ERR_LAYOUT,
+                  "NVFP4 operands must be K-contiguous (packed) with rows a multiple of 32 elements apart, "
+                  "16-byte aligned, and K %% 32 == 0");
+    if ((M - 1) * A.rs / 2 + K / 2 >= lim || (N - 1) * B.rs / 2 + K / 2 >= lim ||
+        (M - 1) * SA.rs + (kb - 1) * SA.cs >= lim || (N - 1) * SB.rs + (kb - 1) * SB.cs >= lim)
+      return fail(SL_ERR_SHAPE, "operands span more than 2^31 bytes");
+    p.sfa = (const uint8_t*)args->sfa.data;
+    p.sfb = (const uint8_t*)args->sfb.data;
+    p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
+    p.sb_rs = SB.rs, p.sb_ks = SB.cs, p.sb_bs = SB.t->layout.rank == 3 ? SB.bs : 0;
+    tile = sl::T256x256_W2x4;  // the dequantising loader exists for the 8-wave kernel
+    P.pub.kernel = sl::K_NVFP4;
+    P.pub.a_load = P.pub.b_load = sl::LOAD_NVFP4;
+    P.pub.tile_k = 64;
+    p.k_tiles = (int32_t)((K + 63) / 64);
+  } else if (mx) {
     p.sfa = (const uint8_t*)args->sfa.data;
     p.sfb = (const uint8_t*)args->sfb.data;
     p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
@@ -394,7 +426,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.pub.split_k = p.splits;
   P.pub.workgroups = total;
   P.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)M * (size_t)N * sizeof(float) : 0;
-  P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * P.pub.tile_k * (mx ? 1 : 2);
+  P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * P.pub.tile_k * (mx && !nvfp4 ? 1 : 2);
   if (P.pub.kernel == sl::K_MX_W8)
     P.pub.lds_bytes += (p.flags & sl::F_SCALE16) ? 2 * (ts.bm + ts.bn) * 16 : ts.stages * (ts.bm + ts.bn) * 4;
   return SL_OK;
@@ -487,7 +519,9 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
   if ((s = check_arch()) != SL_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (P.mx) {
+  if (P.pub.kernel == sl::K_NVFP4) {
+    e = sl::launch_gemm_f16(P.p, P.tile, sl::LOAD_NVFP4, sl::LOAD_NVFP4, st);
+  } else if (P.mx) {
     e = sl::launch_gemm_mx(P.p, P.tile, st);
   } else if (P.ws_bytes) {
     hipMemPool_t pool;

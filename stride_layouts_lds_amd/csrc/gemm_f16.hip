@@ -77,11 +77,8 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
-  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
-  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
-
-  typename LoaderSel<ALOAD, BM, NT, SHIFT>::type la(A, rows_a, p.a_rs, p.a_ks, p.K, wave, lane);
-  typename LoaderSel<BLOAD, BN, NT, SHIFT>::type lb(B, rows_b, p.b_rs, p.b_ks, p.K, wave, lane);
+  auto la = make_loader<ALOAD, BM, NT, SHIFT>(p, 0, tc.batch, m0, rows_a, wave, lane);
+  auto lb = make_loader<BLOAD, BN, NT, SHIFT>(p, 1, tc.batch, n0, rows_b, wave, lane);
 
   floatx4 acc[FM][FN];
 #pragma unroll
@@ -759,6 +756,12 @@ hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32
         return hipErrorInvalidValue;
       default: return launch_tile<LOAD_KVEC, LOAD_KVEC, DT>(p, tile, s);
     }
+  }
+  if (a_load == LOAD_NVFP4 || b_load == LOAD_NVFP4) {
+    // NVFP4: both operands through the dequantising loader, 8-wave kernel
+    if constexpr (DT != DT_F16) return hipErrorInvalidValue;
+    if (tile != T256x256_W2x4 || a_load != LOAD_NVFP4 || b_load != LOAD_NVFP4) return hipErrorInvalidValue;
+    return launch_cfg<256, 256, 2, 4, LOAD_NVFP4, LOAD_NVFP4, 0, DT_F16>(p, s);
   }
   if (a_load == LOAD_MNDMA || b_load == LOAD_MNDMA) {
     // the M-major direct-copy tiles exist for the 8-wave 256x256 kernel

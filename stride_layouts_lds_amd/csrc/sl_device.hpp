@@ -386,6 +386,104 @@ struct LoaderGeneric {
   }
 };
 
+// NVFP4 operand: K-contiguous packed E2M1 (two per byte, even element in
+// the low nibble) with one E4M3 scale per 16 K.  Each thread owns one
+// (row, 32-wide half) of the 64-wide K-tile: one 16-byte load of 32 codes
+// and two scale bytes, decoded in registers to fp16 and multiplied by the
+// scale (E2M1 x E4M3 has at most 5 significant bits and lies in
+// [2^-10, 2688]: exact in fp16), then written as four 16-byte chunks of
+// the K-major fp16 LDS tile.  Past K, or past the valid rows, the copies
+// read zero.
+__device__ __forceinline__ _Float16 e4m3_to_half(uint32_t b) {
+  const uint32_t s = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+  float f;
+  if (e == 15 && m == 7)
+    f = __builtin_nanf("");
+  else if (e == 0)
+    f = (float)m * 0x1p-9f;                                         // subnormal m/8 * 2^-6
+  else
+    f = __builtin_bit_cast(float, ((e + 120) << 23) | (m << 20));  // (1 + m/8) * 2^(e-7)
+  return (_Float16)(s ? -f : f);
+}
+
+// 8 E2M1 codes (nibbles of w, element 0 in the low nibble) -> 8 fp16 bit
+// patterns, two per dword.  Every E2M1 value has a zero low byte in fp16;
+// the high byte comes from an 8-entry byte table selected with v_perm_b32,
+// plus the sign.
+__device__ __forceinline__ u32x4 e2m1x8_to_half8(uint32_t w) {
+  constexpr uint32_t kTabLo = 0x3E3C3800u;  // 0, 0.5, 1, 1.5 (high bytes)
+  constexpr uint32_t kTabHi = 0x46444240u;  // 2, 3, 4, 6
+  const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 / 1,3,5,7
+  const uint32_t he = __builtin_amdgcn_perm(kTabHi, kTabLo, ev & 0x07070707u) | ((ev & 0x08080808u) << 4);
+  const uint32_t ho = __builtin_amdgcn_perm(kTabHi, kTabLo, od & 0x07070707u) | ((od & 0x08080808u) << 4);
+  // dword i = (element 2i, element 2i+1) = bytes [0, he.b_i, 0, ho.b_i]
+  return u32x4{__builtin_amdgcn_perm(ho, he, 0x040C000Cu), __builtin_amdgcn_perm(ho, he, 0x050C010Cu),
+               __builtin_amdgcn_perm(ho, he, 0x060C020Cu), __builtin_amdgcn_perm(ho, he, 0x070C030Cu)};
+}
+
+template <int ROWS, int NT, int SHIFT>
+struct LoaderNVFP4 {
+  static constexpr int PER = ROWS * 2 / NT;  // (row, half) units per thread
+  static_assert(PER >= 1 && ROWS * 2 % NT == 0, "tile too small for the workgroup");
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+  __amdgpu_buffer_rsrc_t rd, rsf;
+  int32_t K;
+  uint32_t sks;
+  uint32_t d_off[PER], s_off[PER];
+  int32_t row[PER], half[PER];
+  bool ok[PER];
+  u32x4 data[PER];
+  uint32_t sc[PER][2];
+
+  __device__ __forceinline__ LoaderNVFP4(const uint8_t* base, const uint8_t* sbase, int32_t rows_valid,
+                                         int64_t rs, int64_t srs, int64_t sks_, int64_t K_) {
+    K = (int32_t)K_;
+    sks = (uint32_t)sks_;
+    rd = make_rsrc(base, rows_valid > 0 ? (uint32_t)((rows_valid - 1) * (rs / 2) + K_ / 2) : 0u);
+    rsf = make_rsrc(sbase, rows_valid > 0 ? (uint32_t)((rows_valid - 1) * srs + (K_ / 16 - 1) * sks_ + 1) : 0u);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int32_t id = u * NT + (int32_t)threadIdx.x;
+      row[u] = id >> 1;
+      half[u] = id & 1;
+      ok[u] = row[u] < rows_valid;
+      d_off[u] = (uint32_t)(row[u] * (rs / 2) + half[u] * 16);
+      s_off[u] = (uint32_t)(row[u] * srs + half[u] * 2 * sks_);
+    }
+  }
+
+  __device__ __forceinline__ void issue(int32_t t, char*) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const bool v = ok[u] && t * 64 + half[u] * 32 < K;
+      data[u] = __builtin_amdgcn_raw_buffer_load_b128(rd, v ? d_off[u] + (uint32_t)(t * 32) : kOutOfRange, 0, 0);
+      const uint32_t s0 = s_off[u] + (uint32_t)(4 * t) * sks;
+      sc[u][0] = __builtin_amdgcn_raw_buffer_load_b8(rsf, v ? s0 : kOutOfRange, 0, 0);
+      sc[u][1] = __builtin_amdgcn_raw_buffer_load_b8(rsf, v ? s0 + sks : kOutOfRange, 0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ uint32_t mul_h2(uint32_t x, _Float16 s) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, x) * half2v{s, s});
+  }
+
+  // (the four products are built as separate values: an in-place loop over
+  // the vector's elements was miscompiled into reuse of element 0)
+  __device__ __forceinline__ void commit(char* lds) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // 8 elements: K = 32 half + 8 j ..
+        const _Float16 s = e4m3_to_half(sc[u][j >> 1]);
+        const u32x4 h = e2m1x8_to_half8(data[u][j]);
+        *(u32x4*)(lds + lds_offset(row[u], (half[u] * 32 + 8 * j) * 2, SHIFT)) =
+            u32x4{mul_h2(h[0], s), mul_h2(h[1], s), mul_h2(h[2], s), mul_h2(h[3], s)};
+      }
+    }
+  }
+};
+
 template <int KIND, int ROWS, int NT, int SHIFT>
 struct LoaderSel;
 template <int ROWS, int NT, int SHIFT>
@@ -404,5 +502,26 @@ template <int ROWS, int NT, int SHIFT>
 struct LoaderSel<LOAD_MNDMA, ROWS, NT, SHIFT> {
   using type = LoaderMNDma<ROWS, NT>;
 };
+template <int ROWS, int NT, int SHIFT>
+struct LoaderSel<LOAD_NVFP4, ROWS, NT, SHIFT> {
+  using type = LoaderNVFP4<ROWS, NT, SHIFT>;
+};
+
+// The loader of operand `op` (0: A rows from m0, 1: B rows from n0) of
+// batch `batch`, `rows_valid` rows of the tile in range.
+template <int KIND, int ROWS, int NT, int SHIFT>
+__device__ __forceinline__ typename LoaderSel<KIND, ROWS, NT, SHIFT>::type make_loader(
+    const GemmParams& p, int op, int32_t batch, int64_t row0, int32_t rows_valid, int32_t wave, int32_t lane) {
+  const int64_t bs = op ? p.b_bs : p.a_bs, rs = op ? p.b_rs : p.a_rs, ks = op ? p.b_ks : p.a_ks;
+  const uint8_t* x = (const uint8_t*)(op ? p.b : p.a);
+  if constexpr (KIND == LOAD_NVFP4) {
+    const int64_t sbs = op ? p.sb_bs : p.sa_bs, srs = op ? p.sb_rs : p.sa_rs, sks = op ? p.sb_ks : p.sa_ks;
+    const uint8_t* sf = (op ? p.sfb : p.sfa) + batch * sbs + row0 * srs;
+    return LoaderNVFP4<ROWS, NT, SHIFT>(x + (batch * bs + row0 * rs) / 2, sf, rows_valid, rs, srs, sks, p.K);
+  } else {
+    return typename LoaderSel<KIND, ROWS, NT, SHIFT>::type(x + 2 * (batch * bs + row0 * rs), rows_valid, rs, ks, p.K,
+                                                           wave, lane);
+  }
+}
 
 }  // namespace sl

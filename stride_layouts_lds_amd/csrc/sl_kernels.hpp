@@ -11,8 +11,10 @@ enum LoadKind : int32_t {
   LOAD_KVEC = 0,    // K contiguous, 16-B aligned: direct HBM->LDS 16-B buffer loads
   LOAD_MNVEC = 1,   // M (or N) contiguous, 16-B aligned: 16-B loads, 8x8 register transpose
   LOAD_GENERIC = 2, // any strides: element loads
-  LOAD_MNDMA = 3    // M (or N) contiguous, 16-B aligned: direct HBM->LDS into an M-major tile,
+  LOAD_MNDMA = 3,   // M (or N) contiguous, 16-B aligned: direct HBM->LDS into an M-major tile,
                     // fragments by transposing LDS reads (8-wave 256x256 kernel)
+  LOAD_NVFP4 = 4    // packed E2M1 with E4M3 scales per 16 K: decoded and scaled in registers,
+                    // written to the K-major fp16 tile (8-wave 256x256 kernel)
 };
 
 // Kernel families (sl_plan.kernel).
@@ -20,7 +22,8 @@ enum KernelKind : int32_t {
   K_F16 = 1,          // fp16, vector loaders
   K_F16_GENERIC = 2,  // fp16 with an element-wise loader on one side
   K_MX = 3,           // MXFP8, 4 waves, v_mfma_scale 16x16x128, scales by byte loads
-  K_MX_W8 = 4         // MXFP8, 8 waves, v_mfma_scale 32x32x64, scales staged in LDS
+  K_MX_W8 = 4,        // MXFP8, 8 waves, v_mfma_scale 32x32x64, scales staged in LDS
+  K_NVFP4 = 5         // NVFP4 dequantised to exact fp16 tiles, fp16 MFMA (8 waves)
 };
 
 // Tile configurations the dispatcher can choose: rows of A, rows of B,

@@ -15,7 +15,7 @@ Scale exponents are integers uniform in [-4, 4] stored as E8M0 bytes e + 127.
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import Dict, Optional, Tuple
+from typing import Sequence, Dict, Optional, Tuple
 
 import numpy as np
 
@@ -28,10 +28,12 @@ class HostOperand:
     storage: np.ndarray
     shape: Tuple[int, ...]
     strides: Tuple[int, ...]
-    kind: str  # 'f16' | 'bf16' | 'e4m3' | 'e8m0'
+    kind: str  # 'f16' | 'bf16' | 'e4m3' | 'e8m0' | 'e2m1' (packed, strides in elements)
 
     @property
     def view(self) -> np.ndarray:
+        if self.kind == "e2m1":
+            raise TypeError("packed E2M1 codes have no numpy view (two elements per byte)")
         it = self.storage.itemsize
         return np.lib.stride_tricks.as_strided(
             self.storage, shape=self.shape, strides=tuple(s * it for s in self.strides),
@@ -62,6 +64,10 @@ class Workload:
     @property
     def bf16(self) -> bool:
         return self.a.kind == "bf16"
+
+    @property
+    def nvfp4(self) -> bool:
+        return self.a.kind == "e2m1"
 
     @property
     def flops(self) -> int:
@@ -129,6 +135,52 @@ def scales(rng, batch: Optional[int], rows: int, kblocks: int, lo: int = -4, hi:
     return HostOperand(codes, (batch, rows, kblocks), (rows * rs, rs, 1), "e8m0")
 
 
+def e2m1_matrix(rng, batch: Optional[int], rows: int, cols: int) -> HostOperand:
+    """(batch?, rows, cols) E2M1 codes, uniform over all 16, packed two per
+    byte along cols (element 2i in the low nibble), rows cols apart."""
+    nb = batch or 1
+    codes = rng.integers(0, 16, (nb * rows, cols)).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8).ravel()
+    if batch is None:
+        return HostOperand(packed, (rows, cols), (cols, 1), "e2m1")
+    return HostOperand(packed, (batch, rows, cols), (rows * cols, cols, 1), "e2m1")
+
+
+def e4m3_scales(rng, batch: Optional[int], rows: int, kblocks: int, lo: int = -4, hi: int = 4,
+                mantissas: Sequence[int] = tuple(range(8))) -> HostOperand:
+    """Positive E4M3 scale codes 2^e * (1 + m/8), e uniform in [lo, hi], m
+    drawn from ``mantissas``."""
+    n = (batch or 1) * rows * kblocks
+    e = rng.integers(lo, hi + 1, n)
+    m = rng.choice(np.array(mantissas), n)
+    codes = (((e + 7) << 3) | m).astype(np.uint8)
+    if batch is None:
+        return HostOperand(codes, (rows, kblocks), (kblocks, 1), "e4m3")
+    return HostOperand(codes, (batch, rows, kblocks), (rows * kblocks, kblocks, 1), "e4m3")
+
+
+def nvfp4_workload(name: str, M: int, N: int, K: int, *, seed: int, batch: Optional[int] = None,
+                   with_c: bool = False, exact: bool = False) -> Workload:
+    """NVFP4: packed E2M1 A and B (codes uniform), one positive E4M3 scale
+    per 16 K (exponents in [-4, 0], any mantissa, which keeps an 8192-term
+    fp16 result finite; with ``exact``, exponents in [-2, 2] and mantissas 0
+    or 4, so every partial sum is exact in fp32), C fp16 normal(0,1) if
+    asked."""
+    rng = np.random.default_rng(seed)
+    a = e2m1_matrix(rng, batch, M, K)
+    b = e2m1_matrix(rng, batch, N, K)
+    kb = -(-K // 16)
+    lo, hi, mans = (-2, 2, (0, 4)) if exact else (-4, 0, tuple(range(8)))
+    sfa = e4m3_scales(rng, batch, M, kb, lo, hi, mans)
+    sfb = e4m3_scales(rng, batch, N, kb, lo, hi, mans)
+    c = matrix(rng, "int4" if exact else "normal", batch, M, N, "row") if with_c else None
+    if batch is None:
+        d_shape, d_strides = (M, N), (N, 1)
+    else:
+        d_shape, d_strides = (batch, M, N), (M * N, N, 1)
+    return Workload(name, M, N, K, batch or 1, a, b, c, sfa, sfb, 16, d_shape, d_strides)
+
+
 def gemm_workload(name: str, M: int, N: int, K: int, *, seed: int, dist: str = "normal",
                   batch: Optional[int] = None, a_major: str = "row", b_major: str = "row",
                   with_c: bool = False, c_dist: Optional[str] = None, mx: bool = False,
@@ -160,6 +212,10 @@ def to_device(op: Optional[HostOperand]):
     import torch
     if op is None:
         return None
+    if op.kind == "e2m1":
+        # packed pairs: torch's float4_e2m1fn_x2 holds two elements per item
+        st = torch.from_numpy(np.ascontiguousarray(op.storage)).to("cuda").view(torch.float4_e2m1fn_x2)
+        return st.as_strided(op.shape[:-1] + (op.shape[-1] // 2,), tuple(x // 2 for x in op.strides[:-1]) + (1,))
     st = torch.from_numpy(np.ascontiguousarray(op.storage))
     st = st.view({"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn,
                   "e8m0": torch.float8_e8m0fnu}[op.kind])

@@ -36,16 +36,29 @@ def d_codes(d) -> np.ndarray:
     return d.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
+def _ora(op, scale: bool = False, nvfp4: bool = False):
+    """An operand as the oracle takes it: a numpy view, or (packed E2M1
+    data, NVFP4's E4M3 scales) raw storage with element strides."""
+    if op is None:
+        return None
+    if op.kind == "e2m1":
+        return OG.packed(op.storage, op.shape, op.strides, OG.E2M1)
+    if scale and nvfp4:
+        return OG.packed(op.storage, op.shape, op.strides, OG.E4M3)
+    return op.view
+
+
+def _operands(w: Workload):
+    nv = w.nvfp4
+    return (_ora(w.a), _ora(w.b), _ora(w.c), _ora(w.sfa, True, nv), _ora(w.sfb, True, nv))
+
+
 def oracle_full(w: Workload):
-    return OG.gemm(w.a.view, w.b.view, w.c.view if w.c else None,
-                   w.sfa.view if w.sfa else None, w.sfb.view if w.sfb else None, block_k=w.block_k,
-                   bf16=w.bf16)
+    return OG.gemm(*_operands(w), block_k=w.block_k, bf16=w.bf16)
 
 
 def oracle_points(w: Workload, pts: np.ndarray):
-    return OG.gemm_points(w.a.view, w.b.view, w.c.view if w.c else None,
-                          w.sfa.view if w.sfa else None, w.sfb.view if w.sfb else None, points=pts,
-                          block_k=w.block_k, bf16=w.bf16)
+    return OG.gemm_points(*_operands(w), points=pts, block_k=w.block_k, bf16=w.bf16)
 
 
 def sample_points(w: Workload, n: int, seed: int = 0) -> np.ndarray:

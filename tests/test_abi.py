@@ -340,3 +340,30 @@ def test_bf16_dtypes(api):
     finally:
         del os.environ["SL_TILE"]
     assert p["tile_m"] == 256 and p["threads"] == 512
+
+
+def test_nvfp4_plan_and_validation(api):
+    """NVFP4: packed E2M1 operands with E4M3 scales per 16 K go to the
+    dequantising 8-wave kernel; E2M1 with E8M0 scales (MXFP4) and packed
+    layouts the loader cannot take are rejected."""
+    E2, E4, E8 = 6, 3, 4
+    M, N, K = 512, 256, 1024
+    a = (BASE_A, E2, (M, K), (K, 1))
+    b = (BASE_B, E2, (N, K), (K, 1))
+    sa = (BASE_C, E4, (M, K // 16), (K // 16, 1))
+    sb = (BASE_C + 0x100000, E4, (N, K // 16), (K // 16, 1))
+    d = rowmajor(BASE_D, (M, N))
+    p = plan(api, a, b, None, d, sa, sb, block_k=16)
+    assert p["kernel"] == api.K_NVFP4 and (p["a_load"], p["b_load"]) == (4, 4)
+    assert p["tile_m"] == p["tile_n"] == 256 and p["tile_k"] == 64 and p["lds_bytes"] == 2 * 512 * 64 * 2
+    s8a = (BASE_C, E8, (M, K // 32), (K // 32, 1))
+    s8b = (BASE_C + 0x100000, E8, (N, K // 32), (K // 32, 1))
+    assert err(api, a, b, None, d, s8a, s8b, block_k=32) == "SL_ERR_DTYPE"
+    assert err(api, a, b, None, d, sa, sb, block_k=32) == "SL_ERR_DTYPE"
+    # K % 32 != 0, an N-contiguous B, a row stride that is not a multiple of 32
+    K2 = 1008
+    assert err(api, (BASE_A, E2, (M, K2), (K2, 1)), (BASE_B, E2, (N, K2), (K2, 1)), None, d,
+               (BASE_C, E4, (M, K2 // 16), (K2 // 16, 1)), (BASE_C + 0x100000, E4, (N, K2 // 16), (K2 // 16, 1)),
+               block_k=16) == "SL_ERR_LAYOUT"
+    assert err(api, a, (BASE_B, E2, (N, K), (1, N)), None, d, sa, sb, block_k=16) == "SL_ERR_LAYOUT"
+    assert err(api, (BASE_A, E2, (M, K), (K + 16, 1)), b, None, d, sa, sb, block_k=16) == "SL_ERR_LAYOUT"

@@ -432,3 +432,40 @@ def test_output_rounding_ties_to_even(api, bf16):
     d_ref, ref, _ = OG.gemm(codes(at), codes(bt), bf16=bf16)
     assert np.array_equal(ref[0][:, 0], 1.0 + np.array(ts))
     assert np.array_equal(h.d_codes(out), d_ref[0])
+
+
+# ------------------------------------------------------------------ NVFP4
+
+NVFP4_EXACT = [
+    # M, N, K, batch, with_c
+    (256, 256, 64, None, False),
+    (300, 264, 512, None, True),
+    (136, 72, 96, 2, True),      # K ends half way through a 64-wide K-tile
+    (520, 300, 1024, None, False),
+]
+
+
+@pytest.mark.parametrize("case", NVFP4_EXACT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_c{int(c[4])}")
+def test_nvfp4_exact_parity(api, case):
+    """Packed E2M1 data, E4M3 scales 2^[-2,2] x {1, 1.5}: every decoded
+    product and partial sum is exact in fp32, so D must equal the oracle
+    bit for bit."""
+    h = H()
+    M, N, K, batch, with_c = case
+    w = I.nvfp4_workload("nvfp4_exact", M, N, K, seed=M + K, batch=batch, with_c=with_c, exact=True)
+    plan = _plan(api, w)
+    h.log(f"nvfp4 exact {case} plan={plan}")
+    assert plan["kernel"] == api.K_NVFP4 and plan["a_load"] == plan["b_load"] == 4
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
+def test_nvfp4_bounded_and_sampled_8192(api):
+    h = H()
+    w = I.nvfp4_workload("nvfp4_1024", 1024, 520, 2048, seed=3, with_c=True)
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, absum = h.oracle_full(w)
+    h.assert_within_bound(d.reshape(d_ref.shape), d_ref, absum, w.name)
+    _sampled(api, I.nvfp4_workload("nvfp4_8192", 8192, 8192, 8192, seed=6), n=1500)
