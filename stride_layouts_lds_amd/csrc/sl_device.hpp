@@ -395,14 +395,12 @@ struct LoaderGeneric {
 // the K-major fp16 LDS tile.  Past K, or past the valid rows, the copies
 // read zero.
 __device__ __forceinline__ _Float16 e4m3_to_half(uint32_t b) {
+  // branch-free: both the normal and the subnormal reading, then selects
   const uint32_t s = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
-  float f;
-  if (e == 15 && m == 7)
-    f = __builtin_nanf("");
-  else if (e == 0)
-    f = (float)m * 0x1p-9f;                                         // subnormal m/8 * 2^-6
-  else
-    f = __builtin_bit_cast(float, ((e + 120) << 23) | (m << 20));  // (1 + m/8) * 2^(e-7)
+  const float normal = __builtin_bit_cast(float, ((e + 120) << 23) | (m << 20));  // (1 + m/8) * 2^(e-7)
+  const float sub = (float)m * 0x1p-9f;                                          // m/8 * 2^-6
+  float f = e == 0 ? sub : normal;
+  f = (e == 15 && m == 7) ? __builtin_nanf("") : f;
   return (_Float16)(s ? -f : f);
 }
 
