@@ -205,13 +205,20 @@ sl_status sl_query_fragment_addresses(int32_t variant, int32_t operand, int64_t*
 /*
  * Device probe of one matrix-core instruction's operand maps: launches one
  * wave per case on `stream` and writes every accumulator register.
- *   mode 0: case c = (lane, slot) of A (c = lane*slots + slot) holds 1.0,
- *           every other A slot 0; B slot (l, s) holds l*slots + s + 1
- *           (f16; for E4M3 instructions see below).
+ * f16 instructions (instr 0/1), case c = (lane, slot) = (c / 8, c % 8):
+ *   mode 0: A (lane, slot) holds 1.0, every other A slot 0; B slot (l, s)
+ *           holds l*8 + s + 1.
  *   mode 1: the same with the roles of A and B swapped.
- *   For instr 2/3 (E4M3) mode 0/1 use B (resp. A) code (l % 16) + 1 in
- *   mode 0/1 and 1.0 scales; mode 2 puts 1.0 at the one-hot A (lane, slot),
- *   B = 1.0 everywhere, and A scale byte of lane l = 127 + l - 32 (B's 127).
+ * Scaled E4M3 instructions (instr 2/3), case c = (lane, byte) = (c / 32,
+ * c % 32), unit (127) scales unless stated:
+ *   mode 0/1: A one-hot 1.0; B byte = E4M3 code 0x20 + lane (0) or
+ *             0x20 + byte (1).
+ *   mode 2/3: the same with A and B swapped.
+ *   mode 4:   A one-hot, B = 1.0, A scale of lane l = 127 + l - 32.
+ *   mode 5:   B one-hot, A = 1.0, B scale of lane l = 127 + l - 32.
+ *   mode 6/7: A in E2M1 (format 4): case = (lane, nibble) of a one-hot 1.0
+ *             among the lane's 32 nibbles (16 bytes, low nibble first); B in
+ *             E4M3 coded as in mode 0 (6) or mode 1 (7).
  * `out` (device, fp32) receives cases * 64 * regs values laid out
  * [case][lane][reg].  Returns the case count through *cases.
  */

@@ -429,6 +429,17 @@ MFMA32_F8_A = TV(shape=((32, 2), (16, 2)), stride=((1, 512), (32, 1024)), rows=3
 MFMA32_F8_B = TV(shape=((32, 2), (16, 2)), stride=((1, 512), (32, 1024)), rows=32, cols=64)
 
 
+# The same instructions with E2M1 data (format 4) take 16 bytes per lane,
+# 32 nibbles, low nibble first.  Nibble v of lane l = l0 + R*l1 holds
+# (m = l0, k = 32*l1 + v): 32 consecutive k, the k-block of 32 that scale
+# lane l1 covers.  (Pinned by the device probe; the f8 byte order, with its
+# two halves 64 or 32 k apart, does not carry over.)
+# v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 A (16 x 128): q = m + 16 k
+MFMA16_F4_A = TV(shape=((16, 4), 32), stride=((1, 512), 16), rows=16, cols=128)
+# v_mfma_scale_f32_32x32x64_f8f6f4, E2M1 A (32 x 64): q = m + 32 k
+MFMA32_F4_A = TV(shape=((32, 2), 32), stride=((1, 1024), 32), rows=32, cols=64)
+
+
 def mfma_scale_owner(rows: int, lane: int) -> Tuple[int, int]:
     """(row, k-block of 32) whose E8M0 scale lane ``lane`` supplies for the
     scaled f8 instructions: row = lane % rows, block = lane // rows (blocks

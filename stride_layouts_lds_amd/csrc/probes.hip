@@ -9,6 +9,7 @@ namespace {
 
 constexpr uint8_t kE4M3One = 0x38;  // 1.0
 constexpr uint8_t kCodeBase = 0x20; // lane/slot-coded E4M3 values start here (0.125)
+constexpr int kFmtE2M1 = 4;         // CBSZ/BLGP format code of FP4 E2M1
 
 // One wave per case.  f16 instructions: case = (lane, slot) of the one-hot
 // operand; the other operand holds lane*8 + slot + 1.
@@ -47,6 +48,9 @@ __global__ __launch_bounds__(64) void probe_mfma_f16(int32_t mode, float* out) {
 //   mode 2/3: B one-hot, A byte = base + lane / base + byte, unit scales
 //   mode 4:   A one-hot, B = 1, A scale of lane l = 127 + l - 32
 //   mode 5:   B one-hot, A = 1, B scale of lane l = 127 + l - 32
+//   mode 6/7: A in E2M1 (format 4): case = (lane, nibble) of a one-hot 1.0
+//             among the lane's 32 nibbles (16 bytes, low nibble first);
+//             B in E4M3 with byte = base + lane / base + byte, unit scales
 template <int INSTR>
 __global__ __launch_bounds__(64) void probe_mfma_f8(int32_t mode, float* out) {
   constexpr int REGS = instr_acc_regs(INSTR);
@@ -79,15 +83,37 @@ __global__ __launch_bounds__(64) void probe_mfma_f8(int32_t mode, float* out) {
   const i32x8 b = {(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3], (int)wb[4], (int)wb[5], (int)wb[6], (int)wb[7]};
   const int32_t sa = mode == 4 ? 127 + lane - 32 : 127;
   const int32_t sb = mode == 5 ? 127 + lane - 32 : 127;
+  // mode 6/7: A one-hot E2M1 1.0 (code 0x2) at nibble hs of lane hl
+  uint32_t w4[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) w4[w] = (lane == hl && hs / 8 == w) ? (0x2u << (4 * (hs % 8))) : 0u;
+  const i32x8 a4 = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3], 0, 0, 0, 0};
+  uint32_t wb4[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int bidx = 0; bidx < 4; ++bidx) v |= (uint32_t)(kCodeBase + (mode == 6 ? lane : 4 * w + bidx)) << (8 * bidx);
+    wb4[w] = v;
+  }
+  const i32x8 b4 = {(int)wb4[0], (int)wb4[1], (int)wb4[2], (int)wb4[3],
+                    (int)wb4[4], (int)wb4[5], (int)wb4[6], (int)wb4[7]};
+  const bool fp4 = mode == 6 || mode == 7;
   float r[REGS];
   if constexpr (INSTR == MFMA16_F8) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
+    if (fp4)
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a4, b4, acc, kFmtE2M1, 0, 0, 127, 0, 127);
+    else
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = acc[i];
   } else {
     floatx16 acc = {};
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
+    if (fp4)
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, acc, kFmtE2M1, 0, 0, 127, 0, 127);
+    else
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
 #pragma unroll
     for (int i = 0; i < 16; ++i) r[i] = acc[i];
   }

@@ -133,3 +133,38 @@ def test_probe_ds_read_tr16(api):
     dump("probe_tr16", got)
     want = np.array(L.ds_read_tr16_b64_expected(addr.tolist(), halves.tolist()), np.uint16)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("instr", [2, 3])
+def test_probe_e2m1_operand_map(api, instr):
+    """A in E2M1 one-hot at (lane, nibble) against an E4M3 B whose map is
+    pinned above: the output row gives m and the B codes (lane-coded, then
+    byte-coded) give k, i.e. the E2M1 (lane, nibble) -> (m, k) map, compared
+    with the reading in the oracle."""
+    from gpu_helpers import dump, log
+    log(f"probe e2m1 instr={instr}")
+    got6 = api.probe_mfma(instr, 6).cpu().numpy()
+    got7 = api.probe_mfma(instr, 7).cpu().numpy()
+    amap, bmap, dmap = L.INSTR_MAPS[instr]
+    famap = L.MFMA16_F4_A if instr == 2 else L.MFMA32_F4_A
+    dec = {float(OG.e4m3_decode(E4M3_BASE + x)): x for x in range(64)}
+    measured, bad = {}, 0
+    for c in range(64 * 32):
+        hl, hs = c // 32, c % 32
+        nz6 = np.argwhere(got6[c] != 0)
+        if len(nz6) == 0:
+            measured[(hl, hs)] = None
+            continue
+        l, i = nz6[0]
+        m, n = dmap(int(l), int(i))
+        lane_b = dec[float(got6[c][l, i])]
+        slot_b = dec[float(got7[c][l, i])]
+        nb, kb = bmap(lane_b, slot_b)
+        measured[(hl, hs)] = (m, kb)
+        if (m, kb) != famap(hl, hs):
+            bad += 1
+    if bad:
+        dump(f"probe_e2m1_{instr}", np.array([[h, s_, *(measured[(h, s_)] or (-1, -1))]
+                                               for h in range(64) for s_ in range(32)], np.int32))
+    assert bad == 0, f"{bad} of 2048 (lane, nibble) differ from the reading; e.g. " + str(
+        [(k, v, famap(*k)) for k, v in list(measured.items()) if v != famap(*k)][:6])
