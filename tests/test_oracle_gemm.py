@@ -383,3 +383,21 @@ def test_nvfp4_gemm_vs_numpy():
     _, ref2, _ = G.gemm(swapped, B, None, SA, SB, block_k=16)
     a_sw = dec2(ca.reshape(M, K // 2, 2)[:, :, ::-1].reshape(M, K)) * np.repeat(dec8(sa), 16, axis=1)
     assert np.array_equal(ref2[0], a_sw @ b_real.T)
+
+
+def test_mxfp4_gemm_vs_numpy():
+    """Packed E2M1 operands with one E8M0 scale per 32 K (MXFP4): the oracle
+    equals numpy's fp64 matmul of the decoded, block-scaled values."""
+    rng = np.random.default_rng(13)
+    M, N, K = 20, 26, 128
+    ca = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    cb = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    sa = rng.integers(124, 131, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(124, 131, (N, K // 32)).astype(np.uint8)
+    dec2 = np.vectorize(G.e2m1_decode)
+    a_real = dec2(ca) * np.repeat(2.0 ** (sa.astype(np.float64) - 127), 32, axis=1)
+    b_real = dec2(cb) * np.repeat(2.0 ** (sb.astype(np.float64) - 127), 32, axis=1)
+    A = G.packed(_pack_e2m1(ca), (M, K), (K, 1), G.E2M1)
+    B = G.packed(_pack_e2m1(cb), (N, K), (K, 1), G.E2M1)
+    d, ref, absum = G.gemm(A, B, None, sa, sb, block_k=32)
+    assert np.array_equal(ref[0], a_real @ b_real.T)
