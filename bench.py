@@ -13,8 +13,8 @@ seed 1) -- the large square case the fp16 throughput target is stated on.
 Other workloads (for measurement only): fp16_4096 (the same recipe at 4096),
 ragged (4000x3000x2056), skinny (8192x128x8192), batched_nn / batched_nt
 (64 x 512^3, A M-contiguous), batched_tn / batched_tt (A K-contiguous),
-mxfp8 (8192^3 MXFP8), nvfp4_8192 (8192^3 NVFP4), bf16_8192 (the default
-recipe in bf16).
+mxfp8 (8192^3 MXFP8), nvfp4_8192 / mxfp4_8192 (8192^3 NVFP4 / MXFP4),
+bf16_8192 (the default recipe in bf16).
 
 The CPU baseline is the oracle (plain fp64 triple loop, all host cores) on a
 bounded sample of output points of the same workload, scaled to TFLOP/s.
@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s and % of dense MFMA peak, fp16 TN GEMM 4096^3/8192^3 on 1 MI355X"
 PEAK_F16 = 2516.6   # TFLOP/s: 256 CUs x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
 PEAK_F8 = 5033.2    # TFLOP/s: 256 CUs x 2.4 GHz x 8192 dense MX-fp8 FLOP/clk/CU
+PEAK_F4 = 10066.3   # TFLOP/s: 256 CUs x 2.4 GHz x 16384 dense MX-fp4 FLOP/clk/CU
 PEAK_HBM = 8000.0   # GB/s
 
 
@@ -52,6 +53,8 @@ def workloads():
         "mxfp8": ("MXFP8 GEMM M=N=K=8192, E4M3 data, E8M0 scale per 32 K, C=0, seed 4", lambda: I.config5(8192)),
         "nvfp4_8192": ("NVFP4 GEMM M=N=K=8192, E2M1 codes uniform, E4M3 scale per 16 K (2^[-4,0] x any mantissa), "
                        "C=0, seed 6", lambda: I.nvfp4_workload("nvfp4_8192", 8192, 8192, 8192, seed=6)),
+        "mxfp4_8192": ("MXFP4 GEMM M=N=K=8192, E2M1 codes uniform, E8M0 scale per 32 K (2^[-4,0]), C=0, seed 7",
+                       lambda: I.mxfp4_workload("mxfp4_8192", 8192, 8192, 8192, seed=7)),
         "bf16_8192": ("bf16 TN GEMM M=N=K=8192, A/B/C normal(0,1) bf16, seed 1",
                       lambda: I.gemm_workload("bf16_tn_8192_c", 8192, 8192, 8192, seed=1, dist="normal",
                                               with_c=True, bf16=True)),
@@ -60,7 +63,7 @@ def workloads():
 
 def algorithmic_bytes(w) -> int:
     """A, B (and scales) read once, C read once if present, D written once."""
-    es = 0.5 if w.nvfp4 else 1 if w.mx else 2
+    es = 0.5 if w.fp4 else 1 if w.mx else 2
     b = int(w.batch * (w.M * w.K + w.N * w.K) * es) + w.batch * w.M * w.N * 2
     if w.c is not None:
         b += w.batch * w.M * w.N * 2
@@ -106,6 +109,8 @@ def cpu_baseline(w, target_s: float = 12.0):
         return op.view
     if w.nvfp4:
         ops = (ora(w.a, OG.E2M1), ora(w.b, OG.E2M1), ora(w.c), ora(w.sfa, OG.E4M3), ora(w.sfb, OG.E4M3))
+    elif w.mxfp4:
+        ops = (ora(w.a, OG.E2M1), ora(w.b, OG.E2M1), ora(w.c), ora(w.sfa), ora(w.sfb))
     else:
         ops = (ora(w.a), ora(w.b), ora(w.c), ora(w.sfa), ora(w.sfb))
 
@@ -194,8 +199,9 @@ def main():
 
     flop = w.flops
     value = flop * args.steps / wall / 1e12
-    # NVFP4 is decoded to fp16 and multiplied on the fp16 matrix cores
-    peak = PEAK_F8 if (w.mx and not w.nvfp4) else PEAK_F16
+    # NVFP4 is decoded to fp16 and multiplied on the fp16 matrix cores;
+    # MXFP4 runs on the scaled MFMAs at the fp4 rate
+    peak = PEAK_F4 if w.mxfp4 else PEAK_F8 if (w.mx and not w.nvfp4) else PEAK_F16
     # the roofline that bounds the workload: MFMA when its arithmetic
     # intensity (algorithmic FLOP per algorithmic byte) is above the ridge
     # point peak / HBM bandwidth, HBM below it
@@ -221,7 +227,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f4e2m1" if w.nvfp4 else "f8e4m3" if w.mx else "bf16" if w.bf16 else "f16",
+        "dtype": "f4e2m1" if w.fp4 else "f8e4m3" if w.mx else "bf16" if w.bf16 else "f16",
         "data": "synthetic",
         "config": {"workload": desc, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
                    "tile": f"{plan['tile_m']}x{plan['tile_n']}x{plan['tile_k']}",

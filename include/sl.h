@@ -169,6 +169,7 @@ int32_t sl_abi_version(void);
  *   instr:   0 v_mfma_f32_16x16x32_f16      1 v_mfma_f32_32x32x16_f16
  *            2 v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)
  *            3 v_mfma_scale_f32_32x32x64_f8f6f4  (E4M3)
+ *            4 / 5 the same two with E2M1 data (32 nibbles per lane)
  *   operand: 0 A (row = m, col = k)   1 B (row = n, col = k)
  *            2 D accumulator (row = m, col = n)
  *            3 scale (row = operand row, col = K block of 32; slot 0 only)

@@ -453,6 +453,8 @@ INSTR_MAPS = {
     1: (MFMA32_F16_A, MFMA32_F16_B, MFMA32_D),
     2: (MFMA16_F8_A, MFMA16_F8_B, MFMA16_D),
     3: (MFMA32_F8_A, MFMA32_F8_B, MFMA32_D),
+    4: (MFMA16_F4_A, MFMA16_F4_A, MFMA16_D),
+    5: (MFMA32_F4_A, MFMA32_F4_A, MFMA32_D),
 }
 
 

@@ -16,6 +16,7 @@ namespace sl {
 namespace {
 
 constexpr int32_t kFmtE4M3 = 0;  // CBSZ/BLGP format code of FP8 E4M3
+constexpr int32_t kFmtE2M1 = 4;  // ... of FP4 E2M1
 
 template <int BM, int BN, int WM, int WN, int SHIFT>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_mx_kernel(const GemmParams p) {
@@ -142,8 +143,18 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_mx_kernel(const GemmParam
 // instruction tile wants block 2s + l / 32 of row l % 32: the lane reads
 // its row's dword, shifts it right by 8 (l / 32) once per K-tile, and
 // passes byte 2s of the result.
-template <int SHIFT, int SV>
+//
+// FMT = E2M1 (MXFP4): the same tile with 256 packed fp4 per 128-byte K-tile
+// row, four 64-wide k-slices, one 16-byte fragment per lane (its 32
+// consecutive k, as the device probe of the operand map shows) and 8 scale bytes per row
+// per K-tile (a 16-byte scale chunk covers two K-tiles; SV = 4 only).
+template <int SHIFT, int SV, int FMT = 0>
 __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) {
+  constexpr bool F4 = FMT == kFmtE2M1;
+  constexpr int KS = F4 ? 4 : 2;     // 64-wide k-slices per K-tile
+  constexpr int SBT = F4 ? 8 : 4;    // scale bytes per row per K-tile
+  constexpr int TPC = 16 / SBT;      // K-tiles per 16-byte scale chunk
+  static_assert(!F4 || SV == 4, "E2M1 data takes 16-byte scale chunks");
   constexpr int BM = 256, BN = 256, WM = 2, NT = 512;
   constexpr int TM = 128, TN = 64;
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -162,31 +173,34 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
-  const char* A = (const char*)p.a + (tc.batch * p.a_bs + m0 * p.a_rs);
-  const char* B = (const char*)p.b + (tc.batch * p.b_bs + n0 * p.b_rs);
+  // byte addressing: E2M1 elements are packed two per byte (the planner
+  // makes strides and K even)
+  constexpr int EPB = F4 ? 2 : 1;  // elements per byte
+  const char* A = (const char*)p.a + (tc.batch * p.a_bs + m0 * p.a_rs) / EPB;
+  const char* B = (const char*)p.b + (tc.batch * p.b_bs + n0 * p.b_rs) / EPB;
 
-  LoaderKVec<BM, NT, SHIFT, 1> la(A, rows_a, p.a_rs, 1, p.K, wave, lane);
-  LoaderKVec<BN, NT, SHIFT, 1> lb(B, rows_b, p.b_rs, 1, p.K, wave, lane);
+  LoaderKVec<BM, NT, SHIFT, 1> la(A, rows_a, p.a_rs / EPB, 1, p.K / EPB, wave, lane);
+  LoaderKVec<BN, NT, SHIFT, 1> lb(B, rows_b, p.b_rs / EPB, 1, p.K / EPB, wave, lane);
 
   // scale copy of this wave: operand (wave / 4), rows 64 (wave % 4) + lane
-  const int32_t kdw = (int32_t)((p.K + 127) / 128);  // scale dwords per row
+  const int32_t kb = (int32_t)((p.K + 31) / 32);  // scale bytes per row
   const bool s_is_b = wave >= 4;
   const uint8_t* S = s_is_b ? p.sfb + tc.batch * p.sb_bs + n0 * p.sb_rs : p.sfa + tc.batch * p.sa_bs + m0 * p.sa_rs;
   const int64_t s_rs = s_is_b ? p.sb_rs : p.sa_rs;
   const int32_t s_rows = s_is_b ? rows_b : rows_a;
-  const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(S, s_rows > 0 ? (uint32_t)((s_rows - 1) * s_rs + 4 * kdw) : 0u);
+  const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(S, s_rows > 0 ? (uint32_t)((s_rows - 1) * s_rs + kb) : 0u);
   const int32_t s_row = 64 * (wave & 3) + lane;
   const uint32_t s_off = s_row < s_rows ? (uint32_t)(s_row * s_rs) : kOutOfRange;
-  // SV 1: dword of K-tile t into the stage; SV 4: 16 bytes (K-tiles 4q..4q+3)
-  // into scale buffer q & 1
+  // SV 1: dword of K-tile t into the stage; SV 4: 16 bytes (K-tiles
+  // TPC q .. TPC q + TPC - 1) into scale buffer q & 1
   auto issue_scales = [&](int32_t t, char* stage) {
     if constexpr (SV == 1) {
-      const uint32_t off = (s_off != kOutOfRange && t < kdw) ? s_off + 4u * (uint32_t)t : kOutOfRange;
+      const uint32_t off = (s_off != kOutOfRange && 4 * t < kb) ? s_off + 4u * (uint32_t)t : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void_t*)(stage + SOFF + (s_is_b ? BM * 4 : 0) + 256 * (wave & 3)),
                                                4, off, 0, 0, 0);
     } else {
       const int32_t q = t;  // chunk index
-      const uint32_t off = (s_off != kOutOfRange && 4 * q < kdw) ? s_off + 16u * (uint32_t)q : kOutOfRange;
+      const uint32_t off = (s_off != kOutOfRange && 16 * q < kb) ? s_off + 16u * (uint32_t)q : kOutOfRange;
       char* buf = smem + 2 * STAGE + (q & 1) * SBUF + (s_is_b ? BM * 16 : 0) + 1024 * (wave & 3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void_t*)buf, 16, off, 0, 0, 0);
     }
@@ -235,31 +249,52 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
     if constexpr (SV == 1) {
       issue_scales(t + 1, nxt);
     } else {
-      // chunk t/4 + 1 into the buffer chunk t/4 - 1 used (retired by the
-      // barrier that ended K-tile t - 1); it lands by K-tile t + 4
-      if ((t & 3) == 0) issue_scales((t >> 2) + 1, nullptr);
+      // chunk t/TPC + 1 into the buffer chunk t/TPC - 1 used (retired by
+      // the barrier that ended K-tile t - 1); it lands by K-tile t + TPC
+      if ((t & (TPC - 1)) == 0) issue_scales(t / TPC + 1, nullptr);
     }
-    uint32_t sa[FM], sb[FN];
+    // this K-tile's scale dwords of each lane's rows, shifted right by
+    // 8 (lane / 32): byte 2 s' of dword s / 2 is then the scale of slice s
+    // (s' = s % 2) for this lane
+    uint32_t sa[FM][SBT / 4], sb[FN][SBT / 4];
     if constexpr (SV == 1) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sa[i] = scale_word(cur, 0, a_row0 + 32 * i + (lane & 31)) >> half_sel;
+      for (int i = 0; i < FM; ++i) sa[i][0] = scale_word(cur, 0, a_row0 + 32 * i + (lane & 31)) >> half_sel;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sb[j] = scale_word(cur, 1, b_row0 + 32 * j + (lane & 31)) >> half_sel;
+      for (int j = 0; j < FN; ++j) sb[j][0] = scale_word(cur, 1, b_row0 + 32 * j + (lane & 31)) >> half_sel;
     } else {
-      if ((t & 3) == 0) {
+      if ((t & (TPC - 1)) == 0) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) sa4[i] = scale_chunk(t >> 2, 0, a_row0 + 32 * i + (lane & 31));
+        for (int i = 0; i < FM; ++i) sa4[i] = scale_chunk(t / TPC, 0, a_row0 + 32 * i + (lane & 31));
 #pragma unroll
-        for (int j = 0; j < FN; ++j) sb4[j] = scale_chunk(t >> 2, 1, b_row0 + 32 * j + (lane & 31));
+        for (int j = 0; j < FN; ++j) sb4[j] = scale_chunk(t / TPC, 1, b_row0 + 32 * j + (lane & 31));
       }
+      const int32_t d0 = (t & (TPC - 1)) * (SBT / 4);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sa[i] = pick(sa4[i], t & 3) >> half_sel;
+      for (int d = 0; d < SBT / 4; ++d) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sb[j] = pick(sb4[j], t & 3) >> half_sel;
+        for (int i = 0; i < FM; ++i) sa[i][d] = pick(sa4[i], d0 + d) >> half_sel;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sb[j][d] = pick(sb4[j], d0 + d) >> half_sel;
+      }
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       i32x8 af[FM], bf[FN];
+      if constexpr (F4) {
+        // 16 bytes: the lane's 32 consecutive k (k = 32 (lane / 32) + v)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const u32x4 v = *(const u32x4*)(cur + lds_offset(a_row0 + 32 * i + (lane & 31), 32 * ks + 16 * (lane >> 5), SHIFT));
+          af[i] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const u32x4 v =
+              *(const u32x4*)(cur + ABYTES + lds_offset(b_row0 + 32 * j + (lane & 31), 32 * ks + 16 * (lane >> 5), SHIFT));
+          bf[j] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        }
+      } else {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const u32x4 lo = *(const u32x4*)(cur + fragment_lds_offset(MFMA32_F8, lane, 0, a_row0 + 32 * i, ks, SHIFT));
@@ -274,14 +309,15 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
             *(const u32x4*)(cur + ABYTES + fragment_lds_offset(MFMA32_F8, lane, 1, b_row0 + 32 * j, ks, SHIFT));
         bf[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
+      }
       // instruction A = our B tile (its scales: sb), instruction B = our A tile
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              bf[j], af[i], acc[i][j], kFmtE4M3, kFmtE4M3, 0, (int)((sb[j] >> (16 * ks)) & 0xFFu), 0,
-              (int)((sa[i] >> (16 * ks)) & 0xFFu));
+              bf[j], af[i], acc[i][j], FMT, FMT, 0, (int)((sb[j][ks >> 1] >> (16 * (ks & 1))) & 0xFFu), 0,
+              (int)((sa[i][ks >> 1] >> (16 * (ks & 1))) & 0xFFu));
     }
     wait_vmem();
     __syncthreads();
@@ -323,7 +359,9 @@ hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, hipStream_t s) {
     case T128x128_W2x2: return launch_cfg<128, 128, 2, 2>(p, s);
     case T256x256_W2x4: {
       dim3 grid((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), block(512);
-      if (p.flags & F_SCALE16)
+      if (p.flags & F_FP4)
+        hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4, kFmtE2M1>), grid, block, 0, s, p);
+      else if (p.flags & F_SCALE16)
         hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4>), grid, block, 0, s, p);
       else
         hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 1>), grid, block, 0, s, p);

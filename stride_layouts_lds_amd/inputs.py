@@ -66,8 +66,16 @@ class Workload:
         return self.a.kind == "bf16"
 
     @property
-    def nvfp4(self) -> bool:
+    def fp4(self) -> bool:
         return self.a.kind == "e2m1"
+
+    @property
+    def nvfp4(self) -> bool:
+        return self.fp4 and self.sfa is not None and self.sfa.kind == "e4m3"
+
+    @property
+    def mxfp4(self) -> bool:
+        return self.fp4 and self.sfa is not None and self.sfa.kind == "e8m0"
 
     @property
     def flops(self) -> int:
@@ -179,6 +187,26 @@ def nvfp4_workload(name: str, M: int, N: int, K: int, *, seed: int, batch: Optio
     else:
         d_shape, d_strides = (batch, M, N), (M * N, N, 1)
     return Workload(name, M, N, K, batch or 1, a, b, c, sfa, sfb, 16, d_shape, d_strides)
+
+
+def mxfp4_workload(name: str, M: int, N: int, K: int, *, seed: int, batch: Optional[int] = None,
+                   with_c: bool = False, exact: bool = False) -> Workload:
+    """MXFP4: packed E2M1 A and B (codes uniform), one E8M0 scale per 32 K
+    with exponents uniform in [-4, 0] (with ``exact``, [-1, 1], so every
+    partial sum of a K <= 2048 problem is exact in fp32), C fp16 if asked."""
+    rng = np.random.default_rng(seed)
+    a = e2m1_matrix(rng, batch, M, K)
+    b = e2m1_matrix(rng, batch, N, K)
+    kb = -(-K // 32)
+    lo, hi = (-1, 1) if exact else (-4, 0)
+    sfa = scales(rng, batch, M, kb, lo, hi)
+    sfb = scales(rng, batch, N, kb, lo, hi)
+    c = matrix(rng, "int4" if exact else "normal", batch, M, N, "row") if with_c else None
+    if batch is None:
+        d_shape, d_strides = (M, N), (N, 1)
+    else:
+        d_shape, d_strides = (batch, M, N), (M * N, N, 1)
+    return Workload(name, M, N, K, batch or 1, a, b, c, sfa, sfb, 32, d_shape, d_strides)
 
 
 def gemm_workload(name: str, M: int, N: int, K: int, *, seed: int, dist: str = "normal",

@@ -49,7 +49,7 @@ def _ora(op, scale: bool = False, nvfp4: bool = False):
 
 
 def _operands(w: Workload):
-    nv = w.nvfp4
+    nv = w.nvfp4  # E4M3 scales (MXFP4's E8M0 scales have numpy views)
     return (_ora(w.a), _ora(w.b), _ora(w.c), _ora(w.sfa, True, nv), _ora(w.sfb, True, nv))
 
 

@@ -183,7 +183,7 @@ def test_mx_validation(api):
 
 # ------------------------------------------------------------------ maps
 
-@pytest.mark.parametrize("instr", [0, 1, 2, 3])
+@pytest.mark.parametrize("instr", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("operand", [0, 1, 2])
 def test_fragment_maps_equal_oracle(api, instr, operand):
     got = api.query_fragment_map(instr, operand)
@@ -344,8 +344,8 @@ def test_bf16_dtypes(api):
 
 def test_nvfp4_plan_and_validation(api):
     """NVFP4: packed E2M1 operands with E4M3 scales per 16 K go to the
-    dequantising 8-wave kernel; E2M1 with E8M0 scales (MXFP4) and packed
-    layouts the loader cannot take are rejected."""
+    dequantising 8-wave kernel (E8M0 scales per 32 make it MXFP4); other
+    scale pairings and packed layouts the loader cannot take are rejected."""
     E2, E4, E8 = 6, 3, 4
     M, N, K = 512, 256, 1024
     a = (BASE_A, E2, (M, K), (K, 1))
@@ -358,8 +358,10 @@ def test_nvfp4_plan_and_validation(api):
     assert p["tile_m"] == p["tile_n"] == 256 and p["tile_k"] == 64 and p["lds_bytes"] == 2 * 512 * 64 * 2
     s8a = (BASE_C, E8, (M, K // 32), (K // 32, 1))
     s8b = (BASE_C + 0x100000, E8, (N, K // 32), (K // 32, 1))
-    assert err(api, a, b, None, d, s8a, s8b, block_k=32) == "SL_ERR_DTYPE"
+    assert plan(api, a, b, None, d, s8a, s8b, block_k=32)["kernel"] == api.K_MXFP4
+    assert err(api, a, b, None, d, s8a, s8b, block_k=16) == "SL_ERR_DTYPE"
     assert err(api, a, b, None, d, sa, sb, block_k=32) == "SL_ERR_DTYPE"
+    assert err(api, a, b, None, d, sa, s8b, block_k=16) == "SL_ERR_DTYPE"
     # K % 32 != 0, an N-contiguous B, a row stride that is not a multiple of 32
     K2 = 1008
     assert err(api, (BASE_A, E2, (M, K2), (K2, 1)), (BASE_B, E2, (N, K2), (K2, 1)), None, d,
@@ -367,3 +369,21 @@ def test_nvfp4_plan_and_validation(api):
                block_k=16) == "SL_ERR_LAYOUT"
     assert err(api, a, (BASE_B, E2, (N, K), (1, N)), None, d, sa, sb, block_k=16) == "SL_ERR_LAYOUT"
     assert err(api, (BASE_A, E2, (M, K), (K + 16, 1)), b, None, d, sa, sb, block_k=16) == "SL_ERR_LAYOUT"
+
+
+def test_mxfp4_plan(api):
+    """MXFP4 (packed E2M1, E8M0 per 32 K) goes to the 8-wave scaled-MFMA
+    kernel with 256-wide K-tiles; K must be a multiple of 512."""
+    E2, E8 = 6, 4
+    M, N, K = 512, 256, 1024
+    a = (BASE_A, E2, (M, K), (K, 1))
+    b = (BASE_B, E2, (N, K), (K, 1))
+    sa = (BASE_C, E8, (M, K // 32), (K // 32, 1))
+    sb = (BASE_C + 0x100000, E8, (N, K // 32), (K // 32, 1))
+    d = rowmajor(BASE_D, (M, N))
+    p = plan(api, a, b, None, d, sa, sb, block_k=32)
+    assert p["kernel"] == api.K_MXFP4 and p["tile_k"] == 256 and p["threads"] == 512
+    K2 = 768
+    assert err(api, (BASE_A, E2, (M, K2), (K2, 1)), (BASE_B, E2, (N, K2), (K2, 1)), None, d,
+               (BASE_C, E8, (M, K2 // 32), (K2 // 32, 1)), (BASE_C + 0x100000, E8, (N, K2 // 32), (K2 // 32, 1)),
+               block_k=32) == "SL_ERR_LAYOUT"

@@ -469,3 +469,34 @@ def test_nvfp4_bounded_and_sampled_8192(api):
     d_ref, _, absum = h.oracle_full(w)
     h.assert_within_bound(d.reshape(d_ref.shape), d_ref, absum, w.name)
     _sampled(api, I.nvfp4_workload("nvfp4_8192", 8192, 8192, 8192, seed=6), n=1500)
+
+
+# ------------------------------------------------------------------ MXFP4
+
+MXFP4_EXACT = [
+    # M, N, K, batch, with_c
+    (256, 256, 512, None, False),
+    (300, 264, 1024, None, True),
+    (136, 72, 512, 2, True),
+    (520, 300, 2048, None, False),
+]
+
+
+@pytest.mark.parametrize("case", MXFP4_EXACT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_c{int(c[4])}")
+def test_mxfp4_exact_parity(api, case):
+    """Packed E2M1 data with E8M0 scales 2^[-1,1]: every product and partial
+    sum is exact in fp32, so D must equal the oracle bit for bit."""
+    h = H()
+    M, N, K, batch, with_c = case
+    w = I.mxfp4_workload("mxfp4_exact", M, N, K, seed=M + K + 1, batch=batch, with_c=with_c, exact=True)
+    plan = _plan(api, w)
+    h.log(f"mxfp4 exact {case} plan={plan}")
+    assert plan["kernel"] == api.K_MXFP4
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
+def test_mxfp4_sampled_8192(api):
+    _sampled(api, I.mxfp4_workload("mxfp4_8192", 8192, 8192, 8192, seed=7), n=1500)
