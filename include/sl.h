@@ -243,6 +243,97 @@ sl_status sl_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t capacit
  */
 sl_status sl_probe_lds(int32_t mode, const void* src, const int32_t* perm, void* out, void* stream);
 
+/*
+ * Host layout algebra on shape:stride layouts given as text, the notation
+ * of "数据布局及其记号" (section "Shape-Stride 模型": "(shape):(stride)",
+ * nested tuples, a coordinate's offset is its dot product with the strides,
+ * coordinates unflattened first-mode-fastest) and the operations
+ * "CuTe 中 A、B 如何加载到 MMA 寄存器" derives its views and fragments with
+ * (sections 2 and 3 and its closing source notes).  Host only, no HIP call.
+ *
+ * Text: "(4,(2,2)):(1,(4,8))", "8:1", "((_2,_2),_4):((_1,72),_2048)".  As in
+ * that page's printed traces, a leading '_' marks a compile-time (static)
+ * integer and a bare one a run-time value.  The distinction decides two
+ * operations only: filter_zeros treats a stride as a broadcast only when it
+ * is a static 0, and make_ordered takes static order values first (by
+ * value) and run-time ones after them, in the order they appear.  Results
+ * print without '_' unless `op` carries SL_LA_MARK_STATIC.
+ *
+ *   op                     a                 b              result
+ *   SL_LA_PARSE            layout or shape   -              a, normalised
+ *   SL_LA_COALESCE         layout            -              size-1 modes dropped, contiguous modes merged
+ *   SL_LA_COMPOSITION      layout A          layout B       A o B (B's hierarchy; A(B(i)) for every i)
+ *   SL_LA_COMPLEMENT       layout            integer N      the modes filling [0, N) around a's image
+ *   SL_LA_RIGHT_INVERSE    layout            -              R with a(R(i)) == i on [0, size(R))
+ *   SL_LA_ZIPPED_DIVIDE    layout            tiler layout   ((tile), (rest)); tiler mode i divides mode i
+ *   SL_LA_FILTER_ZEROS     layout            -              static-0-stride leaves get shape 1
+ *   SL_LA_COMPACT_LEFT     layout or shape   -              compact first-mode-fastest strides,
+ *                                                           size-1 modes stride 0
+ *   SL_LA_MAKE_ORDERED     layout or shape   order tuple    compact strides in the order of b's values
+ *                                                           (or of b's strides if b is a layout)
+ *   SL_LA_LOGICAL_PRODUCT  block             rest           (block, complement(block, size*cosize(rest)) o rest)
+ *   SL_LA_TILED_PRODUCT    block             rest           the same, rest's modes lifted beside block
+ *   SL_LA_FRAGMENT_LIKE    partition         -              make_fragment_like: mode 0 compacted
+ *                                                           left (broadcasts kept), modes 1.. ordered
+ *                                                           by their strides, tiled_product of the two
+ *   SL_LA_TENSOR_LIKE      partition         -              make_ordered over all modes
+ *   SL_LA_EVAL             layout            index          offset of the flat index (decimal)
+ *   SL_LA_SIZE             layout or shape   -              number of coordinates (decimal)
+ *   SL_LA_COSIZE           layout            -              1 + largest offset (decimal)
+ *
+ * The result text (NUL-terminated) goes to `out`; *needed (if not NULL)
+ * gets its size in bytes including the NUL.  Errors: SL_ERR_NULL (a, b or
+ * out NULL), SL_ERR_ARG (unknown op), SL_ERR_LAYOUT (text that does not
+ * parse, or an operation undefined for its operands, e.g. a composition
+ * whose strides do not divide), SL_ERR_SHAPE (out smaller than *needed, or
+ * an EVAL index outside the layout).  The message says which.
+ */
+enum {
+  SL_LA_PARSE = 0,
+  SL_LA_COALESCE = 1,
+  SL_LA_COMPOSITION = 2,
+  SL_LA_COMPLEMENT = 3,
+  SL_LA_RIGHT_INVERSE = 4,
+  SL_LA_ZIPPED_DIVIDE = 5,
+  SL_LA_FILTER_ZEROS = 6,
+  SL_LA_COMPACT_LEFT = 7,
+  SL_LA_MAKE_ORDERED = 8,
+  SL_LA_LOGICAL_PRODUCT = 9,
+  SL_LA_TILED_PRODUCT = 10,
+  SL_LA_FRAGMENT_LIKE = 11,
+  SL_LA_TENSOR_LIKE = 12,
+  SL_LA_EVAL = 13,
+  SL_LA_SIZE = 14,
+  SL_LA_COSIZE = 15,
+  SL_LA_MARK_STATIC = 256
+};
+sl_status sl_layout_op(int32_t op, const char* a, const char* b, char* out, int64_t capacity, int64_t* needed);
+
+/*
+ * Trace of the plan sl_gemm would run for `args` (host only: validation and
+ * kernel selection as sl_gemm_plan, no HIP call): every stage's layout,
+ * computed with the algebra above, one line each as "name: layout  # note",
+ * plus "# note" lines.  The stages follow how "CuTe 中 A、B 如何加载到 MMA
+ * 寄存器" walks one operand from memory to the instruction (section 2: the
+ * TV map of the instruction, the thread's partition of the shared-memory
+ * tile as a composition, its register fragment by make_fragment_like in
+ * section 3), applied to this library's kernels:
+ *   A_instr          (lane, slot) -> m + R k of the instruction's A operand
+ *   A, A_tiles       the operand view, zipped_divide by the workgroup tile
+ *   A_lds, A_copy    the LDS tile before its XOR swizzle (stated beside
+ *                    it), the LDS bytes each copy instruction fills
+ *   A_wave, A_lane0  the wave's (lane, ((slot), repeat, K slice)) partition
+ *                    of the LDS tile, and lane 0's part of it
+ *   A_frag           fragment_like of one K slice: the lane's registers
+ *   (B the same), SFA / SFB / scale_instr for scaled formats,
+ *   D_instr, acc, D_lane0   accumulator TV map, register order, and the D
+ *                    elements of lane 0's registers
+ *   D, C, D_tiles, tile_order, workgroup_tile, workspace (split-K).
+ * Output and errors as sl_layout_op (plus sl_gemm_plan's validation
+ * statuses); pointers in args are only checked, never dereferenced.
+ */
+sl_status sl_describe_plan(const sl_gemm_args* args, char* out, int64_t capacity, int64_t* needed);
+
 #ifdef __cplusplus
 }
 #endif

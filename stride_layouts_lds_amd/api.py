@@ -25,7 +25,14 @@ STATUS = {0: "SL_OK", -1: "SL_ERR_NULL", -2: "SL_ERR_DTYPE", -3: "SL_ERR_SHAPE",
 # every symbol include/sl.h declares
 EXPORTS = ["sl_gemm", "sl_gemm_plan", "sl_status_string", "sl_last_error_message", "sl_abi_version",
            "sl_query_fragment_map", "sl_query_lds_map", "sl_query_fragment_addresses", "sl_probe_mfma",
-           "sl_probe_lds"]
+           "sl_probe_lds", "sl_layout_op", "sl_describe_plan"]
+
+# sl_layout_op operations (include/sl.h)
+LA_OPS = {"parse": 0, "coalesce": 1, "composition": 2, "complement": 3, "right_inverse": 4,
+          "zipped_divide": 5, "filter_zeros": 6, "compact_left": 7, "make_ordered": 8,
+          "logical_product": 9, "tiled_product": 10, "fragment_like": 11, "tensor_like": 12,
+          "eval": 13, "size": 14, "cosize": 15}
+SL_LA_MARK_STATIC = 256
 
 
 class sl_layout(ctypes.Structure):
@@ -88,6 +95,10 @@ def lib() -> ctypes.CDLL:
         L.sl_probe_mfma.argtypes = [i32, i32, vp, i64, P(i64), vp]
         L.sl_probe_lds.restype = i32
         L.sl_probe_lds.argtypes = [i32, vp, vp, vp, vp]
+        L.sl_layout_op.restype = i32
+        L.sl_layout_op.argtypes = [i32, ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p, i64, P(i64)]
+        L.sl_describe_plan.restype = i32
+        L.sl_describe_plan.argtypes = [P(sl_gemm_args), ctypes.c_char_p, i64, P(i64)]
         _lib = L
     return _lib
 
@@ -181,6 +192,41 @@ def gemm(a, b, c=None, out=None, sfa=None, sfb=None, block_k: int = 32, stream: 
         out = torch.empty(shape, dtype=torch.bfloat16 if a.dtype == torch.bfloat16 else torch.float16,
                           device=a.device)
     sl_gemm(make_args(a, b, c, out, sfa, sfb, block_k), stream)
+    return out
+
+
+def _text_call(fn) -> str:
+    """Runs fn(buffer, capacity, needed) and grows the buffer once if needed."""
+    need = ctypes.c_int64(0)
+    buf = ctypes.create_string_buffer(1 << 14)
+    st = fn(buf, len(buf), ctypes.byref(need))
+    if st == -3 and need.value > len(buf):
+        buf = ctypes.create_string_buffer(need.value)
+        st = fn(buf, len(buf), ctypes.byref(need))
+    _check(st)
+    return buf.value.decode()
+
+
+def layout_op(op: str, a: str, b=None, mark_static: bool = False) -> str:
+    """sl_layout_op by name: layout_op("composition", "(16,16):(16,1)", "(2,2,2):(16,8,128)")."""
+    code = LA_OPS[op] | (SL_LA_MARK_STATIC if mark_static else 0)
+    bb = None if b is None else str(b).encode()
+    return _text_call(lambda buf, cap, need: lib().sl_layout_op(code, a.encode(), bb, buf, cap, need))
+
+
+def describe_plan(args: sl_gemm_args) -> str:
+    """sl_describe_plan: the layout of every stage of the planned GEMM."""
+    return _text_call(lambda buf, cap, need: lib().sl_describe_plan(ctypes.byref(args), buf, cap, need))
+
+
+def describe_stages(text: str) -> dict:
+    """{name: layout text} of the stage lines of a describe_plan trace."""
+    out = {}
+    for line in text.splitlines():
+        if line.startswith("#") or ": " not in line:
+            continue
+        name, rest = line.split(": ", 1)
+        out[name] = rest.split("  #", 1)[0].strip()
     return out
 
 

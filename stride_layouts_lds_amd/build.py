@@ -19,8 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstride_layouts_lds.so")
-SOURCES = ["api.cpp", "gemm_f16.hip", "gemm_mx.hip", "probes.hip"]
-HEADERS = ["sl_maps.hpp", "sl_kernels.hpp", "sl_device.hpp"]
+SOURCES = ["api.cpp", "describe.cpp", "layout_algebra.cpp", "gemm_f16.hip", "gemm_mx.hip", "probes.hip"]
+HEADERS = ["sl_maps.hpp", "sl_kernels.hpp", "sl_device.hpp", "layout_algebra.hpp", "describe.hpp"]
 ARCH = "gfx950"
 
 

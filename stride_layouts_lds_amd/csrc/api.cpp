@@ -8,10 +8,13 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <string>
 
 #include "../../include/sl.h"
+#include "describe.hpp"
+#include "layout_algebra.hpp"
 #include "sl_kernels.hpp"
 #include "sl_maps.hpp"
 
@@ -516,6 +519,51 @@ sl_status check_arch() {
   return SL_OK;
 }
 
+// Copies `text` into the caller's buffer; *needed gets its size with the
+// terminating NUL.  A buffer too small for it returns SL_ERR_SHAPE.
+sl_status emit_text(const std::string& text, char* out, int64_t capacity, int64_t* needed) {
+  const int64_t n = (int64_t)text.size() + 1;
+  if (needed) *needed = n;
+  if (!out) return fail(SL_ERR_NULL, "out is NULL");
+  if (capacity < n) {
+    if (capacity > 0) out[0] = '\0';
+    return fail(SL_ERR_SHAPE, "output buffer of %lld bytes, %lld needed", (long long)capacity, (long long)n);
+  }
+  memcpy(out, text.c_str(), (size_t)n);
+  return SL_OK;
+}
+
+// "layout" text, or a shape tuple alone (strides 0)
+sl::la::Layout parse_any(const char* text) {
+  const std::string t(text);
+  return t.find(':') == std::string::npos ? sl::la::parse_shape(t) : sl::la::parse(t);
+}
+
+// an order tuple "(_2048,(144,288))" (or a layout, whose strides are the
+// order values) as a layout whose strides carry the values
+sl::la::Layout parse_order(const char* text) {
+  const std::string t(text);
+  if (t.find(':') != std::string::npos) return sl::la::parse(t);
+  std::function<sl::la::Layout(const sl::la::Layout&)> mv = [&](const sl::la::Layout& l) {
+    if (l.leaf) {
+      sl::la::Layout m = sl::la::Layout::mode(1, l.shape);
+      m.stride_static = l.shape_static;
+      return m;
+    }
+    std::vector<sl::la::Layout> k;
+    for (const auto& x : l.kids) k.push_back(mv(x));
+    return sl::la::Layout::tuple(std::move(k));
+  };
+  return mv(sl::la::parse_shape(t));
+}
+
+int64_t parse_int(const char* text) {
+  char* end = nullptr;
+  const long long v = strtoll(text, &end, 10);
+  if (end == text || *end != '\0') throw sl::la::Error{std::string("expected an integer, got \"") + text + "\""};
+  return v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -700,6 +748,87 @@ sl_status sl_probe_lds(int32_t mode, const void* src, const int32_t* perm, void*
   const hipError_t e = sl::launch_probe_lds(mode, src, perm, out, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SL_ERR_LAUNCH, "probe launch failed: %s", hipGetErrorString(e));
   return SL_OK;
+}
+
+sl_status sl_layout_op(int32_t op, const char* a, const char* b, char* out, int64_t capacity, int64_t* needed) {
+  g_msg.clear();
+  namespace la = sl::la;
+  if (!a) return fail(SL_ERR_NULL, "a is NULL");
+  const bool mark = (op & SL_LA_MARK_STATIC) != 0;
+  op &= ~SL_LA_MARK_STATIC;
+  const bool binary = op == SL_LA_COMPOSITION || op == SL_LA_COMPLEMENT || op == SL_LA_ZIPPED_DIVIDE ||
+                      op == SL_LA_MAKE_ORDERED || op == SL_LA_LOGICAL_PRODUCT || op == SL_LA_TILED_PRODUCT ||
+                      op == SL_LA_EVAL;
+  if (binary && !b) return fail(SL_ERR_NULL, "b is NULL");
+  std::string r;
+  try {
+    switch (op) {
+      case SL_LA_PARSE: r = la::to_string(parse_any(a), mark); break;
+      case SL_LA_COALESCE: r = la::to_string(la::coalesce(la::parse(a)), mark); break;
+      case SL_LA_COMPOSITION: r = la::to_string(la::composition(la::parse(a), la::parse(b)), mark); break;
+      case SL_LA_COMPLEMENT: r = la::to_string(la::complement(la::parse(a), parse_int(b)), mark); break;
+      case SL_LA_RIGHT_INVERSE: r = la::to_string(la::right_inverse(la::parse(a)), mark); break;
+      case SL_LA_ZIPPED_DIVIDE: r = la::to_string(la::zipped_divide(la::parse(a), la::parse(b)), mark); break;
+      case SL_LA_FILTER_ZEROS: r = la::to_string(la::filter_zeros(la::parse(a)), mark); break;
+      case SL_LA_COMPACT_LEFT: r = la::to_string(la::compact_left(parse_any(a)), mark); break;
+      case SL_LA_MAKE_ORDERED: r = la::to_string(la::make_ordered(parse_any(a), parse_order(b)), mark); break;
+      case SL_LA_LOGICAL_PRODUCT: r = la::to_string(la::logical_product(la::parse(a), la::parse(b)), mark); break;
+      case SL_LA_TILED_PRODUCT: r = la::to_string(la::tiled_product(la::parse(a), la::parse(b)), mark); break;
+      case SL_LA_FRAGMENT_LIKE: r = la::to_string(la::fragment_like(la::parse(a)), mark); break;
+      case SL_LA_TENSOR_LIKE: r = la::to_string(la::tensor_like(la::parse(a)), mark); break;
+      case SL_LA_EVAL: {
+        const int64_t i = parse_int(b);
+        const la::Layout l = la::parse(a);
+        if (i < 0 || i >= la::size(l)) return fail(SL_ERR_SHAPE, "index %lld outside [0, %lld)", (long long)i, (long long)la::size(l));
+        r = std::to_string(la::eval(l, i));
+        break;
+      }
+      case SL_LA_SIZE: r = std::to_string(la::size(parse_any(a))); break;
+      case SL_LA_COSIZE: r = std::to_string(la::cosize(la::parse(a))); break;
+      default: return fail(SL_ERR_ARG, "unknown layout op %d", op);
+    }
+  } catch (const la::Error& e) {
+    return fail(SL_ERR_LAYOUT, "%s", e.what.c_str());
+  } catch (const std::exception& e) {
+    return fail(SL_ERR_LAYOUT, "%s", e.what());
+  }
+  return emit_text(r, out, capacity, needed);
+}
+
+sl_status sl_describe_plan(const sl_gemm_args* args, char* out, int64_t capacity, int64_t* needed) {
+  Plan P;
+  const sl_status s = plan_gemm(args, &P);
+  if (s != SL_OK) return s;
+  if (P.empty) return emit_text("# empty product: nothing is launched\n", out, capacity, needed);
+  const sl::TileShape& ts = sl::kTiles[P.tile];
+  const sl::GemmParams& p = P.p;
+  sl::DescribeInput in{};
+  in.kernel = P.pub.kernel;
+  in.a_load = P.pub.a_load;
+  in.b_load = P.pub.b_load;
+  in.bm = ts.bm, in.bn = ts.bn, in.bk = P.pub.tile_k;
+  in.wm = ts.wm, in.wn = ts.wn, in.stages = ts.stages;
+  in.splits = p.splits, in.split_tiles = p.split_tiles, in.group_m = p.group_m;
+  in.tiles_m = p.tiles_m, in.tiles_n = p.tiles_n;
+  in.workgroups = P.pub.workgroups, in.batch = P.pub.batch, in.M = p.M, in.N = p.N, in.K = p.K;
+  in.a_bs = p.a_bs, in.a_rs = p.a_rs, in.a_cs = p.a_ks;
+  in.b_bs = p.b_bs, in.b_rs = p.b_rs, in.b_cs = p.b_ks;
+  in.c_bs = p.c_bs, in.c_rs = p.c_rs, in.c_cs = p.c_cs;
+  in.d_bs = p.d_bs, in.d_rs = p.d_rs, in.d_cs = p.d_cs;
+  in.sa_rs = p.sa_rs, in.sa_cs = p.sa_ks, in.sb_rs = p.sb_rs, in.sb_cs = p.sb_ks;
+  in.a_batched = args->a.layout.rank == 3, in.b_batched = args->b.layout.rank == 3;
+  in.c_batched = args->c.layout.rank == 3, in.d_batched = args->d.layout.rank == 3;
+  in.has_c = (p.flags & sl::F_HAS_C) != 0;
+  in.flags = p.flags;
+  in.block_k = args->block_k;
+  in.lds_bytes = P.pub.lds_bytes;
+  std::string text;
+  try {
+    text = sl::describe_plan(in);
+  } catch (const std::exception& e) {
+    return fail(SL_ERR_LAYOUT, "%s", e.what());
+  }
+  return emit_text(text, out, capacity, needed);
 }
 
 }  // extern "C"
