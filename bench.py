@@ -73,9 +73,14 @@ def algorithmic_bytes(w) -> int:
 
 
 def source_hash() -> str:
+    """Hash of the sources that decide what runs on the GPU (kernels, device
+    headers, the planner); the host-only layout algebra and plan trace are
+    left out."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "stride_layouts_lds_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f.startswith(("layout_algebra.", "describe.")):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
