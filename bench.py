@@ -138,6 +138,36 @@ def cpu_baseline(w, target_s: float = 12.0):
                       f"{dt:.1f} s on {threads} threads"}
 
 
+def per_launch_timing(api, margs, sid, stream, reps: int) -> dict:
+    """Per-launch event timings, median and best: back to back ("warm": the
+    inputs may sit in the 256 MB Infinity Cache from the previous launch) and
+    "cold", after reading a 512 MiB buffer before each launch so that the
+    inputs come from HBM.  The flush reads rather than writes: a written
+    buffer would leave the cache full of dirty lines whose write-back then
+    lands inside the timed launch."""
+    import torch
+    flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device="cuda")
+    out = {}
+    for kind in ("warm", "cold"):
+        ts = []
+        for r in range(reps):
+            if kind == "cold":
+                flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            api.sl_gemm(margs, sid)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        out[kind + "_median_us"] = round(ts[len(ts) // 2], 2)
+        out[kind + "_best_us"] = round(ts[0], 2)
+    out["reps"] = reps
+    out["flush_bytes"] = flush.numel() * 4
+    del flush
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +232,8 @@ def main():
     print(f"[bench] {args.steps} steps in {wall:.4f} s; {kern_ms * 1e3:.1f} us per launch (events)",
           file=sys.stderr, flush=True)
 
+    timing = per_launch_timing(api, margs, sid, stream, reps=max(10, min(args.steps, 30)))
+
     flop = w.flops
     value = flop * args.steps / wall / 1e12
     # NVFP4 is decoded to fp16 and multiplied on the fp16 matrix cores;
@@ -238,6 +270,7 @@ def main():
                    "tile": f"{plan['tile_m']}x{plan['tile_n']}x{plan['tile_k']}",
                    "workgroups": plan["workgroups"], "peak_frac": round(value / peak, 4)},
         "roofline": roof,
+        "timing": timing,
     }
     if rank == 0 and not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

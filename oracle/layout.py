@@ -439,6 +439,15 @@ MFMA16_F4_A = TV(shape=((16, 4), 32), stride=((1, 512), 16), rows=16, cols=128)
 # v_mfma_scale_f32_32x32x64_f8f6f4, E2M1 A (32 x 64): q = m + 32 k
 MFMA32_F4_A = TV(shape=((32, 2), 32), stride=((1, 1024), 32), rows=32, cols=64)
 
+# The same instructions with 6-bit data (format 2 E2M3, format 3 E3M2): a
+# lane's 32 values are one little-endian bit stream over six dwords (value v
+# at bits 6v .. 6v+5).  Reading: value v of lane l = l0 + R*l1 holds
+# (m = l0, k = 32*l1 + v), the E2M1 order (32 values per lane, one k-block
+# of 32 per scale lane).  Parity unpinned by the pages; pinned by the device
+# probe.
+MFMA16_F6_A = TV(shape=((16, 4), 32), stride=((1, 512), 16), rows=16, cols=128)
+MFMA32_F6_A = TV(shape=((32, 2), 32), stride=((1, 1024), 32), rows=32, cols=64)
+
 
 def mfma_scale_owner(rows: int, lane: int) -> Tuple[int, int]:
     """(row, k-block of 32) whose E8M0 scale lane ``lane`` supplies for the

@@ -724,7 +724,7 @@ sl_status sl_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t capacit
   g_msg.clear();
   if (instr < 0 || instr > 3) return fail(SL_ERR_ARG, "instr %d", instr);
   const bool f8 = instr >= 2;
-  if (mode < 0 || mode > (f8 ? 7 : 1)) return fail(SL_ERR_ARG, "mode %d", mode);
+  if (mode < 0 || mode > (f8 ? 11 : 1)) return fail(SL_ERR_ARG, "mode %d", mode);
   const int64_t nc = 64 * (int64_t)sl::instr_in_slots(instr);
   const int64_t need = nc * 64 * sl::instr_acc_regs(instr);
   if (cases) *cases = nc;

@@ -9,7 +9,9 @@ namespace {
 
 constexpr uint8_t kE4M3One = 0x38;  // 1.0
 constexpr uint8_t kCodeBase = 0x20; // lane/slot-coded E4M3 values start here (0.125)
-constexpr int kFmtE2M1 = 4;         // CBSZ/BLGP format code of FP4 E2M1
+constexpr int kFmtE2M3 = 2;         // CBSZ/BLGP format codes: FP6 E2M3,
+constexpr int kFmtE3M2 = 3;         // BF6 E3M2,
+constexpr int kFmtE2M1 = 4;         // FP4 E2M1
 
 // One wave per case.  f16 instructions: case = (lane, slot) of the one-hot
 // operand; the other operand holds lane*8 + slot + 1.
@@ -99,11 +101,44 @@ __global__ __launch_bounds__(64) void probe_mfma_f8(int32_t mode, float* out) {
   const i32x8 b4 = {(int)wb4[0], (int)wb4[1], (int)wb4[2], (int)wb4[3],
                     (int)wb4[4], (int)wb4[5], (int)wb4[6], (int)wb4[7]};
   const bool fp4 = mode == 6 || mode == 7;
+  // mode 8-11: A one-hot 1.0 in a 6-bit format at value hs of lane hl, the
+  // 32 values of a lane packed as one little-endian bit stream (value v at
+  // bits 6v .. 6v+5 of six dwords): E2M3 (modes 8/9, 1.0 = 0b001000) or
+  // E3M2 (modes 10/11, 1.0 = 0b001100); B as in modes 6/7
+  const bool fp6 = mode >= 8;
+  const uint32_t one6 = mode >= 10 ? 0x0Cu : 0x08u;
+  const int32_t bit = 6 * hs;
+  uint32_t w6[6];
+#pragma unroll
+  for (int w = 0; w < 6; ++w) {
+    uint32_t v = 0;
+    if (lane == hl) {
+      if (bit / 32 == w) v |= one6 << (bit % 32);
+      if (bit / 32 + 1 == w && bit % 32 > 26) v |= one6 >> (32 - bit % 32);
+    }
+    w6[w] = v;
+  }
+  const i32x8 a6 = {(int)w6[0], (int)w6[1], (int)w6[2], (int)w6[3], (int)w6[4], (int)w6[5], 0, 0};
+  uint32_t wb6[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int bidx = 0; bidx < 4; ++bidx)
+      v |= (uint32_t)(kCodeBase + ((mode & 1) == 0 ? lane : 4 * w + bidx)) << (8 * bidx);
+    wb6[w] = v;
+  }
+  const i32x8 b6 = {(int)wb6[0], (int)wb6[1], (int)wb6[2], (int)wb6[3],
+                    (int)wb6[4], (int)wb6[5], (int)wb6[6], (int)wb6[7]};
   float r[REGS];
   if constexpr (INSTR == MFMA16_F8) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     if (fp4)
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a4, b4, acc, kFmtE2M1, 0, 0, 127, 0, 127);
+    else if (fp6 && mode >= 10)
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a6, b6, acc, kFmtE3M2, 0, 0, 127, 0, 127);
+    else if (fp6)
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a6, b6, acc, kFmtE2M3, 0, 0, 127, 0, 127);
     else
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
 #pragma unroll
@@ -112,6 +147,10 @@ __global__ __launch_bounds__(64) void probe_mfma_f8(int32_t mode, float* out) {
     floatx16 acc = {};
     if (fp4)
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a4, b4, acc, kFmtE2M1, 0, 0, 127, 0, 127);
+    else if (fp6 && mode >= 10)
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a6, b6, acc, kFmtE3M2, 0, 0, 127, 0, 127);
+    else if (fp6)
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a6, b6, acc, kFmtE2M3, 0, 0, 127, 0, 127);
     else
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
 #pragma unroll

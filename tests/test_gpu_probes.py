@@ -168,3 +168,47 @@ def test_probe_e2m1_operand_map(api, instr):
                                                for h in range(64) for s_ in range(32)], np.int32))
     assert bad == 0, f"{bad} of 2048 (lane, nibble) differ from the reading; e.g. " + str(
         [(k, v, famap(*k)) for k, v in list(measured.items()) if v != famap(*k)][:6])
+
+
+def _measured_onehot_map(api, instr, mode_lane, mode_slot):
+    """(lane, value) -> (m, k) of a one-hot A against the byte-coded E4M3 B
+    (lane codes in mode_lane, slot codes in mode_slot); None where the
+    one-hot produced no output."""
+    got_l = api.probe_mfma(instr, mode_lane).cpu().numpy()
+    got_s = api.probe_mfma(instr, mode_slot).cpu().numpy()
+    amap, bmap, dmap = L.INSTR_MAPS[instr]
+    dec = {float(OG.e4m3_decode(E4M3_BASE + x)): x for x in range(64)}
+    measured = {}
+    for c in range(64 * 32):
+        hl, hs = c // 32, c % 32
+        nz = np.argwhere(got_l[c] != 0)
+        if len(nz) == 0:
+            measured[(hl, hs)] = None
+            continue
+        l, i = nz[0]
+        m, n = dmap(int(l), int(i))
+        lane_b, slot_b = dec.get(float(got_l[c][l, i])), dec.get(float(got_s[c][l, i]))
+        if lane_b is None or slot_b is None:
+            measured[(hl, hs)] = (-2, -2)  # not a single B value: the one-hot did not read as 1.0
+            continue
+        measured[(hl, hs)] = (m, bmap(lane_b, slot_b)[1])
+    return measured
+
+
+@pytest.mark.parametrize("instr", [2, 3])
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_probe_fp6_operand_map(api, instr, fmt):
+    """A in a 6-bit format (E2M3 or E3M2), one-hot 1.0 at (lane, value) with
+    a lane's 32 values packed as a little-endian bit stream, against the
+    pinned E4M3 B: the measured (lane, value) -> (m, k) map against the
+    oracle's reading."""
+    from gpu_helpers import dump, log
+    log(f"probe fp6 instr={instr} fmt={fmt}")
+    modes = (8, 9) if fmt == "e2m3" else (10, 11)
+    measured = _measured_onehot_map(api, instr, *modes)
+    want = L.MFMA16_F6_A if instr == 2 else L.MFMA32_F6_A
+    bad = [(k, v, want(*k)) for k, v in measured.items() if v != want(*k)]
+    if bad:
+        dump(f"probe_fp6_{fmt}_{instr}", np.array([[h, s_, *(measured[(h, s_)] or (-1, -1))]
+                                                   for h in range(64) for s_ in range(32)], np.int32))
+    assert not bad, f"{len(bad)} of 2048 (lane, value) differ from the reading; e.g. {bad[:6]}"
