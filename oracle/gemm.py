@@ -27,7 +27,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gemm_ref.c")
 LIB = os.path.join(HERE, "libgemm_oracle.so")
 
-F16, F32, E4M3, E8M0, BF16, E2M1 = 1, 2, 3, 4, 5, 6
+F16, F32, E4M3, E8M0, BF16, E2M1, E2M3, E3M2 = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 class _Tensor(ctypes.Structure):
@@ -70,6 +70,11 @@ def lib():
         L.go_bf16_encode.argtypes = [ctypes.c_double]
         L.go_e2m1_decode.restype = ctypes.c_double
         L.go_e2m1_decode.argtypes = [ctypes.c_uint8]
+        for name in ("go_e2m3_decode", "go_e3m2_decode"):
+            getattr(L, name).restype = ctypes.c_double
+            getattr(L, name).argtypes = [ctypes.c_uint8]
+        L.go_fp6_code.restype = ctypes.c_uint8
+        L.go_fp6_code.argtypes = [ctypes.c_void_p, ctypes.c_int64]
         L.go_e4m3_decode.restype = ctypes.c_double
         L.go_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.go_e8m0_decode.restype = ctypes.c_double
@@ -94,7 +99,8 @@ _DT = {np.dtype(np.uint16): F16, np.dtype(np.float16): F16, np.dtype(np.float32)
 
 def packed(storage: np.ndarray, shape: Sequence[int], strides: Sequence[int], dtype: int = None):
     """An operand given as raw storage plus a shape and ELEMENT strides, for
-    formats numpy cannot view (E2M1, two elements per byte)."""
+    formats numpy cannot view (E2M1, two elements per byte; E2M3 / E3M2, a
+    6-bit little-endian bit stream)."""
     return ("packed", np.ascontiguousarray(storage), tuple(shape), tuple(strides), dtype)
 
 
@@ -228,6 +234,20 @@ def bf16_encode(x: float) -> int:
 
 def e2m1_decode(code: int) -> float:
     return lib().go_e2m1_decode(code)
+
+
+def e2m3_decode(code: int) -> float:
+    return lib().go_e2m3_decode(code)
+
+
+def e3m2_decode(code: int) -> float:
+    return lib().go_e3m2_decode(code)
+
+
+def fp6_code(storage: np.ndarray, offset: int) -> int:
+    """The 6-bit code at element offset ``offset`` of a packed byte array."""
+    buf = np.ascontiguousarray(storage, dtype=np.uint8)
+    return lib().go_fp6_code(buf.ctypes.data, offset)
 
 
 def e4m3_decode(code: int) -> float:

@@ -27,6 +27,13 @@
  *    operands are packed two per byte along K: element offset o (in
  *    elements, from the descriptor's strides) is byte o / 2, low nibble for
  *    even o, high nibble for odd o.
+ *  - MXFP6 (the block-scaled product with 6-bit data and E8M0 scales per
+ *    32 K): FP6 E2M3 (bias 1, three significand bits, subnormals m/8, max
+ *    7.5) or FP6 E3M2 (bias 3, two significand bits, subnormals m/16, max
+ *    28), both without infinities or NaN (OCP MX v1.0).  Packed along K as
+ *    one little-endian bit stream: element offset o occupies bits 6o ..
+ *    6o+5, bit 0 being the least significant bit of byte 0 (four elements
+ *    in three bytes).
  *  - bf16 (the same product in the other 16-bit format; the pages name only
  *    fp16) is the upper half of IEEE binary32: bias 127, 7 stored
  *    significand bits, subnormals, inf/NaN; encoded the same way.
@@ -44,7 +51,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { GO_F16 = 1, GO_F32 = 2, GO_E4M3 = 3, GO_E8M0 = 4, GO_BF16 = 5, GO_E2M1 = 6 };
+enum { GO_F16 = 1, GO_F32 = 2, GO_E4M3 = 3, GO_E8M0 = 4, GO_BF16 = 5, GO_E2M1 = 6, GO_E2M3 = 7, GO_E3M2 = 8 };
 
 typedef struct {
   const void* data; /* NULL: absent (C = 0, or no scales) */
@@ -148,12 +155,37 @@ double go_e2m1_decode(uint8_t c) {
   return sgn ? -v : v;
 }
 
+/* E2M3: sign, 2-bit exponent (bias 1), 3-bit fraction */
+double go_e2m3_decode(uint8_t c) {
+  int sgn = (c >> 5) & 1, e = (c >> 3) & 3, m = c & 7;
+  double v = e == 0 ? m / 8.0 : ldexp(1.0 + m / 8.0, e - 1);
+  return sgn ? -v : v;
+}
+
+/* E3M2: sign, 3-bit exponent (bias 3), 2-bit fraction */
+double go_e3m2_decode(uint8_t c) {
+  int sgn = (c >> 5) & 1, e = (c >> 2) & 7, m = c & 3;
+  double v = e == 0 ? ldexp(m / 4.0, -2) : ldexp(1.0 + m / 4.0, e - 3);
+  return sgn ? -v : v;
+}
+
+/* the 6-bit code at element offset o of a packed bit stream */
+uint8_t go_fp6_code(const uint8_t* bytes, int64_t o) {
+  const int64_t bit = 6 * o;
+  const int sh = (int)(bit & 7);
+  unsigned v = bytes[bit >> 3] >> sh;
+  if (sh > 2) v |= (unsigned)bytes[(bit >> 3) + 1] << (8 - sh);
+  return (uint8_t)(v & 63);
+}
+
 /* decoding tables, filled once from the functions above */
 static double g_f16_tab[65536];
 static double g_bf16_tab[65536];
 static double g_e4m3_tab[256];
 static double g_e8m0_tab[256];
 static double g_e2m1_tab[16];
+static double g_e2m3_tab[64];
+static double g_e3m2_tab[64];
 static pthread_once_t g_tab_once = PTHREAD_ONCE_INIT;
 
 static void fill_tables(void) {
@@ -166,6 +198,10 @@ static void fill_tables(void) {
     g_e8m0_tab[i] = go_e8m0_decode((uint8_t)i);
   }
   for (int i = 0; i < 16; ++i) g_e2m1_tab[i] = go_e2m1_decode((uint8_t)i);
+  for (int i = 0; i < 64; ++i) {
+    g_e2m3_tab[i] = go_e2m3_decode((uint8_t)i);
+    g_e3m2_tab[i] = go_e3m2_decode((uint8_t)i);
+  }
 }
 
 /* ------------------------------------------------------- element addressing */
@@ -190,6 +226,8 @@ static double element(const go_tensor* t, int64_t b, int64_t i, int64_t j) {
       const uint8_t byte = ((const uint8_t*)t->data)[o >> 1];
       return g_e2m1_tab[(o & 1) ? byte >> 4 : byte & 15];
     }
+    case GO_E2M3: return g_e2m3_tab[go_fp6_code((const uint8_t*)t->data, o)];
+    case GO_E3M2: return g_e3m2_tab[go_fp6_code((const uint8_t*)t->data, o)];
     default: return NAN;
   }
 }

@@ -401,3 +401,81 @@ def test_mxfp4_gemm_vs_numpy():
     B = G.packed(_pack_e2m1(cb), (N, K), (K, 1), G.E2M1)
     d, ref, absum = G.gemm(A, B, None, sa, sb, block_k=32)
     assert np.array_equal(ref[0], a_real @ b_real.T)
+
+
+# ------------------------------------------------------------------ MXFP6
+
+def _fp8_values(dtype):
+    import torch
+    return torch.arange(256, dtype=torch.uint8).view(dtype).double().numpy()
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_decode_against_the_8_bit_formats(fmt):
+    """OCP MX v1.0 FP6: the 32 non-negative E2M3 codes are, in increasing
+    order, exactly the E4M3 values in [0, 7.5] on the 1/8 grid (three
+    significand bits, subnormal step 1/8, max 7.5); the E3M2 codes likewise
+    the E5M2 values in [0, 28] on the 1/16 grid (two significand bits,
+    subnormal step 1/16, max 28).  The 8-bit values come from torch's float8
+    types; bit 5 is the sign; no infinities or NaN."""
+    import torch
+    if fmt == "e2m3":
+        dec, ref, top, grid = G.e2m3_decode, _fp8_values(torch.float8_e4m3fn), 7.5, 8
+    else:
+        dec, ref, top, grid = G.e3m2_decode, _fp8_values(torch.float8_e5m2), 28.0, 16
+    v = [dec(c) for c in range(64)]
+    pos = v[:32]
+    want = sorted({x for x in ref if np.isfinite(x) and 0 <= x <= top and (x * grid) == int(x * grid)})
+    assert pos == want and len(want) == 32 and pos[-1] == top
+    assert all(v[32 + i] == -pos[i] for i in range(32)) and np.signbit(v[32])
+    assert all(np.isfinite(x) for x in v)
+
+
+def _pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """(rows, K) 6-bit codes -> (rows, 3K/4) bytes: each row one little-endian
+    bit stream, code j at bits 6j .. 6j+5 (numpy's bit unpacking, written
+    independently of the oracle's extraction)."""
+    rows, K = codes.shape
+    bits = ((codes[:, :, None] >> np.arange(6)) & 1).astype(np.uint8).reshape(rows, 6 * K)
+    return np.packbits(bits, axis=1, bitorder="little")
+
+
+def test_fp6_packing_order():
+    rng = np.random.default_rng(21)
+    codes = rng.integers(0, 64, (3, 64)).astype(np.uint8)
+    packed_rows = _pack_fp6(codes)
+    assert packed_rows.shape == (3, 48)
+    flat = packed_rows.reshape(-1)
+    for r in range(3):
+        for j in range(64):
+            assert G.fp6_code(flat, r * 64 + j) == codes[r, j]
+    # byte-level check of the first four codes (three bytes)
+    c = codes[0, :4].astype(int)
+    word = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18)
+    assert list(flat[:3]) == [word & 255, (word >> 8) & 255, (word >> 16) & 255]
+
+
+@pytest.mark.parametrize("fa,fb", [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2")])
+def test_mxfp6_gemm_vs_numpy(fa, fb):
+    """Packed 6-bit operands with one E8M0 scale per 32 K (MXFP6): the oracle
+    equals numpy's fp64 matmul of the decoded, block-scaled values."""
+    rng = np.random.default_rng(22)
+    M, N, K = 18, 22, 128
+    ca = rng.integers(0, 64, (M, K)).astype(np.uint8)
+    cb = rng.integers(0, 64, (N, K)).astype(np.uint8)
+    sa = rng.integers(124, 131, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(124, 131, (N, K // 32)).astype(np.uint8)
+    code = {"e2m3": G.E2M3, "e3m2": G.E3M2}
+    dec = {"e2m3": np.vectorize(G.e2m3_decode), "e3m2": np.vectorize(G.e3m2_decode)}
+    a_real = dec[fa](ca) * np.repeat(2.0 ** (sa.astype(np.float64) - 127), 32, axis=1)
+    b_real = dec[fb](cb) * np.repeat(2.0 ** (sb.astype(np.float64) - 127), 32, axis=1)
+    A = G.packed(_pack_fp6(ca), (M, K), (K, 1), code[fa])
+    B = G.packed(_pack_fp6(cb), (N, K), (K, 1), code[fb])
+    d, ref, absum = G.gemm(A, B, None, sa, sb, block_k=32)
+    assert np.array_equal(ref[0], a_real @ b_real.T)
+    assert np.array_equal(absum[0], np.abs(a_real) @ np.abs(b_real).T)
+    # a transposed storage of A (K rows of M packed codes) through strides
+    # (1, M): element (m, k) at offset k*M + m
+    At = G.packed(_pack_fp6(np.ascontiguousarray(ca.T).reshape(1, -1)), (M, K), (1, M), code[fa])
+    _, ref_t, _ = G.gemm(At, B, None, sa, sb, block_k=32)
+    assert np.array_equal(ref_t[0], ref[0])
