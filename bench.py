@@ -55,6 +55,8 @@ def workloads():
                        "C=0, seed 6", lambda: I.nvfp4_workload("nvfp4_8192", 8192, 8192, 8192, seed=6)),
         "mxfp4_8192": ("MXFP4 GEMM M=N=K=8192, E2M1 codes uniform, E8M0 scale per 32 K (2^[-4,0]), C=0, seed 7",
                        lambda: I.mxfp4_workload("mxfp4_8192", 8192, 8192, 8192, seed=7)),
+        "mxfp6_8192": ("MXFP6 GEMM M=N=K=8192, FP6 E2M3 codes uniform, E8M0 scale per 32 K (2^[-4,0]), C=0, "
+                       "seed 8", lambda: I.mxfp6_workload("mxfp6_8192", 8192, 8192, 8192, seed=8)),
         "bf16_8192": ("bf16 TN GEMM M=N=K=8192, A/B/C normal(0,1) bf16, seed 1",
                       lambda: I.gemm_workload("bf16_tn_8192_c", 8192, 8192, 8192, seed=1, dist="normal",
                                               with_c=True, bf16=True)),
@@ -63,7 +65,7 @@ def workloads():
 
 def algorithmic_bytes(w) -> int:
     """A, B (and scales) read once, C read once if present, D written once."""
-    es = 0.5 if w.fp4 else 1 if w.mx else 2
+    es = 0.5 if w.fp4 else 0.75 if w.fp6 else 1 if w.mx else 2
     b = int(w.batch * (w.M * w.K + w.N * w.K) * es) + w.batch * w.M * w.N * 2
     if w.c is not None:
         b += w.batch * w.M * w.N * 2
@@ -109,13 +111,16 @@ def cpu_baseline(w, target_s: float = 12.0):
     def ora(op, code=None):
         if op is None:
             return None
-        if code is not None:  # raw storage with element strides (packed E2M1, NVFP4 scales)
+        if code is not None:  # raw storage with element strides (packed E2M1 / 6-bit, NVFP4 scales)
             return OG.packed(op.storage, op.shape, op.strides, code)
         return op.view
     if w.nvfp4:
         ops = (ora(w.a, OG.E2M1), ora(w.b, OG.E2M1), ora(w.c), ora(w.sfa, OG.E4M3), ora(w.sfb, OG.E4M3))
     elif w.mxfp4:
         ops = (ora(w.a, OG.E2M1), ora(w.b, OG.E2M1), ora(w.c), ora(w.sfa), ora(w.sfb))
+    elif w.fp6:
+        code = OG.E2M3 if w.a.kind == "e2m3" else OG.E3M2
+        ops = (ora(w.a, code), ora(w.b, code), ora(w.c), ora(w.sfa), ora(w.sfb))
     else:
         ops = (ora(w.a), ora(w.b), ora(w.c), ora(w.sfa), ora(w.sfb))
 
@@ -238,7 +243,8 @@ def main():
     value = flop * args.steps / wall / 1e12
     # NVFP4 is decoded to fp16 and multiplied on the fp16 matrix cores;
     # MXFP4 runs on the scaled MFMAs at the fp4 rate
-    peak = PEAK_F4 if w.mxfp4 else PEAK_F8 if (w.mx and not w.nvfp4) else PEAK_F16
+    # MXFP6 runs at the fp4 rate too (dense fp6 and fp4: 10.1 PFLOP/s)
+    peak = PEAK_F4 if (w.mxfp4 or w.fp6) else PEAK_F8 if (w.mx and not w.nvfp4) else PEAK_F16
     # the roofline that bounds the workload: MFMA when its arithmetic
     # intensity (algorithmic FLOP per algorithmic byte) is above the ridge
     # point peak / HBM bandwidth, HBM below it
@@ -264,7 +270,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f4e2m1" if w.fp4 else "f8e4m3" if w.mx else "bf16" if w.bf16 else "f16",
+        "dtype": ("f4e2m1" if w.fp4 else ("f6" + w.a.kind[1:]) if w.fp6 else "f8e4m3" if w.mx
+                  else "bf16" if w.bf16 else "f16"),
         "data": "synthetic",
         "config": {"workload": desc, "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
                    "tile": f"{plan['tile_m']}x{plan['tile_n']}x{plan['tile_k']}",

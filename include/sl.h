@@ -73,8 +73,12 @@ typedef enum {
   SL_F8_E4M3 = 3, /* OCP MX E4M3 (bias 7, max 448, S.1111.111 = NaN) */
   SL_E8M0 = 4,    /* OCP MX E8M0 scale: 2^(b-127), 255 = NaN */
   SL_BF16 = 5,    /* bfloat16: binary32's sign and 8-bit exponent, 7 stored significand bits */
-  SL_F4_E2M1 = 6  /* OCP MX E2M1 (bias 1, max 6), packed two per byte along the unit-stride
+  SL_F4_E2M1 = 6, /* OCP MX E2M1 (bias 1, max 6), packed two per byte along the unit-stride
                      (K) axis: element offset o is byte o/2, low nibble for even o */
+  SL_F6_E2M3 = 7, /* OCP MX FP6 E2M3 (bias 1, 3 significand bits, max 7.5), packed as one
+                     little-endian bit stream along the unit-stride (K) axis: element offset
+                     o occupies bits 6o .. 6o+5, bit 0 = least significant bit of byte 0 */
+  SL_F6_E3M2 = 8  /* OCP MX FP6 E3M2 (bias 3, 2 significand bits, max 28), packed as E2M3 */
 } sl_dtype;
 
 typedef enum {
@@ -121,7 +125,9 @@ typedef struct {
                          element loader, 3 mxfp8 (4 waves, 16x16x128
                          instruction), 4 mxfp8 (8 waves, 32x32x64 instruction,
                          scales staged in LDS), 5 nvfp4 (decoded to fp16 in
-                         the loader, fp16 instruction) */
+                         the loader, fp16 instruction), 6 mxfp4 and 7 mxfp6
+                         (8 waves, 32x32x64 scaled instruction with E2M1 or
+                         6-bit data) */
   int32_t a_load;     /* 0 K-contiguous vector, 1 M-contiguous vector (register
                          transpose), 2 generic, 3 M-contiguous direct copy into
                          an M-major LDS tile read by transposing reads */
@@ -145,6 +151,12 @@ typedef struct {
  * b SL_F4_E2M1 (packed, K-contiguous, row strides multiples of 32, 16-byte
  * aligned, K % 32 == 0), sfa/sfb SL_F8_E4M3, block_k == 16, D f16.  bf16
  * is the same product in another 16-bit format; the pages name fp16 only.
+ * MXFP4 (a, b SL_F4_E2M1 with SL_E8M0 scales, block_k 32) and MXFP6 (a, b
+ * both SL_F6_E2M3 or both SL_F6_E3M2, SL_E8M0 scales, block_k 32) are the
+ * block-scaled product with 4- and 6-bit data: packed K-contiguous rows on
+ * 16-byte boundaries (row strides multiples of 32 (fp4) or 64 (fp6)
+ * elements), K % 512 == 0, and scale rows K-contiguous on 16-byte
+ * boundaries with row strides multiples of 16.
  * `stream` is a hipStream_t.  Asynchronous; see Conventions.
  */
 sl_status sl_gemm(const sl_gemm_args* args, void* stream);
@@ -170,6 +182,7 @@ int32_t sl_abi_version(void);
  *            2 v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)
  *            3 v_mfma_scale_f32_32x32x64_f8f6f4  (E4M3)
  *            4 / 5 the same two with E2M1 data (32 nibbles per lane)
+ *            6 / 7 the same two with 6-bit E2M3 or E3M2 data (32 values per lane)
  *   operand: 0 A (row = m, col = k)   1 B (row = n, col = k)
  *            2 D accumulator (row = m, col = n)
  *            3 scale (row = operand row, col = K block of 32; slot 0 only)
@@ -220,6 +233,10 @@ sl_status sl_query_fragment_addresses(int32_t variant, int32_t operand, int64_t*
  *   mode 6/7: A in E2M1 (format 4): case = (lane, nibble) of a one-hot 1.0
  *             among the lane's 32 nibbles (16 bytes, low nibble first); B in
  *             E4M3 coded as in mode 0 (6) or mode 1 (7).
+ *   mode 8/9, 10/11: A in FP6 E2M3 (format 2; modes 8, 9) or E3M2 (format
+ *             3; modes 10, 11): case = (lane, value) of a one-hot 1.0 among
+ *             the lane's 32 values, packed as one little-endian 6-bit stream
+ *             over six dwords; B coded as in mode 0 (even) or mode 1 (odd).
  * `out` (device, fp32) receives cases * 64 * regs values laid out
  * [case][lane][reg].  Returns the case count through *cases.
  */

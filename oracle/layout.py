@@ -464,6 +464,8 @@ INSTR_MAPS = {
     3: (MFMA32_F8_A, MFMA32_F8_B, MFMA32_D),
     4: (MFMA16_F4_A, MFMA16_F4_A, MFMA16_D),
     5: (MFMA32_F4_A, MFMA32_F4_A, MFMA32_D),
+    6: (MFMA16_F6_A, MFMA16_F6_A, MFMA16_D),
+    7: (MFMA32_F6_A, MFMA32_F6_A, MFMA32_D),
 }
 
 

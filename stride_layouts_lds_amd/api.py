@@ -16,8 +16,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libstride_layouts_lds.so")
 
-SL_F16, SL_F32, SL_F8_E4M3, SL_E8M0, SL_BF16, SL_F4_E2M1 = 1, 2, 3, 4, 5, 6
-K_F16, K_F16_GENERIC, K_MX, K_MX_W8, K_NVFP4, K_MXFP4 = 1, 2, 3, 4, 5, 6
+SL_F16, SL_F32, SL_F8_E4M3, SL_E8M0, SL_BF16, SL_F4_E2M1, SL_F6_E2M3, SL_F6_E3M2 = 1, 2, 3, 4, 5, 6, 7, 8
+K_F16, K_F16_GENERIC, K_MX, K_MX_W8, K_NVFP4, K_MXFP4, K_MXFP6 = 1, 2, 3, 4, 5, 6, 7
 STATUS = {0: "SL_OK", -1: "SL_ERR_NULL", -2: "SL_ERR_DTYPE", -3: "SL_ERR_SHAPE", -4: "SL_ERR_LAYOUT",
           -5: "SL_ERR_ALIGN", -6: "SL_ERR_ALIAS", -7: "SL_ERR_ARCH", -8: "SL_ERR_LAUNCH", -9: "SL_ERR_ARG",
           -10: "SL_ERR_NOMEM"}
@@ -135,8 +135,19 @@ def _torch_dtype_code(x, override: Optional[int]) -> int:
     return table[x.dtype]
 
 
+class PackedTensor:
+    """Packed sub-byte data torch has no dtype for (6-bit E2M3 / E3M2): the
+    storage bytes (a device uint8 tensor), the sl_dtype code, and the
+    (batch?, rows, cols) shape with strides in elements."""
+
+    def __init__(self, storage, dtype: int, shape, strides):
+        self.storage, self.dtype, self.shape, self.strides = storage, dtype, tuple(shape), tuple(strides)
+
+
 def tensor_desc(x, dtype: Optional[int] = None) -> sl_tensor:
-    """Descriptor of a torch tensor (None: absent operand)."""
+    """Descriptor of a torch tensor or PackedTensor (None: absent operand)."""
+    if isinstance(x, PackedTensor):
+        return desc(x.storage.data_ptr(), x.dtype, x.shape, x.strides)
     if x is None:
         t = sl_tensor()
         t.data = None

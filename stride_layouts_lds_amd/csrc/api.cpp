@@ -41,6 +41,8 @@ int elem_size(int32_t dt) {
     case SL_F8_E4M3: return 1;
     case SL_E8M0: return 1;
     case SL_F4_E2M1: return 1;  // two elements per byte: byte_range halves the span
+    case SL_F6_E2M3:
+    case SL_F6_E3M2: return 1;  // four elements per three bytes: byte_range scales the span
     default: return 0;
   }
 }
@@ -90,6 +92,8 @@ void byte_range(const View& v, int64_t batch, uintptr_t* lo, uintptr_t* hi) {
   *lo = (uintptr_t)v.t->data;
   if (v.t->dtype == SL_F4_E2M1)
     *hi = (uintptr_t)v.t->data + (uintptr_t)(last / 2 + 1);
+  else if (v.t->dtype == SL_F6_E2M3 || v.t->dtype == SL_F6_E3M2)
+    *hi = (uintptr_t)v.t->data + (uintptr_t)((6 * last + 5) / 8 + 1);
   else
     *hi = (uintptr_t)v.t->data + (uintptr_t)((last + 1) * es);
 }
@@ -176,9 +180,15 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   // E2M1 data: NVFP4 (E4M3 scales per 16) or MXFP4 (E8M0 scales per 32)
   const bool nvfp4 = fp4 && args->sfa.dtype == SL_F8_E4M3;
   const bool mxfp4 = fp4 && !nvfp4;
-  const bool mx = args->a.dtype == SL_F8_E4M3 || fp4;
+  // 6-bit data: MXFP6 (E8M0 scales per 32)
+  const bool mxfp6 = args->a.dtype == SL_F6_E2M3 || args->a.dtype == SL_F6_E3M2;
+  const bool mx = args->a.dtype == SL_F8_E4M3 || fp4 || mxfp6;
   // dtypes
-  if (nvfp4) {
+  if (mxfp6) {
+    if (args->b.dtype != args->a.dtype) return fail(SL_ERR_DTYPE, "b must have a's 6-bit format");
+    if (args->sfa.dtype != SL_E8M0 || args->sfb.dtype != SL_E8M0 || args->block_k != 32)
+      return fail(SL_ERR_DTYPE, "6-bit operands take e8m0 sfa and sfb with block_k 32");
+  } else if (nvfp4) {
     if (args->b.dtype != SL_F4_E2M1) return fail(SL_ERR_DTYPE, "b must be f4_e2m1 when a is");
     if (args->sfb.dtype != SL_F8_E4M3 || args->block_k != 16)
       return fail(SL_ERR_DTYPE, "NVFP4 takes f8_e4m3 sfa and sfb with block_k 16");
@@ -252,7 +262,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.pub.k = K;
   P.empty = batch == 0 || M == 0 || N == 0;
   if (P.empty) {
-    P.pub.kernel = nvfp4 ? sl::K_NVFP4 : mxfp4 ? sl::K_MXFP4 : mx ? sl::K_MX : sl::K_F16;
+    P.pub.kernel = nvfp4 ? sl::K_NVFP4 : mxfp4 ? sl::K_MXFP4 : mxfp6 ? sl::K_MXFP6 : mx ? sl::K_MX : sl::K_F16;
     return SL_OK;
   }
 
@@ -331,6 +341,36 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     P.pub.a_load = P.pub.b_load = sl::LOAD_NVFP4;
     P.pub.tile_k = 64;
     p.k_tiles = (int32_t)((K + 63) / 64);
+  } else if (mxfp6) {
+    // packed 6-bit rows in the 8-wave scaled-MFMA kernel: K-contiguous rows
+    // a multiple of 64 elements (48 bytes) apart on 16-byte boundaries, so
+    // every row and K-tile (128 values, 96 bytes) starts on a 16-byte chunk;
+    // 16-byte scale chunks as for MXFP4: K a multiple of 512
+    auto packed_ok = [&](const View& X) {
+      return X.cs == 1 && X.rs % 64 == 0 && (uintptr_t)X.t->data % 16 == 0 &&
+             (X.t->layout.rank == 2 || X.bs % 64 == 0);
+    };
+    auto chunk_rows = [&](const View& S) {
+      return S.cs == 1 && S.rs % 16 == 0 && (uintptr_t)S.t->data % 16 == 0 &&
+             (S.t->layout.rank == 2 || S.bs % 16 == 0);
+    };
+    if (!packed_ok(A) || !packed_ok(B) || K % 512 != 0 || !chunk_rows(SA) || !chunk_rows(SB))
+      return fail(SL_ERR_LAYOUT,
+                  "MXFP6 operands must be K-contiguous (packed) with rows a multiple of 64 elements apart, "
+                  "16-byte aligned, K %% 512 == 0, and scale rows K-contiguous, 16-byte aligned");
+    if ((M - 1) * A.rs / 4 * 3 + K / 4 * 3 >= lim || (N - 1) * B.rs / 4 * 3 + K / 4 * 3 >= lim ||
+        (M - 1) * SA.rs + kb >= lim || (N - 1) * SB.rs + kb >= lim)
+      return fail(SL_ERR_SHAPE, "operands span more than 2^31 bytes");
+    p.sfa = (const uint8_t*)args->sfa.data;
+    p.sfb = (const uint8_t*)args->sfb.data;
+    p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
+    p.sb_rs = SB.rs, p.sb_ks = SB.cs, p.sb_bs = SB.t->layout.rank == 3 ? SB.bs : 0;
+    p.flags |= (args->a.dtype == SL_F6_E2M3 ? sl::F_FP6 : sl::F_FP6_E3M2) | sl::F_SCALE16;
+    tile = sl::T256x256_W2x4;
+    P.pub.kernel = sl::K_MXFP6;
+    P.pub.a_load = P.pub.b_load = sl::LOAD_KVEC;
+    P.pub.tile_k = 128;
+    p.k_tiles = (int32_t)(K / 128);
   } else if (mxfp4) {
     // packed E2M1 in the 8-wave scaled-MFMA kernel: the NVFP4 packing rules,
     // and 16-byte scale chunks (rows of a multiple of 16 blocks, 16-byte
@@ -467,7 +507,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.pub.workgroups = total;
   P.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)M * (size_t)N * sizeof(float) : 0;
   P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * P.pub.tile_k * (mx && !nvfp4 ? 1 : 2);
-  if (P.pub.kernel == sl::K_MXFP4) P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * 128 + 2 * (ts.bm + ts.bn) * 16;
+  if (P.pub.kernel == sl::K_MXFP4 || P.pub.kernel == sl::K_MXFP6)
+    P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * 128 + 2 * (ts.bm + ts.bn) * 16;
   if (P.pub.kernel == sl::K_MX_W8)
     P.pub.lds_bytes += (p.flags & sl::F_SCALE16) ? 2 * (ts.bm + ts.bn) * 16 : ts.stages * (ts.bm + ts.bn) * 4;
   return SL_OK;
@@ -631,7 +672,7 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
 sl_status sl_query_fragment_map(int32_t instr, int32_t operand, int32_t* lane, int32_t* slot, int32_t* row,
                                 int32_t* col, int64_t capacity, int64_t* count) {
   g_msg.clear();
-  if (instr < 0 || instr > 5) return fail(SL_ERR_ARG, "instr %d", instr);
+  if (instr < 0 || instr > 7) return fail(SL_ERR_ARG, "instr %d", instr);
   if (operand < 0 || operand > 3) return fail(SL_ERR_ARG, "operand %d", operand);
   if ((operand == sl::OP_SCALE) && instr < 2) return fail(SL_ERR_ARG, "instr %d has no scale operand", instr);
   const int32_t slots = operand == sl::OP_D ? sl::instr_acc_regs(instr) : operand == sl::OP_SCALE ? 1

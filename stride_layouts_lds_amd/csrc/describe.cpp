@@ -82,6 +82,11 @@ InstrInfo instr_of(const DescribeInput& in) {
     case K_MX: return {MFMA16_F8, "v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 data, E8M0 scales)", 16, 128, 16};
     case K_MX_W8: return {MFMA32_F8, "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 data, E8M0 scales)", 32, 64, 16};
     case K_MXFP4: return {MFMA32_F4, "v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1 data, E8M0 scales)", 32, 64, 32};
+    case K_MXFP6:
+      return {MFMA32_F6,
+              std::string("v_mfma_scale_f32_32x32x64_f8f6f4 (") + ((in.flags & F_FP6) ? "E2M3" : "E3M2") +
+                  " data, E8M0 scales)",
+              32, 64, 32};
     default:
       return {MFMA16_F16, bf16 ? "v_mfma_f32_16x16x32_bf16" : "v_mfma_f32_16x16x32_f16", 16, 32, 8};
   }
@@ -94,7 +99,9 @@ Layout slot_modes(const InstrInfo& I, int64_t unit) {
     case MFMA16_F8:
     case MFMA32_F8: return T({S(16, unit), S(2, unit * (I.k / 2))});  // two 16-byte pieces, K_I/2 apart
     case MFMA16_F4:
-    case MFMA32_F4: return T({S(32, unit)});
+    case MFMA32_F4:
+    case MFMA16_F6:
+    case MFMA32_F6: return T({S(32, unit)});
     default: return T({S(8, unit)});
   }
 }
@@ -129,6 +136,7 @@ const char* kernel_name(int32_t k) {
     case K_MX_W8: return "MXFP8 GEMM, 8 waves, scales staged in LDS";
     case K_NVFP4: return "NVFP4 GEMM, dequantised to fp16 tiles";
     case K_MXFP4: return "MXFP4 GEMM, 8 waves, scales staged in LDS";
+    case K_MXFP6: return "MXFP6 GEMM, 8 waves, scales staged in LDS";
     default: return "?";
   }
 }
@@ -150,8 +158,9 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
   const int32_t F = TR / I.rows;                          // instruction repeats
   const int32_t KS = in.bk / I.k;                         // K slices per K-tile
   const bool fp4 = in.kernel == K_MXFP4;
+  const bool fp6 = in.kernel == K_MXFP6;
   const bool fp8 = in.kernel == K_MX || in.kernel == K_MX_W8;
-  const int32_t RB = fp4 ? in.bk / 2 : fp8 ? in.bk : in.bk * 2;  // LDS bytes per tile row
+  const int32_t RB = fp4 ? in.bk / 2 : fp6 ? 128 : fp8 ? in.bk : in.bk * 2;  // LDS bytes per tile row
   const std::string n(1, name);
   const Layout X = view(rows, in.K, rs, cs, batched, in.batch, bs);
 
@@ -163,8 +172,18 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
   o.note(n + " loader: " + load_name(load));
 
   const bool mmajor = load == LOAD_MNDMA;
-  const Layout tile = mmajor ? T({S(BR, 1), S(in.bk, BR)}) : T({S(BR, in.bk), S(in.bk, 1)});
-  if (mmajor) {
+  // 6-bit data is counted in bits (an element is 6 of them, a row 1024)
+  const Layout tile = mmajor ? T({S(BR, 1), S(in.bk, BR)})
+                      : fp6  ? T({S(BR, 8 * RB), S(in.bk, 6)})
+                             : T({S(BR, in.bk), S(in.bk, 1)});
+  if (fp6) {
+    const int b = log2i(RB / 16), sh = log2i(RB);
+    o.line(n + "_lds", tile,
+           fmt("bits: a K-tile's %d values are the first %d bytes of a %d-byte row (the rest zero, never "
+               "read); byte b of row r at r*%d + 16((b/16) ^ swz(r)) + b%%16, swz(r) = (r ^ (r>>4)&1) & %d: "
+               "Swizzle<%d,4,%d> then Swizzle<1,4,%d> on byte offsets",
+               in.bk, in.bk * 6 / 8, RB, RB, RB / 16 - 1, b, sh - 4, sh));
+  } else if (mmajor) {
     o.line(n + "_lds", tile,
            fmt("M-major: K-row k of %d elements; its 16-byte chunk c at c ^ 2((k&3)|((k>>3)&1)<<2)", BR));
   } else {
@@ -195,6 +214,8 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
               isA ? 'M' : 'N', TR, isA ? " % " : " / ", in.wm));
   const Layout lane0 = T({slots, S(F, I.rows), S(KS, (int64_t)BR * I.k)});
   o.stage(n + "_lane0", [&] { return la::composition(tile, lane0); }, "lane 0's values (the wave partition at lane 0)");
+  if (fp6)
+    o.note(n + " fragments: three 8-byte LDS reads per lane per instruction tile (its 32 values, 24 bytes)");
   o.stage(n + "_frag", [&] { return la::fragment_like(la::composition(tile, T({slots, S(F, I.rows)}))); },
           fmt("fragment_like of one K slice: the registers the lane reads it into (%d values x %d), reloaded "
               "per K slice",
@@ -256,7 +277,8 @@ std::string describe_plan(const DescribeInput& in) {
          fmt("(lane, slot) -> m + %d k of the %dx%d A operand (B: n for m)", I.rows, I.rows, I.k));
   operand(o, in, I, 'A', in.a_load);
   operand(o, in, I, 'B', in.b_load);
-  if (in.kernel == K_MX || in.kernel == K_MX_W8 || in.kernel == K_MXFP4 || in.kernel == K_NVFP4) {
+  if (in.kernel == K_MX || in.kernel == K_MX_W8 || in.kernel == K_MXFP4 || in.kernel == K_MXFP6 ||
+      in.kernel == K_NVFP4) {
     const int64_t kb = (in.K + in.block_k - 1) / in.block_k;
     const char* fmt_s = in.kernel == K_NVFP4 ? "E4M3" : "E8M0";
     o.line("SFA", T({R(in.M, in.sa_rs), R(kb, in.sa_cs)}), fmt("%s scale of A(m, %d j .. %d j + %d)", fmt_s,

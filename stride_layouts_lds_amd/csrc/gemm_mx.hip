@@ -16,6 +16,8 @@ namespace sl {
 namespace {
 
 constexpr int32_t kFmtE4M3 = 0;  // CBSZ/BLGP format code of FP8 E4M3
+constexpr int32_t kFmtE2M3 = 2;  // ... of FP6 E2M3
+constexpr int32_t kFmtE3M2 = 3;  // ... of FP6 E3M2
 constexpr int32_t kFmtE2M1 = 4;  // ... of FP4 E2M1
 
 template <int BM, int BN, int WM, int WN, int SHIFT>
@@ -148,13 +150,21 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_mx_kernel(const GemmParam
 // row, four 64-wide k-slices, one 16-byte fragment per lane (its 32
 // consecutive k, as the device probe of the operand map shows) and 8 scale bytes per row
 // per K-tile (a 16-byte scale chunk covers two K-tiles; SV = 4 only).
+//
+// FMT = E2M3 or E3M2 (MXFP6): 128 values per K-tile row are 96 bytes of
+// a 6-bit stream, held in the first 96 bytes of the 128-byte LDS row (the
+// loader zero-fills the rest, which is never read).  Two 64-wide k-slices;
+// a lane's 32 consecutive k (the probed operand order) are 24 bytes, read
+// as three 8-byte pieces; 4 scale bytes per row per K-tile, as for E4M3.
 template <int SHIFT, int SV, int FMT = 0>
 __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) {
   constexpr bool F4 = FMT == kFmtE2M1;
+  constexpr bool F6 = FMT == kFmtE2M3 || FMT == kFmtE3M2;
   constexpr int KS = F4 ? 4 : 2;     // 64-wide k-slices per K-tile
   constexpr int SBT = F4 ? 8 : 4;    // scale bytes per row per K-tile
   constexpr int TPC = 16 / SBT;      // K-tiles per 16-byte scale chunk
-  static_assert(!F4 || SV == 4, "E2M1 data takes 16-byte scale chunks");
+  constexpr int TB = F6 ? 96 : kRowBytes;  // bytes of a row per K-tile
+  static_assert(!(F4 || F6) || SV == 4, "E2M1 and 6-bit data take 16-byte scale chunks");
   constexpr int BM = 256, BN = 256, WM = 2, NT = 512;
   constexpr int TM = 128, TN = 64;
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -173,14 +183,15 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
-  // byte addressing: E2M1 elements are packed two per byte (the planner
-  // makes strides and K even)
-  constexpr int EPB = F4 ? 2 : 1;  // elements per byte
-  const char* A = (const char*)p.a + (tc.batch * p.a_bs + m0 * p.a_rs) / EPB;
-  const char* B = (const char*)p.b + (tc.batch * p.b_bs + n0 * p.b_rs) / EPB;
+  // byte addressing: E2M1 elements are packed two per byte, 6-bit ones
+  // four per three bytes (the planner makes strides and K multiples of
+  // the packing)
+  auto bytes = [](int64_t elems) -> int64_t { return F4 ? elems / 2 : F6 ? elems / 4 * 3 : elems; };
+  const char* A = (const char*)p.a + bytes(tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + bytes(tc.batch * p.b_bs + n0 * p.b_rs);
 
-  LoaderKVec<BM, NT, SHIFT, 1> la(A, rows_a, p.a_rs / EPB, 1, p.K / EPB, wave, lane);
-  LoaderKVec<BN, NT, SHIFT, 1> lb(B, rows_b, p.b_rs / EPB, 1, p.K / EPB, wave, lane);
+  LoaderKVec<BM, NT, SHIFT, 1, kRowBytes, TB> la(A, rows_a, bytes(p.a_rs), 1, bytes(p.K), wave, lane);
+  LoaderKVec<BN, NT, SHIFT, 1, kRowBytes, TB> lb(B, rows_b, bytes(p.b_rs), 1, bytes(p.K), wave, lane);
 
   // scale copy of this wave: operand (wave / 4), rows 64 (wave % 4) + lane
   const int32_t kb = (int32_t)((p.K + 31) / 32);  // scale bytes per row
@@ -281,7 +292,20 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       i32x8 af[FM], bf[FN];
-      if constexpr (F4) {
+      if constexpr (F6) {
+        // 24 bytes: the lane's 32 consecutive k, k = 32 (lane / 32) + v
+        const int32_t b0 = 48 * ks + 24 * (lane >> 5);
+        auto frag6 = [&](const char* tile, int32_t row) -> i32x8 {
+          const u32x2 x0 = *(const u32x2*)(tile + lds_offset(row, b0, SHIFT));
+          const u32x2 x1 = *(const u32x2*)(tile + lds_offset(row, b0 + 8, SHIFT));
+          const u32x2 x2 = *(const u32x2*)(tile + lds_offset(row, b0 + 16, SHIFT));
+          return i32x8{(int)x0[0], (int)x0[1], (int)x1[0], (int)x1[1], (int)x2[0], (int)x2[1], 0, 0};
+        };
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = frag6(cur, a_row0 + 32 * i + (lane & 31));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[j] = frag6(cur + ABYTES, b_row0 + 32 * j + (lane & 31));
+      } else if constexpr (F4) {
         // 16 bytes: the lane's 32 consecutive k (k = 32 (lane / 32) + v)
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -361,6 +385,10 @@ hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, hipStream_t s) {
       dim3 grid((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), block(512);
       if (p.flags & F_FP4)
         hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4, kFmtE2M1>), grid, block, 0, s, p);
+      else if (p.flags & F_FP6)
+        hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4, kFmtE2M3>), grid, block, 0, s, p);
+      else if (p.flags & F_FP6_E3M2)
+        hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4, kFmtE3M2>), grid, block, 0, s, p);
       else if (p.flags & F_SCALE16)
         hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4>), grid, block, 0, s, p);
       else

@@ -173,15 +173,20 @@ __device__ __forceinline__ void store_quad(const GemmParams& p, const uint16_t* 
 // i.e. 1024/RB consecutive rows, lane l landing at byte 16*l of that block.
 // The swizzle is therefore realised on the global side: the lane that
 // lands in physical chunk p of row r fetches logical chunk p ^ swz(r).
-template <int ROWS, int NT, int SHIFT, int ELEM, int RB = kRowBytes>
+// TB < RB: a K-tile is TB bytes of each row (packed 6-bit data: 128 values
+// in 96 bytes); the row's chunks past TB are filled with zeros and never
+// read, and K-tile t starts t*TB bytes into the row.
+template <int ROWS, int NT, int SHIFT, int ELEM, int RB = kRowBytes, int TB = RB>
 struct LoaderKVec {
   static constexpr int WAVES = NT / 64;
   static constexpr int CPR = RB / 16;          // chunks per row
   static constexpr int RPI = 1024 / RB;        // rows per wave instruction
   static constexpr int ITERS = ROWS * RB / (NT * 16);
-  static constexpr int KT = RB / ELEM;         // K elements per tile
+  static constexpr int KT = TB / ELEM;         // K elements per tile
   static constexpr int CE = 16 / ELEM;         // K elements per 16-B chunk
+  static constexpr int CT = TB / 16;           // chunks of a row that hold the tile
   static_assert(ITERS >= 1 && ROWS * RB % (NT * 16) == 0, "tile too small for the workgroup");
+  static_assert(TB <= RB && TB % 16 == 0, "tile bytes per row");
 
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t row_off;   // byte offset of this lane's row in instruction 0
@@ -209,9 +214,9 @@ struct LoaderKVec {
     // instruction j covers rows (j*WAVES + wave)*RPI + 0..RPI-1
     const int32_t row = row0 + j * WAVES * RPI;
     const int32_t c = (lane % CPR) ^ swz(row, SHIFT, RB);
-    const uint32_t a = row_off + (uint32_t)j * row_step + (uint32_t)(c * 16) + (uint32_t)(t * RB);
+    const uint32_t a = row_off + (uint32_t)j * row_step + (uint32_t)(c * 16) + (uint32_t)(t * TB);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16,
-                                             (t * KT + c * CE < K) ? a : kOutOfRange, 0, 0, 0);
+                                             (c < CT && t * KT + c * CE < K) ? a : kOutOfRange, 0, 0, 0);
   }
 
   __device__ __forceinline__ void issue(int32_t t, char* lds) const {

@@ -24,7 +24,8 @@ enum KernelKind : int32_t {
   K_MX = 3,           // MXFP8, 4 waves, v_mfma_scale 16x16x128, scales by byte loads
   K_MX_W8 = 4,        // MXFP8, 8 waves, v_mfma_scale 32x32x64, scales staged in LDS
   K_NVFP4 = 5,        // NVFP4 dequantised to exact fp16 tiles, fp16 MFMA (8 waves)
-  K_MXFP4 = 6         // MXFP4, 8 waves, v_mfma_scale 32x32x64 with E2M1 data
+  K_MXFP4 = 6,        // MXFP4, 8 waves, v_mfma_scale 32x32x64 with E2M1 data
+  K_MXFP6 = 7         // MXFP6, 8 waves, v_mfma_scale 32x32x64 with E2M3 or E3M2 data
 };
 
 // Tile configurations the dispatcher can choose: rows of A, rows of B,
@@ -98,6 +99,8 @@ constexpr int32_t F_C_VEC = 4;  // C rows contiguous and 8-B aligned: 4-half loa
 constexpr int32_t F_SCALE16 = 8;  // MX scale rows 16-B aligned, a multiple of 16 blocks long
 constexpr int32_t F_BF16 = 16;    // A, B, C and D are bf16 (else fp16)
 constexpr int32_t F_FP4 = 32;     // MX operands are packed E2M1 (MXFP4), else E4M3
+constexpr int32_t F_FP6 = 64;     // MX operands are packed 6-bit E2M3 (MXFP6)
+constexpr int32_t F_FP6_E3M2 = 128;  // MX operands are packed 6-bit E3M2 (MXFP6)
 
 // element type of the 16-bit GEMM kernels (template argument)
 constexpr int DT_F16 = 0;

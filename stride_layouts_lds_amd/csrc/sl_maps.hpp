@@ -38,7 +38,13 @@ namespace sl {
 
 // (the same scaled instructions with E2M1 data, 16 bytes = 32 nibbles per
 // lane: nibble v of lane l holds row l0, k = 32*l1 + v, 32 consecutive k)
-enum Instr : int32_t { MFMA16_F16 = 0, MFMA32_F16 = 1, MFMA16_F8 = 2, MFMA32_F8 = 3, MFMA16_F4 = 4, MFMA32_F4 = 5 };
+// (and with 6-bit E2M3 / E3M2 data, 32 values per lane as one little-endian
+// 6-bit stream over six dwords: value v of lane l holds row l0, k = 32*l1 +
+// v, the same order as E2M1)
+enum Instr : int32_t {
+  MFMA16_F16 = 0, MFMA32_F16 = 1, MFMA16_F8 = 2, MFMA32_F8 = 3, MFMA16_F4 = 4, MFMA32_F4 = 5,
+  MFMA16_F6 = 6, MFMA32_F6 = 7
+};
 enum Operand : int32_t { OP_A = 0, OP_B = 1, OP_D = 2, OP_SCALE = 3 };
 
 struct Coord {
@@ -46,10 +52,13 @@ struct Coord {
 };
 
 SL_HD constexpr int32_t instr_rows(int32_t instr) {
-  return (instr == MFMA16_F16 || instr == MFMA16_F8 || instr == MFMA16_F4) ? 16 : 32;
+  return (instr == MFMA16_F16 || instr == MFMA16_F8 || instr == MFMA16_F4 || instr == MFMA16_F6) ? 16 : 32;
 }
 SL_HD constexpr int32_t instr_k(int32_t instr) {
-  return instr == MFMA16_F16 ? 32 : instr == MFMA32_F16 ? 16 : (instr == MFMA16_F8 || instr == MFMA16_F4) ? 128 : 64;
+  return instr == MFMA16_F16                                                ? 32
+         : instr == MFMA32_F16                                              ? 16
+         : (instr == MFMA16_F8 || instr == MFMA16_F4 || instr == MFMA16_F6) ? 128
+                                                                            : 64;
 }
 // input slots per lane (elements) for A/B
 SL_HD constexpr int32_t instr_in_slots(int32_t instr) { return (instr == MFMA16_F16 || instr == MFMA32_F16) ? 8 : 32; }
@@ -59,11 +68,12 @@ SL_HD constexpr int32_t instr_acc_regs(int32_t instr) { return instr_rows(instr)
 // (lane, slot) -> (row, col) of operand A or B.
 //   f16:  row = l0, col = 8*l1 + v
 //   f8:   row = l0, col = 16*l1 + v%16 + (K/2)*(v/16)
-//   f4:   row = l0, col = 32*l1 + v
+//   f4, f6: row = l0, col = 32*l1 + v
 SL_HD constexpr Coord operand_map(int32_t instr, int32_t lane, int32_t slot) {
   const int32_t R = instr_rows(instr);
   if (instr_in_slots(instr) == 8) return Coord{lane % R, 8 * (lane / R) + slot};
-  if (instr == MFMA16_F4 || instr == MFMA32_F4) return Coord{lane % R, 32 * (lane / R) + slot};
+  if (instr == MFMA16_F4 || instr == MFMA32_F4 || instr == MFMA16_F6 || instr == MFMA32_F6)
+    return Coord{lane % R, 32 * (lane / R) + slot};
   return Coord{lane % R, 16 * (lane / R) + slot % 16 + (instr_k(instr) / 2) * (slot / 16)};
 }
 

@@ -20,6 +20,9 @@ from typing import Sequence, Dict, Optional, Tuple
 import numpy as np
 
 
+PACKED = ("e2m1", "e2m3", "e3m2")  # sub-byte kinds, packed along the unit-stride axis
+
+
 @dataclass
 class HostOperand:
     """A host operand: raw codes (uint16 fp16 bits, uint8 E4M3/E8M0 bytes)
@@ -28,12 +31,12 @@ class HostOperand:
     storage: np.ndarray
     shape: Tuple[int, ...]
     strides: Tuple[int, ...]
-    kind: str  # 'f16' | 'bf16' | 'e4m3' | 'e8m0' | 'e2m1' (packed, strides in elements)
+    kind: str  # 'f16' | 'bf16' | 'e4m3' | 'e8m0' | 'e2m1' | 'e2m3' | 'e3m2' (packed, strides in elements)
 
     @property
     def view(self) -> np.ndarray:
-        if self.kind == "e2m1":
-            raise TypeError("packed E2M1 codes have no numpy view (two elements per byte)")
+        if self.kind in PACKED:
+            raise TypeError("packed sub-byte codes have no numpy view")
         it = self.storage.itemsize
         return np.lib.stride_tricks.as_strided(
             self.storage, shape=self.shape, strides=tuple(s * it for s in self.strides),
@@ -76,6 +79,10 @@ class Workload:
     @property
     def mxfp4(self) -> bool:
         return self.fp4 and self.sfa is not None and self.sfa.kind == "e8m0"
+
+    @property
+    def fp6(self) -> bool:
+        return self.a.kind in ("e2m3", "e3m2")
 
     @property
     def flops(self) -> int:
@@ -209,6 +216,53 @@ def mxfp4_workload(name: str, M: int, N: int, K: int, *, seed: int, batch: Optio
     return Workload(name, M, N, K, batch or 1, a, b, c, sfa, sfb, 32, d_shape, d_strides)
 
 
+def fp6_matrix(rng, batch: Optional[int], rows: int, cols: int, kind: str, exact: bool = False) -> HostOperand:
+    """(batch?, rows, cols) 6-bit codes packed along cols as one little-endian
+    bit stream per row (code j at bits 6j .. 6j+5; 64-element rows are 48
+    bytes), rows cols apart.  Codes are uniform over all 64, or with
+    ``exact`` built from the fields sign | exponent | significand with
+    significand 0 or half its range and the three exponents just above
+    zero's (E2M3: 1 .. 3, E3M2: 3 .. 5) plus zero, the values
+    {0, +-1, +-1.5, +-2, +-3, +-4, +-6}."""
+    assert cols % 4 == 0
+    nb = batch or 1
+    if exact:
+        if kind == "e2m3":
+            fields = [(e << 3) | m for e in (1, 2, 3) for m in (0, 4)] + [0]
+        else:
+            fields = [(e << 2) | m for e in (3, 4, 5) for m in (0, 2)] + [0]
+        mag = rng.choice(np.array(fields, np.uint8), (nb * rows, cols))
+        codes = (mag | (rng.integers(0, 2, mag.shape).astype(np.uint8) << 5)).astype(np.uint8)
+    else:
+        codes = rng.integers(0, 64, (nb * rows, cols)).astype(np.uint8)
+    bits = ((codes[:, :, None] >> np.arange(6, dtype=np.uint8)) & 1).astype(np.uint8).reshape(nb * rows, 6 * cols)
+    packed = np.packbits(bits, axis=1, bitorder="little").ravel()
+    if batch is None:
+        return HostOperand(packed, (rows, cols), (cols, 1), kind)
+    return HostOperand(packed, (batch, rows, cols), (rows * cols, cols, 1), kind)
+
+
+def mxfp6_workload(name: str, M: int, N: int, K: int, *, seed: int, kind: str = "e2m3",
+                   batch: Optional[int] = None, with_c: bool = False, exact: bool = False) -> Workload:
+    """MXFP6: packed 6-bit A and B of one format (codes uniform; ``exact``:
+    see fp6_matrix), one E8M0 scale per 32 K with exponents uniform in
+    [-4, 0] ([-1, 1] with ``exact``, every partial sum of a K <= 2048
+    problem then exact in fp32), C fp16 if asked."""
+    rng = np.random.default_rng(seed)
+    a = fp6_matrix(rng, batch, M, K, kind, exact)
+    b = fp6_matrix(rng, batch, N, K, kind, exact)
+    kb = -(-K // 32)
+    lo, hi = (-1, 1) if exact else (-4, 0)
+    sfa = scales(rng, batch, M, kb, lo, hi)
+    sfb = scales(rng, batch, N, kb, lo, hi)
+    c = matrix(rng, "int4" if exact else "normal", batch, M, N, "row") if with_c else None
+    if batch is None:
+        d_shape, d_strides = (M, N), (N, 1)
+    else:
+        d_shape, d_strides = (batch, M, N), (M * N, N, 1)
+    return Workload(name, M, N, K, batch or 1, a, b, c, sfa, sfb, 32, d_shape, d_strides)
+
+
 def gemm_workload(name: str, M: int, N: int, K: int, *, seed: int, dist: str = "normal",
                   batch: Optional[int] = None, a_major: str = "row", b_major: str = "row",
                   with_c: bool = False, c_dist: Optional[str] = None, mx: bool = False,
@@ -244,6 +298,11 @@ def to_device(op: Optional[HostOperand]):
         # packed pairs: torch's float4_e2m1fn_x2 holds two elements per item
         st = torch.from_numpy(np.ascontiguousarray(op.storage)).to("cuda").view(torch.float4_e2m1fn_x2)
         return st.as_strided(op.shape[:-1] + (op.shape[-1] // 2,), tuple(x // 2 for x in op.strides[:-1]) + (1,))
+    if op.kind in ("e2m3", "e3m2"):
+        # no torch dtype: the bytes on the device, described by a PackedTensor
+        from .api import PackedTensor, SL_F6_E2M3, SL_F6_E3M2
+        st = torch.from_numpy(np.ascontiguousarray(op.storage)).to("cuda")
+        return PackedTensor(st, SL_F6_E2M3 if op.kind == "e2m3" else SL_F6_E3M2, op.shape, op.strides)
     st = torch.from_numpy(np.ascontiguousarray(op.storage))
     st = st.view({"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn,
                   "e8m0": torch.float8_e8m0fnu}[op.kind])

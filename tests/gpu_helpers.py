@@ -37,12 +37,13 @@ def d_codes(d) -> np.ndarray:
 
 
 def _ora(op, scale: bool = False, nvfp4: bool = False):
-    """An operand as the oracle takes it: a numpy view, or (packed E2M1
-    data, NVFP4's E4M3 scales) raw storage with element strides."""
+    """An operand as the oracle takes it: a numpy view, or (packed E2M1 or
+    6-bit data, NVFP4's E4M3 scales) raw storage with element strides."""
     if op is None:
         return None
-    if op.kind == "e2m1":
-        return OG.packed(op.storage, op.shape, op.strides, OG.E2M1)
+    if op.kind in ("e2m1", "e2m3", "e3m2"):
+        code = {"e2m1": OG.E2M1, "e2m3": OG.E2M3, "e3m2": OG.E3M2}[op.kind]
+        return OG.packed(op.storage, op.shape, op.strides, code)
     if scale and nvfp4:
         return OG.packed(op.storage, op.shape, op.strides, OG.E4M3)
     return op.view

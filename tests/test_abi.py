@@ -183,7 +183,7 @@ def test_mx_validation(api):
 
 # ------------------------------------------------------------------ maps
 
-@pytest.mark.parametrize("instr", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("instr", [0, 1, 2, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("operand", [0, 1, 2])
 def test_fragment_maps_equal_oracle(api, instr, operand):
     got = api.query_fragment_map(instr, operand)
@@ -369,6 +369,41 @@ def test_nvfp4_plan_and_validation(api):
                block_k=16) == "SL_ERR_LAYOUT"
     assert err(api, a, (BASE_B, E2, (N, K), (1, N)), None, d, sa, sb, block_k=16) == "SL_ERR_LAYOUT"
     assert err(api, (BASE_A, E2, (M, K), (K + 16, 1)), b, None, d, sa, sb, block_k=16) == "SL_ERR_LAYOUT"
+
+
+def test_mxfp6_plan(api):
+    """MXFP6 (packed 6-bit E2M3 or E3M2, E8M0 per 32 K) goes to the 8-wave
+    scaled-MFMA kernel with 128-wide K-tiles (96 bytes per row); rows must
+    be multiples of 64 elements apart, K a multiple of 512, both operands
+    in one 6-bit format."""
+    F6A, F6B, E8, E4 = 7, 8, 4, 3
+    M, N, K = 512, 256, 1024
+    a = (BASE_A, F6A, (M, K), (K, 1))
+    b = (BASE_B, F6A, (N, K), (K, 1))
+    sa = (BASE_C, E8, (M, K // 32), (K // 32, 1))
+    sb = (BASE_C + 0x100000, E8, (N, K // 32), (K // 32, 1))
+    d = rowmajor(BASE_D, (M, N))
+    p = plan(api, a, b, None, d, sa, sb, block_k=32)
+    assert p["kernel"] == api.K_MXFP6 and p["tile_k"] == 128 and p["threads"] == 512
+    assert p["lds_bytes"] == 2 * 512 * 128 + 2 * 512 * 16
+    p2 = plan(api, (BASE_A, F6B, (M, K), (K, 1)), (BASE_B, F6B, (N, K), (K, 1)), None, d, sa, sb, block_k=32)
+    assert p2["kernel"] == api.K_MXFP6
+    # mixed formats, E4M3 scales, block 16
+    assert err(api, a, (BASE_B, F6B, (N, K), (K, 1)), None, d, sa, sb, block_k=32) == "SL_ERR_DTYPE"
+    assert err(api, a, b, None, d, (BASE_C, E4, (M, K // 32), (K // 32, 1)),
+               (BASE_C + 0x100000, E4, (N, K // 32), (K // 32, 1)), block_k=32) == "SL_ERR_DTYPE"
+    assert err(api, a, b, None, d, sa, sb, block_k=16) == "SL_ERR_DTYPE"
+    # K % 512, a row stride not a multiple of 64, an N-contiguous B, a base off 16 bytes
+    K2 = 768
+    assert err(api, (BASE_A, F6A, (M, K2), (K2, 1)), (BASE_B, F6A, (N, K2), (K2, 1)), None, d,
+               (BASE_C, E8, (M, K2 // 32), (K2 // 32, 1)), (BASE_C + 0x100000, E8, (N, K2 // 32), (K2 // 32, 1)),
+               block_k=32) == "SL_ERR_LAYOUT"
+    assert err(api, (BASE_A, F6A, (M, K), (K + 32, 1)), b, None, d, sa, sb, block_k=32) == "SL_ERR_LAYOUT"
+    assert err(api, a, (BASE_B, F6A, (N, K), (1, N)), None, d, sa, sb, block_k=32) == "SL_ERR_LAYOUT"
+    assert err(api, (BASE_A + 8, F6A, (M, K), (K, 1)), b, None, d, sa, sb, block_k=32) == "SL_ERR_LAYOUT"
+    # an output overlapping the packed A (bytes = 3/4 of the elements)
+    assert err(api, a, b, None, (BASE_A + M * K * 3 // 4 - 2, 1, (M, N), (N, 1)), sa, sb, block_k=32) == "SL_ERR_ALIAS"
+    assert plan(api, a, b, None, (BASE_A + M * K * 3 // 4, 1, (M, N), (N, 1)), sa, sb, block_k=32)["kernel"] == 7
 
 
 def test_mxfp4_plan(api):

@@ -500,3 +500,49 @@ def test_mxfp4_exact_parity(api, case):
 
 def test_mxfp4_sampled_8192(api):
     _sampled(api, I.mxfp4_workload("mxfp4_8192", 8192, 8192, 8192, seed=7), n=1500)
+
+
+# ------------------------------------------------------------------ MXFP6
+
+MXFP6_EXACT = [
+    # M, N, K, batch, with_c, format
+    (256, 256, 512, None, False, "e2m3"),
+    (256, 256, 512, None, False, "e3m2"),
+    (300, 264, 1024, None, True, "e2m3"),
+    (136, 72, 512, 2, True, "e3m2"),
+    (520, 300, 2048, None, False, "e2m3"),
+    (520, 300, 2048, None, False, "e3m2"),
+]
+
+
+@pytest.mark.parametrize("case", MXFP6_EXACT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_c{int(c[4])}_{c[5]}")
+def test_mxfp6_exact_parity(api, case):
+    """Packed 6-bit data (values {0, +-1, +-1.5, +-2, +-3, +-4, +-6}) with
+    E8M0 scales 2^[-1,1]: every product and partial sum is exact in fp32,
+    so D must equal the oracle bit for bit."""
+    h = H()
+    M, N, K, batch, with_c, kind = case
+    w = I.mxfp6_workload("mxfp6_exact", M, N, K, seed=M + K + 2, kind=kind, batch=batch, with_c=with_c, exact=True)
+    plan = _plan(api, w)
+    h.log(f"mxfp6 exact {case} plan={plan}")
+    assert plan["kernel"] == api.K_MXFP6
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
+@pytest.mark.parametrize("kind", ["e2m3", "e3m2"])
+def test_mxfp6_bounded(api, kind):
+    """All 64 codes, scale exponents [-4, 0], ragged M and N: within the
+    acceptance bound everywhere."""
+    h = H()
+    w = I.mxfp6_workload("mxfp6_bounded", 390, 200, 1024, seed=31, kind=kind, with_c=True)
+    h.log(f"mxfp6 bounded {kind} plan={_plan(api, w)}")
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, absum = h.oracle_full(w)
+    h.assert_within_bound(d.reshape(d_ref.shape), d_ref, absum, w.name)
+
+
+def test_mxfp6_sampled_8192(api):
+    _sampled(api, I.mxfp6_workload("mxfp6_8192", 8192, 8192, 8192, seed=8), n=1500)

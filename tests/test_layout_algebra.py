@@ -372,7 +372,7 @@ def swizzled(byte, row_bytes):
     return row * row_bytes + 16 * ((b // 16) ^ s) + b % 16
 
 
-INSTRS = {1: 0, 3: 2, 4: 3, 6: 5}  # kernel family -> instruction id of its operand map
+INSTRS = {1: 0, 3: 2, 4: 3, 6: 5, 7: 7}  # kernel family -> instruction id of its operand map
 
 
 def check_instr_lines(api, st, kernel):
@@ -476,6 +476,17 @@ def test_trace_other_plans(api):
     _, st, p = trace(api, fp4(BASE_A, (n, n)), fp4(BASE_B, (n, n)), None, rowmajor(BASE_D, (n, n)),
                      rowmajor(BASE_C, (n, n // 16), 3), rowmajor(0x500000000, (n, n // 16), 3), block_k=16)
     assert p["kernel"] == api.K_NVFP4 and st["SFA"] == "(1024,64):(64,1)"
+    # MXFP6: the LDS tile in bits, the wave partition through the probed map
+    fp6 = lambda ptr, shape: (ptr, 7, shape, (shape[1], 1))
+    t6, st, p = trace(api, fp6(BASE_A, (n, n)), fp6(BASE_B, (n, n)), None, rowmajor(BASE_D, (n, n)),
+                      rowmajor(BASE_C, (n, n // 32), 4), rowmajor(0x500000000, (n, n // 32), 4))
+    assert p["kernel"] == api.K_MXFP6 and "E2M3" in t6
+    check_instr_lines(api, st, 7)
+    assert st["A_lds"] == "(256,128):(1024,6)"
+    for lane, slot, row, col in api.query_fragment_map(7, 0):
+        for i, ks in itertools.product(range(4), range(2)):
+            e = ev(st["A_wave"], lane + 64 * (slot + 32 * (i + 4 * ks)))
+            assert divmod(e, 1024) == (32 * i + row, 6 * (64 * ks + col))
     # an empty product and an invalid one
     t, _, _ = trace(api, rowmajor(BASE_A, (0, 64)), rowmajor(BASE_B, (64, 64)), None, rowmajor(BASE_D, (0, 64)))
     assert "empty" in t
