@@ -215,7 +215,8 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
   const Layout lane0 = T({slots, S(F, I.rows), S(KS, (int64_t)BR * I.k)});
   o.stage(n + "_lane0", [&] { return la::composition(tile, lane0); }, "lane 0's values (the wave partition at lane 0)");
   if (fp6)
-    o.note(n + " fragments: three 8-byte LDS reads per lane per instruction tile (its 32 values, 24 bytes)");
+    o.note(n + " fragments: one 16-byte and one 8-byte LDS read per lane per instruction tile (its 32 values, "
+                 "24 bytes)");
   o.stage(n + "_frag", [&] { return la::fragment_like(la::composition(tile, T({slots, S(F, I.rows)}))); },
           fmt("fragment_like of one K slice: the registers the lane reads it into (%d values x %d), reloaded "
               "per K slice",

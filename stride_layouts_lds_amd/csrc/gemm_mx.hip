@@ -155,7 +155,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_mx_kernel(const GemmParam
 // a 6-bit stream, held in the first 96 bytes of the 128-byte LDS row (the
 // loader zero-fills the rest, which is never read).  Two 64-wide k-slices;
 // a lane's 32 consecutive k (the probed operand order) are 24 bytes, read
-// as three 8-byte pieces; 4 scale bytes per row per K-tile, as for E4M3.
+// as one 16-byte and one 8-byte piece; 4 scale bytes per row per K-tile,
+// as for E4M3.
 template <int SHIFT, int SV, int FMT = 0>
 __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) {
   constexpr bool F4 = FMT == kFmtE2M1;
@@ -293,13 +294,21 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
     for (int ks = 0; ks < KS; ++ks) {
       i32x8 af[FM], bf[FN];
       if constexpr (F6) {
-        // 24 bytes: the lane's 32 consecutive k, k = 32 (lane / 32) + v
-        const int32_t b0 = 48 * ks + 24 * (lane >> 5);
+        // 24 bytes: the lane's 32 consecutive k, k = 32 (lane / 32) + v,
+        // i.e. bytes [24 h, 24 h + 24) of the slice's 48 (h = lane / 32):
+        // one 16-byte read of the aligned chunk inside it (bytes 0-15 or
+        // 32-47) and one 8-byte read of the rest (16-23 or 24-31).  The
+        // 8-byte read is served in passes of lanes 0-31 and 32-63, i.e. 32
+        // rows at one half of one chunk, which a 128-byte row pitch can
+        // spread over only 16 bank pairs (2-way); the 16-byte read is
+        // conflict-free under the 32-row swizzle.
+        const int32_t h = lane >> 5;
+        const int32_t bq = 48 * ks + 32 * h, bd = 48 * ks + 16 + 8 * h;
         auto frag6 = [&](const char* tile, int32_t row) -> i32x8 {
-          const u32x2 x0 = *(const u32x2*)(tile + lds_offset(row, b0, SHIFT));
-          const u32x2 x1 = *(const u32x2*)(tile + lds_offset(row, b0 + 8, SHIFT));
-          const u32x2 x2 = *(const u32x2*)(tile + lds_offset(row, b0 + 16, SHIFT));
-          return i32x8{(int)x0[0], (int)x0[1], (int)x1[0], (int)x1[1], (int)x2[0], (int)x2[1], 0, 0};
+          const u32x4 q = *(const u32x4*)(tile + lds_offset(row, bq, SHIFT));
+          const u32x2 d = *(const u32x2*)(tile + lds_offset(row, bd, SHIFT));
+          return h ? i32x8{(int)d[0], (int)d[1], (int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0}
+                   : i32x8{(int)q[0], (int)q[1], (int)q[2], (int)q[3], (int)d[0], (int)d[1], 0, 0};
         };
 #pragma unroll
         for (int i = 0; i < FM; ++i) af[i] = frag6(cur, a_row0 + 32 * i + (lane & 31));
