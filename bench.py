@@ -180,6 +180,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp16_8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--per-launch", type=int, default=30,
+                    help="launches for the per-launch warm and cold timings after the timed region (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 times), the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -237,7 +239,7 @@ def main():
     print(f"[bench] {args.steps} steps in {wall:.4f} s; {kern_ms * 1e3:.1f} us per launch (events)",
           file=sys.stderr, flush=True)
 
-    timing = per_launch_timing(api, margs, sid, stream, reps=max(10, min(args.steps, 30)))
+    timing = per_launch_timing(api, margs, sid, stream, reps=args.per_launch) if args.per_launch > 0 else None
 
     flop = w.flops
     value = flop * args.steps / wall / 1e12

@@ -460,8 +460,13 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       const int64_t auto_splits =
           std::max<int64_t>(1, std::min<int64_t>({8, 256 / std::max<int64_t>(1, t128), T_all / 4}));
       if (kk && tile < 0 && t128 < 128 && auto_splits >= 2) tile = sl::T128x128_SPLITK;
-      if (tile == sl::T128x128_SPLITK && kk) {
-        int64_t splits = env_int("SL_SPLITK", 0) > 0 ? env_int("SL_SPLITK", 0) : auto_splits;
+      const bool split_tile = tile == sl::T128x128_SPLITK || tile == sl::T256x128_SPLITK;
+      if (split_tile && kk) {
+        const sl::TileShape& st = sl::kTiles[tile];
+        const int64_t tt = batch * ((M + st.bm - 1) / st.bm) * ((N + st.bn - 1) / st.bn);
+        const int64_t tile_splits =
+            std::max<int64_t>(1, std::min<int64_t>({8, 256 / std::max<int64_t>(1, tt), T_all / 4}));
+        int64_t splits = env_int("SL_SPLITK", 0) > 0 ? env_int("SL_SPLITK", 0) : tile_splits;
         splits = std::max<int64_t>(1, std::min<int64_t>(splits, std::max<int64_t>(T_all, 1)));
         const int64_t per = (std::max<int64_t>(T_all, 1) + splits - 1) / splits;
         p.split_tiles = (int32_t)per;

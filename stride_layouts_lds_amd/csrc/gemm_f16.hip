@@ -745,6 +745,7 @@ hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32
       case T256x256_W2x4_S5: return launch_ms<256, 256, 2, 4, 5, 64, DT>(p, s);
       case T32x128_STREAM: return launch_ms<32, 128, 1, 4, 6, 128, DT>(p, s);
       case T128x128_SPLITK: return launch_ms<128, 128, 2, 4, 3, 128, DT>(p, s);
+      case T256x128_SPLITK: return launch_ms<256, 128, 4, 2, 3, 128, DT>(p, s);
       case T256x192_W2x4: return launch_cfg<256, 192, 2, 4, LOAD_KVEC, LOAD_KVEC, 0, DT>(p, s);
       case T256x256_PP:
       case T256x256_PPS4:
