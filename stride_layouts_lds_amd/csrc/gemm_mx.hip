@@ -290,9 +290,8 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
         for (int j = 0; j < FN; ++j) sb[j][d] = pick(sb4[j], d0 + d) >> half_sel;
       }
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      i32x8 af[FM], bf[FN];
+    // fragments of k-slice ks (operand maps as probed; see the format notes above)
+    auto read_slice = [&](int ks, i32x8(&af)[FM], i32x8(&bf)[FN]) {
       if constexpr (F6) {
         // 24 bytes: the lane's 32 consecutive k, k = 32 (lane / 32) + v,
         // i.e. bytes [24 h, 24 h + 24) of the slice's 48 (h = lane / 32):
@@ -329,21 +328,23 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
         }
       } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const u32x4 lo = *(const u32x4*)(cur + fragment_lds_offset(MFMA32_F8, lane, 0, a_row0 + 32 * i, ks, SHIFT));
-        const u32x4 hi = *(const u32x4*)(cur + fragment_lds_offset(MFMA32_F8, lane, 1, a_row0 + 32 * i, ks, SHIFT));
-        af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
+        for (int i = 0; i < FM; ++i) {
+          const u32x4 lo = *(const u32x4*)(cur + fragment_lds_offset(MFMA32_F8, lane, 0, a_row0 + 32 * i, ks, SHIFT));
+          const u32x4 hi = *(const u32x4*)(cur + fragment_lds_offset(MFMA32_F8, lane, 1, a_row0 + 32 * i, ks, SHIFT));
+          af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const u32x4 lo =
-            *(const u32x4*)(cur + ABYTES + fragment_lds_offset(MFMA32_F8, lane, 0, b_row0 + 32 * j, ks, SHIFT));
-        const u32x4 hi =
-            *(const u32x4*)(cur + ABYTES + fragment_lds_offset(MFMA32_F8, lane, 1, b_row0 + 32 * j, ks, SHIFT));
-        bf[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        for (int j = 0; j < FN; ++j) {
+          const u32x4 lo =
+              *(const u32x4*)(cur + ABYTES + fragment_lds_offset(MFMA32_F8, lane, 0, b_row0 + 32 * j, ks, SHIFT));
+          const u32x4 hi =
+              *(const u32x4*)(cur + ABYTES + fragment_lds_offset(MFMA32_F8, lane, 1, b_row0 + 32 * j, ks, SHIFT));
+          bf[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
       }
-      }
-      // instruction A = our B tile (its scales: sb), instruction B = our A tile
+    };
+    // instruction A = our B tile (its scales: sb), instruction B = our A tile
+    auto mfma_slice = [&](int ks, const i32x8(&af)[FM], const i32x8(&bf)[FN]) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -351,6 +352,12 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               bf[j], af[i], acc[i][j], FMT, FMT, 0, (int)((sb[j][ks >> 1] >> (16 * (ks & 1))) & 0xFFu), 0,
               (int)((sa[i][ks >> 1] >> (16 * (ks & 1))) & 0xFFu));
+    };
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      i32x8 af[FM], bf[FN];
+      read_slice(ks, af, bf);
+      mfma_slice(ks, af, bf);
     }
     wait_vmem();
     __syncthreads();
