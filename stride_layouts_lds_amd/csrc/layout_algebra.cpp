@@ -8,6 +8,20 @@ namespace sl {
 namespace la {
 namespace {
 
+// Checked arithmetic: results stay below 2^62, beyond which an operation is
+// reported as undefined rather than wrapping.
+constexpr int64_t kLimit = int64_t(1) << 62;
+int64_t mul(int64_t a, int64_t b) {
+  int64_t r;
+  if (__builtin_mul_overflow(a, b, &r) || r > kLimit || r < -kLimit) throw Error{"integer overflow"};
+  return r;
+}
+int64_t add(int64_t a, int64_t b) {
+  int64_t r;
+  if (__builtin_add_overflow(a, b, &r) || r > kLimit || r < -kLimit) throw Error{"integer overflow"};
+  return r;
+}
+
 // ------------------------------------------------------------- parsing
 
 struct Cursor {
@@ -123,6 +137,9 @@ Layout from_modes(const std::vector<Mode>& m) {
 // the stride d out of A's leading shapes, then keep A's modes until their
 // sizes make up s.
 Layout compose_mode(const std::vector<Mode>& a, int64_t s, int64_t d, bool stat) {
+  for (const Mode& m : a)
+    if (m.shape == 0) throw Error{"composition: the layout has an empty mode"};
+  if (s == 0) throw Error{"composition: an empty mode"};
   if (s == 1) return Layout::mode(1, 0, stat);
   if (d == 0) return Layout::mode(s, 0, stat);
   std::vector<Mode> out;
@@ -132,14 +149,14 @@ Layout compose_mode(const std::vector<Mode>& a, int64_t s, int64_t d, bool stat)
     const bool last = i + 1 == a.size();
     if (r > 1) {
       if (last) {
-        D *= r;
+        D = mul(D, r);
         r = 1;
       } else if (r % S == 0) {
         r /= S;
         continue;
       } else if (S % r == 0) {
         S /= r;
-        D *= r;
+        D = mul(D, r);
         r = 1;
       } else {
         throw Error{"composition: stride " + std::to_string(d) + " does not divide the layout's shape"};
@@ -189,7 +206,7 @@ std::vector<int64_t> compact_in_order(const std::vector<Mode>& m, const std::vec
   for (size_t i : idx) {
     if (m[i].shape == 1) continue;
     strides[i] = cur;
-    cur *= m[i].shape;
+    cur = mul(cur, m[i].shape);
   }
   return strides;
 }
@@ -238,7 +255,7 @@ std::vector<Mode> flatten(const Layout& l) {
 
 int64_t size(const Layout& l) {
   int64_t n = 1;
-  for (const Mode& m : flatten(l)) n *= m.shape;
+  for (const Mode& m : flatten(l)) n = mul(n, m.shape);
   return n;
 }
 
@@ -246,16 +263,16 @@ int64_t cosize(const Layout& l) {
   int64_t hi = 0;
   for (const Mode& m : flatten(l)) {
     if (m.shape == 0) return 0;
-    hi += (m.shape - 1) * m.stride;
+    hi = add(hi, mul(m.shape - 1, m.stride));
   }
-  return hi + 1;
+  return add(hi, 1);
 }
 
 int64_t eval(const Layout& l, int64_t index) {
   int64_t off = 0;
   for (const Mode& m : flatten(l)) {
     if (m.shape == 0) return 0;
-    off += (index % m.shape) * m.stride;
+    off = add(off, mul(index % m.shape, m.stride));
     index /= m.shape;
   }
   return off;
@@ -272,8 +289,8 @@ Layout coalesce(const Layout& l) {
   std::vector<Mode> out;
   for (const Mode& m : flatten(l)) {
     if (m.shape == 1) continue;
-    if (!out.empty() && out.back().shape * out.back().stride == m.stride) {
-      out.back().shape *= m.shape;
+    if (!out.empty() && mul(out.back().shape, out.back().stride) == m.stride) {
+      out.back().shape = mul(out.back().shape, m.shape);
       out.back().stat = out.back().stat && m.stat;
       continue;
     }
@@ -297,9 +314,9 @@ Layout complement(const Layout& a, int64_t cosize_target) {
   for (const Mode& x : m) {
     if (x.stride % cur != 0) throw Error{"complement: strides are not nested multiples"};
     if (x.stride / cur > 1) out.push_back({x.stride / cur, cur, stat});
-    cur = x.shape * x.stride;
+    cur = mul(x.shape, x.stride);
   }
-  const int64_t rest = (cosize_target + cur - 1) / cur;
+  const int64_t rest = cosize_target / cur + (cosize_target % cur != 0);
   if (rest > 1) out.push_back({rest, cur, stat});
   return coalesce(from_modes(out));
 }
@@ -314,7 +331,7 @@ Layout right_inverse(const Layout& a) {
   int64_t dom = 1;
   for (const Mode& x : m) {
     if (x.shape > 1 && x.stride > 0) it.push_back({x.shape, x.stride, dom});
-    dom *= x.shape;
+    dom = mul(dom, x.shape);
   }
   std::stable_sort(it.begin(), it.end(), [](const Item& x, const Item& y) { return x.stride < y.stride; });
   std::vector<Mode> out;
@@ -322,7 +339,7 @@ Layout right_inverse(const Layout& a) {
   for (const Item& x : it) {
     if (x.stride != expect) break;  // the inverse covers the contiguous prefix of the image
     out.push_back({x.shape, x.dom, stat});
-    expect *= x.shape;
+    expect = mul(expect, x.shape);
   }
   return coalesce(from_modes(out));
 }
@@ -373,7 +390,7 @@ Layout make_ordered(const Layout& shape, const Layout& order) {
 }
 
 Layout logical_product(const Layout& block, const Layout& rest) {
-  const Layout comp = complement(block, size(block) * cosize(rest));
+  const Layout comp = complement(block, mul(size(block), cosize(rest)));
   return Layout::tuple({block, composition(comp, rest)});
 }
 

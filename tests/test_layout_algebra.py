@@ -344,6 +344,18 @@ def test_layout_op_errors(api):
     assert need.value == len("(4,(2,2)):(1,(4,8))") + 1
     assert api.layout_op("parse", "( 4 , (2,2) ) : ( 1 , (4,8) )") == "(4,(2,2)):(1,(4,8))"
     assert api.layout_op("size", "(4,(2,3))") == "24" and api.layout_op("cosize", "(4,2):(2,1)") == "8"
+    # empty modes and sizes past 2^62 are errors, never a crash or a wrapped value
+    assert status(lambda: api.layout_op("composition", "(0,4):(1,0)", "2:1")) == "SL_ERR_LAYOUT"
+    assert status(lambda: api.layout_op("composition", "(4,4):(1,4)", "(0,2):(1,4)")) == "SL_ERR_LAYOUT"
+    assert status(lambda: api.layout_op("zipped_divide", "(0,8):(8,1)", "(4,4):(1,1)")) == "SL_ERR_LAYOUT"
+    assert api.layout_op("size", "(0,8)") == "0" and api.layout_op("cosize", "(0,8):(8,1)") == "0"
+    big = "(1000000000000,1000000000000):(1,1000000000000)"
+    assert status(lambda: api.layout_op("size", big)) == "SL_ERR_LAYOUT"
+    assert status(lambda: api.layout_op("cosize", big)) == "SL_ERR_LAYOUT"
+    assert status(lambda: api.layout_op("compact_left", "(1000000000000,1000000000000)")) == "SL_ERR_LAYOUT"
+    assert status(lambda: api.layout_op("parse", "(1" + "0" * 19 + "):(1)")) == "SL_ERR_LAYOUT"
+    assert status(lambda: api.layout_op("parse", "(" * 40 + "1" + ")" * 40 + ":" + "(" * 40 + "1" + ")" * 40)) \
+        == "SL_ERR_LAYOUT"
 
 
 # ------------------------------------------------------------ the plan trace
