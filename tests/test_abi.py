@@ -406,6 +406,32 @@ def test_mxfp6_plan(api):
     assert plan(api, a, b, None, (BASE_A + M * K * 3 // 4, 1, (M, N), (N, 1)), sa, sb, block_k=32)["kernel"] == 7
 
 
+def test_size_limits(api):
+    """Dimensions past 2^31 - 1 and packed operands spanning 2^31 bytes or
+    more are SL_ERR_SHAPE before any HIP call; a 16-bit operand has no
+    whole-span limit (its tiles are addressed from their own bases), only a
+    256-row tile must fit 2^31 bytes for the vector loaders."""
+    big = 1 << 31
+    assert err(api, rowmajor(BASE_A, (big, 64)), rowmajor(BASE_B, (64, 64)), None,
+               (BASE_D, 1, (big, 64), (64, 1))) == "SL_ERR_SHAPE"
+    assert err(api, rowmajor(BASE_A, (64, big)), rowmajor(BASE_B, (64, big)), None,
+               rowmajor(BASE_D, (64, 64))) == "SL_ERR_SHAPE"
+    # a 4 GiB fp16 operand plans with the vector loader
+    p = plan(api, rowmajor(BASE_A, (131072, 16384)), rowmajor(BASE_B, (64, 16384)), None,
+             rowmajor(BASE_D, (131072, 64)))
+    assert p["a_load"] == 0
+    # a row stride that puts a 256-row tile past 2^31 bytes takes the element loader
+    p = plan(api, (BASE_A, 1, (512, 64), (1 << 23, 1)), rowmajor(BASE_B, (256, 64)), None,
+             rowmajor(BASE_D, (512, 256)))
+    assert p["a_load"] == 2
+    # packed E2M1: the operand's span must stay below 2^31 bytes
+    E2, E8 = 6, 4
+    M, K = 1 << 18, 16384  # 2 GiB of packed data
+    assert err(api, (BASE_A, E2, (M, K), (K, 1)), (BASE_B, E2, (256, K), (K, 1)), None,
+               rowmajor(0x1000000000, (M, 256)), (BASE_C, E8, (M, K // 32), (K // 32, 1)),
+               (0x2000000000, E8, (256, K // 32), (K // 32, 1)), block_k=32) == "SL_ERR_SHAPE"
+
+
 def test_mxfp4_plan(api):
     """MXFP4 (packed E2M1, E8M0 per 32 K) goes to the 8-wave scaled-MFMA
     kernel with 256-wide K-tiles; K must be a multiple of 512."""
