@@ -130,7 +130,10 @@ typedef struct {
                          6-bit data) */
   int32_t a_load;     /* 0 K-contiguous vector, 1 M-contiguous vector (register
                          transpose), 2 generic, 3 M-contiguous direct copy into
-                         an M-major LDS tile read by transposing reads */
+                         an M-major LDS tile read by transposing reads, 4 NVFP4
+                         decoding loader, 5 the same fetching two K-tiles per
+                         row at once (scale rows K-contiguous on 8-byte
+                         boundaries) */
   int32_t b_load;     /* same, for B */
   int32_t tile_m, tile_n, tile_k;
   int32_t threads;    /* per workgroup */

@@ -336,9 +336,16 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     p.sfb = (const uint8_t*)args->sfb.data;
     p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
     p.sb_rs = SB.rs, p.sb_ks = SB.cs, p.sb_bs = SB.t->layout.rank == 3 ? SB.bs : 0;
+    // one 8-byte load for a row's scales of two K-tiles when the scale rows
+    // are K-contiguous on 8-byte boundaries
+    auto pair_rows = [&](const View& S) {
+      return S.cs == 1 && S.rs % 8 == 0 && (uintptr_t)S.t->data % 8 == 0 &&
+             (S.t->layout.rank == 2 || S.bs % 8 == 0);
+    };
+    const bool pairs = pair_rows(SA) && pair_rows(SB) && env_int("SL_NV_PAIRS", 1);
     tile = sl::T256x256_W2x4;  // the dequantising loader exists for the 8-wave kernel
     P.pub.kernel = sl::K_NVFP4;
-    P.pub.a_load = P.pub.b_load = sl::LOAD_NVFP4;
+    P.pub.a_load = P.pub.b_load = pairs ? sl::LOAD_NVFP4_PAIRS : sl::LOAD_NVFP4;
     P.pub.tile_k = 64;
     p.k_tiles = (int32_t)((K + 63) / 64);
   } else if (mxfp6) {
@@ -652,7 +659,7 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (P.pub.kernel == sl::K_NVFP4) {
-    e = sl::launch_gemm_f16(P.p, P.tile, sl::LOAD_NVFP4, sl::LOAD_NVFP4, st);
+    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
   } else if (P.mx) {
     e = sl::launch_gemm_mx(P.p, P.tile, st);
   } else if (P.ws_bytes) {

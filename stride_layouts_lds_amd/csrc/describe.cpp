@@ -124,6 +124,9 @@ const char* load_name(int32_t l) {
     case LOAD_GENERIC: return "element loads (any strides)";
     case LOAD_MNDMA: return "M-contiguous 16-byte direct HBM->LDS loads into an M-major tile";
     case LOAD_NVFP4: return "packed E2M1 16-byte loads, decoded and scaled to fp16 in registers";
+    case LOAD_NVFP4_PAIRS:
+      return "packed E2M1 16-byte loads of two K-tiles at once, 8-byte scale loads, decoded and scaled to fp16 in "
+             "registers";
     default: return "?";
   }
 }

@@ -758,12 +758,14 @@ hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32
       default: return launch_tile<LOAD_KVEC, LOAD_KVEC, DT>(p, tile, s);
     }
   }
-  if (a_load == LOAD_NVFP4 || b_load == LOAD_NVFP4) {
-    // NVFP4: both operands through the dequantising loader, 8-wave kernel
+  if (a_load == LOAD_NVFP4 || b_load == LOAD_NVFP4 || a_load == LOAD_NVFP4_PAIRS || b_load == LOAD_NVFP4_PAIRS) {
+    // the dequantising loaders exist for the 8-wave 256x256 fp16 kernel
     if constexpr (DT != DT_F16) return hipErrorInvalidValue;
-    if (tile != T256x256_W2x4 || a_load != LOAD_NVFP4 || b_load != LOAD_NVFP4) return hipErrorInvalidValue;
+    if (tile != T256x256_W2x4 || a_load != b_load) return hipErrorInvalidValue;
+    if (a_load == LOAD_NVFP4_PAIRS) return launch_cfg<256, 256, 2, 4, LOAD_NVFP4_PAIRS, LOAD_NVFP4_PAIRS, 0, DT_F16>(p, s);
     return launch_cfg<256, 256, 2, 4, LOAD_NVFP4, LOAD_NVFP4, 0, DT_F16>(p, s);
   }
+
   if (a_load == LOAD_MNDMA || b_load == LOAD_MNDMA) {
     // the M-major direct-copy tiles exist for the 8-wave 256x256 kernel
     if (tile != T256x256_W2x4) return hipErrorInvalidValue;

@@ -424,25 +424,35 @@ __device__ __forceinline__ u32x4 e2m1x8_to_half8(uint32_t w) {
                __builtin_amdgcn_perm(ho, he, 0x060C020Cu), __builtin_amdgcn_perm(ho, he, 0x070C030Cu)};
 }
 
-template <int ROWS, int NT, int SHIFT>
+template <int ROWS, int NT, int SHIFT, bool PAIRS>
 struct LoaderNVFP4 {
   static constexpr int PER = ROWS * 2 / NT;  // (row, half) units per thread
   static_assert(PER >= 1 && ROWS * 2 % NT == 0, "tile too small for the workgroup");
   typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
+  // PAIRS: K-tiles are fetched in pairs.  A unit's two 16-byte pieces (its
+  // half of K-tiles 2p and 2p+1) lie in one 128-byte line and are requested
+  // back to back, and one 8-byte load brings the row's 8 scales of the pair
+  // (scale rows of unit stride on 8-byte boundaries).  issue(t) for even t
+  // loads the pair, for odd t nothing; commit() decodes the tile of the last
+  // issue.  Without PAIRS: one piece and two scale bytes per unit per tile.
+  static constexpr int NB = PAIRS ? 2 : 1;  // tiles held per unit
   __amdgpu_buffer_rsrc_t rd, rsf;
   int32_t K;
   uint32_t sks;
+  int32_t cur;  // tile of the last issue
   uint32_t d_off[PER], s_off[PER];
   int32_t row[PER], half[PER];
   bool ok[PER];
-  u32x4 data[PER];
-  uint32_t sc[PER][2];
+  u32x4 data[PER][NB];
+  u32x2 sc8[PER];        // PAIRS: scale bytes of blocks 4t .. 4t + 7
+  uint32_t sc[PER][2];   // else: the unit's two scale bytes of tile t
 
   __device__ __forceinline__ LoaderNVFP4(const uint8_t* base, const uint8_t* sbase, int32_t rows_valid,
                                          int64_t rs, int64_t srs, int64_t sks_, int64_t K_) {
     K = (int32_t)K_;
     sks = (uint32_t)sks_;
+    cur = 0;
     rd = make_rsrc(base, rows_valid > 0 ? (uint32_t)((rows_valid - 1) * (rs / 2) + K_ / 2) : 0u);
     rsf = make_rsrc(sbase, rows_valid > 0 ? (uint32_t)((rows_valid - 1) * srs + (K_ / 16 - 1) * sks_ + 1) : 0u);
 #pragma unroll
@@ -452,18 +462,30 @@ struct LoaderNVFP4 {
       half[u] = id & 1;
       ok[u] = row[u] < rows_valid;
       d_off[u] = (uint32_t)(row[u] * (rs / 2) + half[u] * 16);
-      s_off[u] = (uint32_t)(row[u] * srs + half[u] * 2 * sks_);
+      s_off[u] = (uint32_t)(row[u] * srs + (PAIRS ? 0 : half[u] * 2 * sks_));
     }
   }
 
   __device__ __forceinline__ void issue(int32_t t, char*) {
+    cur = t;
+    if (PAIRS && (t & 1)) return;  // fetched with the pair's first tile
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const int32_t tq = t + q;
+        const bool v = ok[u] && tq * 64 + half[u] * 32 < K;
+        data[u][q] = __builtin_amdgcn_raw_buffer_load_b128(rd, v ? d_off[u] + (uint32_t)(tq * 32) : kOutOfRange, 0, 0);
+      }
       const bool v = ok[u] && t * 64 + half[u] * 32 < K;
-      data[u] = __builtin_amdgcn_raw_buffer_load_b128(rd, v ? d_off[u] + (uint32_t)(t * 32) : kOutOfRange, 0, 0);
-      const uint32_t s0 = s_off[u] + (uint32_t)(4 * t) * sks;
-      sc[u][0] = __builtin_amdgcn_raw_buffer_load_b8(rsf, v ? s0 : kOutOfRange, 0, 0);
-      sc[u][1] = __builtin_amdgcn_raw_buffer_load_b8(rsf, v ? s0 + sks : kOutOfRange, 0, 0);
+      if constexpr (PAIRS) {
+        sc8[u] = __builtin_amdgcn_raw_buffer_load_b64(rsf, ok[u] && t * 64 < K ? s_off[u] + (uint32_t)(4 * t)
+                                                                               : kOutOfRange, 0, 0);
+      } else {
+        const uint32_t s0 = s_off[u] + (uint32_t)(4 * t) * sks;
+        sc[u][0] = __builtin_amdgcn_raw_buffer_load_b8(rsf, v ? s0 : kOutOfRange, 0, 0);
+        sc[u][1] = __builtin_amdgcn_raw_buffer_load_b8(rsf, v ? s0 + sks : kOutOfRange, 0, 0);
+      }
     }
   }
 
@@ -474,12 +496,25 @@ struct LoaderNVFP4 {
   // (the four products are built as separate values: an in-place loop over
   // the vector's elements was miscompiled into reuse of element 0)
   __device__ __forceinline__ void commit(char* lds) const {
+    const int32_t q = PAIRS ? (cur & 1) : 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
+      // the unit's two scales of tile `cur`: blocks 4 cur + 2 half and + 1,
+      // with PAIRS bytes 4 q + 2 half (+1) of the pair's 8
+      uint32_t s2[2];
+      if constexpr (PAIRS) {
+        const uint32_t w = q ? sc8[u][1] : sc8[u][0];
+        s2[0] = (w >> (16 * half[u])) & 0xFF;
+        s2[1] = (w >> (16 * half[u] + 8)) & 0xFF;
+      } else {
+        s2[0] = sc[u][0];
+        s2[1] = sc[u][1];
+      }
+      const u32x4 d = q ? data[u][NB - 1] : data[u][0];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {  // 8 elements: K = 32 half + 8 j ..
-        const _Float16 s = e4m3_to_half(sc[u][j >> 1]);
-        const u32x4 h = e2m1x8_to_half8(data[u][j]);
+        const _Float16 s = e4m3_to_half(s2[j >> 1]);
+        const u32x4 h = e2m1x8_to_half8(d[j]);
         *(u32x4*)(lds + lds_offset(row[u], (half[u] * 32 + 8 * j) * 2, SHIFT)) =
             u32x4{mul_h2(h[0], s), mul_h2(h[1], s), mul_h2(h[2], s), mul_h2(h[3], s)};
       }
@@ -507,7 +542,11 @@ struct LoaderSel<LOAD_MNDMA, ROWS, NT, SHIFT> {
 };
 template <int ROWS, int NT, int SHIFT>
 struct LoaderSel<LOAD_NVFP4, ROWS, NT, SHIFT> {
-  using type = LoaderNVFP4<ROWS, NT, SHIFT>;
+  using type = LoaderNVFP4<ROWS, NT, SHIFT, false>;
+};
+template <int ROWS, int NT, int SHIFT>
+struct LoaderSel<LOAD_NVFP4_PAIRS, ROWS, NT, SHIFT> {
+  using type = LoaderNVFP4<ROWS, NT, SHIFT, true>;
 };
 
 // The loader of operand `op` (0: A rows from m0, 1: B rows from n0) of
@@ -517,10 +556,11 @@ __device__ __forceinline__ typename LoaderSel<KIND, ROWS, NT, SHIFT>::type make_
     const GemmParams& p, int op, int32_t batch, int64_t row0, int32_t rows_valid, int32_t wave, int32_t lane) {
   const int64_t bs = op ? p.b_bs : p.a_bs, rs = op ? p.b_rs : p.a_rs, ks = op ? p.b_ks : p.a_ks;
   const uint8_t* x = (const uint8_t*)(op ? p.b : p.a);
-  if constexpr (KIND == LOAD_NVFP4) {
+  if constexpr (KIND == LOAD_NVFP4 || KIND == LOAD_NVFP4_PAIRS) {
     const int64_t sbs = op ? p.sb_bs : p.sa_bs, srs = op ? p.sb_rs : p.sa_rs, sks = op ? p.sb_ks : p.sa_ks;
     const uint8_t* sf = (op ? p.sfb : p.sfa) + batch * sbs + row0 * srs;
-    return LoaderNVFP4<ROWS, NT, SHIFT>(x + (batch * bs + row0 * rs) / 2, sf, rows_valid, rs, srs, sks, p.K);
+    return typename LoaderSel<KIND, ROWS, NT, SHIFT>::type(x + (batch * bs + row0 * rs) / 2, sf, rows_valid, rs,
+                                                           srs, sks, p.K);
   } else {
     return typename LoaderSel<KIND, ROWS, NT, SHIFT>::type(x + 2 * (batch * bs + row0 * rs), rows_valid, rs, ks, p.K,
                                                            wave, lane);

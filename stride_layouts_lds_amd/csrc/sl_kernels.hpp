@@ -13,6 +13,7 @@ enum LoadKind : int32_t {
   LOAD_GENERIC = 2, // any strides: element loads
   LOAD_MNDMA = 3,   // M (or N) contiguous, 16-B aligned: direct HBM->LDS into an M-major tile,
                     // fragments by transposing LDS reads (8-wave 256x256 kernel)
+  LOAD_NVFP4_PAIRS = 5,  // the same, fetching two K-tiles per row at once (8-byte scale loads)
   LOAD_NVFP4 = 4    // packed E2M1 with E4M3 scales per 16 K: decoded and scaled in registers,
                     // written to the K-major fp16 tile (8-wave 256x256 kernel)
 };

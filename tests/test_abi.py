@@ -354,8 +354,14 @@ def test_nvfp4_plan_and_validation(api):
     sb = (BASE_C + 0x100000, E4, (N, K // 16), (K // 16, 1))
     d = rowmajor(BASE_D, (M, N))
     p = plan(api, a, b, None, d, sa, sb, block_k=16)
-    assert p["kernel"] == api.K_NVFP4 and (p["a_load"], p["b_load"]) == (4, 4)
+    # scale rows K-contiguous on 8-byte boundaries: the paired loader (5)
+    assert p["kernel"] == api.K_NVFP4 and (p["a_load"], p["b_load"]) == (5, 5)
     assert p["tile_m"] == p["tile_n"] == 256 and p["tile_k"] == 64 and p["lds_bytes"] == 2 * 512 * 64 * 2
+    # scale rows padded to an odd length, or column-major scales: the per-tile loader (4)
+    sa_odd = (BASE_C, E4, (M, K // 16), (K // 16 + 1, 1))
+    assert plan(api, a, b, None, d, sa_odd, sb, block_k=16)["a_load"] == 4
+    sa_cm = (BASE_C, E4, (M, K // 16), (1, M))
+    assert plan(api, a, b, None, d, sa_cm, sb, block_k=16)["a_load"] == 4
     s8a = (BASE_C, E8, (M, K // 32), (K // 32, 1))
     s8b = (BASE_C + 0x100000, E8, (N, K // 32), (K // 32, 1))
     assert plan(api, a, b, None, d, s8a, s8b, block_k=32)["kernel"] == api.K_MXFP4
