@@ -481,8 +481,11 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       }
       // the ping-pong variants (tiles 9-14) are fp16 only
       const bool pingpong = tile >= sl::T256x256_PP && tile <= sl::T256x256_PPG;
-      if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T256x256_W2x4_P) || (bf16 && pingpong)) {
-        const int32_t big = sl::T256x256_W2x4;
+      // the 4-wave ring kernel needs K-contiguous operands and a K-tile
+      const bool ring_ok = kk && K > 0;
+      if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T256x256_W2x4_P) || (bf16 && pingpong) ||
+          (tile == sl::T256x256_W4R && !ring_ok)) {
+        const int32_t big = ring_ok ? sl::T256x256_W4R : sl::T256x256_W2x4;
         tile = big;
         double best = 1e300;
         for (int t : {big, (int32_t)sl::T256x192_W2x4, (int32_t)sl::T256x128_W2x2, (int32_t)sl::T128x256_W2x2,
@@ -523,6 +526,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * 128 + 2 * (ts.bm + ts.bn) * 16;
   if (P.pub.kernel == sl::K_MX_W8)
     P.pub.lds_bytes += (p.flags & sl::F_SCALE16) ? 2 * (ts.bm + ts.bn) * 16 : ts.stages * (ts.bm + ts.bn) * 4;
+  if (tile == sl::T256x256_W4R) P.pub.lds_bytes = 5 * ts.bm * P.pub.tile_k * 2;  // five operand K-tiles
   return SL_OK;
 }
 
@@ -861,6 +865,7 @@ sl_status sl_describe_plan(const sl_gemm_args* args, char* out, int64_t capacity
   in.b_load = P.pub.b_load;
   in.bm = ts.bm, in.bn = ts.bn, in.bk = P.pub.tile_k;
   in.wm = ts.wm, in.wn = ts.wn, in.stages = ts.stages;
+  in.ring = P.tile == sl::T256x256_W4R;
   in.splits = p.splits, in.split_tiles = p.split_tiles, in.group_m = p.group_m;
   in.tiles_m = p.tiles_m, in.tiles_n = p.tiles_n;
   in.workgroups = P.pub.workgroups, in.batch = P.pub.batch, in.M = p.M, in.N = p.N, in.K = p.K;

@@ -271,9 +271,16 @@ std::string describe_plan(const DescribeInput& in) {
   Out o;
   const InstrInfo I = instr_of(in);
   const int32_t NT = in.wm * in.wn * 64;
-  o.note(fmt("kernel %d: %s; tile %dx%dx%d, %d waves (%d x %d), wave tile %dx%d, %d LDS stages, %d LDS bytes", in.kernel,
-             kernel_name(in.kernel), in.bm, in.bn, in.bk, NT / 64, in.wm, in.wn, in.bm / in.wm, in.bn / in.wn,
-             in.stages, in.lds_bytes));
+  if (in.ring)
+    o.note(fmt("kernel %d: %s; tile %dx%dx%d, %d waves (%d x %d), wave tile %dx%d with accumulators in AGPRs; LDS "
+               "a ring of five operand K-tiles (operand tile q = A of K-tile q/2 for even q, B for odd q, in slot "
+               "q %% 5), %d LDS bytes",
+               in.kernel, kernel_name(in.kernel), in.bm, in.bn, in.bk, NT / 64, in.wm, in.wn, in.bm / in.wm,
+               in.bn / in.wn, in.lds_bytes));
+  else
+    o.note(fmt("kernel %d: %s; tile %dx%dx%d, %d waves (%d x %d), wave tile %dx%d, %d LDS stages, %d LDS bytes",
+               in.kernel, kernel_name(in.kernel), in.bm, in.bn, in.bk, NT / 64, in.wm, in.wn, in.bm / in.wm,
+               in.bn / in.wn, in.stages, in.lds_bytes));
   o.note(fmt("M=%lld N=%lld K=%lld batch=%lld: %lld workgroups of %d threads, split_k %d", (long long)in.M,
              (long long)in.N, (long long)in.K, (long long)in.batch, (long long)in.workgroups, NT, in.splits));
   o.note("instruction: " + I.name + " (issued with the B tile as its first operand)");

@@ -21,6 +21,7 @@ struct DescribeInput {
   int32_t flags;    // GemmParams flags
   int32_t block_k;  // scale block (MX 32, NVFP4 16)
   int32_t lds_bytes;
+  bool ring;  // LDS as a ring of five operand K-tiles (the 4-wave 256x256 kernel)
 };
 
 // One line per stage: "name: layout  # note" (the layout parses back with

@@ -24,12 +24,32 @@ template <int FM, int FN, int DT = DT_F16>
 __device__ __forceinline__ void epilogue(const floatx4 (&acc)[FM][FN], const GemmParams& p, int32_t batch,
                                          int64_t m_base, int64_t n_base, int32_t lane) {
   uint16_t* D = (uint16_t*)p.d + batch * p.d_bs;
-  const uint16_t* C = (p.flags & F_HAS_C) ? (const uint16_t*)p.c + batch * p.c_bs : nullptr;
+  if (p.flags & F_HAS_C) {
+    // every C load of the lane is issued before its first D store (C may
+    // be D itself: each element is read before it is written)
+    const uint16_t* C = (const uint16_t*)p.c + batch * p.c_bs;
+    u16x4 cq[FM][FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      store_quad<DT>(p, C, D, m_base + 16 * i + (lane & 15), n_base + 16 * j + 4 * (lane >> 4), acc[i][j]);
+      for (int j = 0; j < FN; ++j)
+        cq[i][j] = load_c_quad(p, C, m_base + 16 * i + (lane & 15), n_base + 16 * j + 4 * (lane >> 4));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        floatx4 v = acc[i][j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += to_f32<DT>(cq[i][j][r]);
+        store_d_quad<DT>(p, D, m_base + 16 * i + (lane & 15), n_base + 16 * j + 4 * (lane >> 4), v);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        store_d_quad<DT>(p, D, m_base + 16 * i + (lane & 15), n_base + 16 * j + 4 * (lane >> 4), acc[i][j]);
+  }
 }
 
 // Split-K partial: acc[i][j] (same layout as the epilogue's) goes to
@@ -263,6 +283,147 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
     store_partial<FM, FN>(acc, p, tc.split, tc.batch, m0 + a_row0, n0 + b_row0, lane);
   else
     epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+}
+
+// MFMA whose accumulator is pinned to AGPRs (the "a" constraint): a
+// 128x128 wave block needs 256 accumulator registers per lane, which only
+// the AGPR file can hold beside the operand fragments.  The statement is
+// opaque to the compiler, which therefore inserts no wait states before the
+// result is read: a kernel using it reads its accumulators only after an
+// explicit idle (see the end of gemm_f16_w4r_kernel).
+template <int DT>
+__device__ __forceinline__ void mfma_acc(floatx4& c, const half8& a, const half8& b) {
+  if constexpr (DT == DT_F16)
+    asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Four waves, one per SIMD, each computing a 128x128 block of the 256x256
+// tile (8x8 MFMA tiles, accumulators in AGPRs, two sets of operand
+// fragments in VGPRs).  With one wave per SIMD every latency is hidden in
+// software: the LDS reads of the next k-slice and the HBM->LDS copies are
+// interleaved one by one with the MFMAs of the current slice.  LDS is a
+// ring of five 32 KiB slots, each one operand K-tile (256 rows x 64 K in
+// the XOR-swizzled layout): operand tile q (A of K-tile q/2 for even q, B
+// for odd q) sits in slot q % 5, so the two tiles being read and three in
+// flight fit the 160 KiB of a CU.  Requires K-contiguous operands and at
+// least one K-tile.
+template <int SHIFT, int DT>
+__global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p) {
+  constexpr int BM = 256, BN = 256, FM = 8, FN = 8;
+  constexpr int SLOT = 256 * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[5 * SLOT];
+  using LD = LoaderKVec<256, 256, SHIFT, 2>;
+  constexpr int LOADS = LD::ITERS;
+  static_assert(LOADS == 8, "copy layout");
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t wm = wave & 1, wn = wave >> 1;
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
+  LD la(A, rows_a, p.a_rs, 1, p.K, wave, lane);
+  LD lb(B, rows_b, p.b_rs, 1, p.K, wave, lane);
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int32_t a_row0 = wm * 128, b_row0 = wn * 128;
+  const int32_t T = p.k_tiles;  // at least 1 (the planner's condition for this kernel)
+  __builtin_assume(T >= 1);
+  auto kt = [&](int32_t u) { return u < T ? u : T; };
+  auto slot = [&](int32_t q) { return smem + q * SLOT; };
+  auto rd = [&](const char* base, int32_t row, int ks) {
+    return *(const half8*)(base + fragment_lds_offset(MFMA16_F16, lane, 0, row, ks, SHIFT));
+  };
+  half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+
+  la.issue(kt(0), slot(0));
+  lb.issue(kt(0), slot(1));
+  la.issue(kt(1), slot(2));
+  wait_vmem_n<LOADS>();
+  phase_barrier();
+  // the first tile's part (1) computes with zero fragments (adds nothing)
+#pragma unroll
+  for (int i = 0; i < FM; ++i) fa1[i] = half8{};
+#pragma unroll
+  for (int j = 0; j < FN; ++j) fb1[j] = half8{};
+
+  // Tile t: (1) reads of slice 0 into set 0, the second half of tile
+  // t-1's slice 1 on set 1, copy of B(t+1) into A(t-1)'s slot; (2) slice 0
+  // on set 0, reads of slice 1 into set 1, copy of A(t+2) into B(t-1)'s
+  // slot; (3) the first half of slice 1; barrier.  Each copy has at least
+  // one K-tile of compute to land; at the barrier ending tile t only A(t+2)
+  // may still be in flight.
+  int32_t sa = 0;  // slot of A(t); B(t) in the next one
+  int32_t t = 0;
+  do {  // T >= 1: one path into the epilogue keeps the accumulators in place
+    const int32_t sb = sa == 4 ? 0 : sa + 1;
+    const int32_t s3 = sa + 3 >= 5 ? sa - 2 : sa + 3, s4 = sa == 0 ? 4 : sa - 1;
+    const char* cA = slot(sa);
+    const char* cB = slot(sb);
+    // (1)
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      if (g < 8)
+        fb0[g] = rd(cB, b_row0 + 16 * g, 0);
+      else
+        fa0[g - 8] = rd(cA, a_row0 + 16 * (g - 8), 0);
+      if (!(g & 1)) lb.issue_one(kt(t + 1), slot(s3), g >> 1);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = 2 * g + q, i = FM / 2 + e / FN, j = e % FN;
+        mfma_acc<DT>(acc[i][j], fb1[j], fa1[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // (2)
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      if (g < 8)
+        fb1[g] = rd(cB, b_row0 + 16 * g, 1);
+      else
+        fa1[g - 8] = rd(cA, a_row0 + 16 * (g - 8), 1);
+      if (g & 1) la.issue_one(kt(t + 2), slot(s4), g >> 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * g + q, i = e / FN, j = e % FN;
+        mfma_acc<DT>(acc[i][j], fb0[j], fa0[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // (3)
+#pragma unroll
+    for (int i = 0; i < FM / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma_acc<DT>(acc[i][j], fb1[j], fa1[i]);
+    wait_vmem_n<LOADS>();
+    phase_barrier();
+    sa = sa + 2 >= 5 ? sa - 3 : sa + 2;
+  } while (++t < T);
+  // the last tile's second half of slice 1
+#pragma unroll
+  for (int i = FM / 2; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) mfma_acc<DT>(acc[i][j], fb1[j], fa1[i]);
+  wait_vmem();
+  // The MFMAs above are inline assembly, so the compiler inserts no wait
+  // states before their results are read: idle 32 cycles (more than the
+  // instruction's passes need), then re-define every accumulator in an
+  // empty volatile statement, which orders every read after the idle.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                 "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+  epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
 }
 
 // D = round(C + sum_s ws[s]) to D's format over every output, four
@@ -747,6 +908,12 @@ hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32
       case T128x128_SPLITK: return launch_ms<128, 128, 2, 4, 3, 128, DT>(p, s);
       case T256x128_SPLITK: return launch_ms<256, 128, 4, 2, 3, 128, DT>(p, s);
       case T256x192_W2x4: return launch_cfg<256, 192, 2, 4, LOAD_KVEC, LOAD_KVEC, 0, DT>(p, s);
+      case T256x256_W4R: {
+        if (p.k_tiles < 1 || p.splits != 1) return hipErrorInvalidValue;  // the kernel runs at least one K-tile
+        const dim3 g((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), b(256);
+        hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT>), g, b, 0, s, p);
+        return hipGetLastError();
+      }
       case T256x256_PP:
       case T256x256_PPS4:
       case T256x256_PPS5:

@@ -59,8 +59,15 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts.
 constexpr int32_t kRsrcWord3 = 0x00020000;
 
+// The base and size are the same in every lane; reading them from the first
+// lane tells the compiler so, and keeps the resource in scalar registers
+// (a resource it cannot prove uniform is issued once per distinct value).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)u, (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3);
 }
 
 // Wait until every vector-memory operation of this wave (including
@@ -131,31 +138,41 @@ __device__ __forceinline__ TileCoord map_tile(int32_t bid, int32_t total, int32_
 // when the row is contiguous and aligned (F_D_VEC / F_C_VEC) and all four
 // columns are in range.
 // ---------------------------------------------------------------------------
+// C's four values at (m, n..n+3) as 16-bit codes (zero where out of range)
+__device__ __forceinline__ u16x4 load_c_quad(const GemmParams& p, const uint16_t* C, int64_t m, int64_t n) {
+  u16x4 cv = {0, 0, 0, 0};
+  if (m >= p.M || n >= p.N) return cv;
+  const uint16_t* cp = C + m * p.c_rs + n * p.c_cs;
+  if (n + 3 < p.N && (p.flags & F_C_VEC)) return *(const u16x4*)cp;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (n + r < p.N) cv[r] = cp[r * p.c_cs];
+  return cv;
+}
+
+// D(m, n..n+3) = round(v) to DT, predicated on m < M and n + r < N
 template <int DT = DT_F16>
-__device__ __forceinline__ void store_quad(const GemmParams& p, const uint16_t* C, uint16_t* D, int64_t m,
-                                           int64_t n, floatx4 v) {
+__device__ __forceinline__ void store_d_quad(const GemmParams& p, uint16_t* D, int64_t m, int64_t n, floatx4 v) {
   if (m >= p.M || n >= p.N) return;
-  const bool full = n + 3 < p.N;
-  if (p.flags & F_HAS_C) {
-    const uint16_t* cp = C + m * p.c_rs + n * p.c_cs;
-    if (full && (p.flags & F_C_VEC)) {
-      const u16x4 cv = *(const u16x4*)cp;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] += to_f32<DT>(cv[r]);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (n + r < p.N) v[r] += to_f32<DT>(cp[r * p.c_cs]);
-    }
-  }
   uint16_t* dp = D + m * p.d_rs + n * p.d_cs;
-  if (full && (p.flags & F_D_VEC)) {
+  if (n + 3 < p.N && (p.flags & F_D_VEC)) {
     *(u16x4*)dp = u16x4{from_f32<DT>(v[0]), from_f32<DT>(v[1]), from_f32<DT>(v[2]), from_f32<DT>(v[3])};
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (n + r < p.N) dp[r * p.d_cs] = from_f32<DT>(v[r]);
   }
+}
+
+template <int DT = DT_F16>
+__device__ __forceinline__ void store_quad(const GemmParams& p, const uint16_t* C, uint16_t* D, int64_t m,
+                                           int64_t n, floatx4 v) {
+  if (p.flags & F_HAS_C) {
+    const u16x4 cv = load_c_quad(p, C, m, n);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] += to_f32<DT>(cv[r]);
+  }
+  store_d_quad<DT>(p, D, m, n, v);
 }
 
 // ---------------------------------------------------------------------------

@@ -339,7 +339,35 @@ def test_bf16_dtypes(api):
                  (BASE_D, BF, (4096, 4096), (4096, 1)))
     finally:
         del os.environ["SL_TILE"]
-    assert p["tile_m"] == 256 and p["threads"] == 512
+    assert p["tile_m"] == 256 and p["threads"] == 256 and p["lds_bytes"] == 5 * 256 * 128
+
+
+def test_ring_tile_choice(api):
+    """K-contiguous fp16 and bf16 outputs that fill the chip take the 4-wave
+    256x256 ring kernel (tile 19: 256 threads, five 32 KiB operand K-tiles);
+    K = 0, M- or N-contiguous operands and an explicit other tile do not."""
+    big = [rowmajor(BASE_A, (8192, 8192)), rowmajor(BASE_B, (8192, 8192)), rowmajor(BASE_C, (8192, 8192)),
+           rowmajor(BASE_D, (8192, 8192))]
+    p = plan(api, *big)
+    assert (p["tile_m"], p["tile_n"], p["threads"], p["lds_bytes"]) == (256, 256, 256, 163840)
+    # K = 0: the ring kernel runs at least one K-tile, so the 8-wave kernel does it
+    k0 = plan(api, rowmajor(BASE_A, (4096, 0)), rowmajor(BASE_B, (4096, 0)), rowmajor(BASE_C, (4096, 4096)),
+              rowmajor(BASE_D, (4096, 4096)))
+    assert k0["threads"] == 512
+    a_mn = (BASE_A, F16, (8192, 8192), (1, 8192))
+    p = plan(api, a_mn, big[1], None, big[3])
+    assert p["threads"] == 512 and p["a_load"] == 3
+    for tile, threads in (("4", 512), ("19", 256)):
+        os.environ["SL_TILE"] = tile
+        try:
+            p = plan(api, *big)
+            k0 = plan(api, rowmajor(BASE_A, (4096, 0)), rowmajor(BASE_B, (4096, 0)), None,
+                      rowmajor(BASE_D, (4096, 4096)))
+        finally:
+            del os.environ["SL_TILE"]
+        assert p["threads"] == threads and k0["threads"] == 512
+    text = api.describe_plan(api.make_args(*(api.desc(*x) for x in big), None, None, 32))
+    assert "ring of five operand K-tiles" in text and "163840 LDS bytes" in text
 
 
 def test_nvfp4_plan_and_validation(api):

@@ -68,7 +68,7 @@ def test_exact_integer_parity(api, case):
 
 # every fp16 tile configuration the planner can be told to use (SL_TILE),
 # on K-contiguous operands, over several output tiles with ragged edges
-F16_TILES = list(range(18))
+F16_TILES = list(range(18)) + [19]
 
 
 @pytest.mark.parametrize("tile", F16_TILES)
@@ -195,6 +195,46 @@ def test_odd_strides_take_the_element_loader(api):
     from oracle import gemm as OG
     d_ref, _, _ = OG.gemm(a_st.view(np.uint16)[:, :K], b_st.view(np.uint16)[:, ::2])
     assert np.array_equal(h.d_codes(out), d_ref[0])
+
+
+RING = [
+    # M, N, K, batch, with_c: the 4-wave ring kernel (tile 19) at one K-tile,
+    # a K below one tile, ragged edges in M, N and K, batches, long K
+    (256, 256, 64, None, False),
+    (256, 256, 8, None, True),
+    (520, 300, 328, None, True),
+    (1000, 776, 1032, 2, True),
+    (264, 520, 4104, None, False),
+]
+
+
+@pytest.mark.parametrize("case", RING, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_c{int(c[4])}")
+def test_ring_kernel_exact_parity(api, case, monkeypatch):
+    h = H()
+    monkeypatch.setenv("SL_TILE", "19")
+    M, N, K, batch, with_c = case
+    w = I.gemm_workload("ring", M, N, K, seed=M + N + K + 19, dist="int4", batch=batch, with_c=with_c)
+    plan = _plan(api, w)
+    h.log(f"ring {case} plan={plan}")
+    assert plan["lds_bytes"] == 163840  # five 32 KiB operand K-tiles: the ring kernel
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
+def test_ring_kernel_in_place(api, monkeypatch):
+    """C == D through the ring kernel: every C element is read before its
+    D element is written."""
+    import torch
+    h = H()
+    monkeypatch.setenv("SL_TILE", "19")
+    w = I.gemm_workload("ring_inplace", 520, 264, 200, seed=23, dist="int4", with_c=True)
+    d_ref, _, _ = h.oracle_full(w)
+    c = h.to_device(w.c).contiguous()
+    api.gemm(h.to_device(w.a), h.to_device(w.b), c, out=c)
+    torch.cuda.synchronize()
+    assert np.array_equal(h.d_codes(c), d_ref[0])
 
 
 def test_in_place_c_equals_d(api):
@@ -382,6 +422,8 @@ BF16_EXACT = [
     (520, 300, 328, None, "row", "row", True, 7),
     (520, 300, 328, None, "row", "row", True, 15),
     (520, 300, 328, None, "row", "row", True, 5),
+    (520, 300, 328, None, "row", "row", True, 19),
+    (1000, 776, 1032, 2, "row", "row", True, 19),
 ]
 
 

@@ -1,0 +1,124 @@
+"""The 4-wave 256x256 kernel (gemm_f16_w4r_kernel) issues its MFMAs as inline
+assembly on accumulators pinned to AGPRs, so the compiler inserts no wait
+states around them and would not notice if it moved an accumulator while an
+MFMA still writes it.  These host checks read the library's own gfx950 code
+(the device code object built from gemm_f16.hip, disassembled with ROCm's
+llvm-objdump) and verify, for the fp16 and bf16 instantiations:
+
+- the accumulators never move between the first and the last MFMA (no AGPR
+  reads, writes or copies, no scratch traffic anywhere in the kernel);
+- every MFMA accumulates in place, and an accumulator is written again only
+  after at least 16 other instructions (straight-line, and around the
+  K-loop);
+- no vector-ALU write reaches an MFMA operand within 4 instructions;
+- after the last MFMA, at least 18 wait states pass before the first
+  accumulator is read (the instruction's passes plus two need fewer).
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+LLVM = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin")
+KERNELS = {
+    "fp16": "_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi0EEEvNS_10GemmParamsE",
+    "bf16": "_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi1EEEvNS_10GemmParamsE",
+}
+
+
+@pytest.fixture(scope="module")
+def code_objects(tmp_path_factory):
+    from stride_layouts_lds_amd import api as A
+    if not os.path.exists(A.LIB_PATH):
+        from stride_layouts_lds_amd import build
+        build.build(verbose=False)
+    for tool in ("llvm-objcopy", "clang-offload-bundler", "llvm-objdump"):
+        if not os.path.exists(os.path.join(LLVM, tool)):
+            pytest.skip(f"{tool} not found under {LLVM}")
+    d = tmp_path_factory.mktemp("code")
+    fat = d / "fatbin.bin"
+    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}", A.LIB_PATH, str(d / "x")],
+                   check=True, capture_output=True)
+    data = fat.read_bytes()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = [m.start() for m in re.finditer(re.escape(magic), data)]
+    assert starts, "no offload bundle in the library"
+    cos = []
+    for k, a in enumerate(starts):
+        b = starts[k + 1] if k + 1 < len(starts) else len(data)
+        bundle = d / f"b{k}.bin"
+        bundle.write_bytes(data[a:b])
+        co = d / f"b{k}.co"
+        subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle", "--type=o", f"--input={bundle}",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"], check=True, capture_output=True)
+        cos.append(str(co))
+    return cos
+
+
+def disassemble(cos, symbol):
+    for co in cos:
+        r = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", f"--disassemble-symbols={symbol}",
+                            co], check=True, capture_output=True, text=True)
+        lines = [l.split("//")[0].strip() for l in r.stdout.splitlines()]
+        lines = [l for l in lines if l and not l.endswith(">:") and not l.startswith("Disassembly")
+                 and ":" not in l.split()[0]]
+        if any(l.startswith("v_mfma") for l in lines):
+            return lines
+    raise AssertionError(f"{symbol} not found in the library's code objects")
+
+
+def regs(tok):
+    m = re.match(r"([vas])\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([vas])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+@pytest.mark.parametrize("dtype", sorted(KERNELS))
+def test_ring_kernel_accumulator_discipline(code_objects, dtype):
+    L = disassemble(code_objects, KERNELS[dtype])
+    ops = [l.replace(",", " ").split() for l in L]
+    mf = [k for k, o in enumerate(ops) if o[0].startswith("v_mfma")]
+    assert len(mf) == 160, f"{len(mf)} MFMAs (128 in the K-loop and 32 after it expected)"
+    first, last = mf[0], mf[-1]
+
+    assert not [l for l in L if l.startswith("scratch_")], "scratch traffic"
+    moved = [L[k] for k in range(first, last) if ops[k][0].startswith("v_accvgpr")]
+    assert not moved, f"accumulators moved inside the MFMA stream: {moved[:3]}"
+
+    # accumulate in place; the same accumulator rewritten only after >= 16
+    # instructions, in straight-line order and around the K-loop (the first
+    # 128 MFMAs, taken cyclically)
+    for k in mf:
+        assert ops[k][1] == ops[k][4], f"not accumulating in place: {L[k]}"
+    seen = {}
+    for k in mf:
+        if ops[k][1] in seen:
+            assert k - seen[ops[k][1]] >= 16, f"{L[k]} within 16 instructions of its previous write"
+        seen[ops[k][1]] = k
+    loop = mf[:128]
+    span = loop[-1] - loop[0] + 1
+    for a in range(128):
+        for b in range(a + 1, 128):
+            if ops[loop[a]][1] == ops[loop[b]][1]:
+                assert loop[a] + span - loop[b] >= 16, "accumulator rewritten too soon around the loop"
+
+    # no vector-ALU write to an MFMA operand within 4 instructions
+    last_write = {}
+    for k, o in enumerate(ops):
+        if o[0].startswith("v_mfma"):
+            for r in regs(o[2]) | regs(o[3]):
+                w = last_write.get(r)
+                assert w is None or k - w >= 4, f"{L[w]} feeds {L[k]} too closely"
+        elif o[0].startswith("v_") and len(o) > 1:
+            for r in regs(o[1]):
+                last_write[r] = k
+
+    # wait states between the last MFMA and the first accumulator read
+    reads = [k for k in range(last, len(L)) if ops[k][0] == "v_accvgpr_read_b32"]
+    assert reads, "accumulators never read"
+    nops = sum(int(o[1]) + 1 for o in ops[last + 1:reads[0]] if o[0] == "s_nop")
+    assert nops >= 18, f"{nops} wait states before the first accumulator read"

@@ -399,10 +399,15 @@ def check_instr_lines(api, st, kernel):
         assert ev(st["D_instr"], lane + 64 * reg) == col + R * row
 
 
-def test_trace_fp16_square(api):
+@pytest.mark.parametrize("tile,fn", [(4, 4), (19, 8)])
+def test_trace_fp16_square(api, tile, fn, monkeypatch):
+    """Tile 4: 8 waves, each 128x64 (4 instruction tiles along N); tile 19
+    (the automatic choice): 4 waves, each 128x128 (8 along N)."""
+    monkeypatch.setenv("SL_TILE", str(tile))
     n = 8192
     t, st, p = trace(api, rowmajor(BASE_A, (n, n)), rowmajor(BASE_B, (n, n)), rowmajor(BASE_C, (n, n)),
                      rowmajor(BASE_D, (n, n)))
+    assert p["threads"] == (512 if tile == 4 else 256)
     for name in ("A_instr", "A", "A_tiles", "A_lds", "A_copy", "A_wave", "A_lane0", "A_frag", "B_wave",
                  "D_instr", "acc", "D_lane0", "D", "C", "D_tiles", "tile_order", "workgroup_tile"):
         assert name in st, name
@@ -423,13 +428,13 @@ def test_trace_fp16_square(api):
             if i == 0 and ks == 0:
                 assert swizzled(2 * e, 128) == fa[lane * 8 + slot]
     # registers: one K slice, 8 halves per instruction tile, tiles in order
-    assert st["A_frag"] == "((8),8):((1),8)" and st["B_frag"] == "((8),4):((1),8)"
+    assert st["A_frag"] == "((8),8):((1),8)" and st["B_frag"] == f"((8),{fn}):((1),8)"
     # every copy instruction fills 1 KiB of LDS, the tile once
     assert sorted(ev(st["A_copy"], x) for x in range(size_of(st["A_copy"]))) == list(range(0, 256 * 128, 16))
     # accumulators: lane 0's (r, i, j) is D(16 i, 16 j + r)
-    for r, i, j in itertools.product(range(4), range(8), range(4)):
+    for r, i, j in itertools.product(range(4), range(8), range(fn)):
         assert ev(st["D_lane0"], r + 4 * (i + 8 * j)) == 16 * i * n + 16 * j + r
-        assert ev(st["acc"], r + 4 * (i + 8 * j)) == (i * 4 + j) * 4 + r
+        assert ev(st["acc"], r + 4 * (i + 8 * j)) == (i * fn + j) * 4 + r
     # workgroup -> tile: XCD x = b % 8 takes order range x*128.., the order
     # walks groups of 8 tile-rows column by column
     tiles_m = n // 256
