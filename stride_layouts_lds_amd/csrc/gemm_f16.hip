@@ -285,6 +285,54 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
     epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
 }
 
+// Epilogue of a wave's 128x128 block through a private 32 KiB LDS region,
+// for full tiles with contiguous, 8-byte aligned C and D rows: the block is
+// written in two halves of 64 rows as fp32 (row-major, 16-byte chunk q of
+// row r at chunk q ^ (r % 16): conflict-free for both the accumulator-order
+// writes and the row-order reads), read back one row-contiguous 16-byte
+// piece per lane, added to C and stored, so that 32 consecutive lanes cover
+// one 128-column row and every C load and D store instruction touches eight
+// 64-byte lines (the accumulator order touches 16 rows per instruction).
+// All C loads are issued first and overlap the LDS passes.
+template <int DT>
+__device__ __forceinline__ void epilogue_rows(const floatx4 (&acc)[8][8], const GemmParams& p, int32_t batch,
+                                              int64_t m_base, int64_t n_base, int32_t lane, char* region) {
+  uint16_t* D = (uint16_t*)p.d + batch * p.d_bs;
+  const bool has_c = p.flags & F_HAS_C;
+  const int32_t l0 = lane & 15, l1 = lane >> 4;
+  const int32_t q = lane & 31, r_lane = lane >> 5;  // row-order piece: chunk q of row 2 it + r_lane
+  u16x4 cq[2][32];
+  if (has_c) {
+    const uint16_t* C = (const uint16_t*)p.c + batch * p.c_bs;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int it = 0; it < 32; ++it)
+        cq[h][it] = *(const u16x4*)(C + (m_base + 64 * h + 2 * it + r_lane) * p.c_rs + n_base + 4 * q);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int32_t r = 16 * i + l0;
+        *(floatx4*)(region + r * 512 + 16 * ((4 * j + l1) ^ l0)) = acc[4 * h + i][j];
+      }
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+      const int32_t r = 2 * it + r_lane;
+      floatx4 v = *(const floatx4*)(region + r * 512 + 16 * (q ^ (r & 15)));
+      if (has_c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += to_f32<DT>(cq[h][it][e]);
+      }
+      *(u16x4*)(D + (m_base + 64 * h + r) * p.d_rs + n_base + 4 * q) =
+          u16x4{from_f32<DT>(v[0]), from_f32<DT>(v[1]), from_f32<DT>(v[2]), from_f32<DT>(v[3])};
+    }
+  }
+}
+
 // MFMA whose accumulator is pinned to AGPRs (the "a" constraint): a
 // 128x128 wave block needs 256 accumulator registers per lane, which only
 // the AGPR file can hold beside the operand fragments.  The statement is
@@ -308,8 +356,10 @@ __device__ __forceinline__ void mfma_acc(floatx4& c, const half8& a, const half8
 // the XOR-swizzled layout): operand tile q (A of K-tile q/2 for even q, B
 // for odd q) sits in slot q % 5, so the two tiles being read and three in
 // flight fit the 160 KiB of a CU.  Requires K-contiguous operands and at
-// least one K-tile.
-template <int SHIFT, int DT>
+// least one K-tile.  ROWS: every tile is full and C and D rows are
+// contiguous and 8-byte aligned, so the epilogue goes through LDS
+// (epilogue_rows); otherwise the per-quad epilogue.
+template <int SHIFT, int DT, bool ROWS>
 __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p) {
   constexpr int BM = 256, BN = 256, FM = 8, FN = 8;
   constexpr int SLOT = 256 * kRowBytes;
@@ -415,15 +465,27 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
     for (int j = 0; j < FN; ++j) mfma_acc<DT>(acc[i][j], fb1[j], fa1[i]);
   wait_vmem();
   // The MFMAs above are inline assembly, so the compiler inserts no wait
-  // states before their results are read: idle 32 cycles (more than the
-  // instruction's passes need), then re-define every accumulator in an
-  // empty volatile statement, which orders every read after the idle.
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  // states before their results are read.  Empty volatile statements that
+  // re-define every accumulator hold the MFMAs before an idle of 32 cycles
+  // (more than the instruction's passes need) and every read after it
+  // (volatile statements keep their order).
+  auto pin = [&] {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-    asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
-                 "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
-  epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+    for (int i = 0; i < FM; ++i)
+      asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                   "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+  };
+  pin();
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  pin();
+  if constexpr (ROWS) {
+    // every wave's copies have landed and its reads of the ring are done:
+    // the LDS is free for the per-wave epilogue regions
+    __syncthreads();
+    epilogue_rows<DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane, smem + wave * 32768);
+  } else {
+    epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  }
 }
 
 // D = round(C + sum_s ws[s]) to D's format over every output, four
@@ -911,7 +973,12 @@ hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32
       case T256x256_W4R: {
         if (p.k_tiles < 1 || p.splits != 1) return hipErrorInvalidValue;  // the kernel runs at least one K-tile
         const dim3 g((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), b(256);
-        hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT>), g, b, 0, s, p);
+        const bool rows = p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
+                          (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
+        if (rows)
+          hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT, true>), g, b, 0, s, p);
+        else
+          hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT, false>), g, b, 0, s, p);
         return hipGetLastError();
       }
       case T256x256_PP:

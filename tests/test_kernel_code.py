@@ -3,7 +3,8 @@ assembly on accumulators pinned to AGPRs, so the compiler inserts no wait
 states around them and would not notice if it moved an accumulator while an
 MFMA still writes it.  These host checks read the library's own gfx950 code
 (the device code object built from gemm_f16.hip, disassembled with ROCm's
-llvm-objdump) and verify, for the fp16 and bf16 instantiations:
+llvm-objdump) and verify, for its four instantiations (fp16 and bf16, each
+with the row epilogue through LDS and with the per-quad one):
 
 - the accumulators never move between the first and the last MFMA (no AGPR
   reads, writes or copies, no scratch traffic anywhere in the kernel);
@@ -22,9 +23,10 @@ import subprocess
 import pytest
 
 LLVM = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin")
+# (element type, epilogue through LDS rows or per accumulator quad)
 KERNELS = {
-    "fp16": "_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi0EEEvNS_10GemmParamsE",
-    "bf16": "_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi1EEEvNS_10GemmParamsE",
+    f"{dt}_{ep}": f"_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi{d}ELb{r}EEEvNS_10GemmParamsE"
+    for d, dt in ((0, "fp16"), (1, "bf16")) for r, ep in ((1, "rows"), (0, "quads"))
 }
 
 
@@ -117,8 +119,9 @@ def test_ring_kernel_accumulator_discipline(code_objects, dtype):
             for r in regs(o[1]):
                 last_write[r] = k
 
-    # wait states between the last MFMA and the first accumulator read
-    reads = [k for k in range(last, len(L)) if ops[k][0] == "v_accvgpr_read_b32"]
+    # wait states between the last MFMA and the first instruction that reads
+    # an accumulator (an AGPR copy, or an LDS or memory write of AGPR data)
+    reads = [k for k in range(last + 1, len(L)) if any(regs(t) and next(iter(regs(t)))[0] == "a" for t in ops[k][1:])]
     assert reads, "accumulators never read"
     nops = sum(int(o[1]) + 1 for o in ops[last + 1:reads[0]] if o[0] == "s_nop")
-    assert nops >= 18, f"{nops} wait states before the first accumulator read"
+    assert nops >= 18, f"{nops} wait states before the first accumulator read ({L[reads[0]]})"
