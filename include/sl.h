@@ -127,7 +127,9 @@ typedef struct {
                          scales staged in LDS), 5 nvfp4 (decoded to fp16 in
                          the loader, fp16 instruction), 6 mxfp4 and 7 mxfp6
                          (8 waves, 32x32x64 scaled instruction with E2M1 or
-                         6-bit data) */
+                         6-bit data), 8 mxfp8 (4 waves, 32x32x64 instruction,
+                         LDS ring, scales in registers: scale rows of a
+                         multiple of 16 blocks on 16-byte boundaries) */
   int32_t a_load;     /* 0 K-contiguous vector, 1 M-contiguous vector (register
                          transpose), 2 generic, 3 M-contiguous direct copy into
                          an M-major LDS tile read by transposing reads, 4 NVFP4

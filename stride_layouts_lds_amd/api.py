@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libstride_layouts_lds.so")
 
 SL_F16, SL_F32, SL_F8_E4M3, SL_E8M0, SL_BF16, SL_F4_E2M1, SL_F6_E2M3, SL_F6_E3M2 = 1, 2, 3, 4, 5, 6, 7, 8
-K_F16, K_F16_GENERIC, K_MX, K_MX_W8, K_NVFP4, K_MXFP4, K_MXFP6 = 1, 2, 3, 4, 5, 6, 7
+K_F16, K_F16_GENERIC, K_MX, K_MX_W8, K_NVFP4, K_MXFP4, K_MXFP6, K_MX_W4R = 1, 2, 3, 4, 5, 6, 7, 8
 STATUS = {0: "SL_OK", -1: "SL_ERR_NULL", -2: "SL_ERR_DTYPE", -3: "SL_ERR_SHAPE", -4: "SL_ERR_LAYOUT",
           -5: "SL_ERR_ALIGN", -6: "SL_ERR_ALIAS", -7: "SL_ERR_ARCH", -8: "SL_ERR_LAUNCH", -9: "SL_ERR_ARG",
           -10: "SL_ERR_NOMEM"}

@@ -431,7 +431,11 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
              (S.t->layout.rank == 2 || S.bs % 16 == 0);
     };
     if (kb % 16 == 0 && chunk_rows(SA) && chunk_rows(SB) && env_int("SL_SCALE16", 1)) p.flags |= sl::F_SCALE16;
-    const bool valid = tile == sl::T256x256_W2x4 ? wide_ok : tile >= 0 && tile <= sl::T128x128_W2x2;
+    // the 4-wave ring kernel: 16-byte scale chunks and at least one K-tile
+    const bool ring_ok = (p.flags & sl::F_SCALE16) && K > 0;
+    const bool valid = tile == sl::T256x256_W2x4  ? wide_ok
+                       : tile == sl::T256x256_W4R ? ring_ok
+                                                  : tile >= 0 && tile <= sl::T128x128_W2x2;
     if (!valid) {
       tile = sl::T256x128_W2x2;
       double best = 1e300;
@@ -440,8 +444,11 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
         const double c = tile_cost(sl::kTiles[t], batch, M, N, K);
         if (c < best) best = c, tile = t;
       }
+      if (tile == sl::T256x256_W2x4 && ring_ok) tile = sl::T256x256_W4R;
     }
-    P.pub.kernel = tile == sl::T256x256_W2x4 ? sl::K_MX_W8 : sl::K_MX;
+    P.pub.kernel = tile == sl::T256x256_W4R   ? sl::K_MX_W4R
+                   : tile == sl::T256x256_W2x4 ? sl::K_MX_W8
+                                               : sl::K_MX;
     P.pub.a_load = P.pub.b_load = sl::LOAD_KVEC;
     P.pub.tile_k = 128;
     p.k_tiles = (int32_t)((K + 127) / 128);
@@ -526,7 +533,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * 128 + 2 * (ts.bm + ts.bn) * 16;
   if (P.pub.kernel == sl::K_MX_W8)
     P.pub.lds_bytes += (p.flags & sl::F_SCALE16) ? 2 * (ts.bm + ts.bn) * 16 : ts.stages * (ts.bm + ts.bn) * 4;
-  if (tile == sl::T256x256_W4R) P.pub.lds_bytes = 5 * ts.bm * P.pub.tile_k * 2;  // five operand K-tiles
+  if (tile == sl::T256x256_W4R) P.pub.lds_bytes = 5 * ts.bm * 128;  // five operand K-tiles of 128-byte rows
   return SL_OK;
 }
 

@@ -80,7 +80,8 @@ InstrInfo instr_of(const DescribeInput& in) {
   const bool bf16 = in.flags & F_BF16;
   switch (in.kernel) {
     case K_MX: return {MFMA16_F8, "v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 data, E8M0 scales)", 16, 128, 16};
-    case K_MX_W8: return {MFMA32_F8, "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 data, E8M0 scales)", 32, 64, 16};
+    case K_MX_W8:
+    case K_MX_W4R: return {MFMA32_F8, "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 data, E8M0 scales)", 32, 64, 16};
     case K_MXFP4: return {MFMA32_F4, "v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1 data, E8M0 scales)", 32, 64, 32};
     case K_MXFP6:
       return {MFMA32_F6,
@@ -140,6 +141,7 @@ const char* kernel_name(int32_t k) {
     case K_NVFP4: return "NVFP4 GEMM, dequantised to fp16 tiles";
     case K_MXFP4: return "MXFP4 GEMM, 8 waves, scales staged in LDS";
     case K_MXFP6: return "MXFP6 GEMM, 8 waves, scales staged in LDS";
+    case K_MX_W4R: return "MXFP8 GEMM, 4 waves, scales loaded into registers";
     default: return "?";
   }
 }
@@ -162,7 +164,7 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
   const int32_t KS = in.bk / I.k;                         // K slices per K-tile
   const bool fp4 = in.kernel == K_MXFP4;
   const bool fp6 = in.kernel == K_MXFP6;
-  const bool fp8 = in.kernel == K_MX || in.kernel == K_MX_W8;
+  const bool fp8 = in.kernel == K_MX || in.kernel == K_MX_W8 || in.kernel == K_MX_W4R;
   const int32_t RB = fp4 ? in.bk / 2 : fp6 ? 128 : fp8 ? in.bk : in.bk * 2;  // LDS bytes per tile row
   const std::string n(1, name);
   const Layout X = view(rows, in.K, rs, cs, batched, in.batch, bs);
@@ -288,8 +290,8 @@ std::string describe_plan(const DescribeInput& in) {
          fmt("(lane, slot) -> m + %d k of the %dx%d A operand (B: n for m)", I.rows, I.rows, I.k));
   operand(o, in, I, 'A', in.a_load);
   operand(o, in, I, 'B', in.b_load);
-  if (in.kernel == K_MX || in.kernel == K_MX_W8 || in.kernel == K_MXFP4 || in.kernel == K_MXFP6 ||
-      in.kernel == K_NVFP4) {
+  if (in.kernel == K_MX || in.kernel == K_MX_W8 || in.kernel == K_MX_W4R || in.kernel == K_MXFP4 ||
+      in.kernel == K_MXFP6 || in.kernel == K_NVFP4) {
     const int64_t kb = (in.K + in.block_k - 1) / in.block_k;
     const char* fmt_s = in.kernel == K_NVFP4 ? "E4M3" : "E8M0";
     o.line("SFA", T({R(in.M, in.sa_rs), R(kb, in.sa_cs)}), fmt("%s scale of A(m, %d j .. %d j + %d)", fmt_s,
@@ -301,7 +303,10 @@ std::string describe_plan(const DescribeInput& in) {
     } else {
       o.line("scale_instr", T({S(I.rows, 1), S(64 / I.rows, I.rows)}),
              fmt("scale lane -> row + %d (K block of 32) of the instruction", I.rows));
-      if (in.kernel != K_MX)
+      if (in.kernel == K_MX_W4R)
+        o.note("scales: one 16-byte load per row per 4 K-tiles straight into registers (the LDS holds the "
+               "ring); a lane takes dword t % 4 for K-tile t, shifted right by 8 (lane / 32)");
+      else if (in.kernel != K_MX)
         o.note((in.flags & F_SCALE16)
                    ? fmt("scales: one 16-byte chunk per row per %d K-tiles, staged in two LDS buffers of %d bytes",
                          in.kernel == K_MXFP4 ? 2 : 4, (in.bm + in.bn) * 16)

@@ -285,31 +285,15 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
     epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
 }
 
-// Epilogue of a wave's 128x128 block through a private 32 KiB LDS region,
-// for full tiles with contiguous, 8-byte aligned C and D rows: the block is
-// written in two halves of 64 rows as fp32 (row-major, 16-byte chunk q of
-// row r at chunk q ^ (r % 16): conflict-free for both the accumulator-order
-// writes and the row-order reads), read back one row-contiguous 16-byte
-// piece per lane, added to C and stored, so that 32 consecutive lanes cover
-// one 128-column row and every C load and D store instruction touches eight
-// 64-byte lines (the accumulator order touches 16 rows per instruction).
-// All C loads are issued first and overlap the LDS passes.
+// Epilogue of a wave's 128x128 block through a private 32 KiB LDS region
+// (rows_load_c / rows_store_half): here the accumulator-order writes, 16
+// rows x one 16-byte chunk per instruction.
 template <int DT>
 __device__ __forceinline__ void epilogue_rows(const floatx4 (&acc)[8][8], const GemmParams& p, int32_t batch,
                                               int64_t m_base, int64_t n_base, int32_t lane, char* region) {
-  uint16_t* D = (uint16_t*)p.d + batch * p.d_bs;
-  const bool has_c = p.flags & F_HAS_C;
   const int32_t l0 = lane & 15, l1 = lane >> 4;
-  const int32_t q = lane & 31, r_lane = lane >> 5;  // row-order piece: chunk q of row 2 it + r_lane
   u16x4 cq[2][32];
-  if (has_c) {
-    const uint16_t* C = (const uint16_t*)p.c + batch * p.c_bs;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int it = 0; it < 32; ++it)
-        cq[h][it] = *(const u16x4*)(C + (m_base + 64 * h + 2 * it + r_lane) * p.c_rs + n_base + 4 * q);
-  }
+  rows_load_c(p, batch, m_base, n_base, lane, cq);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -317,19 +301,9 @@ __device__ __forceinline__ void epilogue_rows(const floatx4 (&acc)[8][8], const 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int32_t r = 16 * i + l0;
-        *(floatx4*)(region + r * 512 + 16 * ((4 * j + l1) ^ l0)) = acc[4 * h + i][j];
+        *(floatx4*)(region + rows_chunk(r, 4 * j + l1)) = acc[4 * h + i][j];
       }
-#pragma unroll
-    for (int it = 0; it < 32; ++it) {
-      const int32_t r = 2 * it + r_lane;
-      floatx4 v = *(const floatx4*)(region + r * 512 + 16 * (q ^ (r & 15)));
-      if (has_c) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += to_f32<DT>(cq[h][it][e]);
-      }
-      *(u16x4*)(D + (m_base + 64 * h + r) * p.d_rs + n_base + 4 * q) =
-          u16x4{from_f32<DT>(v[0]), from_f32<DT>(v[1]), from_f32<DT>(v[2]), from_f32<DT>(v[3])};
-    }
+    rows_store_half<DT>(p, batch, m_base + 64 * h, n_base, lane, region, cq[h]);
   }
 }
 

@@ -381,6 +381,243 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
   }
 }
 
+// Scaled MFMA (E4M3 x E4M3, 32x32x64) whose accumulator is pinned to AGPRs,
+// as mfma_acc in the fp16 kernels: the compiler inserts no wait states for
+// it, so the kernel reads its accumulators only after an explicit idle.
+// Each scale register holds the lane's scale bytes of both k-slices of a
+// K-tile; S selects byte 2S (the op_sel_hi bit of each scale operand).
+template <int S>
+__device__ __forceinline__ void mfma_scale_acc(floatx16& c, const i32x8& a, const i32x8& b, uint32_t sa, uint32_t sb) {
+  if constexpr (S == 0)
+    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+        : "+a"(c)
+        : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  else
+    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[1,1,0]"
+        : "+a"(c)
+        : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
+// MXFP8 on the fp16 ring kernel's schedule: 4 waves, one per SIMD, each a
+// 128 x 128 block as 4 x 4 tiles of v_mfma_scale_f32_32x32x64_f8f6f4 with
+// the accumulators in AGPRs; LDS a ring of five 32 KiB operand K-tiles (256
+// rows x 128 E4M3), operand tile q (A of K-tile q/2 for even q, B for odd q)
+// in slot q % 5.  Per K-tile: (1) reads of slice 0, the second half of the
+// previous tile's slice 1, the copy of B(t+1); (2) slice 0 with the reads of
+// slice 1 and the copy of A(t+2) interleaved; (3) the first half of slice
+// 1; one barrier.  The ring takes all of the LDS, so the scales go straight
+// to registers: per four K-tiles each lane loads the 16-byte scale chunk of
+// each of its rows (4 of A, 4 of B; scale rows of a multiple of 16 blocks
+// on 16-byte boundaries), issued before the copies of the K-tile that
+// precedes their first use, so the barrier that ends it also waits for
+// them.  For K-tile t a lane takes dword t % 4 of each chunk, shifted right
+// by 8 (lane / 32): byte 2s is then its scale for slice s.  ROWS: the row
+// epilogue through LDS (full tiles, vector C/D).
+template <int SHIFT, bool ROWS>
+__global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p) {
+  constexpr int BM = 256, BN = 256, FM = 4, FN = 4;
+  constexpr int SLOT = 256 * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[5 * SLOT];
+  using LD = LoaderKVec<256, 256, SHIFT, 1>;
+  constexpr int LOADS = LD::ITERS;
+  static_assert(LOADS == 8, "copy layout");
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t wm = wave & 1, wn = wave >> 1;
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  const char* A = (const char*)p.a + (tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + (tc.batch * p.b_bs + n0 * p.b_rs);
+  LD la(A, rows_a, p.a_rs, 1, p.K, wave, lane);
+  LD lb(B, rows_b, p.b_rs, 1, p.K, wave, lane);
+  const int32_t a_row0 = wm * 128, b_row0 = wn * 128;
+
+  // scale chunks of the lane's rows a_row0 + 32 i + lane % 32 (and of B)
+  const int32_t kb = (int32_t)((p.K + 31) / 32);
+  const uint8_t* SA = p.sfa + tc.batch * p.sa_bs + m0 * p.sa_rs;
+  const uint8_t* SB = p.sfb + tc.batch * p.sb_bs + n0 * p.sb_rs;
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(SA, rows_a > 0 ? (uint32_t)((rows_a - 1) * p.sa_rs + kb) : 0u);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(SB, rows_b > 0 ? (uint32_t)((rows_b - 1) * p.sb_rs + kb) : 0u);
+  uint32_t soa[FM], sob[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int32_t r = a_row0 + 32 * i + (lane & 31);
+    soa[i] = r < rows_a ? (uint32_t)(r * p.sa_rs) : kOutOfRange;
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int32_t r = b_row0 + 32 * j + (lane & 31);
+    sob[j] = r < rows_b ? (uint32_t)(r * p.sb_rs) : kOutOfRange;
+  }
+  u32x4 sa4[FM], sb4[FN];
+  auto load_chunk = [&](int32_t q) {
+    const bool in = 16 * q < kb;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      sa4[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rsa, in && soa[i] != kOutOfRange ? soa[i] + 16u * (uint32_t)q : kOutOfRange, 0, 0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      sb4[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          rsb, in && sob[j] != kOutOfRange ? sob[j] + 16u * (uint32_t)q : kOutOfRange, 0, 0);
+  };
+  auto pick = [](const u32x4& v, int32_t d) -> uint32_t {
+    return d == 0 ? v[0] : d == 1 ? v[1] : d == 2 ? v[2] : v[3];
+  };
+  const int32_t half_sel = 8 * (lane >> 5);
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
+  const int32_t T = p.k_tiles;  // at least 1 (the planner's condition for this kernel)
+  __builtin_assume(T >= 1);
+  auto kt = [&](int32_t u) { return u < T ? u : T; };
+  auto slot = [&](int32_t q) { return smem + q * SLOT; };
+  auto rd = [&](const char* base, int32_t row0, int ks) -> i32x8 {
+    const u32x4 lo = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 0, row0, ks, SHIFT));
+    const u32x4 hi = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 1, row0, ks, SHIFT));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  i32x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  uint32_t sac[FM], sbc[FN], sap[FM], sbp[FN];  // scale registers of this K-tile and of the previous one
+
+  load_chunk(0);
+  la.issue(kt(0), slot(0));
+  lb.issue(kt(0), slot(1));
+  la.issue(kt(1), slot(2));
+  wait_vmem_n<LOADS>();  // the first scale chunk, A(0), B(0)
+  phase_barrier();
+  // the first tile's part (1) computes with zero fragments (adds nothing)
+#pragma unroll
+  for (int i = 0; i < FM; ++i) fa1[i] = i32x8{}, sap[i] = 0;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) fb1[j] = i32x8{}, sbp[j] = 0;
+
+  // Four K-tiles per iteration, so that the scale chunk is loaded at a fixed
+  // place without a branch in the loop (a branch there made the compiler
+  // copy accumulators); past T the tiles are zero (their copies are out of
+  // range) and add nothing.
+  const int32_t T4 = (T + 3) & ~3;
+  int32_t sa = 0;  // slot of A(t); B(t) in the next one
+  int32_t t0 = 0;
+  do {  // T >= 1: one path into the epilogue keeps the accumulators in place
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int32_t t = t0 + d;
+      const int32_t sb = sa == 4 ? 0 : sa + 1;
+      const int32_t s3 = sa + 3 >= 5 ? sa - 2 : sa + 3, s4 = sa == 0 ? 4 : sa - 1;
+      const char* cA = slot(sa);
+      const char* cB = slot(sb);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sac[i] = pick(sa4[i], d) >> half_sel;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sbc[j] = pick(sb4[j], d) >> half_sel;
+      // (1)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if (g < 4)
+          fb0[g] = rd(cB, b_row0 + 32 * g, 0);
+        else
+          fa0[g - 4] = rd(cA, a_row0 + 32 * (g - 4), 0);
+        lb.issue_one(kt(t + 1), slot(s3), g);
+        const int i = FM / 2 + g / FN, j = g % FN;
+        mfma_scale_acc<1>(acc[i][j], fb1[j], fa1[i], sbp[j], sap[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the next four K-tiles' scales, once this chunk's last dword is taken
+      if (d == 3) load_chunk((t >> 2) + 1);
+      // (2)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if (g < 4)
+          fb1[g] = rd(cB, b_row0 + 32 * g, 1);
+        else
+          fa1[g - 4] = rd(cA, a_row0 + 32 * (g - 4), 1);
+        la.issue_one(kt(t + 2), slot(s4), g);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int e = 2 * g + q, i = e / FN, j = e % FN;
+          mfma_scale_acc<0>(acc[i][j], fb0[j], fa0[i], sbc[j], sac[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // (3)
+#pragma unroll
+      for (int i = 0; i < FM / 2; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma_scale_acc<1>(acc[i][j], fb1[j], fa1[i], sbc[j], sac[i]);
+      wait_vmem_n<LOADS>();
+      phase_barrier();
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sap[i] = sac[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sbp[j] = sbc[j];
+      sa = sa + 2 >= 5 ? sa - 3 : sa + 2;
+    }
+    t0 += 4;
+  } while (t0 < T4);
+  // the last tile's second half of slice 1
+#pragma unroll
+  for (int i = FM / 2; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) mfma_scale_acc<1>(acc[i][j], fb1[j], fa1[i], sbp[j], sap[i]);
+  wait_vmem();
+  // empty volatile statements re-defining every accumulator hold the MFMAs
+  // before an idle of 32 cycles and every read after it
+  auto pin = [&] {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]));
+  };
+  pin();
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  pin();
+
+  // accumulator register r of tile (i, j): instruction row (our n)
+  // 8 (r / 4) + 4 (lane / 32) + r % 4, instruction column (our m) lane % 32
+  if constexpr (ROWS) {
+    __syncthreads();  // every copy landed, every read of the ring done
+    char* region = smem + wave * 32768;
+    const int64_t m_base = m0 + a_row0, n_base = n0 + b_row0;
+    u16x4 cq[2][32];
+    rows_load_c(p, tc.batch, m_base, n_base, lane, cq);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const floatx16& a = acc[2 * h + ii][j];
+            *(floatx4*)(region + rows_chunk(32 * ii + (lane & 31), 8 * j + 2 * g + (lane >> 5))) =
+                floatx4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          }
+      rows_store_half<DT_F16>(p, tc.batch, m_base + 64 * h, n_base, lane, region, cq[h]);
+    }
+  } else {
+    uint16_t* D = (uint16_t*)p.d + tc.batch * p.d_bs;
+    const uint16_t* C = (p.flags & F_HAS_C) ? (const uint16_t*)p.c + tc.batch * p.c_bs : nullptr;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + a_row0 + 32 * i + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + b_row0 + 32 * j + 8 * g + 4 * (lane >> 5);
+          const floatx16& a = acc[i][j];
+          store_quad<DT_F16>(p, C, D, m, n, floatx4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]});
+        }
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
@@ -409,6 +646,19 @@ hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, hipStream_t s) {
         hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 4>), grid, block, 0, s, p);
       else
         hipLaunchKernelGGL((gemm_mx_w8_kernel<0, 1>), grid, block, 0, s, p);
+      return hipGetLastError();
+    }
+    case T256x256_W4R: {
+      // E4M3 with 16-byte scale chunks and at least one K-tile
+      if (p.k_tiles < 1 || !(p.flags & F_SCALE16) || (p.flags & (F_FP4 | F_FP6 | F_FP6_E3M2)))
+        return hipErrorInvalidValue;
+      dim3 grid((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), block(256);
+      const bool rows = p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
+                        (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
+      if (rows)
+        hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, true>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, false>), grid, block, 0, s, p);
       return hipGetLastError();
     }
     default: return hipErrorInvalidValue;

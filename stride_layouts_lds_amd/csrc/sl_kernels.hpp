@@ -26,7 +26,8 @@ enum KernelKind : int32_t {
   K_MX_W8 = 4,        // MXFP8, 8 waves, v_mfma_scale 32x32x64, scales staged in LDS
   K_NVFP4 = 5,        // NVFP4 dequantised to exact fp16 tiles, fp16 MFMA (8 waves)
   K_MXFP4 = 6,        // MXFP4, 8 waves, v_mfma_scale 32x32x64 with E2M1 data
-  K_MXFP6 = 7         // MXFP6, 8 waves, v_mfma_scale 32x32x64 with E2M3 or E3M2 data
+  K_MXFP6 = 7,        // MXFP6, 8 waves, v_mfma_scale 32x32x64 with E2M3 or E3M2 data
+  K_MX_W4R = 8        // MXFP8, 4 waves each 128x128, v_mfma_scale 32x32x64, LDS ring, scales in registers
 };
 
 // Tile configurations the dispatcher can choose: rows of A, rows of B,

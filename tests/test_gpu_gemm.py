@@ -331,7 +331,34 @@ def test_mx_exact_parity(api, case, monkeypatch):
     assert mism == 0, f"{mism} elements differ"
 
 
-@pytest.mark.parametrize("tile", [1, 3, 4])
+MX_RING = [
+    # M, N, K, batch, scale row padding, with C: the 4-wave MXFP8 ring kernel
+    # (16-byte scale chunks, so K is a multiple of 512 or just below one)
+    (256, 256, 512, None, 0, False),    # one tile, one group of four K-tiles, row epilogue
+    (264, 136, 496, None, 0, True),     # ragged M, N and K: per-quad epilogue
+    (256, 200, 1536, 2, 0, True),       # batched, 48 blocks per row
+    (264, 136, 1024, None, 16, False),  # padded scale rows 48 bytes apart
+    (512, 512, 2048, None, 0, True),    # four full tiles, 16 K-tiles, row epilogue with C
+]
+
+
+@pytest.mark.parametrize("case", MX_RING, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_p{c[4]}_c{int(c[5])}")
+def test_mx_ring_exact_parity(api, case, monkeypatch):
+    h = H()
+    monkeypatch.setenv("SL_TILE", "19")
+    M, N, K, batch, pad, with_c = case
+    w = I.gemm_workload("mx_ring", M, N, K, seed=K + M + 7, dist="int4", batch=batch, mx=True,
+                        scale_range=(-2, 2), scale_pad=pad, with_c=with_c)
+    plan = _plan(api, w)
+    h.log(f"mx ring {case} plan={plan}")
+    assert plan["kernel"] == api.K_MX_W4R and plan["lds_bytes"] == 163840
+    d = h.d_codes(h.run_library(w))
+    d_ref, _, _ = h.oracle_full(w)
+    mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
+    assert mism == 0, f"{mism} elements differ"
+
+
+@pytest.mark.parametrize("tile", [1, 3, 4, 19])
 def test_mx_kernels_agree_on_one_input(api, tile, monkeypatch):
     """The same normal-valued MXFP8 problem through each MX kernel (tile
     forced), every element within the bound."""
@@ -340,7 +367,7 @@ def test_mx_kernels_agree_on_one_input(api, tile, monkeypatch):
     w = I.gemm_workload("mx_tiles", 300, 264, 512, seed=77, dist="normal", mx=True, with_c=True)
     plan = _plan(api, w)
     h.log(f"mx tile {tile} plan={plan}")
-    assert plan["kernel"] == (api.K_MX_W8 if tile == 4 else api.K_MX)
+    assert plan["kernel"] == {4: api.K_MX_W8, 19: api.K_MX_W4R}.get(tile, api.K_MX)
     d = h.d_codes(h.run_library(w))
     d_ref, _, absum = h.oracle_full(w)
     h.assert_within_bound(d.reshape(d_ref.shape), d_ref, absum, f"mx tile {tile}")

@@ -1,17 +1,18 @@
-"""The 4-wave 256x256 kernel (gemm_f16_w4r_kernel) issues its MFMAs as inline
-assembly on accumulators pinned to AGPRs, so the compiler inserts no wait
-states around them and would not notice if it moved an accumulator while an
-MFMA still writes it.  These host checks read the library's own gfx950 code
-(the device code object built from gemm_f16.hip, disassembled with ROCm's
-llvm-objdump) and verify, for its four instantiations (fp16 and bf16, each
-with the row epilogue through LDS and with the per-quad one):
+"""The 4-wave 256x256 kernels (gemm_f16_w4r_kernel, gemm_mx_w4r_kernel) issue
+their MFMAs as inline assembly on accumulators pinned to AGPRs, so the
+compiler inserts no wait states around them and would not notice if it moved
+an accumulator while an MFMA still writes it.  These host checks read the
+library's own gfx950 code (the device code objects built from gemm_f16.hip
+and gemm_mx.hip, disassembled with ROCm's llvm-objdump) and verify, for every instantiation (fp16, bf16 and MXFP8,
+each with the row epilogue through LDS and with the per-quad one):
 
 - the accumulators never move between the first and the last MFMA (no AGPR
   reads, writes or copies, no scratch traffic anywhere in the kernel);
 - every MFMA accumulates in place, and an accumulator is written again only
   after at least 16 other instructions (straight-line, and around the
   K-loop);
-- no vector-ALU write reaches an MFMA operand within 4 instructions;
+- no vector-ALU write reaches an MFMA operand (data or scale) within 4
+  instructions;
 - after the last MFMA, at least 18 wait states pass before the first
   accumulator is read (the instruction's passes plus two need fewer).
 """
@@ -23,11 +24,17 @@ import subprocess
 import pytest
 
 LLVM = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin")
-# (element type, epilogue through LDS rows or per accumulator quad)
+# (element type, epilogue through LDS rows or per accumulator quad): symbol,
+# MFMAs in all (the K-loop's first, then the ones after it)
 KERNELS = {
-    f"{dt}_{ep}": f"_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi{d}ELb{r}EEEvNS_10GemmParamsE"
+    f"{dt}_{ep}": (f"_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi{d}ELb{r}EEEvNS_10GemmParamsE", 160)
     for d, dt in ((0, "fp16"), (1, "bf16")) for r, ep in ((1, "rows"), (0, "quads"))
 }
+# the MXFP8 ring kernel: four K-tiles of 32 scaled MFMAs per loop iteration, 8 after it
+KERNELS.update({
+    f"mxfp8_{ep}": (f"_ZN2sl12_GLOBAL__N_118gemm_mx_w4r_kernelILi0ELb{r}EEEvNS_10GemmParamsE", 136)
+    for r, ep in ((1, "rows"), (0, "quads"))
+})
 
 
 @pytest.fixture(scope="module")
@@ -81,10 +88,11 @@ def regs(tok):
 
 @pytest.mark.parametrize("dtype", sorted(KERNELS))
 def test_ring_kernel_accumulator_discipline(code_objects, dtype):
-    L = disassemble(code_objects, KERNELS[dtype])
+    symbol, count = KERNELS[dtype]
+    L = disassemble(code_objects, symbol)
     ops = [l.replace(",", " ").split() for l in L]
     mf = [k for k, o in enumerate(ops) if o[0].startswith("v_mfma")]
-    assert len(mf) == 160, f"{len(mf)} MFMAs (128 in the K-loop and 32 after it expected)"
+    assert len(mf) == count, f"{len(mf)} MFMAs ({count} expected: 128 in the K-loop, the rest after it)"
     first, last = mf[0], mf[-1]
 
     assert not [l for l in L if l.startswith("scratch_")], "scratch traffic"
@@ -112,7 +120,8 @@ def test_ring_kernel_accumulator_discipline(code_objects, dtype):
     last_write = {}
     for k, o in enumerate(ops):
         if o[0].startswith("v_mfma"):
-            for r in regs(o[2]) | regs(o[3]):
+            # operands A and B, and the scale registers of the scaled form
+            for r in regs(o[2]) | regs(o[3]) | set().union(*(regs(x) for x in o[5:7])):
                 w = last_write.get(r)
                 assert w is None or k - w >= 4, f"{L[w]} feeds {L[k]} too closely"
         elif o[0].startswith("v_") and len(o) > 1:

@@ -454,11 +454,23 @@ def test_trace_m_major_and_mx(api):
         for i, ks in itertools.product(range(8), range(2)):
             e = ev(st["A_wave"], lane + 64 * (slot + 8 * (i + 8 * ks)))
             assert divmod(e, 256) == (32 * ks + col, 16 * i + row)
-    # MXFP8, 8 waves, 32x32x64: bytes (row, k) of the 128-byte tile rows
-    _, st, p = trace(api, rowmajor(BASE_A, (n, n), 3), rowmajor(BASE_B, (n, n), 3), None,
+
+
+@pytest.mark.parametrize("tile,fn", [(None, 4), (4, 2)])
+def test_trace_mx(api, tile, fn, monkeypatch):
+    """MXFP8 on 32x32x64: the automatic choice (the 4-wave ring kernel, each
+    wave 128x128: 4 instruction tiles along N) and the 8-wave kernel (tile 4,
+    each wave 128x64: 2 along N)."""
+    if tile is not None:
+        monkeypatch.setenv("SL_TILE", str(tile))
+    n = 4096
+    # bytes (row, k) of the 128-byte tile rows
+    t, st, p = trace(api, rowmajor(BASE_A, (n, n), 3), rowmajor(BASE_B, (n, n), 3), None,
                      rowmajor(BASE_D, (n, n)), rowmajor(BASE_C, (n, n // 32), 4),
                      rowmajor(0x500000000, (n, n // 32), 4))
-    assert p["kernel"] == api.K_MX_W8
+    assert p["kernel"] == (api.K_MX_W4R if tile is None else api.K_MX_W8)
+    if tile is None:
+        assert p["lds_bytes"] == 5 * 256 * 128 and "straight into registers" in t
     check_instr_lines(api, st, 4)
     lds, es = api.query_lds_map(4, 0)
     fm = api.query_fragment_map(3, 0)
@@ -469,7 +481,7 @@ def test_trace_m_major_and_mx(api):
             assert swizzled(e, 128) == lds[32 * i + row, 64 * ks + col]
     for lane in range(64):
         assert ev(st["scale_instr"], lane) == lane % 32 + 32 * (lane // 32)
-    for r, i, j in itertools.product(range(16), range(4), range(2)):
+    for r, i, j in itertools.product(range(16), range(4), range(fn)):
         # register r of tile (i, j): n = 8 (r / 4) + r % 4 for lane 0
         assert ev(st["D_lane0"], r + 16 * (i + 4 * j)) == 32 * i * n + 32 * j + 8 * (r // 4) + r % 4
 
