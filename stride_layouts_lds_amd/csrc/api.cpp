@@ -373,7 +373,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
     p.sb_rs = SB.rs, p.sb_ks = SB.cs, p.sb_bs = SB.t->layout.rank == 3 ? SB.bs : 0;
     p.flags |= (args->a.dtype == SL_F6_E2M3 ? sl::F_FP6 : sl::F_FP6_E3M2) | sl::F_SCALE16;
-    tile = sl::T256x256_W2x4;
+    // the 4-wave ring kernel unless K = 0 (or the 8-wave tile is asked for)
+    tile = K > 0 && tile != sl::T256x256_W2x4 ? sl::T256x256_W4R : sl::T256x256_W2x4;
     P.pub.kernel = sl::K_MXFP6;
     P.pub.a_load = P.pub.b_load = sl::LOAD_KVEC;
     P.pub.tile_k = 128;
@@ -402,7 +403,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
     p.sb_rs = SB.rs, p.sb_ks = SB.cs, p.sb_bs = SB.t->layout.rank == 3 ? SB.bs : 0;
     p.flags |= sl::F_FP4 | sl::F_SCALE16;
-    tile = sl::T256x256_W2x4;
+    // the 4-wave ring kernel unless K = 0 (or the 8-wave tile is asked for)
+    tile = K > 0 && tile != sl::T256x256_W2x4 ? sl::T256x256_W4R : sl::T256x256_W2x4;
     P.pub.kernel = sl::K_MXFP4;
     P.pub.a_load = P.pub.b_load = sl::LOAD_KVEC;
     P.pub.tile_k = 256;

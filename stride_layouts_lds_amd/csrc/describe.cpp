@@ -139,8 +139,8 @@ const char* kernel_name(int32_t k) {
     case K_MX: return "MXFP8 GEMM, 4 waves";
     case K_MX_W8: return "MXFP8 GEMM, 8 waves, scales staged in LDS";
     case K_NVFP4: return "NVFP4 GEMM, dequantised to fp16 tiles";
-    case K_MXFP4: return "MXFP4 GEMM, 8 waves, scales staged in LDS";
-    case K_MXFP6: return "MXFP6 GEMM, 8 waves, scales staged in LDS";
+    case K_MXFP4: return "MXFP4 GEMM, scaled 32x32x64 instruction on E2M1 data";
+    case K_MXFP6: return "MXFP6 GEMM, scaled 32x32x64 instruction on 6-bit data";
     case K_MX_W4R: return "MXFP8 GEMM, 4 waves, scales loaded into registers";
     default: return "?";
   }
@@ -303,9 +303,10 @@ std::string describe_plan(const DescribeInput& in) {
     } else {
       o.line("scale_instr", T({S(I.rows, 1), S(64 / I.rows, I.rows)}),
              fmt("scale lane -> row + %d (K block of 32) of the instruction", I.rows));
-      if (in.kernel == K_MX_W4R)
-        o.note("scales: one 16-byte load per row per 4 K-tiles straight into registers (the LDS holds the "
-               "ring); a lane takes dword t % 4 for K-tile t, shifted right by 8 (lane / 32)");
+      if (in.ring)
+        o.note(fmt("scales: one 16-byte load per row per %d K-tiles straight into registers (the LDS holds the "
+                   "ring); slice s takes dword s / 2 of its K-tile's scale bytes, shifted right by 8 (lane / 32)",
+                   in.kernel == K_MXFP4 ? 2 : 4));
       else if (in.kernel != K_MX)
         o.note((in.flags & F_SCALE16)
                    ? fmt("scales: one 16-byte chunk per row per %d K-tiles, staged in two LDS buffers of %d bytes",

@@ -10,6 +10,8 @@
 // any scale strides (scale lane l covers (row l % 16, K block l / 16) of
 // its operand, so lane l fetches the byte SF[row0 + l % 16][4 t + l / 16]
 // for K-tile t), and the 8-wave one below for dword-aligned scale rows.
+#include <type_traits>
+
 #include "sl_device.hpp"
 
 namespace sl {
@@ -381,44 +383,105 @@ __global__ __launch_bounds__(512, 2) void gemm_mx_w8_kernel(const GemmParams p) 
   }
 }
 
-// Scaled MFMA (E4M3 x E4M3, 32x32x64) whose accumulator is pinned to AGPRs,
-// as mfma_acc in the fp16 kernels: the compiler inserts no wait states for
-// it, so the kernel reads its accumulators only after an explicit idle.
-// Each scale register holds the lane's scale bytes of both k-slices of a
-// K-tile; S selects byte 2S (the op_sel_hi bit of each scale operand).
-template <int S>
-__device__ __forceinline__ void mfma_scale_acc(floatx16& c, const i32x8& a, const i32x8& b, uint32_t sa, uint32_t sb) {
-  if constexpr (S == 0)
-    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
-        : "+a"(c)
-        : "v"(a), "v"(b), "v"(sa), "v"(sb));
-  else
-    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[1,1,0]"
-        : "+a"(c)
-        : "v"(a), "v"(b), "v"(sa), "v"(sb));
-}
+typedef int32_t i32x6 __attribute__((ext_vector_type(6)));
 
-// MXFP8 on the fp16 ring kernel's schedule: 4 waves, one per SIMD, each a
-// 128 x 128 block as 4 x 4 tiles of v_mfma_scale_f32_32x32x64_f8f6f4 with
+// Scaled 32x32x64 MFMA whose accumulator is pinned to AGPRs, as mfma_acc in
+// the fp16 kernels: the compiler inserts no wait states for it, so a kernel
+// reads its accumulators only after an explicit idle.  FMT is the data
+// format of both operands (the cbsz / blgp fields; the operand holds 8, 6
+// or 4 registers for 8-, 6- or 4-bit data).  Each scale register holds the
+// lane's scale bytes of two k-slices; S selects byte 2S (the op_sel_hi bit
+// of each scale operand).
+#define SL_MFMA_SCALE(MODS)                                                                       \
+  asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 " MODS : "+a"(c) : "v"(a), "v"(b), \
+      "v"(sa), "v"(sb))
+template <int FMT, int S>
+__device__ __forceinline__ void mfma_scale_acc(floatx16& c, i32x8 a, i32x8 b, uint32_t sa, uint32_t sb) {
+  if constexpr (FMT == kFmtE4M3) {
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0]");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0]");
+  } else if constexpr (FMT == kFmtE2M3) {
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0] cbsz:2 blgp:2");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0] cbsz:2 blgp:2");
+  } else if constexpr (FMT == kFmtE3M2) {
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0] cbsz:3 blgp:3");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0] cbsz:3 blgp:3");
+  } else {
+    static_assert(FMT == kFmtE2M1, "data format");
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0] cbsz:4 blgp:4");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0] cbsz:4 blgp:4");
+  }
+}
+template <int FMT, int S>
+__device__ __forceinline__ void mfma_scale_acc(floatx16& c, i32x6 a, i32x6 b, uint32_t sa, uint32_t sb) {
+  if constexpr (FMT == kFmtE4M3) {
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0]");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0]");
+  } else if constexpr (FMT == kFmtE2M3) {
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0] cbsz:2 blgp:2");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0] cbsz:2 blgp:2");
+  } else if constexpr (FMT == kFmtE3M2) {
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0] cbsz:3 blgp:3");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0] cbsz:3 blgp:3");
+  } else {
+    static_assert(FMT == kFmtE2M1, "data format");
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0] cbsz:4 blgp:4");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0] cbsz:4 blgp:4");
+  }
+}
+template <int FMT, int S>
+__device__ __forceinline__ void mfma_scale_acc(floatx16& c, u32x4 a, u32x4 b, uint32_t sa, uint32_t sb) {
+  if constexpr (FMT == kFmtE4M3) {
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0]");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0]");
+  } else if constexpr (FMT == kFmtE2M3) {
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0] cbsz:2 blgp:2");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0] cbsz:2 blgp:2");
+  } else if constexpr (FMT == kFmtE3M2) {
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0] cbsz:3 blgp:3");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0] cbsz:3 blgp:3");
+  } else {
+    static_assert(FMT == kFmtE2M1, "data format");
+    if constexpr (S == 0) SL_MFMA_SCALE("op_sel_hi:[0,0,0] cbsz:4 blgp:4");
+    else SL_MFMA_SCALE("op_sel_hi:[1,1,0] cbsz:4 blgp:4");
+  }
+}
+#undef SL_MFMA_SCALE
+
+// The MX formats on the fp16 ring kernel's schedule: 4 waves, one per SIMD,
+// each a 128 x 128 block as 4 x 4 tiles of v_mfma_scale_f32_32x32x64 with
 // the accumulators in AGPRs; LDS a ring of five 32 KiB operand K-tiles (256
-// rows x 128 E4M3), operand tile q (A of K-tile q/2 for even q, B for odd q)
-// in slot q % 5.  Per K-tile: (1) reads of slice 0, the second half of the
-// previous tile's slice 1, the copy of B(t+1); (2) slice 0 with the reads of
-// slice 1 and the copy of A(t+2) interleaved; (3) the first half of slice
-// 1; one barrier.  The ring takes all of the LDS, so the scales go straight
-// to registers: per four K-tiles each lane loads the 16-byte scale chunk of
-// each of its rows (4 of A, 4 of B; scale rows of a multiple of 16 blocks
-// on 16-byte boundaries), issued before the copies of the K-tile that
-// precedes their first use, so the barrier that ends it also waits for
-// them.  For K-tile t a lane takes dword t % 4 of each chunk, shifted right
-// by 8 (lane / 32): byte 2s is then its scale for slice s.  ROWS: the row
-// epilogue through LDS (full tiles, vector C/D).
-template <int SHIFT, bool ROWS>
+// rows of 128 bytes: 128 E4M3, 128 6-bit values in the first 96 bytes, or
+// 256 E2M1), operand tile q (A of K-tile q/2 for even q, B for odd q) in
+// slot q % 5.  A K-tile is KS 64-wide k-slices (2, or 4 for E2M1); fragment
+// sets 0 and 1 alternate between slices.  Per K-tile: (1) reads of slice 0,
+// the second half of the previous tile's last slice, the copy of B(t+1);
+// then every slice but the last with the reads of the next slice (and, in
+// slice 0, the copy of A(t+2)) interleaved; the first half of the last
+// slice; one barrier.  The ring takes all of the LDS, so the scales go
+// straight to registers: per TPC K-tiles each lane loads the 16-byte scale
+// chunk of each of its rows (4 of A, 4 of B; scale rows of a multiple of 16
+// blocks on 16-byte boundaries), issued before the copies of the K-tile
+// that precedes their first use, so the barrier that ends it also waits for
+// them; the loop runs TPC K-tiles per iteration so that this load needs no
+// branch (a branch in the loop made the compiler copy accumulators; past T
+// the tiles are zero and add nothing).  Slice s takes dword s / 2 of its
+// K-tile's scale bytes, shifted right by 8 (lane / 32): byte 2 (s % 2) is
+// then the lane's scale.  ROWS: the row epilogue through LDS (full tiles,
+// vector C/D).
+template <int SHIFT, bool ROWS, int FMT>
 __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p) {
+  constexpr bool F4 = FMT == kFmtE2M1;
+  constexpr bool F6 = FMT == kFmtE2M3 || FMT == kFmtE3M2;
+  constexpr int KS = F4 ? 4 : 2;        // 64-wide k-slices per K-tile
+  constexpr int SD = KS / 2;            // scale dwords per row per K-tile
+  constexpr int TPC = 4 / SD;           // K-tiles per 16-byte scale chunk
+  constexpr int TB = F6 ? 96 : kRowBytes;  // bytes of a row per K-tile
+  using Frag = std::conditional_t<F4, u32x4, std::conditional_t<F6, i32x6, i32x8>>;
   constexpr int BM = 256, BN = 256, FM = 4, FN = 4;
   constexpr int SLOT = 256 * kRowBytes;
   __shared__ __attribute__((aligned(1024))) char smem[5 * SLOT];
-  using LD = LoaderKVec<256, 256, SHIFT, 1>;
+  using LD = LoaderKVec<256, 256, SHIFT, 1, kRowBytes, TB>;
   constexpr int LOADS = LD::ITERS;
   static_assert(LOADS == 8, "copy layout");
 
@@ -429,10 +492,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
-  const char* A = (const char*)p.a + (tc.batch * p.a_bs + m0 * p.a_rs);
-  const char* B = (const char*)p.b + (tc.batch * p.b_bs + n0 * p.b_rs);
-  LD la(A, rows_a, p.a_rs, 1, p.K, wave, lane);
-  LD lb(B, rows_b, p.b_rs, 1, p.K, wave, lane);
+  // byte addressing: E2M1 packs two values per byte, 6-bit data four per
+  // three bytes (the planner makes strides and K multiples of the packing)
+  auto bytes = [](int64_t elems) -> int64_t { return F4 ? elems / 2 : F6 ? elems / 4 * 3 : elems; };
+  const char* A = (const char*)p.a + bytes(tc.batch * p.a_bs + m0 * p.a_rs);
+  const char* B = (const char*)p.b + bytes(tc.batch * p.b_bs + n0 * p.b_rs);
+  LD la(A, rows_a, bytes(p.a_rs), 1, bytes(p.K), wave, lane);
+  LD lb(B, rows_b, bytes(p.b_rs), 1, bytes(p.K), wave, lane);
   const int32_t a_row0 = wm * 128, b_row0 = wn * 128;
 
   // scale chunks of the lane's rows a_row0 + 32 i + lane % 32 (and of B)
@@ -464,9 +530,6 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
       sb4[j] = __builtin_amdgcn_raw_buffer_load_b128(
           rsb, in && sob[j] != kOutOfRange ? sob[j] + 16u * (uint32_t)q : kOutOfRange, 0, 0);
   };
-  auto pick = [](const u32x4& v, int32_t d) -> uint32_t {
-    return d == 0 ? v[0] : d == 1 ? v[1] : d == 2 ? v[2] : v[3];
-  };
   const int32_t half_sel = 8 * (lane >> 5);
 
   floatx16 acc[FM][FN];
@@ -478,94 +541,139 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
   __builtin_assume(T >= 1);
   auto kt = [&](int32_t u) { return u < T ? u : T; };
   auto slot = [&](int32_t q) { return smem + q * SLOT; };
-  auto rd = [&](const char* base, int32_t row0, int ks) -> i32x8 {
-    const u32x4 lo = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 0, row0, ks, SHIFT));
-    const u32x4 hi = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 1, row0, ks, SHIFT));
-    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  // fragment of k-slice ks for row block row0 (the probed operand orders:
+  // E4M3 two 16-byte pieces K/2 apart; E2M1 the lane's 32 consecutive k in
+  // 16 bytes; 6-bit data its 32 consecutive k in 24 bytes)
+  auto rd = [&](const char* base, int32_t row0, int ks) -> Frag {
+    if constexpr (F4) {
+      return *(const u32x4*)(base + lds_offset(row0 + (lane & 31), 32 * ks + 16 * (lane >> 5), SHIFT));
+    } else if constexpr (F6) {
+      // three 8-byte reads at lane-dependent addresses into fixed registers:
+      // assembling the 16 + 8 byte reads of the 8-wave kernel needs a
+      // lane-dependent register select, a vector-ALU write too close to
+      // the (inline-assembly) MFMA that reads it
+      const int32_t row = row0 + (lane & 31), b0 = 48 * ks + 24 * (lane >> 5);
+      const u32x2 x = *(const u32x2*)(base + lds_offset(row, b0, SHIFT));
+      const u32x2 y = *(const u32x2*)(base + lds_offset(row, b0 + 8, SHIFT));
+      const u32x2 z = *(const u32x2*)(base + lds_offset(row, b0 + 16, SHIFT));
+      return i32x6{(int)x[0], (int)x[1], (int)y[0], (int)y[1], (int)z[0], (int)z[1]};
+    } else {
+      const u32x4 lo = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 0, row0, ks, SHIFT));
+      const u32x4 hi = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 1, row0, ks, SHIFT));
+      return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
   };
-  i32x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  uint32_t sac[FM], sbc[FN], sap[FM], sbp[FN];  // scale registers of this K-tile and of the previous one
+  Frag fa[2][FM], fb[2][FN];  // fragment sets 0 and 1
+  uint32_t sac[SD][FM], sbc[SD][FN];  // scale registers of this K-tile
+  uint32_t sap[FM], sbp[FN];          // ... of the previous one's last dword
+  // slice s of the current K-tile on set s % 2, tiles e0 .. e0 + n - 1 in
+  // (i, j) order; S = s % 2 picks the byte
+  auto mfma_range = [&](auto s_c, int e0, int n) {
+    constexpr int s = decltype(s_c)::value;
+#pragma unroll
+    for (int e = e0; e < e0 + n; ++e) {
+      const int i = e / FN, j = e % FN;
+      mfma_scale_acc<FMT, s % 2>(acc[i][j], fb[s % 2][j], fa[s % 2][i], sbc[s / 2][j], sac[s / 2][i]);
+    }
+  };
 
+  // Every MFMA operand written by a vector-ALU instruction (the zero
+  // fragments and scales below, each K-tile's scale registers) is written
+  // before an idle of 5 cycles that nothing crosses: the inline-assembly
+  // MFMAs get no wait states from the compiler.
+  auto valu_fence = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 4" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   load_chunk(0);
   la.issue(kt(0), slot(0));
   lb.issue(kt(0), slot(1));
   la.issue(kt(1), slot(2));
-  wait_vmem_n<LOADS>();  // the first scale chunk, A(0), B(0)
-  phase_barrier();
   // the first tile's part (1) computes with zero fragments (adds nothing)
 #pragma unroll
-  for (int i = 0; i < FM; ++i) fa1[i] = i32x8{}, sap[i] = 0;
+  for (int i = 0; i < FM; ++i) fa[1][i] = Frag{}, sap[i] = 0;
 #pragma unroll
-  for (int j = 0; j < FN; ++j) fb1[j] = i32x8{}, sbp[j] = 0;
+  for (int j = 0; j < FN; ++j) fb[1][j] = Frag{}, sbp[j] = 0;
+  wait_vmem_n<LOADS>();  // the first scale chunk, A(0), B(0)
+  phase_barrier();
 
-  // Four K-tiles per iteration, so that the scale chunk is loaded at a fixed
-  // place without a branch in the loop (a branch there made the compiler
-  // copy accumulators); past T the tiles are zero (their copies are out of
-  // range) and add nothing.
-  const int32_t T4 = (T + 3) & ~3;
+  const int32_t TT = (T + TPC - 1) / TPC * TPC;
   int32_t sa = 0;  // slot of A(t); B(t) in the next one
   int32_t t0 = 0;
   do {  // T >= 1: one path into the epilogue keeps the accumulators in place
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < TPC; ++d) {
       const int32_t t = t0 + d;
       const int32_t sb = sa == 4 ? 0 : sa + 1;
       const int32_t s3 = sa + 3 >= 5 ? sa - 2 : sa + 3, s4 = sa == 0 ? 4 : sa - 1;
       const char* cA = slot(sa);
       const char* cB = slot(sb);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sac[i] = pick(sa4[i], d) >> half_sel;
+      for (int w = 0; w < SD; ++w) {
+        auto pick = [](const u32x4& v, int k) -> uint32_t { return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3]; };
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sbc[j] = pick(sb4[j], d) >> half_sel;
-      // (1)
+        for (int i = 0; i < FM; ++i) sac[w][i] = pick(sa4[i], SD * d + w) >> half_sel;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) sbc[w][j] = pick(sb4[j], SD * d + w) >> half_sel;
+        // opaque from here on, so that the compiler cannot recompute them
+        // next to the MFMAs
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(sac[w][i]));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(sbc[w][j]));
+      }
+      valu_fence();
+      // (1): reads of slice 0, the previous K-tile's last slice (second half), copy of B(t+1)
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         if (g < 4)
-          fb0[g] = rd(cB, b_row0 + 32 * g, 0);
+          fb[0][g] = rd(cB, b_row0 + 32 * g, 0);
         else
-          fa0[g - 4] = rd(cA, a_row0 + 32 * (g - 4), 0);
+          fa[0][g - 4] = rd(cA, a_row0 + 32 * (g - 4), 0);
         lb.issue_one(kt(t + 1), slot(s3), g);
         const int i = FM / 2 + g / FN, j = g % FN;
-        mfma_scale_acc<1>(acc[i][j], fb1[j], fa1[i], sbp[j], sap[i]);
+        mfma_scale_acc<FMT, 1>(acc[i][j], fb[1][j], fa[1][i], sbp[j], sap[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // the next four K-tiles' scales, once this chunk's last dword is taken
-      if (d == 3) load_chunk((t >> 2) + 1);
-      // (2)
+      // the next chunk's scales, once this chunk's last dword is taken
+      if (d == TPC - 1) load_chunk((t + 1) / TPC);
+      // every slice but the last, with the reads of the next one
+      auto middle = [&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        if (g < 4)
-          fb1[g] = rd(cB, b_row0 + 32 * g, 1);
-        else
-          fa1[g - 4] = rd(cA, a_row0 + 32 * (g - 4), 1);
-        la.issue_one(kt(t + 2), slot(s4), g);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int e = 2 * g + q, i = e / FN, j = e % FN;
-          mfma_scale_acc<0>(acc[i][j], fb0[j], fa0[i], sbc[j], sac[i]);
+        for (int g = 0; g < 8; ++g) {
+          if (g < 4)
+            fb[(s + 1) % 2][g] = rd(cB, b_row0 + 32 * g, s + 1);
+          else
+            fa[(s + 1) % 2][g - 4] = rd(cA, a_row0 + 32 * (g - 4), s + 1);
+          if (s == 0) la.issue_one(kt(t + 2), slot(s4), g);
+          mfma_range(s_c, 2 * g, 2);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      };
+      middle(std::integral_constant<int, 0>{});
+      if constexpr (KS == 4) {
+        middle(std::integral_constant<int, 1>{});
+        middle(std::integral_constant<int, 2>{});
       }
-      // (3)
-#pragma unroll
-      for (int i = 0; i < FM / 2; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) mfma_scale_acc<1>(acc[i][j], fb1[j], fa1[i], sbc[j], sac[i]);
+      // the last slice, first half
+      mfma_range(std::integral_constant<int, KS - 1>{}, 0, 8);
       wait_vmem_n<LOADS>();
       phase_barrier();
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sap[i] = sac[i];
+      for (int i = 0; i < FM; ++i) sap[i] = sac[SD - 1][i];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sbp[j] = sbc[j];
+      for (int j = 0; j < FN; ++j) sbp[j] = sbc[SD - 1][j];
       sa = sa + 2 >= 5 ? sa - 3 : sa + 2;
     }
-    t0 += 4;
-  } while (t0 < T4);
-  // the last tile's second half of slice 1
+    t0 += TPC;
+  } while (t0 < TT);
+  // the last tile's last slice, second half
 #pragma unroll
   for (int i = FM / 2; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) mfma_scale_acc<1>(acc[i][j], fb1[j], fa1[i], sbp[j], sap[i]);
+    for (int j = 0; j < FN; ++j) mfma_scale_acc<FMT, 1>(acc[i][j], fb[1][j], fa[1][i], sbp[j], sap[i]);
   wait_vmem();
   // empty volatile statements re-defining every accumulator hold the MFMAs
   // before an idle of 32 cycles and every read after it
@@ -649,16 +757,26 @@ hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, hipStream_t s) {
       return hipGetLastError();
     }
     case T256x256_W4R: {
-      // E4M3 with 16-byte scale chunks and at least one K-tile
-      if (p.k_tiles < 1 || !(p.flags & F_SCALE16) || (p.flags & (F_FP4 | F_FP6 | F_FP6_E3M2)))
-        return hipErrorInvalidValue;
+      // 16-byte scale chunks and at least one K-tile
+      if (p.k_tiles < 1 || !(p.flags & F_SCALE16)) return hipErrorInvalidValue;
       dim3 grid((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), block(256);
       const bool rows = p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
                         (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
-      if (rows)
-        hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, true>), grid, block, 0, s, p);
+      auto go = [&](auto fmt) {
+        constexpr int F = decltype(fmt)::value;
+        if (rows)
+          hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, true, F>), grid, block, 0, s, p);
+        else
+          hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, false, F>), grid, block, 0, s, p);
+      };
+      if (p.flags & F_FP4)
+        go(std::integral_constant<int, kFmtE2M1>{});
+      else if (p.flags & F_FP6)
+        go(std::integral_constant<int, kFmtE2M3>{});
+      else if (p.flags & F_FP6_E3M2)
+        go(std::integral_constant<int, kFmtE3M2>{});
       else
-        hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, false>), grid, block, 0, s, p);
+        go(std::integral_constant<int, kFmtE4M3>{});
       return hipGetLastError();
     }
     default: return hipErrorInvalidValue;

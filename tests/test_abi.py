@@ -418,8 +418,8 @@ def test_mxfp6_plan(api):
     sb = (BASE_C + 0x100000, E8, (N, K // 32), (K // 32, 1))
     d = rowmajor(BASE_D, (M, N))
     p = plan(api, a, b, None, d, sa, sb, block_k=32)
-    assert p["kernel"] == api.K_MXFP6 and p["tile_k"] == 128 and p["threads"] == 512
-    assert p["lds_bytes"] == 2 * 512 * 128 + 2 * 512 * 16
+    assert p["kernel"] == api.K_MXFP6 and p["tile_k"] == 128 and p["threads"] == 256
+    assert p["lds_bytes"] == 5 * 256 * 128  # the 4-wave ring kernel
     p2 = plan(api, (BASE_A, F6B, (M, K), (K, 1)), (BASE_B, F6B, (N, K), (K, 1)), None, d, sa, sb, block_k=32)
     assert p2["kernel"] == api.K_MXFP6
     # mixed formats, E4M3 scales, block 16
@@ -467,8 +467,9 @@ def test_size_limits(api):
 
 
 def test_mxfp4_plan(api):
-    """MXFP4 (packed E2M1, E8M0 per 32 K) goes to the 8-wave scaled-MFMA
-    kernel with 256-wide K-tiles; K must be a multiple of 512."""
+    """MXFP4 (packed E2M1, E8M0 per 32 K) goes to the 4-wave scaled-MFMA
+    ring kernel with 256-wide K-tiles (the 8-wave one when asked for tile 4
+    or K = 0); K must be a multiple of 512."""
     E2, E8 = 6, 4
     M, N, K = 512, 256, 1024
     a = (BASE_A, E2, (M, K), (K, 1))
@@ -477,7 +478,17 @@ def test_mxfp4_plan(api):
     sb = (BASE_C + 0x100000, E8, (N, K // 32), (K // 32, 1))
     d = rowmajor(BASE_D, (M, N))
     p = plan(api, a, b, None, d, sa, sb, block_k=32)
-    assert p["kernel"] == api.K_MXFP4 and p["tile_k"] == 256 and p["threads"] == 512
+    assert p["kernel"] == api.K_MXFP4 and p["tile_k"] == 256 and p["threads"] == 256
+    assert p["lds_bytes"] == 5 * 256 * 128
+    os.environ["SL_TILE"] = "4"
+    try:
+        p4 = plan(api, a, b, None, d, sa, sb, block_k=32)
+    finally:
+        del os.environ["SL_TILE"]
+    assert p4["threads"] == 512 and p4["lds_bytes"] == 2 * 768 * 128 - 2 * 256 * 128 + 2 * 768 * 16 - 2 * 256 * 16
+    z = plan(api, (BASE_A, E2, (M, 0), (512, 1)), (BASE_B, E2, (N, 0), (512, 1)), None, d,
+             (BASE_C, E8, (M, 0), (16, 1)), (BASE_C + 0x100000, E8, (N, 0), (16, 1)), block_k=32)
+    assert z["threads"] == 512
     K2 = 768
     assert err(api, (BASE_A, E2, (M, K2), (K2, 1)), (BASE_B, E2, (N, K2), (K2, 1)), None, d,
                (BASE_C, E8, (M, K2 // 32), (K2 // 32, 1)), (BASE_C + 0x100000, E8, (N, K2 // 32), (K2 // 32, 1)),

@@ -3,8 +3,8 @@ their MFMAs as inline assembly on accumulators pinned to AGPRs, so the
 compiler inserts no wait states around them and would not notice if it moved
 an accumulator while an MFMA still writes it.  These host checks read the
 library's own gfx950 code (the device code objects built from gemm_f16.hip
-and gemm_mx.hip, disassembled with ROCm's llvm-objdump) and verify, for every instantiation (fp16, bf16 and MXFP8,
-each with the row epilogue through LDS and with the per-quad one):
+and gemm_mx.hip, disassembled with ROCm's llvm-objdump) and verify, for every instantiation (fp16, bf16, MXFP8, MXFP6
+and MXFP4, each with the row epilogue through LDS and with the per-quad one):
 
 - the accumulators never move between the first and the last MFMA (no AGPR
   reads, writes or copies, no scratch traffic anywhere in the kernel);
@@ -30,10 +30,11 @@ KERNELS = {
     f"{dt}_{ep}": (f"_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi{d}ELb{r}EEEvNS_10GemmParamsE", 160)
     for d, dt in ((0, "fp16"), (1, "bf16")) for r, ep in ((1, "rows"), (0, "quads"))
 }
-# the MXFP8 ring kernel: four K-tiles of 32 scaled MFMAs per loop iteration, 8 after it
+# the MX ring kernel: 128 scaled MFMAs per loop iteration (four K-tiles of 32
+# for 8- and 6-bit data, two of 64 for E2M1), 8 after it
 KERNELS.update({
-    f"mxfp8_{ep}": (f"_ZN2sl12_GLOBAL__N_118gemm_mx_w4r_kernelILi0ELb{r}EEEvNS_10GemmParamsE", 136)
-    for r, ep in ((1, "rows"), (0, "quads"))
+    f"{fn}_{ep}": (f"_ZN2sl12_GLOBAL__N_118gemm_mx_w4r_kernelILi0ELb{r}ELi{f}EEEvNS_10GemmParamsE", 136)
+    for f, fn in ((0, "mxfp8"), (2, "mxfp6_e2m3"), (3, "mxfp6_e3m2"), (4, "mxfp4")) for r, ep in ((1, "rows"), (0, "quads"))
 })
 
 
