@@ -490,26 +490,33 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       }
       // the ping-pong variants (tiles 9-14) are fp16 only
       const bool pingpong = tile >= sl::T256x256_PP && tile <= sl::T256x256_PPG;
-      // the 4-wave ring kernel needs K-contiguous operands and a K-tile
-      const bool ring_ok = kk && K > 0;
-      if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T256x256_W2x4_P) || (bf16 && pingpong) ||
-          (tile == sl::T256x256_W4R && !ring_ok)) {
-        const int32_t big = ring_ok ? sl::T256x256_W4R : sl::T256x256_W2x4;
+      // the 4-wave ring kernels need at least one K-tile and K- or M/N-
+      // contiguous vector operands (the 256x192 one K-contiguous ones).
+      // With M/N-contiguous operands the 8-wave kernel is the automatic
+      // choice: on the batched 64 x 512^3 shapes the ring kernel's
+      // transposing fragment reads made it 20-50% slower.
+      const bool vec = (la == sl::LOAD_KVEC || la == sl::LOAD_MNVEC) && (lb == sl::LOAD_KVEC || lb == sl::LOAD_MNVEC);
+      const bool ring_ok = vec && K > 0;
+      const bool ring = tile == sl::T256x256_W4R || tile == sl::T256x192_W4R;
+      if (tile < 0 || tile >= sl::T_COUNT || (!kk && tile > sl::T256x256_W2x4_P && !ring) ||
+          (bf16 && pingpong) || (ring && !ring_ok) || (tile == sl::T256x192_W4R && !kk)) {
+        const int32_t big = ring_ok && kk ? sl::T256x256_W4R : sl::T256x256_W2x4;
+        const int32_t wide = kk && K > 0 ? sl::T256x192_W4R : sl::T256x192_W2x4;
         tile = big;
         double best = 1e300;
-        for (int t : {big, (int32_t)sl::T256x192_W2x4, (int32_t)sl::T256x128_W2x2, (int32_t)sl::T128x256_W2x2,
+        for (int t : {big, wide, (int32_t)sl::T256x128_W2x2, (int32_t)sl::T128x256_W2x2,
                       (int32_t)sl::T128x128_W2x2, (int32_t)sl::T32x128_STREAM}) {
-          if ((t == sl::T32x128_STREAM || t == sl::T256x192_W2x4) && !kk) continue;
+          if ((t == sl::T32x128_STREAM || t == wide) && !kk) continue;
           const double c = tile_cost(sl::kTiles[t], batch, M, N, K);
           if (c < best) best = c, tile = t;
         }
       }
       P.pub.kernel = sl::K_F16;
     }
-    // M- (N-) contiguous operands of the 8-wave 256x256 kernel are copied
-    // straight into an M-major LDS tile (SL_MN_LOADER=1 keeps the register-
-    // transposing loader)
-    if (tile == sl::T256x256_W2x4 && env_int("SL_MN_LOADER", 3) == 3) {
+    // M- (N-) contiguous operands of the 256x256 ring kernel and of the
+    // 8-wave 256x256 kernel are copied straight into an M-major LDS tile
+    // (SL_MN_LOADER=1 keeps the register-transposing loader on the latter)
+    if (tile == sl::T256x256_W4R || (tile == sl::T256x256_W2x4 && env_int("SL_MN_LOADER", 3) == 3)) {
       if (la == sl::LOAD_MNVEC) la = sl::LOAD_MNDMA;
       if (lb == sl::LOAD_MNVEC) lb = sl::LOAD_MNDMA;
     }
@@ -535,7 +542,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * 128 + 2 * (ts.bm + ts.bn) * 16;
   if (P.pub.kernel == sl::K_MX_W8)
     P.pub.lds_bytes += (p.flags & sl::F_SCALE16) ? 2 * (ts.bm + ts.bn) * 16 : ts.stages * (ts.bm + ts.bn) * 4;
-  if (tile == sl::T256x256_W4R) P.pub.lds_bytes = 5 * ts.bm * 128;  // five operand K-tiles of 128-byte rows
+  if (tile == sl::T256x256_W4R || tile == sl::T256x192_W4R)
+    P.pub.lds_bytes = 5 * 256 * 128;  // five 32 KiB operand K-tile slots
   return SL_OK;
 }
 
@@ -874,7 +882,7 @@ sl_status sl_describe_plan(const sl_gemm_args* args, char* out, int64_t capacity
   in.b_load = P.pub.b_load;
   in.bm = ts.bm, in.bn = ts.bn, in.bk = P.pub.tile_k;
   in.wm = ts.wm, in.wn = ts.wn, in.stages = ts.stages;
-  in.ring = P.tile == sl::T256x256_W4R;
+  in.ring = P.tile == sl::T256x256_W4R || P.tile == sl::T256x192_W4R;
   in.splits = p.splits, in.split_tiles = p.split_tiles, in.group_m = p.group_m;
   in.tiles_m = p.tiles_m, in.tiles_n = p.tiles_n;
   in.workgroups = P.pub.workgroups, in.batch = P.pub.batch, in.M = p.M, in.N = p.N, in.K = p.K;

@@ -321,26 +321,32 @@ __device__ __forceinline__ void mfma_acc(floatx4& c, const half8& a, const half8
     asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
-// Four waves, one per SIMD, each computing a 128x128 block of the 256x256
-// tile (8x8 MFMA tiles, accumulators in AGPRs, two sets of operand
-// fragments in VGPRs).  With one wave per SIMD every latency is hidden in
-// software: the LDS reads of the next k-slice and the HBM->LDS copies are
-// interleaved one by one with the MFMAs of the current slice.  LDS is a
-// ring of five 32 KiB slots, each one operand K-tile (256 rows x 64 K in
-// the XOR-swizzled layout): operand tile q (A of K-tile q/2 for even q, B
-// for odd q) sits in slot q % 5, so the two tiles being read and three in
-// flight fit the 160 KiB of a CU.  Requires K-contiguous operands and at
-// least one K-tile.  ROWS: every tile is full and C and D rows are
+// Four waves, one per SIMD, each computing a 128 x BN/2 block of the
+// 256 x BN tile (8 x BN/32 MFMA tiles, accumulators in AGPRs, two sets of
+// operand fragments in VGPRs).  With one wave per SIMD every latency is
+// hidden in software: the LDS reads of the next k-slice and the HBM->LDS
+// copies are interleaved one by one with the MFMAs of the current slice.
+// LDS is a ring of five 32 KiB slots, each one operand K-tile of 64 K (the
+// XOR-swizzled K-major layout, or for ALOAD / BLOAD = LOAD_MNDMA the
+// M-major one read by transposing reads): operand tile q (A of K-tile q/2
+// for even q, B for odd q) sits in slot q % 5, so the two tiles being read
+// and three in flight fit the 160 KiB of a CU.  Requires at least one
+// K-tile.  ROWS (BN = 256 only): every tile is full and C and D rows are
 // contiguous and 8-byte aligned, so the epilogue goes through LDS
 // (epilogue_rows); otherwise the per-quad epilogue.
-template <int SHIFT, int DT, bool ROWS>
+//
+// Tile t: (1) reads of slice 0 into set 0, the second half of tile t-1's
+// slice 1 on set 1, copy of B(t+1) into A(t-1)'s slot; (2) slice 0 on set
+// 0, reads of slice 1 into set 1, copy of A(t+2) into B(t-1)'s slot; (3)
+// the first half of slice 1; barrier.  Each copy has at least one K-tile of
+// compute to land; at the barrier ending tile t only A(t+2) may still be in
+// flight.
+template <int SHIFT, int DT, bool ROWS, int ALOAD = LOAD_KVEC, int BLOAD = LOAD_KVEC, int BN = 256>
 __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p) {
-  constexpr int BM = 256, BN = 256, FM = 8, FN = 8;
+  constexpr int BM = 256, FM = 8, FN = BN / 32;
   constexpr int SLOT = 256 * kRowBytes;
+  static_assert(!ROWS || BN == 256, "the row epilogue covers 128-column wave blocks");
   __shared__ __attribute__((aligned(1024))) char smem[5 * SLOT];
-  using LD = LoaderKVec<256, 256, SHIFT, 2>;
-  constexpr int LOADS = LD::ITERS;
-  static_assert(LOADS == 8, "copy layout");
 
   const int32_t lane = threadIdx.x & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -349,43 +355,44 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
   const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
-  const char* A = (const char*)p.a + 2 * (tc.batch * p.a_bs + m0 * p.a_rs);
-  const char* B = (const char*)p.b + 2 * (tc.batch * p.b_bs + n0 * p.b_rs);
-  LD la(A, rows_a, p.a_rs, 1, p.K, wave, lane);
-  LD lb(B, rows_b, p.b_rs, 1, p.K, wave, lane);
+  auto la = make_loader<ALOAD, BM, 256, SHIFT>(p, 0, tc.batch, m0, rows_a, wave, lane);
+  auto lb = make_loader<BLOAD, BN, 256, SHIFT>(p, 1, tc.batch, n0, rows_b, wave, lane);
+  constexpr int LOADS = decltype(la)::ITERS;    // copy instructions per A tile
+  constexpr int BLOADS = decltype(lb)::ITERS;   // ... per B tile
+  static_assert(LOADS == 8 && BLOADS <= 8, "copy layout");
 
   floatx4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int32_t a_row0 = wm * 128, b_row0 = wn * 128;
+  const int32_t a_row0 = wm * 128, b_row0 = wn * (BN / 2);
   const int32_t T = p.k_tiles;  // at least 1 (the planner's condition for this kernel)
   __builtin_assume(T >= 1);
   auto kt = [&](int32_t u) { return u < T ? u : T; };
   auto slot = [&](int32_t q) { return smem + q * SLOT; };
-  auto rd = [&](const char* base, int32_t row, int ks) {
-    return *(const half8*)(base + fragment_lds_offset(MFMA16_F16, lane, 0, row, ks, SHIFT));
-  };
   half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  // read r of a slice's FN + FM fragment reads (B's first)
+  auto read = [&](const char* cA, const char* cB, int r, int ks, half8(&fa)[FM], half8(&fb)[FN]) {
+    if (r < FN)
+      fb[r] = read_frag<BLOAD, BN, SHIFT>(cB, lane, b_row0 + 16 * r, ks);
+    else
+      fa[r - FN] = read_frag<ALOAD, BM, SHIFT>(cA, lane, a_row0 + 16 * (r - FN), ks);
+  };
+  constexpr int NR = FN + FM;  // fragment reads per slice (at most 16)
+  constexpr int NH = 4 * FN;   // MFMAs in half a slice
 
   la.issue(kt(0), slot(0));
   lb.issue(kt(0), slot(1));
   la.issue(kt(1), slot(2));
-  wait_vmem_n<LOADS>();
-  phase_barrier();
   // the first tile's part (1) computes with zero fragments (adds nothing)
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa1[i] = half8{};
 #pragma unroll
   for (int j = 0; j < FN; ++j) fb1[j] = half8{};
+  wait_vmem_n<LOADS>();
+  phase_barrier();
 
-  // Tile t: (1) reads of slice 0 into set 0, the second half of tile
-  // t-1's slice 1 on set 1, copy of B(t+1) into A(t-1)'s slot; (2) slice 0
-  // on set 0, reads of slice 1 into set 1, copy of A(t+2) into B(t-1)'s
-  // slot; (3) the first half of slice 1; barrier.  Each copy has at least
-  // one K-tile of compute to land; at the barrier ending tile t only A(t+2)
-  // may still be in flight.
   int32_t sa = 0;  // slot of A(t); B(t) in the next one
   int32_t t = 0;
   do {  // T >= 1: one path into the epilogue keeps the accumulators in place
@@ -396,14 +403,11 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
     // (1)
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      if (g < 8)
-        fb0[g] = rd(cB, b_row0 + 16 * g, 0);
-      else
-        fa0[g - 8] = rd(cA, a_row0 + 16 * (g - 8), 0);
-      if (!(g & 1)) lb.issue_one(kt(t + 1), slot(s3), g >> 1);
+      if (g < NR) read(cA, cB, g, 0, fa0, fb0);
+      if (!(g & 1) && g / 2 < BLOADS) lb.issue_one(kt(t + 1), slot(s3), g >> 1);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int e = 2 * g + q, i = FM / 2 + e / FN, j = e % FN;
+      for (int e = g * NH / 16; e < (g + 1) * NH / 16; ++e) {
+        const int i = FM / 2 + e / FN, j = e % FN;
         mfma_acc<DT>(acc[i][j], fb1[j], fa1[i]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -411,14 +415,11 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
     // (2)
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      if (g < 8)
-        fb1[g] = rd(cB, b_row0 + 16 * g, 1);
-      else
-        fa1[g - 8] = rd(cA, a_row0 + 16 * (g - 8), 1);
+      if (g < NR) read(cA, cB, g, 1, fa1, fb1);
       if (g & 1) la.issue_one(kt(t + 2), slot(s4), g >> 1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * g + q, i = e / FN, j = e % FN;
+      for (int e = g * 2 * NH / 16; e < (g + 1) * 2 * NH / 16; ++e) {
+        const int i = e / FN, j = e % FN;
         mfma_acc<DT>(acc[i][j], fb0[j], fa0[i]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -446,8 +447,8 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
   auto pin = [&] {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
-                   "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+#pragma unroll
+      for (int j = 0; j < FN; j += 2) asm volatile("" : "+a"(acc[i][j]), "+a"(acc[i][j + 1]));
   };
   pin();
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -918,6 +919,24 @@ hipError_t launch_pingpong(const GemmParams& p, int32_t tile, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the ring kernel (tiles 19 and 20): at least one K-tile, no K-split; the
+// row epilogue when every 256 x 256 tile is full and C and D rows allow it
+template <int DT, int AL, int BL, int BN>
+hipError_t launch_ring(const GemmParams& p, hipStream_t s) {
+  if (p.k_tiles < 1 || p.splits != 1) return hipErrorInvalidValue;
+  const dim3 g((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), b(256);
+  const bool rows = BN == 256 && p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
+                    (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
+  if constexpr (BN == 256) {
+    if (rows) {
+      hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT, true, AL, BL, BN>), g, b, 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT, false, AL, BL, BN>), g, b, 0, s, p);
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load, hipStream_t s) {
   if (a_load == LOAD_GENERIC || b_load == LOAD_GENERIC) {
@@ -944,17 +963,8 @@ hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32
       case T128x128_SPLITK: return launch_ms<128, 128, 2, 4, 3, 128, DT>(p, s);
       case T256x128_SPLITK: return launch_ms<256, 128, 4, 2, 3, 128, DT>(p, s);
       case T256x192_W2x4: return launch_cfg<256, 192, 2, 4, LOAD_KVEC, LOAD_KVEC, 0, DT>(p, s);
-      case T256x256_W4R: {
-        if (p.k_tiles < 1 || p.splits != 1) return hipErrorInvalidValue;  // the kernel runs at least one K-tile
-        const dim3 g((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), b(256);
-        const bool rows = p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
-                          (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
-        if (rows)
-          hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT, true>), g, b, 0, s, p);
-        else
-          hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT, false>), g, b, 0, s, p);
-        return hipGetLastError();
-      }
+      case T256x256_W4R: return launch_ring<DT, LOAD_KVEC, LOAD_KVEC, 256>(p, s);
+      case T256x192_W4R: return launch_ring<DT, LOAD_KVEC, LOAD_KVEC, 192>(p, s);
       case T256x256_PP:
       case T256x256_PPS4:
       case T256x256_PPS5:
@@ -975,7 +985,14 @@ hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32
   }
 
   if (a_load == LOAD_MNDMA || b_load == LOAD_MNDMA) {
-    // the M-major direct-copy tiles exist for the 8-wave 256x256 kernel
+    // the M-major direct-copy tiles exist for the 256x256 ring kernel and
+    // the 8-wave 256x256 kernel
+    if (tile == T256x256_W4R) {
+      if (a_load == LOAD_MNDMA && b_load == LOAD_KVEC) return launch_ring<DT, LOAD_MNDMA, LOAD_KVEC, 256>(p, s);
+      if (a_load == LOAD_KVEC && b_load == LOAD_MNDMA) return launch_ring<DT, LOAD_KVEC, LOAD_MNDMA, 256>(p, s);
+      if (a_load == LOAD_MNDMA && b_load == LOAD_MNDMA) return launch_ring<DT, LOAD_MNDMA, LOAD_MNDMA, 256>(p, s);
+      return hipErrorInvalidValue;
+    }
     if (tile != T256x256_W2x4) return hipErrorInvalidValue;
     if (a_load == LOAD_MNDMA && b_load == LOAD_KVEC)
       return launch_cfg<256, 256, 2, 4, LOAD_MNDMA, LOAD_KVEC, 0, DT>(p, s);

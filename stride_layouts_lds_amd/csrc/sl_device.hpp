@@ -386,18 +386,20 @@ struct LoaderMNDma {
     rsrc = make_rsrc(base, bytes);
   }
 
+  // one copy instruction: the j-th 1 KiB block of this wave in K-tile t
+  __device__ __forceinline__ void issue_one(int32_t t, char* lds, int j) const {
+    const int32_t blk = j * WAVES + wave;             // 1 KiB block of the tile
+    const int32_t kr = blk * RPI + lane / CPR;        // K-row inside the tile
+    const int32_t c = (lane % CPR) ^ mn_swz(kr);      // logical chunk this lane fetches
+    const int32_t k = t * 64 + kr;
+    const bool ok = k < K && c * 8 < rows_valid;
+    const uint32_t off = (uint32_t)(((int64_t)k * ks + c * 8) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + blk * 1024), 16, ok ? off : kOutOfRange,
+                                             0, 0, 0);
+  }
   __device__ __forceinline__ void issue(int32_t t, char* lds) const {
 #pragma unroll
-    for (int j = 0; j < ITERS; ++j) {
-      const int32_t blk = j * WAVES + wave;             // 1 KiB block of the tile
-      const int32_t kr = blk * RPI + lane / CPR;        // K-row inside the tile
-      const int32_t c = (lane % CPR) ^ mn_swz(kr);      // logical chunk this lane fetches
-      const int32_t k = t * 64 + kr;
-      const bool ok = k < K && c * 8 < rows_valid;
-      const uint32_t off = (uint32_t)(((int64_t)k * ks + c * 8) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + blk * 1024), 16, ok ? off : kOutOfRange,
-                                               0, 0, 0);
-    }
+    for (int j = 0; j < ITERS; ++j) issue_one(t, lds, j);
   }
   __device__ __forceinline__ void commit(char*) const {}
 };

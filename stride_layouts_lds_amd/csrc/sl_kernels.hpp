@@ -54,7 +54,8 @@ enum TileCfg : int32_t {
   T256x192_W2x4 = 17,   // 8 waves, each 128x48 (fills the chip on ~4000 x 3000 outputs)
   T256x128_SPLITK = 18, // 8 waves (4 along M), each 64x64; 3 stages; K split (tall skinny outputs)
   T256x256_W4R = 19,    // 4 waves, each 128x128 (AGPR accumulators); a ring of five operand K-tiles in LDS
-  T_COUNT = 20
+  T256x192_W4R = 20,    // the same with 256x192 tiles, each wave 128x96
+  T_COUNT = 21
 };
 
 struct TileShape {
@@ -68,7 +69,7 @@ constexpr TileShape kTiles[T_COUNT] = {
     {256, 256, 2, 4, 64, 2}, {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5},
     {256, 256, 2, 4, 32, 4}, {256, 256, 2, 4, 32, 5}, {256, 256, 2, 4, 64, 2},
     {32, 128, 1, 4, 64, 6}, {128, 128, 2, 4, 64, 3}, {256, 192, 2, 4, 64, 2},
-    {256, 128, 4, 2, 64, 3}, {256, 256, 2, 2, 64, 2}};
+    {256, 128, 4, 2, 64, 3}, {256, 256, 2, 2, 64, 2}, {256, 192, 2, 2, 64, 2}};
 
 struct GemmParams {
   const void* a;  // element (b, m, k) at a + b*a_bs + m*a_rs + k*a_ks

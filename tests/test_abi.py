@@ -343,9 +343,10 @@ def test_bf16_dtypes(api):
 
 
 def test_ring_tile_choice(api):
-    """K-contiguous fp16 and bf16 outputs that fill the chip take the 4-wave
-    256x256 ring kernel (tile 19: 256 threads, five 32 KiB operand K-tiles);
-    K = 0, M- or N-contiguous operands and an explicit other tile do not."""
+    """fp16 and bf16 outputs with K-contiguous operands that fill the chip
+    take the 4-wave ring kernels (tile 19, 256x256; tile 20, 256x192; 256
+    threads, five 32 KiB operand K-tiles); K = 0 and an explicit other tile
+    do not; M/N-contiguous operands take it only when asked for tile 19."""
     big = [rowmajor(BASE_A, (8192, 8192)), rowmajor(BASE_B, (8192, 8192)), rowmajor(BASE_C, (8192, 8192)),
            rowmajor(BASE_D, (8192, 8192))]
     p = plan(api, *big)
@@ -354,9 +355,20 @@ def test_ring_tile_choice(api):
     k0 = plan(api, rowmajor(BASE_A, (4096, 0)), rowmajor(BASE_B, (4096, 0)), rowmajor(BASE_C, (4096, 4096)),
               rowmajor(BASE_D, (4096, 4096)))
     assert k0["threads"] == 512
+    # M- or N-contiguous operands: the 8-wave kernel with direct M-major
+    # copies, or the ring kernel with them when asked for tile 19
     a_mn = (BASE_A, F16, (8192, 8192), (1, 8192))
     p = plan(api, a_mn, big[1], None, big[3])
     assert p["threads"] == 512 and p["a_load"] == 3
+    os.environ["SL_TILE"] = "19"
+    try:
+        p = plan(api, a_mn, big[1], None, big[3])
+    finally:
+        del os.environ["SL_TILE"]
+    assert p["threads"] == 256 and p["a_load"] == 3 and p["lds_bytes"] == 163840
+    # a ragged output that 256x192 tiles fill better: the 256x192 ring kernel
+    r = plan(api, rowmajor(BASE_A, (4000, 2056)), rowmajor(BASE_B, (3000, 2056)), None, rowmajor(BASE_D, (4000, 3000)))
+    assert (r["tile_m"], r["tile_n"], r["threads"], r["lds_bytes"]) == (256, 192, 256, 163840)
     for tile, threads in (("4", 512), ("19", 256)):
         os.environ["SL_TILE"] = tile
         try:

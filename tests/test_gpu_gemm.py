@@ -68,7 +68,7 @@ def test_exact_integer_parity(api, case):
 
 # every fp16 tile configuration the planner can be told to use (SL_TILE),
 # on K-contiguous operands, over several output tiles with ragged edges
-F16_TILES = list(range(18)) + [19]
+F16_TILES = list(range(18)) + [19, 20]
 
 
 @pytest.mark.parametrize("tile", F16_TILES)
@@ -96,10 +96,13 @@ MN_DIRECT = [
 ]
 
 
+@pytest.mark.parametrize("tile", [4, 19])
 @pytest.mark.parametrize("case", MN_DIRECT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_{c[4]}{c[5]}")
-def test_exact_parity_m_major_direct_copy(api, case, monkeypatch):
+def test_exact_parity_m_major_direct_copy(api, case, tile, monkeypatch):
+    """The 8-wave kernel (tile 4) and the ring kernel (tile 19) with direct
+    M-major copies and transposing fragment reads."""
     h = H()
-    monkeypatch.setenv("SL_TILE", "4")
+    monkeypatch.setenv("SL_TILE", str(tile))
     M, N, K, batch, am, bm, with_c = case
     w = I.gemm_workload("mn_direct", M, N, K, seed=M + 2 * N + K, dist="int4", batch=batch, a_major=am,
                         b_major=bm, with_c=with_c)

@@ -3,8 +3,9 @@ their MFMAs as inline assembly on accumulators pinned to AGPRs, so the
 compiler inserts no wait states around them and would not notice if it moved
 an accumulator while an MFMA still writes it.  These host checks read the
 library's own gfx950 code (the device code objects built from gemm_f16.hip
-and gemm_mx.hip, disassembled with ROCm's llvm-objdump) and verify, for every instantiation (fp16, bf16, MXFP8, MXFP6
-and MXFP4, each with the row epilogue through LDS and with the per-quad one):
+and gemm_mx.hip, disassembled with ROCm's llvm-objdump) and verify, for the instantiations listed in KERNELS (fp16 and
+bf16 with K- or M-major loaders and 256- or 192-wide tiles, MXFP8, MXFP6 and
+MXFP4; row and per-quad epilogues):
 
 - the accumulators never move between the first and the last MFMA (no AGPR
   reads, writes or copies, no scratch traffic anywhere in the kernel);
@@ -24,16 +25,23 @@ import subprocess
 import pytest
 
 LLVM = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin")
-# (element type, epilogue through LDS rows or per accumulator quad): symbol,
-# MFMAs in all (the K-loop's first, then the ones after it)
+# name: (symbol, MFMAs of one K-loop iteration, MFMAs after the loop).
+# 16-bit ring kernels: element type, epilogue through LDS rows or per
+# accumulator quad, loaders (K-major, or M-major direct copies), tile width
+F16 = "_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi{d}ELb{r}ELi{al}ELi{bl}ELi{bn}EEEvNS_10GemmParamsE"
 KERNELS = {
-    f"{dt}_{ep}": (f"_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi{d}ELb{r}EEEvNS_10GemmParamsE", 160)
+    f"{dt}_{ep}": (F16.format(d=d, r=r, al=0, bl=0, bn=256), 128, 32)
     for d, dt in ((0, "fp16"), (1, "bf16")) for r, ep in ((1, "rows"), (0, "quads"))
 }
+KERNELS.update({
+    f"fp16_mn{al}{bl}_{ep}": (F16.format(d=0, r=r, al=al, bl=bl, bn=256), 128, 32)
+    for al, bl in ((3, 0), (0, 3), (3, 3)) for r, ep in ((1, "rows"), (0, "quads"))
+})
+KERNELS.update({f"{dt}_256x192": (F16.format(d=d, r=0, al=0, bl=0, bn=192), 96, 24) for d, dt in ((0, "fp16"), (1, "bf16"))})
 # the MX ring kernel: 128 scaled MFMAs per loop iteration (four K-tiles of 32
 # for 8- and 6-bit data, two of 64 for E2M1), 8 after it
 KERNELS.update({
-    f"{fn}_{ep}": (f"_ZN2sl12_GLOBAL__N_118gemm_mx_w4r_kernelILi0ELb{r}ELi{f}EEEvNS_10GemmParamsE", 136)
+    f"{fn}_{ep}": (f"_ZN2sl12_GLOBAL__N_118gemm_mx_w4r_kernelILi0ELb{r}ELi{f}EEEvNS_10GemmParamsE", 128, 8)
     for f, fn in ((0, "mxfp8"), (2, "mxfp6_e2m3"), (3, "mxfp6_e3m2"), (4, "mxfp4")) for r, ep in ((1, "rows"), (0, "quads"))
 })
 
@@ -89,11 +97,11 @@ def regs(tok):
 
 @pytest.mark.parametrize("dtype", sorted(KERNELS))
 def test_ring_kernel_accumulator_discipline(code_objects, dtype):
-    symbol, count = KERNELS[dtype]
+    symbol, in_loop, after = KERNELS[dtype]
     L = disassemble(code_objects, symbol)
     ops = [l.replace(",", " ").split() for l in L]
     mf = [k for k, o in enumerate(ops) if o[0].startswith("v_mfma")]
-    assert len(mf) == count, f"{len(mf)} MFMAs ({count} expected: 128 in the K-loop, the rest after it)"
+    assert len(mf) == in_loop + after, f"{len(mf)} MFMAs ({in_loop} in the K-loop and {after} after it expected)"
     first, last = mf[0], mf[-1]
 
     assert not [l for l in L if l.startswith("scratch_")], "scratch traffic"
@@ -110,10 +118,10 @@ def test_ring_kernel_accumulator_discipline(code_objects, dtype):
         if ops[k][1] in seen:
             assert k - seen[ops[k][1]] >= 16, f"{L[k]} within 16 instructions of its previous write"
         seen[ops[k][1]] = k
-    loop = mf[:128]
+    loop = mf[:in_loop]
     span = loop[-1] - loop[0] + 1
-    for a in range(128):
-        for b in range(a + 1, 128):
+    for a in range(in_loop):
+        for b in range(a + 1, in_loop):
             if ops[loop[a]][1] == ops[loop[b]][1]:
                 assert loop[a] + span - loop[b] >= 16, "accumulator rewritten too soon around the loop"
 
