@@ -461,10 +461,10 @@ __device__ __forceinline__ void mfma_scale_acc(floatx16& c, u32x4 a, u32x4 b, ui
 // slice; one barrier.  The ring takes all of the LDS, so the scales go
 // straight to registers: per TPC K-tiles each lane loads the 16-byte scale
 // chunk of each of its rows (4 of A, 4 of B; scale rows of a multiple of 16
-// blocks on 16-byte boundaries), issued before the copies of the K-tile
-// that precedes their first use, so the barrier that ends it also waits for
-// them; the loop runs TPC K-tiles per iteration so that this load needs no
-// branch (a branch in the loop made the compiler copy accumulators; past T
+// blocks on 16-byte boundaries) into a second register set, issued two
+// K-tiles before their first use after that K-tile's copies (its barrier
+// lets them stay in flight, the next one waits for them); the loop runs
+// TPC K-tiles per iteration so that this load needs no branch (a branch in the loop made the compiler copy accumulators; past T
 // the tiles are zero and add nothing).  Slice s takes dword s / 2 of its
 // K-tile's scale bytes, shifted right by 8 (lane / 32): byte 2 (s % 2) is
 // then the lane's scale.  ROWS: the row epilogue through LDS (full tiles,
@@ -518,16 +518,16 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
     const int32_t r = b_row0 + 32 * j + (lane & 31);
     sob[j] = r < rows_b ? (uint32_t)(r * p.sb_rs) : kOutOfRange;
   }
-  u32x4 sa4[FM], sb4[FN];
-  auto load_chunk = [&](int32_t q) {
+  u32x4 sa4[FM], sb4[FN], na4[FM], nb4[FN];  // scale chunks in use and next
+  auto load_chunk = [&](int32_t q, u32x4(&xa)[FM], u32x4(&xb)[FN]) {
     const bool in = 16 * q < kb;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      sa4[i] = __builtin_amdgcn_raw_buffer_load_b128(
+      xa[i] = __builtin_amdgcn_raw_buffer_load_b128(
           rsa, in && soa[i] != kOutOfRange ? soa[i] + 16u * (uint32_t)q : kOutOfRange, 0, 0);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      sb4[j] = __builtin_amdgcn_raw_buffer_load_b128(
+      xb[j] = __builtin_amdgcn_raw_buffer_load_b128(
           rsb, in && sob[j] != kOutOfRange ? sob[j] + 16u * (uint32_t)q : kOutOfRange, 0, 0);
   };
   const int32_t half_sel = 8 * (lane >> 5);
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
     asm volatile("s_nop 4" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  load_chunk(0);
+  load_chunk(0, sa4, sb4);
   la.issue(kt(0), slot(0));
   lb.issue(kt(0), slot(1));
   la.issue(kt(1), slot(2));
@@ -636,8 +636,6 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
         mfma_scale_acc<FMT, 1>(acc[i][j], fb[1][j], fa[1][i], sbp[j], sap[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // the next chunk's scales, once this chunk's last dword is taken
-      if (d == TPC - 1) load_chunk((t + 1) / TPC);
       // every slice but the last, with the reads of the next one
       auto middle = [&](auto s_c) {
         constexpr int s = decltype(s_c)::value;
@@ -653,13 +651,20 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
         }
       };
       middle(std::integral_constant<int, 0>{});
+      // the next chunk's scales, two K-tiles before their first use, after
+      // this K-tile's copies: the barrier that ends it lets them (and the
+      // copy of A(t+2)) stay in flight, the next one waits for them
+      if (d == TPC - 2) load_chunk(t0 / TPC + 1, na4, nb4);
       if constexpr (KS == 4) {
         middle(std::integral_constant<int, 1>{});
         middle(std::integral_constant<int, 2>{});
       }
       // the last slice, first half
       mfma_range(std::integral_constant<int, KS - 1>{}, 0, 8);
-      wait_vmem_n<LOADS>();
+      if (d == TPC - 2)
+        wait_vmem_n<LOADS + FM + FN>();
+      else
+        wait_vmem_n<LOADS>();
       phase_barrier();
 #pragma unroll
       for (int i = 0; i < FM; ++i) sap[i] = sac[SD - 1][i];
@@ -667,6 +672,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
       for (int j = 0; j < FN; ++j) sbp[j] = sbc[SD - 1][j];
       sa = sa + 2 >= 5 ? sa - 3 : sa + 2;
     }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sa4[i] = na4[i];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sb4[j] = nb4[j];
     t0 += TPC;
   } while (t0 < TT);
   // the last tile's last slice, second half
