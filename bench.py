@@ -124,23 +124,30 @@ def cpu_baseline(w, target_s: float = 12.0):
     else:
         ops = (ora(w.a), ora(w.b), ora(w.c), ora(w.sfa), ora(w.sfb))
 
-    def run(n):
+    def run(n, nthreads):
         pts = np.stack([rng.integers(0, w.batch, n), rng.integers(0, w.M, n), rng.integers(0, w.N, n)], 1)
         t0 = time.perf_counter()
-        OG.gemm_points(*ops, points=pts, block_k=w.block_k, nthreads=threads, bf16=w.bf16)
+        OG.gemm_points(*ops, points=pts, block_k=w.block_k, nthreads=nthreads, bf16=w.bf16)
         return time.perf_counter() - t0
 
-    n = max(threads * 4, 64)
-    dt = run(n)
-    while dt < 0.5:
-        n *= 4
-        dt = run(n)
-    n = max(n, int(n * target_s / dt))
-    dt = run(n)
+    def timed(nthreads, seconds):
+        n = max(nthreads * 4, 64)
+        dt = run(n, nthreads)
+        while dt < 0.5:
+            n *= 4
+            dt = run(n, nthreads)
+        n = max(n, int(n * seconds / dt))
+        return n, run(n, nthreads)
+
+    n, dt = timed(threads, target_s)
     flop = 2.0 * w.K * n
+    # the same oracle on one thread, on a smaller sample
+    n1, dt1 = timed(1, target_s / 4)
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} output elements of the same workload (each a {w.K}-term fp64 dot product), "
-                      f"{dt:.1f} s on {threads} threads"}
+                      f"{dt:.1f} s on {threads} threads",
+            "single_thread": {"value": round(2.0 * w.K * n1 / dt1 / 1e12, 6), "unit": "TFLOP/s",
+                              "sample": f"{n1} output elements, {dt1:.1f} s on 1 thread"}}
 
 
 def per_launch_timing(api, margs, sid, stream, reps: int) -> dict:
