@@ -343,7 +343,10 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
              (S.t->layout.rank == 2 || S.bs % 8 == 0);
     };
     const bool pairs = pair_rows(SA) && pair_rows(SB) && env_int("SL_NV_PAIRS", 1);
-    tile = sl::T256x256_W2x4;  // the dequantising loader exists for the 8-wave kernel
+    // the 8-wave kernel; the 4-wave ring schedule (tile 19, K > 0) only when
+    // asked for: with one wave per SIMD the decode between the MFMAs made
+    // it 25% slower on 8192^3
+    tile = K > 0 && tile == sl::T256x256_W4R ? sl::T256x256_W4R : sl::T256x256_W2x4;
     P.pub.kernel = sl::K_NVFP4;
     P.pub.a_load = P.pub.b_load = pairs ? sl::LOAD_NVFP4_PAIRS : sl::LOAD_NVFP4;
     P.pub.tile_k = 64;
@@ -543,7 +546,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   if (P.pub.kernel == sl::K_MX_W8)
     P.pub.lds_bytes += (p.flags & sl::F_SCALE16) ? 2 * (ts.bm + ts.bn) * 16 : ts.stages * (ts.bm + ts.bn) * 4;
   if (tile == sl::T256x256_W4R || tile == sl::T256x192_W4R)
-    P.pub.lds_bytes = 5 * 256 * 128;  // five 32 KiB operand K-tile slots
+    P.pub.lds_bytes = nvfp4 ? 2 * 512 * 128   // two fp16 stages (the packed data waits in registers)
+                            : 5 * 256 * 128;  // five 32 KiB operand K-tile slots
   return SL_OK;
 }
 

@@ -463,6 +463,129 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
   }
 }
 
+// NVFP4 on the ring kernel's schedule: 4 waves, one per SIMD, each a
+// 128 x 128 block (8 x 8 fp16 MFMA tiles, accumulators in AGPRs).  The
+// decoding loaders (PAIRS: two K-tiles per fetch) bring K-tile t+2's packed
+// E2M1 data and E4M3 scales into registers during K-tile t, and during K-tile
+// t+1 decode them to fp16 (exact) and write the stage of the next K-tile, so
+// every fetch has a K-tile of compute to land and LDS holds two fp16 stages
+// (128 KiB).  Tile t: (1) reads of slice 0 into set 0, the second half of
+// tile t-1's slice 1 on set 1, and the decode of A's K-tile t+1 into the
+// idle stage one 16-byte piece at a time between the MFMAs, then the fetch
+// of A's K-tile t+2; (2) slice 0 on set 0 with the reads of slice 1 and B's
+// decode, then B's fetch; (3) the first half of slice 1; barrier.  (Decoding
+// a whole tile at once stalls the one wave of the SIMD: 35% slower.)  ROWS: the
+// row epilogue through LDS (full tiles, vector C/D).
+template <int SHIFT, bool PAIRS, bool ROWS>
+__global__ __launch_bounds__(256, 1) void gemm_nvfp4_w4r_kernel(const GemmParams p) {
+  constexpr int BM = 256, BN = 256, FM = 8, FN = 8;
+  constexpr int KIND = PAIRS ? LOAD_NVFP4_PAIRS : LOAD_NVFP4;
+  constexpr int ABYTES = BM * kRowBytes, STAGE = ABYTES + BN * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t wm = wave & 1, wn = wave >> 1;
+  const TileCoord tc = map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, p.batch);
+  const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
+  const int32_t rows_a = (int32_t)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int32_t rows_b = (int32_t)(p.N - n0 < BN ? p.N - n0 : BN);
+  auto la = make_loader<KIND, BM, 256, SHIFT>(p, 0, tc.batch, m0, rows_a, wave, lane);
+  auto lb = make_loader<KIND, BN, 256, SHIFT>(p, 1, tc.batch, n0, rows_b, wave, lane);
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int32_t a_row0 = wm * 128, b_row0 = wn * 128;
+  const int32_t T = p.k_tiles;  // at least 1 (the planner's condition for this kernel)
+  __builtin_assume(T >= 1);
+  auto kt = [&](int32_t u) { return u < T ? u : T; };
+  half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto read = [&](const char* st, int r, int ks, half8(&fa)[FM], half8(&fb)[FN]) {
+    if (r < FN)
+      fb[r] = read_frag<KIND, BN, SHIFT>(st + ABYTES, lane, b_row0 + 16 * r, ks);
+    else
+      fa[r - FN] = read_frag<KIND, BM, SHIFT>(st, lane, a_row0 + 16 * (r - FN), ks);
+  };
+
+  // K-tile 0 into stage 0; K-tile 1 fetched
+  la.issue(0, nullptr);
+  lb.issue(0, nullptr);
+  la.commit(smem);
+  lb.commit(smem + ABYTES);
+  la.issue(kt(1), nullptr);
+  lb.issue(kt(1), nullptr);
+  // the first tile's part (1) computes with zero fragments (adds nothing)
+#pragma unroll
+  for (int i = 0; i < FM; ++i) fa1[i] = half8{};
+#pragma unroll
+  for (int j = 0; j < FN; ++j) fb1[j] = half8{};
+  phase_barrier();
+
+  int32_t t = 0;
+  do {  // T >= 1: one path into the epilogue keeps the accumulators in place
+    const char* cur = smem + (t & 1) * STAGE;
+    char* nxt = smem + ((t + 1) & 1) * STAGE;
+    // (1), with A's K-tile t+1 decoded piece by piece
+    constexpr int PARTS = decltype(la)::PARTS;
+    static_assert(PARTS <= 16, "decode pieces per part");
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      read(cur, g, 0, fa0, fb0);
+      if (g * PARTS % 16 == 0) la.commit_part(nxt, g * PARTS / 16 / 4, g * PARTS / 16 % 4);
+#pragma unroll
+      for (int e = 2 * g; e < 2 * g + 2; ++e) {
+        const int i = FM / 2 + e / FN, j = e % FN;
+        mfma_acc<DT_F16>(acc[i][j], fb1[j], fa1[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    la.issue(kt(t + 2), nullptr);  // A's K-tile t+2 (past the end: fully out of range)
+    // (2), with B's K-tile t+1 decoded piece by piece
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      read(cur, g, 1, fa1, fb1);
+      if (g * PARTS % 16 == 0) lb.commit_part(nxt + ABYTES, g * PARTS / 16 / 4, g * PARTS / 16 % 4);
+#pragma unroll
+      for (int e = 4 * g; e < 4 * g + 4; ++e) {
+        const int i = e / FN, j = e % FN;
+        mfma_acc<DT_F16>(acc[i][j], fb0[j], fa0[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lb.issue(kt(t + 2), nullptr);
+    // (3)
+#pragma unroll
+    for (int i = 0; i < FM / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) mfma_acc<DT_F16>(acc[i][j], fb1[j], fa1[i]);
+    phase_barrier();  // K-tile t+1 written by every wave; K-tile t's reads done
+  } while (++t < T);
+  // the last tile's second half of slice 1
+#pragma unroll
+  for (int i = FM / 2; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) mfma_acc<DT_F16>(acc[i][j], fb1[j], fa1[i]);
+  wait_vmem();  // the fetches past the end
+  auto pin = [&] {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; j += 2) asm volatile("" : "+a"(acc[i][j]), "+a"(acc[i][j + 1]));
+  };
+  pin();
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  pin();
+  if constexpr (ROWS) {
+    __syncthreads();
+    epilogue_rows<DT_F16>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane, smem + wave * 32768);
+  } else {
+    epilogue<FM, FN, DT_F16>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  }
+}
+
 // D = round(C + sum_s ws[s]) to D's format over every output, four
 // consecutive n per thread (grid-stride).  The partial planes are
 // [batch][M][N] fp32, contiguous.
@@ -977,9 +1100,23 @@ hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32
     }
   }
   if (a_load == LOAD_NVFP4 || b_load == LOAD_NVFP4 || a_load == LOAD_NVFP4_PAIRS || b_load == LOAD_NVFP4_PAIRS) {
-    // the dequantising loaders exist for the 8-wave 256x256 fp16 kernel
+    // the dequantising loaders exist for the 4-wave ring schedule and the
+    // 8-wave 256x256 fp16 kernel
     if constexpr (DT != DT_F16) return hipErrorInvalidValue;
-    if (tile != T256x256_W2x4 || a_load != b_load) return hipErrorInvalidValue;
+    if (a_load != b_load) return hipErrorInvalidValue;
+    if (tile == T256x256_W4R) {
+      if (p.k_tiles < 1 || p.splits != 1) return hipErrorInvalidValue;
+      const dim3 g((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), b(256);
+      const bool rows = p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
+                        (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
+      const bool pairs = a_load == LOAD_NVFP4_PAIRS;
+      if (pairs && rows) hipLaunchKernelGGL((gemm_nvfp4_w4r_kernel<0, true, true>), g, b, 0, s, p);
+      if (pairs && !rows) hipLaunchKernelGGL((gemm_nvfp4_w4r_kernel<0, true, false>), g, b, 0, s, p);
+      if (!pairs && rows) hipLaunchKernelGGL((gemm_nvfp4_w4r_kernel<0, false, true>), g, b, 0, s, p);
+      if (!pairs && !rows) hipLaunchKernelGGL((gemm_nvfp4_w4r_kernel<0, false, false>), g, b, 0, s, p);
+      return hipGetLastError();
+    }
+    if (tile != T256x256_W2x4) return hipErrorInvalidValue;
     if (a_load == LOAD_NVFP4_PAIRS) return launch_cfg<256, 256, 2, 4, LOAD_NVFP4_PAIRS, LOAD_NVFP4_PAIRS, 0, DT_F16>(p, s);
     return launch_cfg<256, 256, 2, 4, LOAD_NVFP4, LOAD_NVFP4, 0, DT_F16>(p, s);
   }

@@ -559,32 +559,32 @@ struct LoaderNVFP4 {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, x) * half2v{s, s});
   }
 
-  // (the four products are built as separate values: an in-place loop over
-  // the vector's elements was miscompiled into reuse of element 0)
-  __device__ __forceinline__ void commit(char* lds) const {
+  // One 16-byte piece of the fp16 tile: unit u's 8 elements K = 32 half +
+  // 8 j .. of tile `cur` (its scale: block 4 cur + 2 half + j / 2, with PAIRS
+  // byte 4 q + 2 half + j / 2 of the pair's 8).  The four products are built
+  // as separate values: an in-place loop over the vector's elements was
+  // miscompiled into reuse of element 0.
+  __device__ __forceinline__ void commit_part(char* lds, int u, int j) const {
     const int32_t q = PAIRS ? (cur & 1) : 0;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      // the unit's two scales of tile `cur`: blocks 4 cur + 2 half and + 1,
-      // with PAIRS bytes 4 q + 2 half (+1) of the pair's 8
-      uint32_t s2[2];
-      if constexpr (PAIRS) {
-        const uint32_t w = q ? sc8[u][1] : sc8[u][0];
-        s2[0] = (w >> (16 * half[u])) & 0xFF;
-        s2[1] = (w >> (16 * half[u] + 8)) & 0xFF;
-      } else {
-        s2[0] = sc[u][0];
-        s2[1] = sc[u][1];
-      }
-      const u32x4 d = q ? data[u][NB - 1] : data[u][0];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {  // 8 elements: K = 32 half + 8 j ..
-        const _Float16 s = e4m3_to_half(s2[j >> 1]);
-        const u32x4 h = e2m1x8_to_half8(d[j]);
-        *(u32x4*)(lds + lds_offset(row[u], (half[u] * 32 + 8 * j) * 2, SHIFT)) =
-            u32x4{mul_h2(h[0], s), mul_h2(h[1], s), mul_h2(h[2], s), mul_h2(h[3], s)};
-      }
+    uint32_t sb;
+    if constexpr (PAIRS) {
+      const uint32_t w = q ? sc8[u][1] : sc8[u][0];
+      sb = (w >> (16 * half[u] + 8 * (j >> 1))) & 0xFF;
+    } else {
+      sb = sc[u][j >> 1];
     }
+    const _Float16 s = e4m3_to_half(sb);
+    const u32x4 d = q ? data[u][NB - 1] : data[u][0];
+    const u32x4 h = e2m1x8_to_half8(d[j]);
+    *(u32x4*)(lds + lds_offset(row[u], (half[u] * 32 + 8 * j) * 2, SHIFT)) =
+        u32x4{mul_h2(h[0], s), mul_h2(h[1], s), mul_h2(h[2], s), mul_h2(h[3], s)};
+  }
+  static constexpr int PARTS = PER * 4;  // commit_part calls of one tile
+  __device__ __forceinline__ void commit(char* lds) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) commit_part(lds, u, j);
   }
 };
 

@@ -516,15 +516,20 @@ NVFP4_EXACT = [
     (300, 264, 512, None, True),
     (136, 72, 96, 2, True),      # K ends half way through a 64-wide K-tile
     (520, 300, 1024, None, False),
+    (512, 512, 320, None, True),   # full tiles with C: the row epilogue; an odd number of K-tiles
 ]
 
 
 @pytest.mark.parametrize("case", NVFP4_EXACT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_c{int(c[4])}")
-def test_nvfp4_exact_parity(api, case):
+@pytest.mark.parametrize("tile", [None, 19])
+def test_nvfp4_exact_parity(api, case, tile, monkeypatch):
     """Packed E2M1 data, E4M3 scales 2^[-2,2] x {1, 1.5}: every decoded
     product and partial sum is exact in fp32, so D must equal the oracle
-    bit for bit."""
+    bit for bit.  The automatic plan (the 8-wave kernel) and the 4-wave
+    ring schedule (tile 19, 128 KiB of LDS)."""
     h = H()
+    if tile is not None:
+        monkeypatch.setenv("SL_TILE", str(tile))
     M, N, K, batch, with_c = case
     w = I.nvfp4_workload("nvfp4_exact", M, N, K, seed=M + K, batch=batch, with_c=with_c, exact=True)
     plan = _plan(api, w)
@@ -532,6 +537,7 @@ def test_nvfp4_exact_parity(api, case):
     # scale rows of a multiple of 8 bytes take the paired loader (5), others the per-tile one (4)
     kind = 5 if (K // 16) % 8 == 0 and os.environ.get("SL_NV_PAIRS", "1") != "0" else 4
     assert plan["kernel"] == api.K_NVFP4 and plan["a_load"] == plan["b_load"] == kind
+    assert plan["lds_bytes"] == (131072 if tile == 19 and K > 0 else 2 * 512 * 128)
     d = h.d_codes(h.run_library(w))
     d_ref, _, _ = h.oracle_full(w)
     mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)

@@ -38,6 +38,11 @@ KERNELS.update({
     for al, bl in ((3, 0), (0, 3), (3, 3)) for r, ep in ((1, "rows"), (0, "quads"))
 })
 KERNELS.update({f"{dt}_256x192": (F16.format(d=d, r=0, al=0, bl=0, bn=192), 96, 24) for d, dt in ((0, "fp16"), (1, "bf16"))})
+# NVFP4 on the ring schedule (decoding loaders, per K-tile or per pair)
+KERNELS.update({
+    f"nvfp4_{pn}_{ep}": (f"_ZN2sl12_GLOBAL__N_121gemm_nvfp4_w4r_kernelILi0ELb{pr}ELb{r}EEEvNS_10GemmParamsE", 128, 32)
+    for pr, pn in ((1, "pairs"), (0, "tiles")) for r, ep in ((1, "rows"), (0, "quads"))
+})
 # the MX ring kernel: 128 scaled MFMAs per loop iteration (four K-tiles of 32
 # for 8- and 6-bit data, two of 64 for E2M1), 8 after it
 KERNELS.update({
