@@ -454,6 +454,8 @@ BF16_EXACT = [
     (520, 300, 328, None, "row", "row", True, 5),
     (520, 300, 328, None, "row", "row", True, 19),
     (1000, 776, 1032, 2, "row", "row", True, 19),
+    (520, 300, 328, None, "row", "row", True, 20),
+    (264, 520, 200, 2, "col", "row", True, 19),   # M-major A through the ring kernel's direct copies
 ]
 
 
