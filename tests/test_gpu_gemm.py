@@ -293,6 +293,30 @@ def test_broadcast_b_across_batch(api):
     assert np.array_equal(h.d_codes(out), d_ref)
 
 
+@pytest.mark.parametrize("M,N", [(512, 256), (300, 264)], ids=["rows", "quads"])
+def test_ring_kernel_broadcast_a_and_c(api, M, N, monkeypatch):
+    """A and C shared across a batch of B (batch stride 0 on both) through
+    the ring kernel, with the row epilogue (full tiles) and the per-quad one
+    (ragged edges)."""
+    import torch
+    h = H()
+    monkeypatch.setenv("SL_TILE", "19")
+    rng = np.random.default_rng(M + N)
+    nb, K = 3, 576
+    A = rng.integers(-4, 5, (M, K)).astype(np.float16)
+    B = rng.integers(-4, 5, (nb, N, K)).astype(np.float16)
+    C = rng.integers(-64, 65, (M, N)).astype(np.float16)
+    a = torch.from_numpy(A).cuda().unsqueeze(0).expand(nb, M, K)
+    c = torch.from_numpy(C).cuda().unsqueeze(0).expand(nb, M, N)
+    out = api.gemm(a, torch.from_numpy(B).cuda(), c)
+    torch.cuda.synchronize()
+    from oracle import gemm as OG
+    av = np.lib.stride_tricks.as_strided(A.view(np.uint16), (nb, M, K), (0, 2 * K, 2))
+    cv = np.lib.stride_tricks.as_strided(C.view(np.uint16), (nb, M, N), (0, 2 * N, 2))
+    d_ref, _, _ = OG.gemm(av, B.view(np.uint16), cv)
+    assert np.array_equal(h.d_codes(out), d_ref)
+
+
 MX_EXACT = [
     # M, N, K, batch, scale row padding, kernel the planner must pick when
     # asked for the 8-wave tile
