@@ -126,8 +126,10 @@ typedef struct {
                          instruction), 4 mxfp8 (8 waves, 32x32x64 instruction,
                          scales staged in LDS), 5 nvfp4 (decoded to fp16 in
                          the loader, fp16 instruction), 6 mxfp4 and 7 mxfp6
-                         (8 waves, 32x32x64 scaled instruction with E2M1 or
-                         6-bit data), 8 mxfp8 (4 waves, 32x32x64 instruction,
+                         (32x32x64 scaled instruction with E2M1 or 6-bit
+                         data: 4 waves on an LDS ring, scales in registers;
+                         8 waves when K == 0 or tile 4 is asked for),
+                         8 mxfp8 (4 waves, 32x32x64 instruction,
                          LDS ring, scales in registers: scale rows of a
                          multiple of 16 blocks on 16-byte boundaries) */
   int32_t a_load;     /* 0 K-contiguous vector, 1 M-contiguous vector (register
@@ -162,6 +164,11 @@ typedef struct {
  * 16-byte boundaries (row strides multiples of 32 (fp4) or 64 (fp6)
  * elements), K % 512 == 0, and scale rows K-contiguous on 16-byte
  * boundaries with row strides multiples of 16.
+ * Sizes: M, N, K and the batch count below 2^31 (else SL_ERR_SHAPE).  An
+ * operand may span any number of bytes; 256 of its rows (one tile) must
+ * span fewer than 2^31 bytes for the vector loaders of 16-bit operands
+ * (else the slower element loader runs), and for packed 4/6-bit data and
+ * scale tensors (else SL_ERR_SHAPE).
  * `stream` is a hipStream_t.  Asynchronous; see Conventions.
  */
 sl_status sl_gemm(const sl_gemm_args* args, void* stream);

@@ -252,6 +252,17 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   }
   const int64_t lim = (int64_t)1 << 31;
   if (M >= lim || N >= lim || K >= lim || batch >= lim) return fail(SL_ERR_SHAPE, "a dimension exceeds 2^31-1");
+  // Every kernel addresses an operand from its tile's first row with 64-bit
+  // pointer arithmetic and 32-bit offsets inside the tile (at most 256
+  // rows): only one tile's span must stay below 2^31 bytes, not the whole
+  // operand's.  `row_bytes` and `k_bytes` are the packed byte counts of the
+  // row stride and of K.
+  auto tile_span_ok = [&](const View& X, int64_t row_bytes, int64_t k_bytes) {
+    return (std::min<int64_t>(X.rows, 256) - 1) * row_bytes + k_bytes < lim;
+  };
+  auto scale_span_ok = [&](const View& S) {
+    return (std::min<int64_t>(S.rows, 256) - 1) * S.rs + (kb - 1) * S.cs + 1 < lim;
+  };
 
   Plan& P = *out;
   memset(&P, 0, sizeof P);
@@ -329,9 +340,9 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       return fail(SL_ERR_LAYOUT,
                   "NVFP4 operands must be K-contiguous (packed) with rows a multiple of 32 elements apart, "
                   "16-byte aligned, and K %% 32 == 0");
-    if ((M - 1) * A.rs / 2 + K / 2 >= lim || (N - 1) * B.rs / 2 + K / 2 >= lim ||
-        (M - 1) * SA.rs + (kb - 1) * SA.cs >= lim || (N - 1) * SB.rs + (kb - 1) * SB.cs >= lim)
-      return fail(SL_ERR_SHAPE, "operands span more than 2^31 bytes");
+    if (!tile_span_ok(A, A.rs / 2, K / 2) || !tile_span_ok(B, B.rs / 2, K / 2) || !scale_span_ok(SA) ||
+        !scale_span_ok(SB))
+      return fail(SL_ERR_SHAPE, "a 256-row tile of an operand spans 2^31 bytes or more");
     p.sfa = (const uint8_t*)args->sfa.data;
     p.sfb = (const uint8_t*)args->sfb.data;
     p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
@@ -368,9 +379,9 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       return fail(SL_ERR_LAYOUT,
                   "MXFP6 operands must be K-contiguous (packed) with rows a multiple of 64 elements apart, "
                   "16-byte aligned, K %% 512 == 0, and scale rows K-contiguous, 16-byte aligned");
-    if ((M - 1) * A.rs / 4 * 3 + K / 4 * 3 >= lim || (N - 1) * B.rs / 4 * 3 + K / 4 * 3 >= lim ||
-        (M - 1) * SA.rs + kb >= lim || (N - 1) * SB.rs + kb >= lim)
-      return fail(SL_ERR_SHAPE, "operands span more than 2^31 bytes");
+    if (!tile_span_ok(A, A.rs / 4 * 3, K / 4 * 3) || !tile_span_ok(B, B.rs / 4 * 3, K / 4 * 3) ||
+        !scale_span_ok(SA) || !scale_span_ok(SB))
+      return fail(SL_ERR_SHAPE, "a 256-row tile of an operand spans 2^31 bytes or more");
     p.sfa = (const uint8_t*)args->sfa.data;
     p.sfb = (const uint8_t*)args->sfb.data;
     p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
@@ -398,9 +409,9 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
       return fail(SL_ERR_LAYOUT,
                   "MXFP4 operands must be K-contiguous (packed) with rows a multiple of 32 elements apart, "
                   "16-byte aligned, K %% 512 == 0, and scale rows K-contiguous, 16-byte aligned");
-    if ((M - 1) * A.rs / 2 + K / 2 >= lim || (N - 1) * B.rs / 2 + K / 2 >= lim ||
-        (M - 1) * SA.rs + kb >= lim || (N - 1) * SB.rs + kb >= lim)
-      return fail(SL_ERR_SHAPE, "operands span more than 2^31 bytes");
+    if (!tile_span_ok(A, A.rs / 2, K / 2) || !tile_span_ok(B, B.rs / 2, K / 2) || !scale_span_ok(SA) ||
+        !scale_span_ok(SB))
+      return fail(SL_ERR_SHAPE, "a 256-row tile of an operand spans 2^31 bytes or more");
     p.sfa = (const uint8_t*)args->sfa.data;
     p.sfb = (const uint8_t*)args->sfb.data;
     p.sa_rs = SA.rs, p.sa_ks = SA.cs, p.sa_bs = SA.t->layout.rank == 3 ? SA.bs : 0;
@@ -421,8 +432,8 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
     if (la != sl::LOAD_KVEC || lb != sl::LOAD_KVEC)
       return fail(SL_ERR_LAYOUT,
                   "MXFP8 operands must be K-contiguous with 16-byte aligned rows and K %% 16 == 0");
-    if ((M - 1) * SA.rs + (kb - 1) * SA.cs >= lim || (N - 1) * SB.rs + (kb - 1) * SB.cs >= lim)
-      return fail(SL_ERR_SHAPE, "scale tensors span more than 2^31 bytes");
+    if (!scale_span_ok(SA) || !scale_span_ok(SB))
+      return fail(SL_ERR_SHAPE, "a 256-row tile of a scale tensor spans 2^31 bytes or more");
     // The 8-wave kernel copies one dword of scales per row and K-tile: the
     // scale rows must be K-contiguous, 4-byte aligned, and hold a multiple
     // of four blocks.

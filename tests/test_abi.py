@@ -453,10 +453,11 @@ def test_mxfp6_plan(api):
 
 
 def test_size_limits(api):
-    """Dimensions past 2^31 - 1 and packed operands spanning 2^31 bytes or
-    more are SL_ERR_SHAPE before any HIP call; a 16-bit operand has no
-    whole-span limit (its tiles are addressed from their own bases), only a
-    256-row tile must fit 2^31 bytes for the vector loaders."""
+    """Dimensions past 2^31 - 1 are SL_ERR_SHAPE before any HIP call.  An
+    operand has no whole-span limit (every kernel addresses a tile from its
+    own first row with 64-bit pointers): only a 256-row tile must span less
+    than 2^31 bytes, for the vector loaders of 16-bit operands (else the
+    element loader) and for packed and scale operands (else SL_ERR_SHAPE)."""
     big = 1 << 31
     assert err(api, rowmajor(BASE_A, (big, 64)), rowmajor(BASE_B, (64, 64)), None,
                (BASE_D, 1, (big, 64), (64, 1))) == "SL_ERR_SHAPE"
@@ -470,12 +471,23 @@ def test_size_limits(api):
     p = plan(api, (BASE_A, 1, (512, 64), (1 << 23, 1)), rowmajor(BASE_B, (256, 64)), None,
              rowmajor(BASE_D, (512, 256)))
     assert p["a_load"] == 2
-    # packed E2M1: the operand's span must stay below 2^31 bytes
+    # packed E2M1: a 2 GiB operand and its 8 MiB of scales plan
     E2, E8 = 6, 4
-    M, K = 1 << 18, 16384  # 2 GiB of packed data
-    assert err(api, (BASE_A, E2, (M, K), (K, 1)), (BASE_B, E2, (256, K), (K, 1)), None,
-               rowmajor(0x1000000000, (M, 256)), (BASE_C, E8, (M, K // 32), (K // 32, 1)),
-               (0x2000000000, E8, (256, K // 32), (K // 32, 1)), block_k=32) == "SL_ERR_SHAPE"
+    M, K = 1 << 18, 16384
+    sa = (BASE_C, E8, (M, K // 32), (K // 32, 1))
+    sb = (0x2000000000, E8, (256, K // 32), (K // 32, 1))
+    p = plan(api, (BASE_A, E2, (M, K), (K, 1)), (BASE_B, E2, (256, K), (K, 1)), None,
+             rowmajor(0x1000000000, (M, 256)), sa, sb, block_k=32)
+    assert p["kernel"] == api.K_MXFP4
+    # ... but not rows 32 MiB apart: one 256-row tile would span 8 GiB
+    rs = 1 << 26
+    assert err(api, (BASE_A, E2, (512, K), (rs, 1)), (BASE_B, E2, (256, K), (K, 1)), None,
+               rowmajor(0x1000000000, (512, 256)), (BASE_C, E8, (512, K // 32), (K // 32, 1)), sb,
+               block_k=32) == "SL_ERR_SHAPE"
+    # nor scale rows 16 MiB apart
+    assert err(api, (BASE_A, E2, (512, K), (K, 1)), (BASE_B, E2, (256, K), (K, 1)), None,
+               rowmajor(0x1000000000, (512, 256)), (BASE_C, E8, (512, K // 32), (1 << 24, 1)), sb,
+               block_k=32) == "SL_ERR_SHAPE"
 
 
 def test_mxfp4_plan(api):

@@ -606,6 +606,35 @@ def test_mxfp4_exact_parity(api, case):
     assert mism == 0, f"{mism} elements differ"
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp6"])
+def test_packed_operand_spanning_3gib(api, fmt):
+    """A packed operand whose 512 rows sit 6 MiB apart spans 3 GiB, past the
+    32-bit byte range of one buffer resource, while each 256-row tile spans
+    1.5 GiB: the kernels address every tile from its own first row."""
+    import torch
+    h = H()
+    M, N, K = 512, 256, 512
+    row_bytes = 6 << 20
+    if fmt == "mxfp4":
+        w = I.mxfp4_workload("mxfp4_span", M, N, K, seed=31, exact=True)
+        per_row = K // 2
+    else:
+        w = I.mxfp6_workload("mxfp6_span", M, N, K, seed=32, kind="e2m3", exact=True)
+        per_row = K // 4 * 3
+    a_rows = np.ascontiguousarray(w.a.storage).reshape(M, per_row)
+    buf = torch.empty((M, row_bytes), dtype=torch.uint8, device="cuda")
+    buf[:, :per_row] = torch.from_numpy(a_rows).cuda()
+    if fmt == "mxfp4":
+        a = buf.view(torch.float4_e2m1fn_x2).as_strided((M, K // 2), (row_bytes, 1))
+    else:
+        a = api.PackedTensor(buf.view(-1), api.SL_F6_E2M3, (M, K), (row_bytes // 3 * 4, 1))
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    api.gemm(a, I.to_device(w.b), None, out=out, sfa=I.to_device(w.sfa), sfb=I.to_device(w.sfb), block_k=32)
+    torch.cuda.synchronize()
+    d_ref, _, _ = h.oracle_full(w)
+    assert np.array_equal(h.d_codes(out), d_ref[0])
+
+
 def test_mxfp4_sampled_8192(api):
     _sampled(api, I.mxfp4_workload("mxfp4_8192", 8192, 8192, 8192, seed=7), n=1500)
 
