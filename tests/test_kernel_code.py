@@ -34,7 +34,8 @@ KERNELS = {
     for d, dt in ((0, "fp16"), (1, "bf16")) for r, ep in ((1, "rows"), (0, "quads"))
 }
 KERNELS.update({
-    f"fp16_mn{al}{bl}_{ep}": (F16.format(d=0, r=r, al=al, bl=bl, bn=256), 128, 32)
+    f"{dt}_mn{al}{bl}_{ep}": (F16.format(d=d, r=r, al=al, bl=bl, bn=256), 128, 32)
+    for d, dt in ((0, "fp16"), (1, "bf16"))
     for al, bl in ((3, 0), (0, 3), (3, 3)) for r, ep in ((1, "rows"), (0, "quads"))
 })
 KERNELS.update({f"{dt}_256x192": (F16.format(d=d, r=0, al=0, bl=0, bn=192), 96, 24) for d, dt in ((0, "fp16"), (1, "bf16"))})
