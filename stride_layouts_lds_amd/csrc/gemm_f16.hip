@@ -339,8 +339,12 @@ __device__ __forceinline__ void mfma_acc(floatx4& c, const half8& a, const half8
 // slice 1 on set 1, copy of B(t+1) into A(t-1)'s slot; (2) slice 0 on set
 // 0, reads of slice 1 into set 1, copy of A(t+2) into B(t-1)'s slot; (3)
 // the first half of slice 1; barrier.  Each copy has at least one K-tile of
-// compute to land; at the barrier ending tile t only A(t+2) may still be in
-// flight.
+// compute to land; at the barrier ending tile t only A(t+2) (and the C line
+// load issued just before it) may still be in flight.  In the last four
+// K-tiles every lane also loads one 128-byte line of the wave's C block
+// (4 bytes into LDS bytes that A(t+2)'s first copy overwrites next), so the
+// epilogue's C reads find C in L2 or the Infinity Cache: all CUs finish
+// their tiles together, and C read then from HBM is a burst at the end.
 template <int SHIFT, int DT, bool ROWS, int ALOAD = LOAD_KVEC, int BLOAD = LOAD_KVEC, int BN = 256>
 __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p) {
   constexpr int BM = 256, FM = 8, FN = BN / 32;
@@ -382,6 +386,19 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
   constexpr int NR = FN + FM;  // fragment reads per slice (at most 16)
   constexpr int NH = 4 * FN;   // MFMAs in half a slice
 
+  // C of this wave's block, pulled into the caches during the last four
+  // K-tiles (one dword per 128-byte line, a line per lane): the epilogue's
+  // C reads then hit L2 / the Infinity Cache instead of HBM
+  const bool pf_on = (p.flags & F_HAS_C) && (p.flags & F_C_VEC);
+  const int32_t pf_rows = rows_a - a_row0 < 128 ? rows_a - a_row0 : 128;
+  const int32_t pf_cols = rows_b - b_row0 < BN / 2 ? rows_b - b_row0 : BN / 2;
+  const uint16_t* pf_base = (const uint16_t*)p.c + (pf_on ? tc.batch * p.c_bs + (m0 + a_row0) * p.c_rs + n0 + b_row0 : 0);
+  const __amdgpu_buffer_rsrc_t pf_rsrc =
+      make_rsrc(pf_base, pf_on && pf_rows > 0 && pf_cols > 0 ? (uint32_t)(((pf_rows - 1) * p.c_rs + pf_cols) * 2) : 0u);
+  const int32_t pf_r = lane >> 1, pf_c = 64 * (lane & 1);
+  const uint32_t pf_off = (uint32_t)((pf_r * p.c_rs + pf_c) * 2);
+  const uint32_t pf_step = (uint32_t)(32 * p.c_rs * 2);
+
   la.issue(kt(0), slot(0));
   lb.issue(kt(0), slot(1));
   la.issue(kt(1), slot(2));
@@ -416,6 +433,15 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       if (g < NR) read(cA, cB, g, 1, fa1, fb1);
+      if (g == 0) {
+        // one C line per lane into the bytes A(t+2)'s first copy overwrites
+        // next (loads return in order); out of range before the last four
+        // K-tiles, so the count of loads in flight stays fixed
+        const int32_t k = t - (T - 4);
+        const bool in = k >= 0 && 32 * k + pf_r < pf_rows && pf_c < pf_cols;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pf_rsrc, (lds_void_t*)(slot(s4) + wave * 1024), 4,
+                                                 in ? pf_off + (uint32_t)k * pf_step : kOutOfRange, 0, 0, 0);
+      }
       if (g & 1) la.issue_one(kt(t + 2), slot(s4), g >> 1);
 #pragma unroll
       for (int e = g * 2 * NH / 16; e < (g + 1) * 2 * NH / 16; ++e) {
@@ -429,7 +455,8 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
     for (int i = 0; i < FM / 2; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) mfma_acc<DT>(acc[i][j], fb1[j], fa1[i]);
-    wait_vmem_n<LOADS>();
+    // in flight after this: the C line load and A(t+2)'s copies
+    wait_vmem_n<LOADS + 1>();
     phase_barrier();
     sa = sa + 2 >= 5 ? sa - 3 : sa + 2;
   } while (++t < T);
