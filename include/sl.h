@@ -36,13 +36,14 @@
  *    address range with A, B, C or the scales returns SL_ERR_ALIAS.
  *  - M == 0 or N == 0 (or batch == 0) is a no-op returning SL_OK.  K == 0
  *    gives D = C (or D = 0).
- *  - Ownership: the caller owns every buffer and sl_gemm() keeps no pointer
- *    after it returns.  The one allocation the library makes is the fp32
- *    workspace of a split-K plan (sl_plan.split_k > 1): it comes from a
- *    library-private stream-ordered pool on the current device and is
- *    allocated and freed on `stream` around the two kernels (so calls on
- *    different streams never share one); the pool keeps freed memory for
- *    reuse until the process ends.  Its failure returns SL_ERR_NOMEM.
+ *  - Ownership: the caller owns every buffer, the library allocates no
+ *    device memory, and sl_gemm() keeps no pointer after it returns.  A
+ *    split-K plan (sl_plan.split_k > 1) needs an fp32 workspace of
+ *    sl_plan.workspace_bytes (also given by sl_gemm_workspace_bytes()),
+ *    which the caller passes in sl_gemm_args.workspace: device memory,
+ *    16-byte aligned, overlapping no operand, and not used by anything
+ *    else until the call's kernels have finished on `stream`.  Plans
+ *    without a split ignore the workspace fields.
  *  - Execution: validation runs on the host before any HIP call; a failure
  *    returns a negative sl_status and sets the thread-local message.  On
  *    success the kernel is launched asynchronously on `stream` (a
@@ -65,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SL_ABI_VERSION 1
+#define SL_ABI_VERSION 2
 
 typedef enum {
   SL_F16 = 1,     /* IEEE binary16 */
@@ -91,8 +92,7 @@ typedef enum {
   SL_ERR_ALIAS = -6,  /* D overlaps an input (other than C == D exactly) */
   SL_ERR_ARCH = -7,   /* the current device is not gfx950 */
   SL_ERR_LAUNCH = -8, /* the HIP runtime reported an error */
-  SL_ERR_ARG = -9,    /* an invalid enum or query argument */
-  SL_ERR_NOMEM = -10  /* the split-K workspace could not be allocated */
+  SL_ERR_ARG = -9     /* an invalid enum or query argument */
 } sl_status;
 
 /* A shape:stride layout S[(shape):(stride)], counted in elements. */
@@ -117,6 +117,9 @@ typedef struct {
   sl_tensor sfa;   /* (batch?, M, ceil(K/block_k)) e8m0 (MXFP8) or f8_e4m3 (NVFP4) */
   sl_tensor sfb;   /* (batch?, N, ceil(K/block_k)) same dtype as sfa       */
   int32_t block_k; /* 32 for MXFP8, 16 for NVFP4; ignored for f16 / bf16   */
+  void* workspace;          /* device memory for a split-K plan's fp32 partial
+                               sums (NULL when the plan has no split) */
+  int64_t workspace_bytes;  /* its size in bytes */
 } sl_gemm_args;
 
 /* What sl_gemm would launch for these arguments (host only, no HIP call). */
@@ -141,11 +144,13 @@ typedef struct {
   int32_t b_load;     /* same, for B */
   int32_t tile_m, tile_n, tile_k;
   int32_t threads;    /* per workgroup */
-  int32_t split_k;    /* K partitions (1: none); > 1 adds a workspace of
-                         split_k * batch * m * n fp32 and a reduction kernel */
+  int32_t split_k;    /* K partitions (1: none); > 1 needs a workspace of
+                         split_k * batch * m * n fp32 and adds a reduction
+                         kernel */
   int64_t workgroups; /* total workgroups launched */
   int32_t lds_bytes;  /* LDS per workgroup */
   int64_t batch, m, n, k;
+  int64_t workspace_bytes; /* bytes of workspace sl_gemm needs (0: none) */
 } sl_plan;
 
 /*
@@ -169,13 +174,24 @@ typedef struct {
  * span fewer than 2^31 bytes for the vector loaders of 16-bit operands
  * (else the slower element loader runs), and for packed 4/6-bit data and
  * scale tensors (else SL_ERR_SHAPE).
+ * A split-K plan reads args->workspace: NULL returns SL_ERR_NULL, fewer
+ * than the plan's workspace bytes SL_ERR_SHAPE, an address not on a 16-byte
+ * boundary SL_ERR_ALIGN, and a range overlapping an operand SL_ERR_ALIAS,
+ * all before any HIP call.
  * `stream` is a hipStream_t.  Asynchronous; see Conventions.
  */
 sl_status sl_gemm(const sl_gemm_args* args, void* stream);
 
 /* Validation and kernel selection only: fills *plan, launches nothing and
- * makes no HIP call.  Same status codes as sl_gemm. */
+ * makes no HIP call.  Same status codes as sl_gemm, except that the
+ * workspace fields are not checked. */
 sl_status sl_gemm_plan(const sl_gemm_args* args, sl_plan* plan);
+
+/* Bytes of workspace sl_gemm needs for these arguments (0 when the plan has
+ * no K-split), from the same validation and kernel selection as
+ * sl_gemm_plan; host only.  Errors as sl_gemm_plan, SL_ERR_NULL for a NULL
+ * `bytes`. */
+sl_status sl_gemm_workspace_bytes(const sl_gemm_args* args, int64_t* bytes);
 
 /* Static text for a status code (never NULL). */
 const char* sl_status_string(int32_t status);

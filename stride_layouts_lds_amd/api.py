@@ -19,12 +19,11 @@ LIB_PATH = os.path.join(HERE, "libstride_layouts_lds.so")
 SL_F16, SL_F32, SL_F8_E4M3, SL_E8M0, SL_BF16, SL_F4_E2M1, SL_F6_E2M3, SL_F6_E3M2 = 1, 2, 3, 4, 5, 6, 7, 8
 K_F16, K_F16_GENERIC, K_MX, K_MX_W8, K_NVFP4, K_MXFP4, K_MXFP6, K_MX_W4R = 1, 2, 3, 4, 5, 6, 7, 8
 STATUS = {0: "SL_OK", -1: "SL_ERR_NULL", -2: "SL_ERR_DTYPE", -3: "SL_ERR_SHAPE", -4: "SL_ERR_LAYOUT",
-          -5: "SL_ERR_ALIGN", -6: "SL_ERR_ALIAS", -7: "SL_ERR_ARCH", -8: "SL_ERR_LAUNCH", -9: "SL_ERR_ARG",
-          -10: "SL_ERR_NOMEM"}
+          -5: "SL_ERR_ALIGN", -6: "SL_ERR_ALIAS", -7: "SL_ERR_ARCH", -8: "SL_ERR_LAUNCH", -9: "SL_ERR_ARG"}
 
 # every symbol include/sl.h declares
-EXPORTS = ["sl_gemm", "sl_gemm_plan", "sl_status_string", "sl_last_error_message", "sl_abi_version",
-           "sl_query_fragment_map", "sl_query_lds_map", "sl_query_fragment_addresses", "sl_probe_mfma",
+EXPORTS = ["sl_gemm", "sl_gemm_plan", "sl_gemm_workspace_bytes", "sl_status_string", "sl_last_error_message",
+           "sl_abi_version", "sl_query_fragment_map", "sl_query_lds_map", "sl_query_fragment_addresses", "sl_probe_mfma",
            "sl_probe_lds", "sl_layout_op", "sl_describe_plan"]
 
 # sl_layout_op operations (include/sl.h)
@@ -45,7 +44,8 @@ class sl_tensor(ctypes.Structure):
 
 class sl_gemm_args(ctypes.Structure):
     _fields_ = [("a", sl_tensor), ("b", sl_tensor), ("c", sl_tensor), ("d", sl_tensor), ("sfa", sl_tensor),
-                ("sfb", sl_tensor), ("block_k", ctypes.c_int32)]
+                ("sfb", sl_tensor), ("block_k", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_int64)]
 
 
 class sl_plan(ctypes.Structure):
@@ -53,7 +53,7 @@ class sl_plan(ctypes.Structure):
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("split_k", ctypes.c_int32), ("workgroups", ctypes.c_int64),
                 ("lds_bytes", ctypes.c_int32), ("batch", ctypes.c_int64), ("m", ctypes.c_int64),
-                ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
 
 class SLError(RuntimeError):
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.sl_gemm.argtypes = [P(sl_gemm_args), vp]
         L.sl_gemm_plan.restype = i32
         L.sl_gemm_plan.argtypes = [P(sl_gemm_args), P(sl_plan)]
+        L.sl_gemm_workspace_bytes.restype = i32
+        L.sl_gemm_workspace_bytes.argtypes = [P(sl_gemm_args), P(i64)]
         L.sl_status_string.restype = ctypes.c_char_p
         L.sl_status_string.argtypes = [i32]
         L.sl_last_error_message.restype = ctypes.c_char_p
@@ -165,13 +167,24 @@ def tensor_desc(x, dtype: Optional[int] = None) -> sl_tensor:
     return desc(x.data_ptr(), _torch_dtype_code(x, dtype), tuple(x.shape), tuple(x.stride()))
 
 
-def make_args(a, b, c=None, d=None, sfa=None, sfb=None, block_k: int = 32) -> sl_gemm_args:
-    """Arguments from descriptors (sl_tensor) or torch tensors."""
+def make_args(a, b, c=None, d=None, sfa=None, sfb=None, block_k: int = 32, workspace=None) -> sl_gemm_args:
+    """Arguments from descriptors (sl_tensor) or torch tensors; ``workspace``
+    is a device tensor (its bytes) or None."""
     args = sl_gemm_args()
     for name, v in (("a", a), ("b", b), ("c", c), ("d", d), ("sfa", sfa), ("sfb", sfb)):
         setattr(args, name, v if isinstance(v, sl_tensor) else tensor_desc(v))
     args.block_k = block_k
+    set_workspace(args, workspace)
     return args
+
+
+def set_workspace(args: sl_gemm_args, workspace) -> None:
+    """Point args at a device tensor's bytes as the split-K workspace (None: none)."""
+    if workspace is None:
+        args.workspace, args.workspace_bytes = None, 0
+    else:
+        args.workspace = workspace.data_ptr() or None
+        args.workspace_bytes = workspace.numel() * workspace.element_size()
 
 
 # ---------------------------------------------------------------------------
@@ -185,24 +198,47 @@ def sl_gemm(args: sl_gemm_args, stream: Optional[int] = None) -> None:
     _check(lib().sl_gemm(ctypes.byref(args), ctypes.c_void_p(stream)))
 
 
+def sl_gemm_workspace_bytes(args: sl_gemm_args) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().sl_gemm_workspace_bytes(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def workspace_for(args: sl_gemm_args, device=None):
+    """A torch uint8 device tensor of the workspace bytes the plan needs
+    (None when it needs none)."""
+    n = sl_gemm_workspace_bytes(args)
+    if n == 0:
+        return None
+    import torch
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
 def sl_gemm_plan(args: sl_gemm_args) -> dict:
     p = sl_plan()
     _check(lib().sl_gemm_plan(ctypes.byref(args), ctypes.byref(p)))
     return {f: getattr(p, f) for f, _ in sl_plan._fields_}
 
 
-def gemm(a, b, c=None, out=None, sfa=None, sfb=None, block_k: int = 32, stream: Optional[int] = None):
+def gemm(a, b, c=None, out=None, sfa=None, sfb=None, block_k: int = 32, stream: Optional[int] = None,
+         workspace=None):
     """D = A B^T + C on torch tensors (any strides).  ``a``: (batch?, M, K)
     fp16, bf16 or float8_e4m3fn; ``b``: (batch?, N, K); ``c``: (batch?, M, N)
     of D's dtype (bf16 for bf16 operands, else fp16) or None; ``sfa``/``sfb``: float8_e8m0fnu scales (batch?, rows, K/32) for
-    the MX form.  Returns ``out`` (allocated by torch if None)."""
+    the MX form.  A split-K plan's workspace is ``workspace`` (a device
+    tensor) or, when None, a torch allocation of the size the library asks
+    for.  Returns ``out`` (allocated by torch if None)."""
     import torch
     if out is None:
         batch = max(x.shape[0] if x is not None and x.dim() == 3 else 0 for x in (a, b, c))
         shape = (a.shape[-2], b.shape[-2]) if batch == 0 else (batch, a.shape[-2], b.shape[-2])
         out = torch.empty(shape, dtype=torch.bfloat16 if a.dtype == torch.bfloat16 else torch.float16,
                           device=a.device)
-    sl_gemm(make_args(a, b, c, out, sfa, sfb, block_k), stream)
+    args = make_args(a, b, c, out, sfa, sfb, block_k)
+    if workspace is None:
+        workspace = workspace_for(args, out.device)
+    set_workspace(args, workspace)
+    sl_gemm(args, stream)
     return out
 
 

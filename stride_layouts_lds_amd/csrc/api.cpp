@@ -130,6 +130,9 @@ struct Plan {
   bool mx;
   bool empty;
   size_t ws_bytes;  // split-K partial sums (0: none)
+  // byte ranges of the operands with data, for the workspace overlap check
+  uintptr_t lo[6], hi[6];
+  int32_t nranges;
 };
 
 int32_t env_int(const char* name, int32_t dflt) {
@@ -295,6 +298,12 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   if (!injective(D, batch)) return fail(SL_ERR_LAYOUT, "d's strides map distinct elements to one address");
   uintptr_t dlo, dhi;
   byte_range(D, batch, &dlo, &dhi);
+  P.nranges = 0;
+  for (int i = 0; i < 6; ++i) {
+    if (!all[i] || !all[i]->t->data || ((i <= 1 || i >= 4) && K == 0)) continue;
+    byte_range(*all[i], batch, &P.lo[P.nranges], &P.hi[P.nranges]);
+    ++P.nranges;
+  }
   for (int i = 0; i < 6; ++i) {
     if (!all[i] || i == 3 || !all[i]->t->data) continue;
     if (i == 2 && args->c.data == args->d.data && same_layout(args->c, args->d)) continue;
@@ -551,6 +560,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.pub.split_k = p.splits;
   P.pub.workgroups = total;
   P.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)M * (size_t)N * sizeof(float) : 0;
+  P.pub.workspace_bytes = (int64_t)P.ws_bytes;
   P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * P.pub.tile_k * (mx && !nvfp4 ? 1 : 2);
   if (P.pub.kernel == sl::K_MXFP4 || P.pub.kernel == sl::K_MXFP6)
     P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * 128 + 2 * (ts.bm + ts.bn) * 16;
@@ -562,32 +572,21 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   return SL_OK;
 }
 
-// The library's stream-ordered memory pool on the current device (split-K
-// workspaces come from it and go back to it on the launch stream, so calls
-// on different streams never share one).  It keeps freed memory for reuse
-// until the process ends.
-sl_status workspace_pool(hipMemPool_t* out) {
-  static std::mutex mu;
-  static hipMemPool_t pools[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(SL_ERR_LAUNCH, "hipGetDevice failed");
-  if (dev < 0 || dev >= 64) return fail(SL_ERR_ARCH, "device index %d out of range", dev);
-  std::lock_guard<std::mutex> g(mu);
-  if (!pools[dev]) {
-    hipMemPoolProps props;
-    memset(&props, 0, sizeof props);
-    props.allocType = hipMemAllocationTypePinned;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = dev;
-    hipMemPool_t pool;
-    hipError_t e = hipMemPoolCreate(&pool, &props);
-    if (e != hipSuccess) return fail(SL_ERR_NOMEM, "hipMemPoolCreate: %s", hipGetErrorString(e));
-    uint64_t keep = UINT64_MAX;
-    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-    if (e != hipSuccess) return fail(SL_ERR_NOMEM, "hipMemPoolSetAttribute: %s", hipGetErrorString(e));
-    pools[dev] = pool;
-  }
-  *out = pools[dev];
+// The caller's split-K workspace: present, large enough, 16-byte aligned
+// (the partial sums are stored 16 bytes at a time) and apart from every
+// operand (the reduction reads it while writing D).
+sl_status check_workspace(const sl_gemm_args* args, const Plan& P) {
+  if (!P.ws_bytes) return SL_OK;
+  if (!args->workspace)
+    return fail(SL_ERR_NULL, "the plan splits K %d ways and needs a workspace of %zu bytes; workspace is NULL",
+                P.pub.split_k, P.ws_bytes);
+  if (args->workspace_bytes < 0 || (uint64_t)args->workspace_bytes < (uint64_t)P.ws_bytes)
+    return fail(SL_ERR_SHAPE, "workspace of %lld bytes, the plan needs %zu", (long long)args->workspace_bytes,
+                P.ws_bytes);
+  const uintptr_t lo = (uintptr_t)args->workspace, hi = lo + P.ws_bytes;
+  if (lo % 16 != 0) return fail(SL_ERR_ALIGN, "workspace is not on a 16-byte boundary");
+  for (int32_t i = 0; i < P.nranges; ++i)
+    if (P.lo[i] < hi && lo < P.hi[i]) return fail(SL_ERR_ALIAS, "workspace overlaps an operand");
   return SL_OK;
 }
 
@@ -673,7 +672,6 @@ const char* sl_status_string(int32_t s) {
     case SL_ERR_ARCH: return "device is not gfx950";
     case SL_ERR_LAUNCH: return "HIP launch error";
     case SL_ERR_ARG: return "invalid argument";
-    case SL_ERR_NOMEM: return "device memory for a workspace could not be obtained";
     default: return "unknown status";
   }
 }
@@ -686,11 +684,21 @@ sl_status sl_gemm_plan(const sl_gemm_args* args, sl_plan* plan) {
   return SL_OK;
 }
 
+sl_status sl_gemm_workspace_bytes(const sl_gemm_args* args, int64_t* bytes) {
+  if (!bytes) return fail(SL_ERR_NULL, "bytes is NULL");
+  Plan P;
+  const sl_status s = plan_gemm(args, &P);
+  if (s != SL_OK) return s;
+  *bytes = P.empty ? 0 : (int64_t)P.ws_bytes;
+  return SL_OK;
+}
+
 sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
   Plan P;
   sl_status s = plan_gemm(args, &P);
   if (s != SL_OK) return s;
   if (P.empty) return SL_OK;
+  if ((s = check_workspace(args, P)) != SL_OK) return s;
   if ((s = check_arch()) != SL_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
@@ -699,17 +707,9 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
   } else if (P.mx) {
     e = sl::launch_gemm_mx(P.p, P.tile, st);
   } else if (P.ws_bytes) {
-    hipMemPool_t pool;
-    if ((s = workspace_pool(&pool)) != SL_OK) return s;
-    void* ws = nullptr;
-    e = hipMallocFromPoolAsync(&ws, P.ws_bytes, pool, st);
-    if (e != hipSuccess)
-      return fail(SL_ERR_NOMEM, "split-K workspace of %zu bytes: %s", P.ws_bytes, hipGetErrorString(e));
-    P.p.ws = (float*)ws;
+    P.p.ws = (float*)args->workspace;
     e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
     if (e == hipSuccess) e = sl::launch_splitk_reduce(P.p, st);
-    const hipError_t ef = hipFreeAsync(ws, st);
-    if (e == hipSuccess) e = ef;
   } else {
     e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
   }

@@ -81,6 +81,27 @@ def sample_points(w: Workload, n: int, seed: int = 0) -> np.ndarray:
     return np.concatenate(pts).astype(np.int64)
 
 
+def tile_points(w: Workload, tile: int = 256, seed: int = 0, max_batches: int = 8) -> np.ndarray:
+    """Every row and every column of every tile x tile block of the output,
+    at least once: in block (tm, tn), of r rows and c columns inside the
+    output, the points (tm*tile + i % r, tn*tile + p(i % c)) for i below
+    max(r, c) and a random permutation p, over up to max_batches batches (the first, the last and
+    random ones between); plus sample_points' edges.  As (batch, m, n)."""
+    rng = np.random.default_rng(seed)
+    B, M, N = w.batch, w.M, w.N
+    bs = sorted({0, B - 1} | set(rng.integers(0, B, max(0, max_batches - 2)).tolist())) if B > 0 else []
+    out = []
+    for b in bs:
+        for tm in range(0, M, tile):
+            for tn in range(0, N, tile):
+                r, c = min(tile, M - tm), min(tile, N - tn)
+                i = np.arange(max(r, c))
+                m, n = tm + i % r, tn + rng.permutation(c)[i % c]
+                out.append(np.stack([np.full(i.size, b), m, n], 1))
+    out.append(sample_points(w, 0, seed))
+    return np.concatenate(out).astype(np.int64)
+
+
 def assert_within_bound(d: np.ndarray, d_ref: np.ndarray, absum: np.ndarray, what: str, bf16: bool = False) -> None:
     bad, wi, wr = OG.check(d, d_ref, absum, bf16=bf16)
     if bad:

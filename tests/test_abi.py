@@ -286,6 +286,41 @@ def test_plan_split_k_for_skinny_outputs(api):
     assert p["split_k"] == 1
 
 
+def test_split_k_workspace_is_the_callers(api):
+    """A split-K plan needs a caller workspace of splits * batch * M * N fp32:
+    the plan and sl_gemm_workspace_bytes report its size, and sl_gemm
+    rejects a missing, short, misaligned or overlapping one before any HIP
+    call (so these run without a GPU).  Unsplit plans need none."""
+    a, b, d = rowmajor(BASE_A, (8192, 8192)), rowmajor(BASE_B, (128, 8192)), rowmajor(BASE_D, (8192, 128))
+    args = api.make_args(api.desc(*a), api.desc(*b), None, api.desc(*d))
+    need = 4 * 8192 * 128 * 4
+    assert api.sl_gemm_workspace_bytes(args) == need
+    assert api.sl_gemm_plan(args)["workspace_bytes"] == need
+
+    def status(ws, nbytes):
+        args.workspace, args.workspace_bytes = ws, nbytes
+        with pytest.raises(api.SLError) as e:
+            api.sl_gemm(args, 0)
+        return e.value.name
+
+    free = 0x500000000
+    assert status(None, 0) == "SL_ERR_NULL"
+    assert status(None, need) == "SL_ERR_NULL"
+    assert status(free, need - 1) == "SL_ERR_SHAPE"
+    assert status(free, -1) == "SL_ERR_SHAPE"
+    assert status(free + 8, need) == "SL_ERR_ALIGN"
+    assert status(BASE_D - 16, need) == "SL_ERR_ALIAS"      # runs into D
+    assert status(BASE_A + 4096, need) == "SL_ERR_ALIAS"    # inside A
+    assert status(BASE_B - need + 16, need) == "SL_ERR_ALIAS"
+    sq = api.make_args(api.desc(*rowmajor(BASE_A, (4096, 4096))), api.desc(*rowmajor(BASE_B, (4096, 4096))), None,
+                       api.desc(*rowmajor(BASE_D, (4096, 4096))))
+    assert api.sl_gemm_workspace_bytes(sq) == 0 and api.sl_gemm_plan(sq)["workspace_bytes"] == 0
+    empty = api.make_args(api.desc(*rowmajor(BASE_A, (0, 64))), api.desc(*rowmajor(BASE_B, (128, 64))), None,
+                          api.desc(*rowmajor(BASE_D, (0, 128))))
+    assert api.sl_gemm_workspace_bytes(empty) == 0
+    assert api.lib().sl_gemm_workspace_bytes(None, None) == -1  # SL_ERR_NULL
+
+
 def test_m_major_tile_is_a_chunk_swizzle(api):
     """The M-major LDS tile (operands copied with M contiguous): a bijection
     onto 256 x 64 halves in which every 16-byte chunk holds 8 consecutive

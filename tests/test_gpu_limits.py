@@ -57,6 +57,8 @@ def check_sampled(api, w, n=600, split=None):
     a, b, c = h.to_device(w.a), h.to_device(w.b), h.to_device(w.c)
     out = torch.empty(w.d_shape, dtype=torch.float16, device="cuda")
     args = api.make_args(a, b, c, out)
+    ws = api.workspace_for(args)
+    api.set_workspace(args, ws)
     plan = api.sl_gemm_plan(args)
     h.log(f"{w.name}: plan {plan}")
     if split is not None:
