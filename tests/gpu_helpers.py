@@ -54,8 +54,25 @@ def _operands(w: Workload):
     return (_ora(w.a), _ora(w.b), _ora(w.c), _ora(w.sfa, True, nv), _ora(w.sfb, True, nv))
 
 
-def oracle_full(w: Workload):
-    return OG.gemm(*_operands(w), block_k=w.block_k, bf16=w.bf16)
+def oracle_full(w: Workload, max_outputs: int = 1 << 23):
+    """The oracle over every output element.  Large outputs go in bands of
+    rows of A (and of C and A's scales), one call per band with a progress
+    line, so that a long check keeps printing; each element is computed the
+    same way either way."""
+    ops = _operands(w)
+    M = w.M
+    if w.batch * M * w.N <= max_outputs or any(x is not None and not isinstance(x, np.ndarray) for x in ops):
+        return OG.gemm(*ops, block_k=w.block_k, bf16=w.bf16)
+    a, b, c, sfa, sfb = ops
+    rows = max(1, max_outputs // (w.batch * w.N))
+    band = lambda x, r0, r1: None if x is None else x[..., r0:r1, :]
+    parts = []
+    for r0 in range(0, M, rows):
+        r1 = min(M, r0 + rows)
+        parts.append(OG.gemm(band(a, r0, r1), b, band(c, r0, r1), band(sfa, r0, r1), sfb, block_k=w.block_k,
+                             bf16=w.bf16))
+        log(f"  oracle rows {r1} of {M}")
+    return tuple(np.concatenate([p[i] for p in parts], axis=-2) for i in range(3))
 
 
 def oracle_points(w: Workload, pts: np.ndarray):
