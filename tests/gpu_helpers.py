@@ -63,16 +63,22 @@ def oracle_full(w: Workload, max_outputs: int = 1 << 23):
     M = w.M
     if w.batch * M * w.N <= max_outputs or any(x is not None and not isinstance(x, np.ndarray) for x in ops):
         return OG.gemm(*ops, block_k=w.block_k, bf16=w.bf16)
-    a, b, c, sfa, sfb = ops
     rows = max(1, max_outputs // (w.batch * w.N))
-    band = lambda x, r0, r1: None if x is None else x[..., r0:r1, :]
     parts = []
     for r0 in range(0, M, rows):
         r1 = min(M, r0 + rows)
-        parts.append(OG.gemm(band(a, r0, r1), b, band(c, r0, r1), band(sfa, r0, r1), sfb, block_k=w.block_k,
-                             bf16=w.bf16))
+        parts.append(oracle_rows(w, r0, r1))
         log(f"  oracle rows {r1} of {M}")
     return tuple(np.concatenate([p[i] for p in parts], axis=-2) for i in range(3))
+
+
+def oracle_rows(w: Workload, r0: int, r1: int):
+    """The oracle over output rows [r0, r1) of every batch: the same call on
+    row bands of A, C and A's scales (numpy views; not for packed data)."""
+    a, b, c, sfa, sfb = _operands(w)
+    band = lambda x: None if x is None else x[..., r0:r1, :]
+    assert all(x is None or isinstance(x, np.ndarray) for x in (a, c, sfa)), "row bands of numpy views only"
+    return OG.gemm(band(a), b, band(c), band(sfa), sfb, block_k=w.block_k, bf16=w.bf16)
 
 
 def oracle_points(w: Workload, pts: np.ndarray):
