@@ -182,6 +182,23 @@ typedef struct {
  */
 sl_status sl_gemm(const sl_gemm_args* args, void* stream);
 
+/*
+ * sl_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same validation, plans and kernels, but a split-K plan keeps its fp32
+ * partial sums in a static device array of the library instead of the
+ * caller's workspace (args->workspace and workspace_bytes are ignored).
+ * The call allocates nothing.  The array holds SL_NO_ALLOC_SCRATCH_BYTES
+ * bytes on each GPU the library runs on and is held until the process ends;
+ * a plan needing more (sl_plan.workspace_bytes) returns SL_ERR_SHAPE before
+ * any HIP call.  Every call on one GPU shares that GPU's array and finds
+ * the previous call's contents there (every partial sum a plan reads is
+ * written by the same call first, so nothing needs clearing); calls that
+ * overlap in time on one GPU, e.g. on two streams, race on it.
+ */
+#define SL_NO_ALLOC_SCRATCH_BYTES (32LL << 20)
+sl_status sl_gemm_no_alloc(const sl_gemm_args* args, void* stream);
+
 /* Validation and kernel selection only: fills *plan, launches nothing and
  * makes no HIP call.  Same status codes as sl_gemm, except that the
  * workspace fields are not checked. */

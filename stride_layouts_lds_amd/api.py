@@ -22,7 +22,7 @@ STATUS = {0: "SL_OK", -1: "SL_ERR_NULL", -2: "SL_ERR_DTYPE", -3: "SL_ERR_SHAPE",
           -5: "SL_ERR_ALIGN", -6: "SL_ERR_ALIAS", -7: "SL_ERR_ARCH", -8: "SL_ERR_LAUNCH", -9: "SL_ERR_ARG"}
 
 # every symbol include/sl.h declares
-EXPORTS = ["sl_gemm", "sl_gemm_plan", "sl_gemm_workspace_bytes", "sl_status_string", "sl_last_error_message",
+EXPORTS = ["sl_gemm", "sl_gemm_no_alloc", "sl_gemm_plan", "sl_gemm_workspace_bytes", "sl_status_string", "sl_last_error_message",
            "sl_abi_version", "sl_query_fragment_map", "sl_query_lds_map", "sl_query_fragment_addresses", "sl_probe_mfma",
            "sl_probe_lds", "sl_layout_op", "sl_describe_plan"]
 
@@ -32,6 +32,7 @@ LA_OPS = {"parse": 0, "coalesce": 1, "composition": 2, "complement": 3, "right_i
           "logical_product": 9, "tiled_product": 10, "fragment_like": 11, "tensor_like": 12,
           "eval": 13, "size": 14, "cosize": 15}
 SL_LA_MARK_STATIC = 256
+SL_NO_ALLOC_SCRATCH_BYTES = 32 << 20  # the static scratch of sl_gemm_no_alloc (include/sl.h)
 
 
 class sl_layout(ctypes.Structure):
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
         L.sl_gemm.restype = i32
         L.sl_gemm.argtypes = [P(sl_gemm_args), vp]
+        L.sl_gemm_no_alloc.restype = i32
+        L.sl_gemm_no_alloc.argtypes = [P(sl_gemm_args), vp]
         L.sl_gemm_plan.restype = i32
         L.sl_gemm_plan.argtypes = [P(sl_gemm_args), P(sl_plan)]
         L.sl_gemm_workspace_bytes.restype = i32
@@ -196,6 +199,13 @@ def sl_gemm(args: sl_gemm_args, stream: Optional[int] = None) -> None:
         import torch
         stream = torch.cuda.current_stream().cuda_stream
     _check(lib().sl_gemm(ctypes.byref(args), ctypes.c_void_p(stream)))
+
+
+def sl_gemm_no_alloc(args: sl_gemm_args, stream: Optional[int] = None) -> None:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    _check(lib().sl_gemm_no_alloc(ctypes.byref(args), ctypes.c_void_p(stream)))
 
 
 def sl_gemm_workspace_bytes(args: sl_gemm_args) -> int:

@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstride_layouts_lds.so")
-SOURCES = ["api.cpp", "describe.cpp", "layout_algebra.cpp", "gemm_f16.hip", "gemm_mx.hip", "probes.hip"]
+SOURCES = ["api.cpp", "describe.cpp", "layout_algebra.cpp", "gemm_f16.hip", "gemm_mx.hip", "probes.hip",
+           "scratch.hip"]
 HEADERS = ["sl_maps.hpp", "sl_kernels.hpp", "sl_device.hpp", "layout_algebra.hpp", "describe.hpp"]
 ARCH = "gfx950"
 

@@ -652,6 +652,24 @@ int64_t parse_int(const char* text) {
   return v;
 }
 
+// The plan's kernels on `stream`; a split-K plan's partial sums go to `ws`.
+sl_status launch_plan(Plan& P, void* ws, hipStream_t st) {
+  hipError_t e;
+  if (P.pub.kernel == sl::K_NVFP4) {
+    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
+  } else if (P.mx) {
+    e = sl::launch_gemm_mx(P.p, P.tile, st);
+  } else if (P.ws_bytes) {
+    P.p.ws = (float*)ws;
+    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
+    if (e == hipSuccess) e = sl::launch_splitk_reduce(P.p, st);
+  } else {
+    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
+  }
+  if (e != hipSuccess) return fail(SL_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return SL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -700,21 +718,26 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream) {
   if (P.empty) return SL_OK;
   if ((s = check_workspace(args, P)) != SL_OK) return s;
   if ((s = check_arch()) != SL_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
-  if (P.pub.kernel == sl::K_NVFP4) {
-    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
-  } else if (P.mx) {
-    e = sl::launch_gemm_mx(P.p, P.tile, st);
-  } else if (P.ws_bytes) {
-    P.p.ws = (float*)args->workspace;
-    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
-    if (e == hipSuccess) e = sl::launch_splitk_reduce(P.p, st);
-  } else {
-    e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
+  return launch_plan(P, args->workspace, (hipStream_t)stream);
+}
+
+static_assert(sl::kScratchBytes == (size_t)SL_NO_ALLOC_SCRATCH_BYTES, "one scratch size");
+
+sl_status sl_gemm_no_alloc(const sl_gemm_args* args, void* stream) {
+  Plan P;
+  sl_status s = plan_gemm(args, &P);
+  if (s != SL_OK) return s;
+  if (P.empty) return SL_OK;
+  if (P.ws_bytes > sl::kScratchBytes)
+    return fail(SL_ERR_SHAPE, "the plan splits K %d ways into %zu bytes of partial sums; the static scratch holds %zu",
+                P.pub.split_k, P.ws_bytes, sl::kScratchBytes);
+  if ((s = check_arch()) != SL_OK) return s;
+  void* ws = nullptr;
+  if (P.ws_bytes) {
+    const hipError_t e = sl::scratch_address(&ws);
+    if (e != hipSuccess) return fail(SL_ERR_LAUNCH, "scratch address: %s", hipGetErrorString(e));
   }
-  if (e != hipSuccess) return fail(SL_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return SL_OK;
+  return launch_plan(P, ws, (hipStream_t)stream);
 }
 
 sl_status sl_query_fragment_map(int32_t instr, int32_t operand, int32_t* lane, int32_t* slot, int32_t* row,

@@ -120,6 +120,13 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
 hipError_t launch_splitk_reduce(const GemmParams& p, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, hipStream_t stream);
 
+// The static device scratch behind sl_gemm_no_alloc (scratch.hip): its size
+// bounds the split-K workspace that entry point can serve, and its device
+// address on the current GPU comes from scratch_address().
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_address(void** out);
+
 hipError_t launch_probe_mfma(int32_t instr, int32_t mode, float* out, int64_t cases, hipStream_t stream);
 hipError_t launch_probe_lds(int32_t mode, const void* src, const int32_t* perm, void* out,
                             hipStream_t stream);

@@ -321,6 +321,27 @@ def test_split_k_workspace_is_the_callers(api):
     assert api.lib().sl_gemm_workspace_bytes(None, None) == -1  # SL_ERR_NULL
 
 
+def test_no_alloc_rejects_plans_beyond_its_scratch(api, monkeypatch):
+    """sl_gemm_no_alloc serves a split-K plan from a static scratch of
+    SL_NO_ALLOC_SCRATCH_BYTES: a plan needing more returns SL_ERR_SHAPE
+    before any HIP call (so this runs without a GPU), whatever workspace
+    the arguments carry; the header and the binding state one size."""
+    text = open(os.path.join(ROOT, "include", "sl.h")).read()
+    assert api.SL_NO_ALLOC_SCRATCH_BYTES == eval(
+        re.search(r"#define SL_NO_ALLOC_SCRATCH_BYTES \((\d+)LL << (\d+)\)", text).expand(r"\1 << \2"))
+    monkeypatch.setenv("SL_TILE", "16")
+    monkeypatch.setenv("SL_SPLITK", "8")
+    M, N, K = 1024, 1152, 8192
+    args = api.make_args(api.desc(*rowmajor(BASE_A, (M, K))), api.desc(*rowmajor(BASE_B, (N, K))), None,
+                         api.desc(*rowmajor(BASE_D, (M, N))))
+    need = api.sl_gemm_workspace_bytes(args)
+    assert need == 8 * M * N * 4 > api.SL_NO_ALLOC_SCRATCH_BYTES
+    args.workspace, args.workspace_bytes = 0x500000000, need
+    with pytest.raises(api.SLError) as e:
+        api.sl_gemm_no_alloc(args, 0)
+    assert e.value.name == "SL_ERR_SHAPE" and "static scratch" in str(e.value)
+
+
 def test_m_major_tile_is_a_chunk_swizzle(api):
     """The M-major LDS tile (operands copied with M contiguous): a bijection
     onto 256 x 64 halves in which every 16-byte chunk holds 8 consecutive
