@@ -178,10 +178,23 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
 
   const bool mmajor = load == LOAD_MNDMA;
   // 6-bit data is counted in bits (an element is 6 of them, a row 1024)
-  const Layout tile = mmajor ? T({S(BR, 1), S(in.bk, BR)})
-                      : fp6  ? T({S(BR, 8 * RB), S(in.bk, 6)})
-                             : T({S(BR, in.bk), S(in.bk, 1)});
-  if (fp6) {
+  // the 4-wave MX kernel lays 6-bit K-tiles out as four 32-value pieces,
+  // 32 bytes apart (LoaderFP6Pieces)
+  const bool pieces = fp6 && in.ring;
+  const Layout tile = mmajor   ? T({S(BR, 1), S(in.bk, BR)})
+                      : pieces ? T({S(BR, 8 * RB), T({S(32, 6), S(in.bk / 32, 256)})})
+                      : fp6    ? T({S(BR, 8 * RB), S(in.bk, 6)})
+                               : T({S(BR, in.bk), S(in.bk, 1)});
+  if (pieces) {
+    const int b = log2i(RB / 16), sh = log2i(RB);
+    o.line(n + "_lds", tile,
+           fmt("bits: a K-tile's %d values as pieces of 32 (24 bytes) at row bytes 32q..32q+23; on rows with "
+               "bit 3 set a piece's last 8 bytes sit 8 bytes further (bit 6 of the bit offset flips with bit 7 "
+               "there), so one 16-byte and one 8-byte read fetch a fragment free of bank conflicts; byte b of "
+               "row r at r*%d + 16((b/16) ^ swz(r)) + b%%16, swz(r) = (r ^ (r>>4)&1) & %d: Swizzle<%d,4,%d> "
+               "then Swizzle<1,4,%d> on byte offsets",
+               in.bk, RB, RB / 16 - 1, b, sh - 4, sh));
+  } else if (fp6) {
     const int b = log2i(RB / 16), sh = log2i(RB);
     o.line(n + "_lds", tile,
            fmt("bits: a K-tile's %d values are the first %d bytes of a %d-byte row (the rest zero, never "
@@ -219,7 +232,10 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
               isA ? 'M' : 'N', TR, isA ? " % " : " / ", in.wm));
   const Layout lane0 = T({slots, S(F, I.rows), S(KS, (int64_t)BR * I.k)});
   o.stage(n + "_lane0", [&] { return la::composition(tile, lane0); }, "lane 0's values (the wave partition at lane 0)");
-  if (fp6)
+  if (pieces)
+    o.note(n + " fragments: one 16-byte read at row byte 32q and one 8-byte read at 32q + 16 + 8 (row bit 3) per "
+                 "lane per instruction tile, q = 2 (K slice) + lane / 32 (its 32 values, 24 bytes)");
+  else if (fp6)
     o.note(n + " fragments: one 16-byte and one 8-byte LDS read per lane per instruction tile (its 32 values, "
                  "24 bytes)");
   o.stage(n + "_frag", [&] { return la::fragment_like(la::composition(tile, T({slots, S(F, I.rows)}))); },

@@ -481,7 +481,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
   constexpr int BM = 256, BN = 256, FM = 4, FN = 4;
   constexpr int SLOT = 256 * kRowBytes;
   __shared__ __attribute__((aligned(1024))) char smem[5 * SLOT];
-  using LD = LoaderKVec<256, 256, SHIFT, 1, kRowBytes, TB>;
+  using LD = std::conditional_t<F6, LoaderFP6Pieces<256, 256, SHIFT>, LoaderKVec<256, 256, SHIFT, 1, kRowBytes, TB>>;
   constexpr int LOADS = LD::ITERS;
   static_assert(LOADS == 8, "copy layout");
 
@@ -497,8 +497,14 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
   auto bytes = [](int64_t elems) -> int64_t { return F4 ? elems / 2 : F6 ? elems / 4 * 3 : elems; };
   const char* A = (const char*)p.a + bytes(tc.batch * p.a_bs + m0 * p.a_rs);
   const char* B = (const char*)p.b + bytes(tc.batch * p.b_bs + n0 * p.b_rs);
-  LD la(A, rows_a, bytes(p.a_rs), 1, bytes(p.K), wave, lane);
-  LD lb(B, rows_b, bytes(p.b_rs), 1, bytes(p.K), wave, lane);
+  auto make_ld = [&](const char* base, int32_t rows, int64_t rs) {
+    if constexpr (F6)
+      return LD(base, rows, bytes(rs), p.K, wave, lane);
+    else
+      return LD(base, rows, bytes(rs), 1, bytes(p.K), wave, lane);
+  };
+  const LD la = make_ld(A, rows_a, p.a_rs);
+  const LD lb = make_ld(B, rows_b, p.b_rs);
   const int32_t a_row0 = wm * 128, b_row0 = wn * 128;
 
   // scale chunks of the lane's rows a_row0 + 32 i + lane % 32 (and of B)
@@ -543,20 +549,17 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
   auto slot = [&](int32_t q) { return smem + q * SLOT; };
   // fragment of k-slice ks for row block row0 (the probed operand orders:
   // E4M3 two 16-byte pieces K/2 apart; E2M1 the lane's 32 consecutive k in
-  // 16 bytes; 6-bit data its 32 consecutive k in 24 bytes)
+  // 16 bytes; 6-bit data its 32 consecutive k in 24 bytes, piece 2 ks +
+  // lane / 32 of the K-tile as LoaderFP6Pieces lays it out: one 16-byte and
+  // one 8-byte read, the same registers on every lane)
   auto rd = [&](const char* base, int32_t row0, int ks) -> Frag {
     if constexpr (F4) {
       return *(const u32x4*)(base + lds_offset(row0 + (lane & 31), 32 * ks + 16 * (lane >> 5), SHIFT));
     } else if constexpr (F6) {
-      // three 8-byte reads at lane-dependent addresses into fixed registers:
-      // assembling the 16 + 8 byte reads of the 8-wave kernel needs a
-      // lane-dependent register select, a vector-ALU write too close to
-      // the (inline-assembly) MFMA that reads it
-      const int32_t row = row0 + (lane & 31), b0 = 48 * ks + 24 * (lane >> 5);
-      const u32x2 x = *(const u32x2*)(base + lds_offset(row, b0, SHIFT));
-      const u32x2 y = *(const u32x2*)(base + lds_offset(row, b0 + 8, SHIFT));
-      const u32x2 z = *(const u32x2*)(base + lds_offset(row, b0 + 16, SHIFT));
-      return i32x6{(int)x[0], (int)x[1], (int)y[0], (int)y[1], (int)z[0], (int)z[1]};
+      const int32_t row = row0 + (lane & 31), b0 = 32 * (2 * ks + (lane >> 5));
+      const u32x4 x = *(const u32x4*)(base + lds_offset(row, b0, SHIFT));
+      const u32x2 y = *(const u32x2*)(base + lds_offset(row, b0 + 16 + 8 * ((row >> 3) & 1), SHIFT));
+      return i32x6{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1]};
     } else {
       const u32x4 lo = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 0, row0, ks, SHIFT));
       const u32x4 hi = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 1, row0, ks, SHIFT));

@@ -274,6 +274,57 @@ def test_fragment_reads_conflict_free_on_gfx950(api, variant, slots_per_piece):
     assert _gfx950_b128_passes(plain) == 8
 
 
+def _gfx950_b64_passes(addrs):
+    """Cycles of one ds_read_b64 under the behaviour measured on gfx950: 64
+    banks of 4 bytes, one pass per 32 lanes (0-31, 32-63), a pass taking as
+    many cycles as the most distinct dwords on one bank."""
+    total = 0
+    for base in (0, 32):
+        banks = {}
+        for l in range(base, base + 32):
+            for w in range(2):
+                dw = addrs[l] // 4 + w
+                banks.setdefault(dw % 64, set()).add(dw)
+        total += max(len(v) for v in banks.values())
+    return total
+
+
+def test_mxfp6_fragment_reads_conflict_free_on_gfx950():
+    """The 4-wave MX kernel's 6-bit fragments: a lane's 32 values (24 bytes,
+    piece q = 2 ks + lane / 32 of the K-tile) are one 16-byte read at row
+    byte 32q and one 8-byte read at 32q + 16 + 8 (row bit 3), through the
+    K-major LDS map (Swizzle<3,4,3> then Swizzle<1,4,7> on byte offsets).
+    Both reads take the minimum passes on every 32-row block and k-slice;
+    the earlier reads of the 24 bytes as three 8-byte pieces at 24q, 24q + 8
+    and 24q + 16 had 2-way conflicts.  The copy that fills the row puts tile
+    bytes [24q, 24q + 24) exactly where these reads find them."""
+    def lds(r, b):
+        return L.swizzle_bms(L.swizzle_bms(r * 128 + b, 3, 4, 3), 1, 4, 7)
+
+    for row0 in range(0, 256, 32):
+        for ks in range(2):
+            rows = [row0 + (l & 31) for l in range(64)]
+            q = [2 * ks + (l >> 5) for l in range(64)]
+            b128 = [lds(rows[l], 32 * q[l]) for l in range(64)]
+            b64 = [lds(rows[l], 32 * q[l] + 16 + 8 * ((rows[l] >> 3) & 1)) for l in range(64)]
+            assert _gfx950_b128_passes(b128) == 4 and _gfx950_b64_passes(b64) == 2, (row0, ks)
+            old = [_gfx950_b64_passes([lds(rows[l], 48 * ks + 24 * (l >> 5) + 8 * i) for l in range(64)])
+                   for i in range(3)]
+            assert max(old) == 4, (row0, ks, old)
+    # the copy: logical chunk c of row r holds tile bytes from 24 (c / 2) on
+    # (even c) or 24 (c / 2) + 16 - 8 (r bit 3) (odd c)
+    for r in range(32):
+        h = (r >> 3) & 1
+        row = {}
+        for c in range(8):
+            src = 24 * (c >> 1) + ((16 - 8 * h) if c & 1 else 0)
+            for x in range(16):
+                row[16 * c + x] = src + x
+        for qq in range(4):
+            got = [row[32 * qq + x] for x in range(16)] + [row[32 * qq + 16 + 8 * h + x] for x in range(8)]
+            assert got == list(range(24 * qq, 24 * qq + 24)), (r, qq)
+
+
 def test_plan_split_k_for_skinny_outputs(api):
     """An 8192 x 128 x 8192 output fills 64 tiles of 128 x 128: the planner
     splits K four ways (256 workgroups); a square 4096^3 is not split."""
