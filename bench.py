@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the strided-layout GEMM on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-vendor]
 
 A step is one call of sl_gemm over the workload's operands, already resident
 in HBM.  W untimed steps, then K steps timed between two device
@@ -20,6 +20,9 @@ bf16_8192 (the default recipe in bf16).
 
 The CPU baseline is the oracle (plain fp64 triple loop, all host cores) on a
 bounded sample of output points of the same workload, scaled to TFLOP/s.
+For context (not a baseline), the single fp16 and MXFP8 products are also
+timed through PyTorch's calls into the vendor library on the same operands
+("vendor_library" in the JSON line; --no-vendor skips it).
 """
 
 from __future__ import annotations
@@ -152,6 +155,53 @@ def cpu_baseline(w, target_s: float = 12.0):
                               "sample": f"{n1} output elements, {dt1:.1f} s on 1 thread"}}
 
 
+def vendor_timing(w, a, b, c, sfa, sfb, out, stream, reps: int = 20):
+    """The vendor library through PyTorch on the same device operands, for
+    context (not a baseline): torch.addmm / torch.mm for the single fp16
+    products with K-contiguous A and B (C + A B^T), torch._scaled_mm with
+    E8M0 block scales for MXFP8.  Average launch time over `reps` launches
+    between HIP events on the launch stream, and the relative Frobenius
+    difference of its D from the library's (`out`, which holds the
+    library's result).  None for the other workloads."""
+    import torch
+    if w.batch != 1 or a.dim() != 2 or b.dim() != 2 or a.stride(1) != 1 or b.stride(1) != 1:
+        return None
+    if w.mx and not (w.fp4 or w.fp6 or w.nvfp4) and w.block_k == 32 and w.c is None:
+        name = "torch._scaled_mm (E4M3 data, E8M0 scale per 32 K)"
+        sa, sb = sfa.view(torch.float8_e8m0fnu), sfb.view(torch.float8_e8m0fnu)
+        a8, b8 = a.view(torch.float8_e4m3fn), b.view(torch.float8_e4m3fn)
+
+        def fn():
+            return torch._scaled_mm(a8, b8.t(), scale_a=sa, scale_b=sb, out_dtype=torch.float16)
+    elif not w.mx and not w.bf16:
+        name = "torch.addmm(C, A, B^T)" if c is not None else "torch.mm(A, B^T)"
+
+        def fn():
+            return torch.addmm(c, a, b.t()) if c is not None else torch.mm(a, b.t())
+    else:
+        return None
+    try:
+        r = fn()
+        torch.cuda.synchronize()
+    except Exception as e:  # this PyTorch build has no such path
+        return {"call": name, "error": f"{type(e).__name__}: {str(e)[:200]}"}
+    ref = out.float()
+    diff = ((r.float() - ref).norm() / ref.norm().clamp_min(1e-30)).item()
+    del r
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    return {"call": name, "launches": reps, "us_per_launch": round(us, 1),
+            "tflops": round(w.flops / (us * 1e-6) / 1e12, 1), "rel_diff_from_library": float(f"{diff:.3e}")}
+
+
 def per_launch_timing(api, margs, sid, stream, reps: int) -> dict:
     """Per-launch event timings, median and best: back to back ("warm": the
     inputs may sit in the 256 MB Infinity Cache from the previous launch) and
@@ -189,6 +239,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp16_8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip timing the vendor library (through PyTorch) on the same operands")
     ap.add_argument("--per-launch", type=int, default=30,
                     help="launches for the per-launch warm and cold timings after the timed region (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -257,6 +309,7 @@ def main():
     # read from HBM, not from the Infinity Cache), so those are always timed
     reps = args.per_launch if mfma_bound else max(args.per_launch, 30)
     timing = per_launch_timing(api, margs, sid, stream, reps=reps) if reps > 0 else None
+    vendor = None if args.no_vendor else vendor_timing(w, a, b, c, sfa, sfb, out, stream)
 
     value = flop * args.steps / wall / 1e12
     # NVFP4 is decoded to fp16 and multiplied on the fp16 matrix cores;
@@ -301,6 +354,8 @@ def main():
         "roofline": roof,
         "timing": timing,
     }
+    if vendor is not None:
+        res["vendor_library"] = vendor
     if rank == 0 and not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w)
