@@ -307,6 +307,23 @@ __device__ __forceinline__ void epilogue_rows(const floatx4 (&acc)[8][8], const 
   }
 }
 
+// The ring kernel reads fragment r of a slice (rows row0 + 16 r ...) at the
+// lane's offset for r's parity plus 4096 (r / 2): with the chunk swizzle at
+// shift 0 a row's swizzle depends on its low three bits and bit 4, i.e. on
+// the lane and on r's parity when row0 is a multiple of 32.  Checked here
+// for every lane and slice at the wave rows the kernel uses.
+constexpr bool frag_offset_splits() {
+  for (int32_t row0 : {0, 96, 128})
+    for (int32_t lane = 0; lane < 64; ++lane)
+      for (int32_t ks = 0; ks < 2; ++ks)
+        for (int32_t r = 0; r < 8; ++r)
+          if (fragment_lds_offset(MFMA16_F16, lane, 0, row0 + 16 * r, ks, 0) !=
+              fragment_lds_offset(MFMA16_F16, lane, 0, row0 + 16 * (r & 1), ks, 0) + 4096 * (r >> 1))
+            return false;
+  return true;
+}
+static_assert(frag_offset_splits(), "fragment offsets split into a parity part and 4096 (r / 2)");
+
 // MFMA whose accumulator is pinned to AGPRs (the "a" constraint): a
 // 128x128 wave block needs 256 accumulator registers per lane, which only
 // the AGPR file can hold beside the operand fragments.  The statement is
@@ -345,7 +362,8 @@ __device__ __forceinline__ void mfma_acc(floatx4& c, const half8& a, const half8
 // (4 bytes into LDS bytes that A(t+2)'s first copy overwrites next), so the
 // epilogue's C reads find C in L2 or the Infinity Cache: all CUs finish
 // their tiles together, and C read then from HBM is a burst at the end.
-template <int SHIFT, int DT, bool ROWS, int ALOAD = LOAD_KVEC, int BLOAD = LOAD_KVEC, int BN = 256>
+template <int SHIFT, int DT, bool ROWS, int ALOAD = LOAD_KVEC, int BLOAD = LOAD_KVEC, int BN = 256,
+          bool KFULL = false>
 __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p) {
   constexpr int BM = 256, FM = 8, FN = BN / 32;
   constexpr int SLOT = 256 * kRowBytes;
@@ -364,6 +382,7 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
   constexpr int LOADS = decltype(la)::ITERS;    // copy instructions per A tile
   constexpr int BLOADS = decltype(lb)::ITERS;   // ... per B tile
   static_assert(LOADS == 8 && BLOADS <= 8, "copy layout");
+  static_assert(!KFULL || (ALOAD == LOAD_KVEC && BLOAD == LOAD_KVEC), "whole K-tiles: K-contiguous operands");
 
   floatx4 acc[FM][FN];
 #pragma unroll
@@ -373,15 +392,61 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
   const int32_t a_row0 = wm * 128, b_row0 = wn * (BN / 2);
   const int32_t T = p.k_tiles;  // at least 1 (the planner's condition for this kernel)
   __builtin_assume(T >= 1);
-  auto kt = [&](int32_t u) { return u < T ? u : T; };
+  // K-tile u's copies; past the last K-tile the look-ahead copies are never
+  // read: fully out of range, or with KFULL (every K-tile whole) the last
+  // K-tile again, so that every copy takes the fast path
+  auto kt = [&](int32_t u) { return u < T ? u : (KFULL ? T - 1 : T); };
   auto slot = [&](int32_t q) { return smem + q * SLOT; };
+  auto copy_a = [&](int32_t u, char* dst, int j) {
+    if constexpr (KFULL) la.issue_full(kt(u), dst, j);
+    else la.issue_one(kt(u), dst, j);
+  };
+  auto copy_b = [&](int32_t u, char* dst, int j) {
+    if constexpr (KFULL) lb.issue_full(kt(u), dst, j);
+    else lb.issue_one(kt(u), dst, j);
+  };
   half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  // Fragment reads of K-contiguous tiles from precomputed LDS addresses:
+  // fragment r of a slice sits at (lane part for r's parity and the slice)
+  // + slot base + 4096 (r / 2) (frag_offset_splits), and the bases of a
+  // K-tile are formed before the barrier that ends the previous one, so no
+  // read waits on fresh vector arithmetic.  M-major tiles read as before.
+  typedef __attribute__((address_space(3))) const half8 lds_h8;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)smem;
+  uint32_t offA[2][2], offB[2][2], bA[2][2], bB[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      offA[ks][par] = lds0 + (uint32_t)fragment_lds_offset(MFMA16_F16, lane, 0, a_row0 + 16 * par, ks, SHIFT);
+      offB[ks][par] = lds0 + (uint32_t)fragment_lds_offset(MFMA16_F16, lane, 0, b_row0 + 16 * par, ks, SHIFT);
+    }
+  auto bases = [&](int32_t qa, int32_t qb) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        bA[ks][par] = offA[ks][par] + (uint32_t)(qa * SLOT);
+        bB[ks][par] = offB[ks][par] + (uint32_t)(qb * SLOT);
+      }
+    // computed here, not next to the reads
+    asm volatile("" : "+v"(bA[0][0]), "+v"(bA[0][1]), "+v"(bA[1][0]), "+v"(bA[1][1]));
+    asm volatile("" : "+v"(bB[0][0]), "+v"(bB[0][1]), "+v"(bB[1][0]), "+v"(bB[1][1]));
+  };
   // read r of a slice's FN + FM fragment reads (B's first)
   auto read = [&](const char* cA, const char* cB, int r, int ks, half8(&fa)[FM], half8(&fb)[FN]) {
-    if (r < FN)
-      fb[r] = read_frag<BLOAD, BN, SHIFT>(cB, lane, b_row0 + 16 * r, ks);
-    else
-      fa[r - FN] = read_frag<ALOAD, BM, SHIFT>(cA, lane, a_row0 + 16 * (r - FN), ks);
+    if (r < FN) {
+      if constexpr (BLOAD == LOAD_KVEC)
+        fb[r] = *(lds_h8*)(uintptr_t)(bB[ks][r & 1] + 4096u * (uint32_t)(r >> 1));
+      else
+        fb[r] = read_frag<BLOAD, BN, SHIFT>(cB, lane, b_row0 + 16 * r, ks);
+    } else {
+      const int i = r - FN;
+      if constexpr (ALOAD == LOAD_KVEC)
+        fa[i] = *(lds_h8*)(uintptr_t)(bA[ks][i & 1] + 4096u * (uint32_t)(i >> 1));
+      else
+        fa[i] = read_frag<ALOAD, BM, SHIFT>(cA, lane, a_row0 + 16 * i, ks);
+    }
   };
   constexpr int NR = FN + FM;  // fragment reads per slice (at most 16)
   constexpr int NH = 4 * FN;   // MFMAs in half a slice
@@ -398,10 +463,21 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
   const int32_t pf_r = lane >> 1, pf_c = 64 * (lane & 1);
   const uint32_t pf_off = (uint32_t)((pf_r * p.c_rs + pf_c) * 2);
   const uint32_t pf_step = (uint32_t)(32 * p.c_rs * 2);
+  // K-tile u's C-line offset, formed a K-tile ahead of its load
+  auto pf_voff = [&](int32_t u) {
+    const int32_t k = u - (T - 4);
+    const bool in = k >= 0 && 32 * k + pf_r < pf_rows && pf_c < pf_cols;
+    uint32_t v = in ? pf_off + (uint32_t)k * pf_step : kOutOfRange;
+    asm volatile("" : "+v"(v));
+    return v;
+  };
 
-  la.issue(kt(0), slot(0));
-  lb.issue(kt(0), slot(1));
-  la.issue(kt(1), slot(2));
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) copy_a(0, slot(0), j);
+#pragma unroll
+  for (int j = 0; j < BLOADS; ++j) copy_b(0, slot(1), j);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) copy_a(1, slot(2), j);
   // the first tile's part (1) computes with zero fragments (adds nothing)
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa1[i] = half8{};
@@ -412,6 +488,11 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
 
   int32_t sa = 0;  // slot of A(t); B(t) in the next one
   int32_t t = 0;
+  bases(0, 1);
+  uint32_t pf_v = pf_voff(0);
+  // one copy of the loop body: a peeled or unswitched copy would give the
+  // accumulators a second path to the epilogue
+#pragma clang loop unroll(disable)
   do {  // T >= 1: one path into the epilogue keeps the accumulators in place
     const int32_t sb = sa == 4 ? 0 : sa + 1;
     const int32_t s3 = sa + 3 >= 5 ? sa - 2 : sa + 3, s4 = sa == 0 ? 4 : sa - 1;
@@ -421,7 +502,7 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       if (g < NR) read(cA, cB, g, 0, fa0, fb0);
-      if (!(g & 1) && g / 2 < BLOADS) lb.issue_one(kt(t + 1), slot(s3), g >> 1);
+      if (!(g & 1) && g / 2 < BLOADS) copy_b(t + 1, slot(s3), g >> 1);
 #pragma unroll
       for (int e = g * NH / 16; e < (g + 1) * NH / 16; ++e) {
         const int i = FM / 2 + e / FN, j = e % FN;
@@ -437,12 +518,9 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
         // one C line per lane into the bytes A(t+2)'s first copy overwrites
         // next (loads return in order); out of range before the last four
         // K-tiles, so the count of loads in flight stays fixed
-        const int32_t k = t - (T - 4);
-        const bool in = k >= 0 && 32 * k + pf_r < pf_rows && pf_c < pf_cols;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(pf_rsrc, (lds_void_t*)(slot(s4) + wave * 1024), 4,
-                                                 in ? pf_off + (uint32_t)k * pf_step : kOutOfRange, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pf_rsrc, (lds_void_t*)(slot(s4) + wave * 1024), 4, pf_v, 0, 0, 0);
       }
-      if (g & 1) la.issue_one(kt(t + 2), slot(s4), g >> 1);
+      if (g & 1) copy_a(t + 2, slot(s4), g >> 1);
 #pragma unroll
       for (int e = g * 2 * NH / 16; e < (g + 1) * 2 * NH / 16; ++e) {
         const int i = e / FN, j = e % FN;
@@ -455,6 +533,12 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
     for (int i = 0; i < FM / 2; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) mfma_acc<DT>(acc[i][j], fb1[j], fa1[i]);
+    // the next K-tile's read bases and C-line offset
+    {
+      const int32_t na = sa + 2 >= 5 ? sa - 3 : sa + 2;
+      bases(na, na == 4 ? 0 : na + 1);
+      pf_v = pf_voff(t + 1);
+    }
     // in flight after this: the C line load and A(t+2)'s copies
     wait_vmem_n<LOADS + 1>();
     phase_barrier();
@@ -1070,13 +1154,27 @@ hipError_t launch_pingpong(const GemmParams& p, int32_t tile, hipStream_t s) {
 }
 
 // the ring kernel (tiles 19 and 20): at least one K-tile, no K-split; the
-// row epilogue when every 256 x 256 tile is full and C and D rows allow it
+// row epilogue when every 256 x 256 tile is full and C and D rows allow it;
+// the whole-K-tile copies when both operands are K-contiguous and K is a
+// multiple of the 64-wide K-tile
 template <int DT, int AL, int BL, int BN>
 hipError_t launch_ring(const GemmParams& p, hipStream_t s) {
   if (p.k_tiles < 1 || p.splits != 1) return hipErrorInvalidValue;
   const dim3 g((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), b(256);
   const bool rows = BN == 256 && p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
                     (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
+  if constexpr (AL == LOAD_KVEC && BL == LOAD_KVEC) {
+    if (p.K % 64 == 0) {
+      if constexpr (BN == 256) {
+        if (rows) {
+          hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT, true, AL, BL, BN, true>), g, b, 0, s, p);
+          return hipGetLastError();
+        }
+      }
+      hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT, false, AL, BL, BN, true>), g, b, 0, s, p);
+      return hipGetLastError();
+    }
+  }
   if constexpr (BN == 256) {
     if (rows) {
       hipLaunchKernelGGL((gemm_f16_w4r_kernel<0, DT, true, AL, BL, BN>), g, b, 0, s, p);

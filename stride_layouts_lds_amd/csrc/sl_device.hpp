@@ -259,6 +259,9 @@ struct LoaderKVec {
   int32_t K;
   int32_t wave;
   int32_t lane;
+  // this lane's byte offset in copy j of K-tile 0 (kOutOfRange for chunks
+  // past the tile's bytes): loop-invariant, for issue_full
+  uint32_t voff[ITERS];
 
   __device__ __forceinline__ LoaderKVec(const void* base, int32_t rows_valid, int64_t rs, int64_t /*ks*/,
                                         int64_t K_, int32_t wave_, int32_t lane_) {
@@ -271,6 +274,11 @@ struct LoaderKVec {
     row0 = wave * RPI + lane / CPR;
     row_off = (uint32_t)(row0 * rs * ELEM);
     row_step = (uint32_t)(WAVES * RPI * rs * ELEM);
+#pragma unroll
+    for (int j = 0; j < ITERS; ++j) {
+      const int32_t c = (lane % CPR) ^ swz(row0 + j * WAVES * RPI, SHIFT, RB);
+      voff[j] = c < CT ? row_off + (uint32_t)j * row_step + (uint32_t)(c * 16) : kOutOfRange;
+    }
   }
 
   // one copy instruction: j-th row block of K-tile t
@@ -281,6 +289,21 @@ struct LoaderKVec {
     const uint32_t a = row_off + (uint32_t)j * row_step + (uint32_t)(c * 16) + (uint32_t)(t * TB);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16,
                                              (c < CT && t * KT + c * CE < K) ? a : kOutOfRange, 0, 0, 0);
+  }
+
+  // The same copy for a K-tile that lies wholly inside K (0 <= t and
+  // (t + 1) * KT <= K): the per-lane offset is voff[j] and the K-tile's
+  // start goes into the instruction's scalar offset, so the copy waits on
+  // no vector arithmetic (next to the MFMA stream a vector result consumed
+  // at once by a memory instruction stalls the wave).  Rows past the valid
+  // ones still read zero: their offset alone is past the resource's bytes.
+  // (The element is copied to a local first: the host compilation pass
+  // drops the launch stubs of kernels that index the member array inside
+  // the builtin's argument list.)
+  __device__ __forceinline__ void issue_full(int32_t t, char* lds, int j) const {
+    const uint32_t v = voff[j];
+    const uint32_t s = (uint32_t)(t * TB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16, v, s, 0, 0);
   }
 
   __device__ __forceinline__ void issue(int32_t t, char* lds) const {

@@ -28,17 +28,20 @@ LLVM = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin")
 # name: (symbol, MFMAs of one K-loop iteration, MFMAs after the loop).
 # 16-bit ring kernels: element type, epilogue through LDS rows or per
 # accumulator quad, loaders (K-major, or M-major direct copies), tile width
-F16 = "_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi{d}ELb{r}ELi{al}ELi{bl}ELi{bn}EEEvNS_10GemmParamsE"
+# tile width and whether every K-tile is whole (copies without per-lane masks)
+F16 = "_ZN2sl12_GLOBAL__N_119gemm_f16_w4r_kernelILi0ELi{d}ELb{r}ELi{al}ELi{bl}ELi{bn}ELb{kf}EEEvNS_10GemmParamsE"
 KERNELS = {
-    f"{dt}_{ep}": (F16.format(d=d, r=r, al=0, bl=0, bn=256), 128, 32)
+    f"{dt}_{ep}{kn}": (F16.format(d=d, r=r, al=0, bl=0, bn=256, kf=kf), 128, 32)
     for d, dt in ((0, "fp16"), (1, "bf16")) for r, ep in ((1, "rows"), (0, "quads"))
+    for kf, kn in ((0, ""), (1, "_kfull"))
 }
 KERNELS.update({
-    f"{dt}_mn{al}{bl}_{ep}": (F16.format(d=d, r=r, al=al, bl=bl, bn=256), 128, 32)
+    f"{dt}_mn{al}{bl}_{ep}": (F16.format(d=d, r=r, al=al, bl=bl, bn=256, kf=0), 128, 32)
     for d, dt in ((0, "fp16"), (1, "bf16"))
     for al, bl in ((3, 0), (0, 3), (3, 3)) for r, ep in ((1, "rows"), (0, "quads"))
 })
-KERNELS.update({f"{dt}_256x192": (F16.format(d=d, r=0, al=0, bl=0, bn=192), 96, 24) for d, dt in ((0, "fp16"), (1, "bf16"))})
+KERNELS.update({f"{dt}_256x192{kn}": (F16.format(d=d, r=0, al=0, bl=0, bn=192, kf=kf), 96, 24)
+                for d, dt in ((0, "fp16"), (1, "bf16")) for kf, kn in ((0, ""), (1, "_kfull"))})
 # NVFP4 on the ring schedule (decoding loaders, per K-tile or per pair)
 KERNELS.update({
     f"nvfp4_{pn}_{ep}": (f"_ZN2sl12_GLOBAL__N_121gemm_nvfp4_w4r_kernelILi0ELb{pr}ELb{r}EEEvNS_10GemmParamsE", 128, 32)
