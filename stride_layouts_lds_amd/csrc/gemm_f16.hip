@@ -383,6 +383,7 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
   constexpr int BLOADS = decltype(lb)::ITERS;   // ... per B tile
   static_assert(LOADS == 8 && BLOADS <= 8, "copy layout");
   static_assert(!KFULL || (ALOAD == LOAD_KVEC && BLOAD == LOAD_KVEC), "whole K-tiles: K-contiguous operands");
+  static_assert(SHIFT == 0, "the fragment addresses are split for the shift-0 swizzle");
 
   floatx4 acc[FM][FN];
 #pragma unroll

@@ -469,7 +469,32 @@ __device__ __forceinline__ void mfma_scale_acc(floatx16& c, u32x4 a, u32x4 b, ui
 // K-tile's scale bytes, shifted right by 8 (lane / 32): byte 2 (s % 2) is
 // then the lane's scale.  ROWS: the row epilogue through LDS (full tiles,
 // vector C/D).
-template <int SHIFT, bool ROWS, int FMT>
+// Lane part q (0..3) of the LDS byte address of a fragment read of the ring
+// kernel, for the 32-row block starting at row0 (shift-0 swizzle): E2M1 one
+// 16-byte read per k-slice (q = slice); 6-bit data a 16- and an 8-byte read
+// per slice (q = 2 slice + read); E4M3 two 16-byte pieces per slice (q = 2
+// slice + piece).  Block g of a wave reads at lane part + 4096 g
+// (mx_offsets_split).
+constexpr int32_t mx_lane_off(int fmt, int32_t row0, int32_t lane, int q) {
+  if (fmt == kFmtE2M1) return lds_offset(row0 + (lane & 31), 32 * q + 16 * (lane >> 5), 0);
+  if (fmt == kFmtE2M3 || fmt == kFmtE3M2) {
+    const int32_t row = row0 + (lane & 31), b0 = 32 * (2 * (q >> 1) + (lane >> 5));
+    return (q & 1) ? lds_offset(row, b0 + 16 + 8 * ((row >> 3) & 1), 0) : lds_offset(row, b0, 0);
+  }
+  return fragment_lds_offset(MFMA32_F8, lane, q & 1, row0, q >> 1, 0);
+}
+constexpr bool mx_offsets_split() {
+  for (int fmt : {(int)kFmtE4M3, (int)kFmtE2M1, (int)kFmtE2M3})
+    for (int32_t row0 : {0, 128})
+      for (int32_t lane = 0; lane < 64; ++lane)
+        for (int q = 0; q < 4; ++q)
+          for (int32_t g = 0; g < 4; ++g)
+            if (mx_lane_off(fmt, row0 + 32 * g, lane, q) != mx_lane_off(fmt, row0, lane, q) + 4096 * g) return false;
+  return true;
+}
+static_assert(mx_offsets_split(), "a 32-row block's fragment addresses are block 0's plus 4096 per block");
+
+template <int SHIFT, bool ROWS, int FMT, bool KFULL = false>
 __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p) {
   constexpr bool F4 = FMT == kFmtE2M1;
   constexpr bool F6 = FMT == kFmtE2M3 || FMT == kFmtE3M2;
@@ -484,6 +509,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
   using LD = std::conditional_t<F6, LoaderFP6Pieces<256, 256, SHIFT>, LoaderKVec<256, 256, SHIFT, 1, kRowBytes, TB>>;
   constexpr int LOADS = LD::ITERS;
   static_assert(LOADS == 8, "copy layout");
+  static_assert(SHIFT == 0, "the fragment addresses are split for the shift-0 swizzle");
 
   const int32_t lane = threadIdx.x & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -545,24 +571,53 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
   const int32_t T = p.k_tiles;  // at least 1 (the planner's condition for this kernel)
   __builtin_assume(T >= 1);
-  auto kt = [&](int32_t u) { return u < T ? u : T; };
+  // K-tile u's copies; past the last K-tile the look-ahead copies are never
+  // read: fully out of range, or with KFULL (every K-tile whole) the last
+  // K-tile again, so that every copy takes the path without vector
+  // arithmetic (issue_full)
+  auto kt = [&](int32_t u) { return u < T ? u : (KFULL ? T - 1 : T); };
   auto slot = [&](int32_t q) { return smem + q * SLOT; };
-  // fragment of k-slice ks for row block row0 (the probed operand orders:
-  // E4M3 two 16-byte pieces K/2 apart; E2M1 the lane's 32 consecutive k in
-  // 16 bytes; 6-bit data its 32 consecutive k in 24 bytes, piece 2 ks +
-  // lane / 32 of the K-tile as LoaderFP6Pieces lays it out: one 16-byte and
-  // one 8-byte read, the same registers on every lane)
-  auto rd = [&](const char* base, int32_t row0, int ks) -> Frag {
+  auto copy = [&](const LD& ld, int32_t u, char* dst, int j) {
+    if constexpr (KFULL) ld.issue_full(kt(u), dst, j);
+    else ld.issue_one(kt(u), dst, j);
+  };
+  // fragment of k-slice ks for row block g of the wave (the probed operand
+  // orders: E4M3 two 16-byte pieces K/2 apart; E2M1 the lane's 32
+  // consecutive k in 16 bytes; 6-bit data its 32 consecutive k in 24 bytes,
+  // piece 2 ks + lane / 32 of the K-tile as LoaderFP6Pieces lays it out: one
+  // 16-byte and one 8-byte read, the same registers on every lane), read at
+  // the K-tile's precomputed bases (lane part + slot) + 4096 g: the bases are
+  // formed before the barrier that ends the previous K-tile, so no read
+  // waits on fresh vector arithmetic
+  typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+  typedef __attribute__((address_space(3))) const u32x2 lds_u2;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)smem;
+  uint32_t offA[4], offB[4], bA[4], bB[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    offA[q] = lds0 + (uint32_t)mx_lane_off(FMT, a_row0, lane, q);
+    offB[q] = lds0 + (uint32_t)mx_lane_off(FMT, b_row0, lane, q);
+  }
+  auto bases = [&](int32_t qa, int32_t qb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bA[q] = offA[q] + (uint32_t)(qa * SLOT);
+      bB[q] = offB[q] + (uint32_t)(qb * SLOT);
+    }
+    asm volatile("" : "+v"(bA[0]), "+v"(bA[1]), "+v"(bA[2]), "+v"(bA[3]));
+    asm volatile("" : "+v"(bB[0]), "+v"(bB[1]), "+v"(bB[2]), "+v"(bB[3]));
+  };
+  auto rd = [&](const uint32_t(&b)[4], int g, int ks) -> Frag {
+    const uint32_t o = 4096u * (uint32_t)g;
     if constexpr (F4) {
-      return *(const u32x4*)(base + lds_offset(row0 + (lane & 31), 32 * ks + 16 * (lane >> 5), SHIFT));
+      return *(lds_u4*)(uintptr_t)(b[ks] + o);
     } else if constexpr (F6) {
-      const int32_t row = row0 + (lane & 31), b0 = 32 * (2 * ks + (lane >> 5));
-      const u32x4 x = *(const u32x4*)(base + lds_offset(row, b0, SHIFT));
-      const u32x2 y = *(const u32x2*)(base + lds_offset(row, b0 + 16 + 8 * ((row >> 3) & 1), SHIFT));
+      const u32x4 x = *(lds_u4*)(uintptr_t)(b[2 * ks] + o);
+      const u32x2 y = *(lds_u2*)(uintptr_t)(b[2 * ks + 1] + o);
       return i32x6{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1]};
     } else {
-      const u32x4 lo = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 0, row0, ks, SHIFT));
-      const u32x4 hi = *(const u32x4*)(base + fragment_lds_offset(MFMA32_F8, lane, 1, row0, ks, SHIFT));
+      const u32x4 lo = *(lds_u4*)(uintptr_t)(b[2 * ks] + o);
+      const u32x4 hi = *(lds_u4*)(uintptr_t)(b[2 * ks + 1] + o);
       return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
   };
@@ -590,9 +645,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
     __builtin_amdgcn_sched_barrier(0);
   };
   load_chunk(0, sa4, sb4);
-  la.issue(kt(0), slot(0));
-  lb.issue(kt(0), slot(1));
-  la.issue(kt(1), slot(2));
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) copy(la, 0, slot(0), j);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) copy(lb, 0, slot(1), j);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) copy(la, 1, slot(2), j);
+  bases(0, 1);
   // the first tile's part (1) computes with zero fragments (adds nothing)
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa[1][i] = Frag{}, sap[i] = 0;
@@ -608,10 +667,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
 #pragma unroll
     for (int d = 0; d < TPC; ++d) {
       const int32_t t = t0 + d;
-      const int32_t sb = sa == 4 ? 0 : sa + 1;
       const int32_t s3 = sa + 3 >= 5 ? sa - 2 : sa + 3, s4 = sa == 0 ? 4 : sa - 1;
-      const char* cA = slot(sa);
-      const char* cB = slot(sb);
 #pragma unroll
       for (int w = 0; w < SD; ++w) {
         auto pick = [](const u32x4& v, int k) -> uint32_t { return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3]; };
@@ -631,10 +687,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         if (g < 4)
-          fb[0][g] = rd(cB, b_row0 + 32 * g, 0);
+          fb[0][g] = rd(bB, g, 0);
         else
-          fa[0][g - 4] = rd(cA, a_row0 + 32 * (g - 4), 0);
-        lb.issue_one(kt(t + 1), slot(s3), g);
+          fa[0][g - 4] = rd(bA, g - 4, 0);
+        copy(lb, t + 1, slot(s3), g);
         const int i = FM / 2 + g / FN, j = g % FN;
         mfma_scale_acc<FMT, 1>(acc[i][j], fb[1][j], fa[1][i], sbp[j], sap[i]);
         __builtin_amdgcn_sched_barrier(0);
@@ -645,10 +701,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
           if (g < 4)
-            fb[(s + 1) % 2][g] = rd(cB, b_row0 + 32 * g, s + 1);
+            fb[(s + 1) % 2][g] = rd(bB, g, s + 1);
           else
-            fa[(s + 1) % 2][g - 4] = rd(cA, a_row0 + 32 * (g - 4), s + 1);
-          if (s == 0) la.issue_one(kt(t + 2), slot(s4), g);
+            fa[(s + 1) % 2][g - 4] = rd(bA, g - 4, s + 1);
+          if (s == 0) copy(la, t + 2, slot(s4), g);
           mfma_range(s_c, 2 * g, 2);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -664,6 +720,11 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
       }
       // the last slice, first half
       mfma_range(std::integral_constant<int, KS - 1>{}, 0, 8);
+      {
+        // the next K-tile's read bases
+        const int32_t na = sa + 2 >= 5 ? sa - 3 : sa + 2;
+        bases(na, na == 4 ? 0 : na + 1);
+      }
       if (d == TPC - 2)
         wait_vmem_n<LOADS + FM + FN>();
       else
@@ -774,12 +835,22 @@ hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, hipStream_t s) {
       dim3 grid((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), block(256);
       const bool rows = p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
                         (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
+      // whole K-tiles (the copies without vector arithmetic): always for the
+      // packed formats (K a multiple of 512), for E4M3 when K is a multiple
+      // of its 128-wide K-tile
       auto go = [&](auto fmt) {
         constexpr int F = decltype(fmt)::value;
-        if (rows)
-          hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, true, F>), grid, block, 0, s, p);
-        else
-          hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, false, F>), grid, block, 0, s, p);
+        if (F != kFmtE4M3 || p.K % 128 == 0) {
+          if (rows)
+            hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, true, F, true>), grid, block, 0, s, p);
+          else
+            hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, false, F, true>), grid, block, 0, s, p);
+        } else if constexpr (F == kFmtE4M3) {
+          if (rows)
+            hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, true, F>), grid, block, 0, s, p);
+          else
+            hipLaunchKernelGGL((gemm_mx_w4r_kernel<0, false, F>), grid, block, 0, s, p);
+        }
       };
       if (p.flags & F_FP4)
         go(std::integral_constant<int, kFmtE2M1>{});

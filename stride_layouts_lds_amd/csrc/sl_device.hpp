@@ -344,6 +344,7 @@ struct LoaderFP6Pieces {
   int32_t K;
   int32_t wave;
   int32_t lane;
+  uint32_t voff[ITERS];  // this lane's byte offset in copy j of K-tile 0 (issue_full)
 
   __device__ __forceinline__ LoaderFP6Pieces(const void* base, int32_t rows_valid, int64_t rs_bytes,
                                              int64_t K_elems, int32_t wave_, int32_t lane_) {
@@ -356,6 +357,12 @@ struct LoaderFP6Pieces {
     row0 = wave * RPI + lane / CPR;
     row_off = (uint32_t)(row0 * rs_bytes);
     row_step = (uint32_t)(WAVES * RPI * rs_bytes);
+#pragma unroll
+    for (int j = 0; j < ITERS; ++j) {
+      const int32_t row = row0 + j * WAVES * RPI;
+      const int32_t c = (lane % CPR) ^ swz(row, SHIFT, RB);
+      voff[j] = row_off + (uint32_t)j * row_step + (uint32_t)chunk_src(c, row);
+    }
   }
 
   // byte of the K-tile that logical chunk c of row `row` starts at
@@ -369,6 +376,14 @@ struct LoaderFP6Pieces {
     const uint32_t a = row_off + (uint32_t)j * row_step + (uint32_t)chunk_src(c, row) + (uint32_t)(t * TB);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16,
                                              t * KT < K ? a : kOutOfRange, 0, 0, 0);
+  }
+
+  // the same copy for a K-tile inside K (0 <= t, (t + 1) * KT <= K), with
+  // no vector arithmetic: as LoaderKVec::issue_full
+  __device__ __forceinline__ void issue_full(int32_t t, char* lds, int j) const {
+    const uint32_t v = voff[j];
+    const uint32_t s = (uint32_t)(t * TB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16, v, s, 0, 0);
   }
 
   __device__ __forceinline__ void issue(int32_t t, char* lds) const {

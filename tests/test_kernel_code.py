@@ -49,9 +49,11 @@ KERNELS.update({
 })
 # the MX ring kernel: 128 scaled MFMAs per loop iteration (four K-tiles of 32
 # for 8- and 6-bit data, two of 64 for E2M1), 8 after it
+# (whole K-tiles for every format; E4M3 also with a partial last K-tile)
 KERNELS.update({
-    f"{fn}_{ep}": (f"_ZN2sl12_GLOBAL__N_118gemm_mx_w4r_kernelILi0ELb{r}ELi{f}EEEvNS_10GemmParamsE", 128, 8)
+    f"{fn}_{ep}{kn}": (f"_ZN2sl12_GLOBAL__N_118gemm_mx_w4r_kernelILi0ELb{r}ELi{f}ELb{kf}EEEvNS_10GemmParamsE", 128, 8)
     for f, fn in ((0, "mxfp8"), (2, "mxfp6_e2m3"), (3, "mxfp6_e3m2"), (4, "mxfp4")) for r, ep in ((1, "rows"), (0, "quads"))
+    for kf, kn in ((1, ""), (0, "_kpart")) if kf == 1 or f == 0
 })
 
 
