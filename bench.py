@@ -164,9 +164,13 @@ def vendor_timing(w, a, b, c, sfa, sfb, out, stream, reps: int = 20):
     difference of its D from the library's (`out`, which holds the
     library's result).  None for the other workloads."""
     import torch
+    if w.mx and (w.fp4 or w.fp6 or w.nvfp4) or (not w.mx and w.bf16):
+        return None  # packed formats, and bf16 (kept off the vendor's bf16 path here)
+    if not isinstance(a, torch.Tensor) or not isinstance(b, torch.Tensor):
+        return None
     if w.batch != 1 or a.dim() != 2 or b.dim() != 2 or a.stride(1) != 1 or b.stride(1) != 1:
         return None
-    if w.mx and not (w.fp4 or w.fp6 or w.nvfp4) and w.block_k == 32 and w.c is None:
+    if w.mx and w.block_k == 32 and w.c is None:
         name = "torch._scaled_mm (E4M3 data, E8M0 scale per 32 K)"
         sa, sb = sfa.view(torch.float8_e8m0fnu), sfb.view(torch.float8_e8m0fnu)
         a8, b8 = a.view(torch.float8_e4m3fn), b.view(torch.float8_e4m3fn)
