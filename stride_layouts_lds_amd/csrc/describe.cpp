@@ -165,7 +165,10 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
   const bool fp4 = in.kernel == K_MXFP4;
   const bool fp6 = in.kernel == K_MXFP6;
   const bool fp8 = in.kernel == K_MX || in.kernel == K_MX_W8 || in.kernel == K_MX_W4R;
-  const int32_t RB = fp4 ? in.bk / 2 : fp6 ? 128 : fp8 ? in.bk : in.bk * 2;  // LDS bytes per tile row
+  // the 4-wave MX kernel packs 6-bit K-tiles: rows 96 bytes apart in LDS
+  // (LoaderFP6Packed); the 8-wave one pads them to 128-byte rows
+  const bool packed = fp6 && in.ring;
+  const int32_t RB = fp4 ? in.bk / 2 : packed ? 96 : fp6 ? 128 : fp8 ? in.bk : in.bk * 2;  // LDS bytes per tile row
   const std::string n(1, name);
   const Layout X = view(rows, in.K, rs, cs, batched, in.batch, bs);
 
@@ -177,23 +180,15 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
   o.note(n + " loader: " + load_name(load));
 
   const bool mmajor = load == LOAD_MNDMA;
-  // 6-bit data is counted in bits (an element is 6 of them, a row 1024)
-  // the 4-wave MX kernel lays 6-bit K-tiles out as four 32-value pieces,
-  // 32 bytes apart (LoaderFP6Pieces)
-  const bool pieces = fp6 && in.ring;
-  const Layout tile = mmajor   ? T({S(BR, 1), S(in.bk, BR)})
-                      : pieces ? T({S(BR, 8 * RB), T({S(32, 6), S(in.bk / 32, 256)})})
-                      : fp6    ? T({S(BR, 8 * RB), S(in.bk, 6)})
-                               : T({S(BR, in.bk), S(in.bk, 1)});
-  if (pieces) {
-    const int b = log2i(RB / 16), sh = log2i(RB);
+  // 6-bit data is counted in bits (an element is 6 of them)
+  const Layout tile = mmajor ? T({S(BR, 1), S(in.bk, BR)})
+                      : fp6  ? T({S(BR, 8 * RB), S(in.bk, 6)})
+                             : T({S(BR, in.bk), S(in.bk, 1)});
+  if (packed) {
     o.line(n + "_lds", tile,
-           fmt("bits: a K-tile's %d values as pieces of 32 (24 bytes) at row bytes 32q..32q+23; on rows with "
-               "bit 3 set a piece's last 8 bytes sit 8 bytes further (bit 6 of the bit offset flips with bit 7 "
-               "there), so one 16-byte and one 8-byte read fetch a fragment free of bank conflicts; byte b of "
-               "row r at r*%d + 16((b/16) ^ swz(r)) + b%%16, swz(r) = (r ^ (r>>4)&1) & %d: Swizzle<%d,4,%d> "
-               "then Swizzle<1,4,%d> on byte offsets",
-               in.bk, RB, RB / 16 - 1, b, sh - 4, sh));
+           fmt("bits: a K-tile's %d values are the %d bytes of a row, rows %d bytes apart, as 6 chunks of 16 "
+               "bytes; chunk c of row r sits at chunk (c + ((r >> 4) & 1)) mod 6 of the row",
+               in.bk, RB, RB));
   } else if (fp6) {
     const int b = log2i(RB / 16), sh = log2i(RB);
     o.line(n + "_lds", tile,
@@ -219,22 +214,31 @@ void operand(Out& o, const DescribeInput& in, const InstrInfo& I, char name, int
       o.line(n + "_copy", T({S(64, 16), S(WV, 1024), S(iters, 1024 * WV)}),
              mmajor ? "LDS bytes filled by (lane, wave, instruction); the lane landing in chunk p of K-row k "
                       "loads chunk p ^ swz(k) of that row"
-                    : "LDS bytes filled by (lane, wave, instruction); the lane landing in chunk p of row r "
-                      "loads chunk p ^ swz(r) of that row");
+             : packed ? "LDS bytes filled by (lane, wave, instruction); the lane landing in chunk p of row r "
+                        "loads chunk (p - ((r >> 4) & 1)) mod 6 of the row's K-tile"
+                      : "LDS bytes filled by (lane, wave, instruction); the lane landing in chunk p of row r "
+                        "loads chunk p ^ swz(r) of that row");
   }
   // wave partition of the LDS tile: (lane, ((slots), repeats, K slices)),
   // first in the tile's coordinates (row + BR * k), then through the tile
   const Layout slots = slot_modes(I, BR);
-  std::vector<Layout> vals{slots, S(F, I.rows), S(KS, (int64_t)BR * I.k)};
-  const Layout part = T({lane_modes(I, BR), T(vals)});
+  // packed 6-bit rows: lane half h takes the K-tile's 32-value blocks 2h
+  // (K slice 0) and 2h + 1 (slice 1), so the lane-half mode steps 64
+  // values and the slice mode 32
+  const int64_t slice_k = packed ? 32 : I.k;
+  std::vector<Layout> vals{slots, S(F, I.rows), S(KS, (int64_t)BR * slice_k)};
+  const Layout lanes = packed ? T({S(I.rows, 1), S(64 / I.rows, (int64_t)BR * 64)}) : lane_modes(I, BR);
+  const Layout part = T({lanes, T(vals)});
   o.stage(n + "_wave", [&] { return la::composition(tile, part); },
           fmt("(lane, ((slot), %c repeat, K slice)) -> element of the LDS tile; wave w starts at row %d*(w%s%d)",
               isA ? 'M' : 'N', TR, isA ? " % " : " / ", in.wm));
-  const Layout lane0 = T({slots, S(F, I.rows), S(KS, (int64_t)BR * I.k)});
+  const Layout lane0 = T({slots, S(F, I.rows), S(KS, (int64_t)BR * slice_k)});
   o.stage(n + "_lane0", [&] { return la::composition(tile, lane0); }, "lane 0's values (the wave partition at lane 0)");
-  if (pieces)
-    o.note(n + " fragments: one 16-byte read at row byte 32q and one 8-byte read at 32q + 16 + 8 (row bit 3) per "
-                 "lane per instruction tile, q = 2 (K slice) + lane / 32 (its 32 values, 24 bytes)");
+  if (packed)
+    o.note(n + " fragments: lane half h = lane / 32 takes blocks 2h and 2h + 1 of the K-tile (its 32 values, "
+                 "24 bytes, per K slice): slice 0 one 16-byte read (chunk 3h) and one 8-byte read (the low half "
+                 "of chunk 3h + 1), slice 1 one 8-byte read (its high half) and one 16-byte read (chunk 3h + 2); "
+                 "the 16-byte reads are free of bank conflicts, the 8-byte reads take two passes");
   else if (fp6)
     o.note(n + " fragments: one 16-byte and one 8-byte LDS read per lane per instruction tile (its 32 values, "
                  "24 bytes)");

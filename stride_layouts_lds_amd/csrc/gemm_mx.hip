@@ -471,15 +471,20 @@ __device__ __forceinline__ void mfma_scale_acc(floatx16& c, u32x4 a, u32x4 b, ui
 // vector C/D).
 // Lane part q (0..3) of the LDS byte address of a fragment read of the ring
 // kernel, for the 32-row block starting at row0 (shift-0 swizzle): E2M1 one
-// 16-byte read per k-slice (q = slice); 6-bit data a 16- and an 8-byte read
-// per slice (q = 2 slice + read); E4M3 two 16-byte pieces per slice (q = 2
-// slice + piece).  Block g of a wave reads at lane part + 4096 g
-// (mx_offsets_split).
+// 16-byte read per k-slice (q = slice); E4M3 two 16-byte pieces per slice
+// (q = 2 slice + piece).  6-bit data (packed rows, LoaderFP6Packed): lane
+// half h = lane / 32 takes the row's 32-value blocks 2h (k-slice 0) and
+// 2h + 1 (slice 1), bytes 48h .. 48h + 47 = chunks 3h .. 3h + 2: slice 0
+// is chunk 3h (q = 0) and the low half of chunk 3h + 1 (q = 1), slice 1
+// the high half of chunk 3h + 1 (q = 2) and chunk 3h + 2 (q = 3).  Block g
+// of a wave reads at lane part + g mx_block_bytes (mx_offsets_split).
+constexpr bool mx_f6(int fmt) { return fmt == kFmtE2M3 || fmt == kFmtE3M2; }
+constexpr int32_t mx_block_bytes(int fmt) { return mx_f6(fmt) ? 32 * 96 : 32 * kRowBytes; }
 constexpr int32_t mx_lane_off(int fmt, int32_t row0, int32_t lane, int q) {
   if (fmt == kFmtE2M1) return lds_offset(row0 + (lane & 31), 32 * q + 16 * (lane >> 5), 0);
-  if (fmt == kFmtE2M3 || fmt == kFmtE3M2) {
-    const int32_t row = row0 + (lane & 31), b0 = 32 * (2 * (q >> 1) + (lane >> 5));
-    return (q & 1) ? lds_offset(row, b0 + 16 + 8 * ((row >> 3) & 1), 0) : lds_offset(row, b0, 0);
+  if (mx_f6(fmt)) {
+    const int32_t row = row0 + (lane & 31), c = 3 * (lane >> 5) + (q + 1) / 2;
+    return 96 * row + 16 * fp6_packed_chunk(row, c) + (q == 2 ? 8 : 0);
   }
   return fragment_lds_offset(MFMA32_F8, lane, q & 1, row0, q >> 1, 0);
 }
@@ -489,10 +494,11 @@ constexpr bool mx_offsets_split() {
       for (int32_t lane = 0; lane < 64; ++lane)
         for (int q = 0; q < 4; ++q)
           for (int32_t g = 0; g < 4; ++g)
-            if (mx_lane_off(fmt, row0 + 32 * g, lane, q) != mx_lane_off(fmt, row0, lane, q) + 4096 * g) return false;
+            if (mx_lane_off(fmt, row0 + 32 * g, lane, q) != mx_lane_off(fmt, row0, lane, q) + mx_block_bytes(fmt) * g)
+              return false;
   return true;
 }
-static_assert(mx_offsets_split(), "a 32-row block's fragment addresses are block 0's plus 4096 per block");
+static_assert(mx_offsets_split(), "a 32-row block's fragment addresses are block 0's plus a fixed step per block");
 
 template <int SHIFT, bool ROWS, int FMT, bool KFULL = false>
 __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p) {
@@ -506,9 +512,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
   constexpr int BM = 256, BN = 256, FM = 4, FN = 4;
   constexpr int SLOT = 256 * kRowBytes;
   __shared__ __attribute__((aligned(1024))) char smem[5 * SLOT];
-  using LD = std::conditional_t<F6, LoaderFP6Pieces<256, 256, SHIFT>, LoaderKVec<256, 256, SHIFT, 1, kRowBytes, TB>>;
-  constexpr int LOADS = LD::ITERS;
-  static_assert(LOADS == 8, "copy layout");
+  using LD = std::conditional_t<F6, LoaderFP6Packed<256, 256>, LoaderKVec<256, 256, SHIFT, 1, kRowBytes, TB>>;
+  constexpr int LOADS = LD::ITERS;  // copies per operand K-tile and wave: 8 (6 for packed 6-bit rows)
+  static_assert(LOADS <= 8, "copy layout");
+  static_assert(!F6 || KFULL, "packed 6-bit K-tiles are whole (K a multiple of 512)");
   static_assert(SHIFT == 0, "the fragment addresses are split for the shift-0 swizzle");
 
   const int32_t lane = threadIdx.x & 63;
@@ -562,7 +569,16 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
       xb[j] = __builtin_amdgcn_raw_buffer_load_b128(
           rsb, in && sob[j] != kOutOfRange ? sob[j] + 16u * (uint32_t)q : kOutOfRange, 0, 0);
   };
+  // a lane's scale bytes of its blocks in k-slices 0 and 1 go to bytes 0
+  // and 2 of its scale register: blocks h and h + 2 of the chunk's dword
+  // (lane half h = lane / 32: a shift by 8 h), for packed 6-bit rows blocks
+  // 2h and 2h + 1 (a byte permute)
   const int32_t half_sel = 8 * (lane >> 5);
+  const uint32_t f6_sel = (lane >> 5) ? 0x03030202u : 0x01010000u;
+  auto lane_scales = [&](uint32_t w4) -> uint32_t {
+    if constexpr (F6) return __builtin_amdgcn_perm(0u, w4, f6_sel);
+    else return w4 >> half_sel;
+  };
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -584,11 +600,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
   // fragment of k-slice ks for row block g of the wave (the probed operand
   // orders: E4M3 two 16-byte pieces K/2 apart; E2M1 the lane's 32
   // consecutive k in 16 bytes; 6-bit data its 32 consecutive k in 24 bytes,
-  // piece 2 ks + lane / 32 of the K-tile as LoaderFP6Pieces lays it out: one
-  // 16-byte and one 8-byte read, the same registers on every lane), read at
-  // the K-tile's precomputed bases (lane part + slot) + 4096 g: the bases are
-  // formed before the barrier that ends the previous K-tile, so no read
-  // waits on fresh vector arithmetic
+  // block 2 (lane / 32) + ks of the packed K-tile: a 16-byte and an 8-byte
+  // read, in an order fixed per k-slice, so the same registers on every
+  // lane), read at the K-tile's precomputed bases (lane part + slot) + g
+  // mx_block_bytes: the bases are formed before the barrier that ends the
+  // previous K-tile, so no read waits on fresh vector arithmetic.  The MFMA
+  // sums the same 64 values per k-slice pair either way; the 6-bit blocks'
+  // order only moves which scale byte a lane passes (lane_scales)
   typedef __attribute__((address_space(3))) const u32x4 lds_u4;
   typedef __attribute__((address_space(3))) const u32x2 lds_u2;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)smem;
@@ -608,13 +626,21 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
     asm volatile("" : "+v"(bB[0]), "+v"(bB[1]), "+v"(bB[2]), "+v"(bB[3]));
   };
   auto rd = [&](const uint32_t(&b)[4], int g, int ks) -> Frag {
-    const uint32_t o = 4096u * (uint32_t)g;
+    const uint32_t o = (uint32_t)mx_block_bytes(FMT) * (uint32_t)g;
     if constexpr (F4) {
       return *(lds_u4*)(uintptr_t)(b[ks] + o);
     } else if constexpr (F6) {
-      const u32x4 x = *(lds_u4*)(uintptr_t)(b[2 * ks] + o);
-      const u32x2 y = *(lds_u2*)(uintptr_t)(b[2 * ks + 1] + o);
-      return i32x6{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1]};
+      // slice 0: 16 bytes then 8; slice 1: 8 bytes then 16 (the block's
+      // bytes in order either way)
+      if (ks == 0) {
+        const u32x4 x = *(lds_u4*)(uintptr_t)(b[0] + o);
+        const u32x2 y = *(lds_u2*)(uintptr_t)(b[1] + o);
+        return i32x6{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1]};
+      } else {
+        const u32x2 y = *(lds_u2*)(uintptr_t)(b[2] + o);
+        const u32x4 x = *(lds_u4*)(uintptr_t)(b[3] + o);
+        return i32x6{(int)y[0], (int)y[1], (int)x[0], (int)x[1], (int)x[2], (int)x[3]};
+      }
     } else {
       const u32x4 lo = *(lds_u4*)(uintptr_t)(b[2 * ks] + o);
       const u32x4 hi = *(lds_u4*)(uintptr_t)(b[2 * ks + 1] + o);
@@ -672,9 +698,9 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
       for (int w = 0; w < SD; ++w) {
         auto pick = [](const u32x4& v, int k) -> uint32_t { return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3]; };
 #pragma unroll
-        for (int i = 0; i < FM; ++i) sac[w][i] = pick(sa4[i], SD * d + w) >> half_sel;
+        for (int i = 0; i < FM; ++i) sac[w][i] = lane_scales(pick(sa4[i], SD * d + w));
 #pragma unroll
-        for (int j = 0; j < FN; ++j) sbc[w][j] = pick(sb4[j], SD * d + w) >> half_sel;
+        for (int j = 0; j < FN; ++j) sbc[w][j] = lane_scales(pick(sb4[j], SD * d + w));
         // opaque from here on, so that the compiler cannot recompute them
         // next to the MFMAs
 #pragma unroll
@@ -690,7 +716,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
           fb[0][g] = rd(bB, g, 0);
         else
           fa[0][g - 4] = rd(bA, g - 4, 0);
-        copy(lb, t + 1, slot(s3), g);
+        if (g < LOADS) copy(lb, t + 1, slot(s3), g);
         const int i = FM / 2 + g / FN, j = g % FN;
         mfma_scale_acc<FMT, 1>(acc[i][j], fb[1][j], fa[1][i], sbp[j], sap[i]);
         __builtin_amdgcn_sched_barrier(0);
@@ -704,7 +730,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
             fb[(s + 1) % 2][g] = rd(bB, g, s + 1);
           else
             fa[(s + 1) % 2][g - 4] = rd(bA, g - 4, s + 1);
-          if (s == 0) copy(la, t + 2, slot(s4), g);
+          if (s == 0 && g < LOADS) copy(la, t + 2, slot(s4), g);
           mfma_range(s_c, 2 * g, 2);
           __builtin_amdgcn_sched_barrier(0);
         }

@@ -313,84 +313,55 @@ struct LoaderKVec {
   __device__ __forceinline__ void commit(char*) const {}
 };
 
-// Packed 6-bit K-tiles (128 values, 96 bytes of a row) for the 4-wave MX
-// kernel's 32x32x64 fragments.  A lane's fragment is 32 consecutive values
-// (24 bytes): piece q = 0..3 of the K-tile.  Piece q occupies row bytes
-// [32q, 32q + 16) (its first 16 bytes) and 8 bytes of [32q + 16, 32q + 32):
-// the first half on rows with bit 3 clear, the second half on rows with it
-// set.  One 16-byte and one 8-byte LDS read then fetch a fragment, with the
-// same register order on every lane; an 8-byte read is served in passes of
-// 32 lanes (32 rows at one piece), where the half flip sends rows r and
-// r ^ 8, which share the chunk swizzle, to different banks.  Each 16-byte
-// copy fills one chunk: chunk 2q with tile bytes [24q, 24q + 16), chunk
-// 2q + 1 with [24q + 16, 24q + 32) or [24q + 8, 24q + 24) (the unused half
-// holds a neighbour's bytes and is never read).  Chunk placement is
-// XOR-swizzled as in LoaderKVec.
-template <int ROWS, int NT, int SHIFT>
-struct LoaderFP6Pieces {
-  static constexpr int RB = kRowBytes;
+// Packed 6-bit K-tiles for the 4-wave MX kernel, copied as they lie: a
+// row's K-tile (128 values, 96 bytes) is 6 consecutive 16-byte chunks of
+// LDS, rows 96 bytes apart, so a K-tile of 256 rows takes 24 copy
+// instructions (a wave's 64 lanes fill 64 consecutive chunks, 10 2/3 rows)
+// where 128-byte LDS rows take 32.  On rows 16-31 of every 32 the chunk
+// order is rotated by one (fp6_packed_chunk): the kernel's 16-byte fragment
+// reads (one chunk of 32 rows, lanes paired as gfx950 serves them) then hit
+// distinct banks; its 8-byte reads take two passes.  Every K-tile must lie
+// inside K (the 4-wave MX kernel's condition: K a multiple of 512).
+SL_HD constexpr int32_t fp6_packed_chunk(int32_t row, int32_t c) { return (c + ((row >> 4) & 1)) % 6; }
+
+template <int ROWS, int NT>
+struct LoaderFP6Packed {
   static constexpr int WAVES = NT / 64;
-  static constexpr int CPR = RB / 16;          // chunks per row
-  static constexpr int RPI = 1024 / RB;        // rows per wave instruction
-  static constexpr int ITERS = ROWS * RB / (NT * 16);
-  static constexpr int TB = 96;                // bytes of a row per K-tile
-  static constexpr int KT = 128;               // values per K-tile
-  static_assert(ITERS >= 1 && ROWS * RB % (NT * 16) == 0, "tile too small for the workgroup");
+  static constexpr int TB = 96;                  // bytes of a row per K-tile
+  static constexpr int KT = 128;                 // values per K-tile
+  static constexpr int INSTR = ROWS * 6 / 64;    // copy instructions per K-tile
+  static constexpr int ITERS = INSTR / WAVES;    // ... per wave
+  static_assert(ROWS * 6 % 64 == 0 && INSTR % WAVES == 0, "tile rows for the workgroup");
 
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t row_off;   // byte offset of this lane's row in instruction 0
-  uint32_t row_step;  // bytes between the row blocks of consecutive instructions
-  int32_t row0;       // this lane's tile row in instruction 0
-  int32_t K;
   int32_t wave;
-  int32_t lane;
-  uint32_t voff[ITERS];  // this lane's byte offset in copy j of K-tile 0 (issue_full)
+  uint32_t voff[ITERS];  // this lane's byte offset in copy j of K-tile 0
 
-  __device__ __forceinline__ LoaderFP6Pieces(const void* base, int32_t rows_valid, int64_t rs_bytes,
-                                             int64_t K_elems, int32_t wave_, int32_t lane_) {
-    K = (int32_t)K_elems;
+  __device__ __forceinline__ LoaderFP6Packed(const void* base, int32_t rows_valid, int64_t rs_bytes,
+                                             int64_t K_elems, int32_t wave_, int32_t lane) {
     wave = wave_;
-    lane = lane_;
     const uint32_t bytes =
         rows_valid > 0 ? (uint32_t)((int64_t)(rows_valid - 1) * rs_bytes + K_elems / 4 * 3) : 0u;
     rsrc = make_rsrc(base, bytes);
-    row0 = wave * RPI + lane / CPR;
-    row_off = (uint32_t)(row0 * rs_bytes);
-    row_step = (uint32_t)(WAVES * RPI * rs_bytes);
 #pragma unroll
     for (int j = 0; j < ITERS; ++j) {
-      const int32_t row = row0 + j * WAVES * RPI;
-      const int32_t c = (lane % CPR) ^ swz(row, SHIFT, RB);
-      voff[j] = row_off + (uint32_t)j * row_step + (uint32_t)chunk_src(c, row);
+      // copy j of this wave fills chunks 64 (j * WAVES + wave) + lane of the
+      // tile: physical chunk p of row `row`, holding the row's chunk c
+      const int32_t g = 64 * (j * WAVES + wave) + lane;
+      const int32_t row = g / 6, p = g % 6;
+      const int32_t c = (p + 6 - ((row >> 4) & 1)) % 6;
+      voff[j] = (uint32_t)(row * rs_bytes) + (uint32_t)(16 * c);
     }
   }
 
-  // byte of the K-tile that logical chunk c of row `row` starts at
-  static __device__ __forceinline__ int32_t chunk_src(int32_t c, int32_t row) {
-    return 24 * (c >> 1) + ((c & 1) ? 16 - 8 * ((row >> 3) & 1) : 0);
-  }
-
-  __device__ __forceinline__ void issue_one(int32_t t, char* lds, int j) const {
-    const int32_t row = row0 + j * WAVES * RPI;
-    const int32_t c = (lane % CPR) ^ swz(row, SHIFT, RB);
-    const uint32_t a = row_off + (uint32_t)j * row_step + (uint32_t)chunk_src(c, row) + (uint32_t)(t * TB);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16,
-                                             t * KT < K ? a : kOutOfRange, 0, 0, 0);
-  }
-
-  // the same copy for a K-tile inside K (0 <= t, (t + 1) * KT <= K), with
-  // no vector arithmetic: as LoaderKVec::issue_full
+  // copy j of K-tile t, with no vector arithmetic: the lane's offset is
+  // voff[j] and the K-tile's start goes into the scalar offset (rows past
+  // the valid ones read zero: their offset alone is past the resource)
   __device__ __forceinline__ void issue_full(int32_t t, char* lds, int j) const {
     const uint32_t v = voff[j];
     const uint32_t s = (uint32_t)(t * TB);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16, v, s, 0, 0);
   }
-
-  __device__ __forceinline__ void issue(int32_t t, char* lds) const {
-#pragma unroll
-    for (int j = 0; j < ITERS; ++j) issue_one(t, lds, j);
-  }
-  __device__ __forceinline__ void commit(char*) const {}
 };
 
 // M- (or N-) contiguous fp16 rows, 16-B aligned: the tile is stored in HBM

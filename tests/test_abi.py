@@ -289,40 +289,47 @@ def _gfx950_b64_passes(addrs):
     return total
 
 
-def test_mxfp6_fragment_reads_conflict_free_on_gfx950():
-    """The 4-wave MX kernel's 6-bit fragments: a lane's 32 values (24 bytes,
-    piece q = 2 ks + lane / 32 of the K-tile) are one 16-byte read at row
-    byte 32q and one 8-byte read at 32q + 16 + 8 (row bit 3), through the
-    K-major LDS map (Swizzle<3,4,3> then Swizzle<1,4,7> on byte offsets).
-    Both reads take the minimum passes on every 32-row block and k-slice;
-    the earlier reads of the 24 bytes as three 8-byte pieces at 24q, 24q + 8
-    and 24q + 16 had 2-way conflicts.  The copy that fills the row puts tile
-    bytes [24q, 24q + 24) exactly where these reads find them."""
-    def lds(r, b):
-        return L.swizzle_bms(L.swizzle_bms(r * 128 + b, 3, 4, 3), 1, 4, 7)
+def test_mxfp6_packed_rows_on_gfx950():
+    """The 4-wave MX kernel's packed 6-bit K-tiles: a row's 96 bytes are 6
+    chunks of 16 bytes, rows 96 bytes apart, chunk c of row r at chunk
+    (c + (r >> 4) & 1) mod 6.  Lane half h = lane / 32 takes blocks 2h
+    (k-slice 0: a 16-byte read of chunk 3h and an 8-byte read of the low
+    half of chunk 3h + 1) and 2h + 1 (slice 1: the high half of chunk 3h + 1
+    and chunk 3h + 2).  The 16-byte reads take the minimum passes on every
+    32-row block; the 8-byte reads take two (every lane of a 32-lane pass
+    reads the same half of a chunk, so only half the banks are reachable),
+    which the loader accepts for a quarter fewer copies than 128-byte rows.
+    The copy (64 consecutive chunks per instruction) puts every byte of the
+    K-tile exactly once where these reads find it."""
+    def pos(r, c):
+        return 96 * r + 16 * ((c + ((r >> 4) & 1)) % 6)
 
-    for row0 in range(0, 256, 32):
-        for ks in range(2):
+    for slot in (0, 32768):
+        for row0 in range(0, 256, 32):
             rows = [row0 + (l & 31) for l in range(64)]
-            q = [2 * ks + (l >> 5) for l in range(64)]
-            b128 = [lds(rows[l], 32 * q[l]) for l in range(64)]
-            b64 = [lds(rows[l], 32 * q[l] + 16 + 8 * ((rows[l] >> 3) & 1)) for l in range(64)]
-            assert _gfx950_b128_passes(b128) == 4 and _gfx950_b64_passes(b64) == 2, (row0, ks)
-            old = [_gfx950_b64_passes([lds(rows[l], 48 * ks + 24 * (l >> 5) + 8 * i) for l in range(64)])
-                   for i in range(3)]
-            assert max(old) == 4, (row0, ks, old)
-    # the copy: logical chunk c of row r holds tile bytes from 24 (c / 2) on
-    # (even c) or 24 (c / 2) + 16 - 8 (r bit 3) (odd c)
-    for r in range(32):
-        h = (r >> 3) & 1
-        row = {}
-        for c in range(8):
-            src = 24 * (c >> 1) + ((16 - 8 * h) if c & 1 else 0)
-            for x in range(16):
-                row[16 * c + x] = src + x
-        for qq in range(4):
-            got = [row[32 * qq + x] for x in range(16)] + [row[32 * qq + 16 + 8 * h + x] for x in range(8)]
-            assert got == list(range(24 * qq, 24 * qq + 24)), (r, qq)
+            h = [l >> 5 for l in range(64)]
+            b128_0 = [slot + pos(rows[l], 3 * h[l]) for l in range(64)]
+            b64_0 = [slot + pos(rows[l], 3 * h[l] + 1) for l in range(64)]
+            b64_1 = [slot + pos(rows[l], 3 * h[l] + 1) + 8 for l in range(64)]
+            b128_1 = [slot + pos(rows[l], 3 * h[l] + 2) for l in range(64)]
+            assert _gfx950_b128_passes(b128_0) == 4 and _gfx950_b128_passes(b128_1) == 4, (slot, row0)
+            assert _gfx950_b64_passes(b64_0) == 4 and _gfx950_b64_passes(b64_1) == 4, (slot, row0)
+    # the copy: chunk g = 64 instruction + lane of the tile is physical chunk
+    # g % 6 of row g / 6 and holds the row's chunk (g % 6 - (row >> 4) & 1) mod 6
+    lds = {}
+    for g in range(256 * 6):
+        r, p = divmod(g, 6)
+        c = (p - ((r >> 4) & 1)) % 6
+        for x in range(16):
+            assert 16 * g + x not in lds
+            lds[16 * g + x] = (r, 16 * c + x)
+    assert len(lds) == 256 * 96
+    for r in range(256):
+        for h in range(2):
+            blk0 = [lds[pos(r, 3 * h) + x] for x in range(16)] + [lds[pos(r, 3 * h + 1) + x] for x in range(8)]
+            blk1 = [lds[pos(r, 3 * h + 1) + 8 + x] for x in range(8)] + [lds[pos(r, 3 * h + 2) + x] for x in range(16)]
+            assert blk0 == [(r, 48 * h + x) for x in range(24)], (r, h)
+            assert blk1 == [(r, 48 * h + 24 + x) for x in range(24)], (r, h)
 
 
 def test_plan_split_k_for_skinny_outputs(api):

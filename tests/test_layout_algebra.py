@@ -511,14 +511,15 @@ def test_trace_other_plans(api):
                       rowmajor(BASE_C, (n, n // 32), 4), rowmajor(0x500000000, (n, n // 32), 4))
     assert p["kernel"] == api.K_MXFP6 and "E2M3" in t6
     check_instr_lines(api, st, 7)
-    # the 4-wave kernel's pieces: value k of a K-tile at bit 256 (k / 32) + 6 (k % 32) of its row (rows
-    # with bit 3 clear; the note states the displacement on the others)
-    assert st["A_lds"] == "(256,(32,4)):(1024,(6,256))"
+    # the 4-wave kernel's packed rows: value k of a K-tile at bit 6 k of its 768-bit row (the chunk
+    # rotation is stated in the line's note); lane half h = col / 32 of the instruction's operand map
+    # takes the K-tile's blocks 2h (K slice 0) and 2h + 1 (slice 1)
+    assert st["A_lds"] == "(256,128):(768,6)"
     for lane, slot, row, col in api.query_fragment_map(7, 0):
         for i, ks in itertools.product(range(4), range(2)):
             e = ev(st["A_wave"], lane + 64 * (slot + 32 * (i + 4 * ks)))
-            k = 64 * ks + col
-            assert divmod(e, 1024) == (32 * i + row, 256 * (k // 32) + 6 * (k % 32))
+            k = 32 * (2 * (col // 32) + ks) + col % 32
+            assert divmod(e, 768) == (32 * i + row, 6 * k)
     # an empty product and an invalid one
     t, _, _ = trace(api, rowmajor(BASE_A, (0, 64)), rowmajor(BASE_B, (64, 64)), None, rowmajor(BASE_D, (0, 64)))
     assert "empty" in t
