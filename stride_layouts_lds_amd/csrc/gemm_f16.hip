@@ -350,7 +350,9 @@ __device__ __forceinline__ void mfma_acc(floatx4& c, const half8& a, const half8
 // and three in flight fit the 160 KiB of a CU.  Requires at least one
 // K-tile.  ROWS (BN = 256 only): every tile is full and C and D rows are
 // contiguous and 8-byte aligned, so the epilogue goes through LDS
-// (epilogue_rows); otherwise the per-quad epilogue.
+// (epilogue_rows); otherwise the per-quad epilogue.  KFULL (K-contiguous
+// operands, K a multiple of 64): every K-tile is whole, so every copy is
+// issue_full, with no vector arithmetic in front of it.
 //
 // Tile t: (1) reads of slice 0 into set 0, the second half of tile t-1's
 // slice 1 on set 1, copy of B(t+1) into A(t-1)'s slot; (2) slice 0 on set
