@@ -140,14 +140,33 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
     if constexpr (PIPE == 1) read_slice(smem, 0, fa0, fb0);
   }
 
-  // Loop body without branches: past the last tile the loads are fully
-  // out of range (they write zeros into the idle buffer) and the reads of
-  // the idle buffer are never consumed.
+  // Past the last tile the loads are fully out of range (they write zeros
+  // into the idle buffer) and the reads of the idle buffer are never
+  // consumed.  With direct copies and every K-tile whole, the copies take
+  // the path without vector arithmetic (issue_full), the one past the last
+  // tile reloading the last tile (not with PIPE 1, whose second fragment
+  // set leaves no registers for the loaders' offsets).
+  constexpr bool direct = PIPE == 0 && (ALOAD == LOAD_KVEC || ALOAD == LOAD_MNDMA) &&
+                          (BLOAD == LOAD_KVEC || BLOAD == LOAD_MNDMA);
+  const bool kfull = direct && p.K % 64 == 0;
   for (int32_t t = 0; t < T; ++t) {
     char* cur = smem + (t & 1) * STAGE;
     char* nxt = smem + ((t + 1) & 1) * STAGE;
-    la.issue(t + 1, nxt);
-    lb.issue(t + 1, nxt + ABYTES);
+    if constexpr (direct) {
+      if (kfull) {
+        const int32_t u = t + 1 < T ? t + 1 : T - 1;
+#pragma unroll
+        for (int j = 0; j < decltype(la)::ITERS; ++j) la.issue_full(u, nxt, j);
+#pragma unroll
+        for (int j = 0; j < decltype(lb)::ITERS; ++j) lb.issue_full(u, nxt + ABYTES, j);
+      } else {
+        la.issue(t + 1, nxt);
+        lb.issue(t + 1, nxt + ABYTES);
+      }
+    } else {
+      la.issue(t + 1, nxt);
+      lb.issue(t + 1, nxt + ABYTES);
+    }
     if constexpr (PIPE == 0) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {

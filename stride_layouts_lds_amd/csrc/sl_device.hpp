@@ -447,6 +447,8 @@ struct LoaderMNDma {
   __amdgpu_buffer_rsrc_t rsrc;
   int32_t K, wave, lane, rows_valid;
   int64_t ks;
+  uint32_t voff[ITERS];  // this lane's byte offset in copy j of K-tile 0 (issue_full)
+  uint32_t kstep;        // bytes between K-tiles
 
   __device__ __forceinline__ LoaderMNDma(const void* base, int32_t rows_valid_, int64_t /*rs*/, int64_t ks_,
                                          int64_t K_, int32_t wave_, int32_t lane_) {
@@ -458,6 +460,22 @@ struct LoaderMNDma {
     const uint32_t bytes =
         (rows_valid_ > 0 && K_ > 0) ? (uint32_t)(((K_ - 1) * ks_ + rows_valid_) * 2) : 0u;
     rsrc = make_rsrc(base, bytes);
+    kstep = (uint32_t)(64 * ks_ * 2);
+#pragma unroll
+    for (int j = 0; j < ITERS; ++j) {
+      const int32_t kr = (j * WAVES + wave) * RPI + lane / CPR;
+      const int32_t c = (lane % CPR) ^ mn_swz(kr);
+      voff[j] = c * 8 < rows_valid_ ? (uint32_t)(((int64_t)kr * ks_ + c * 8) * 2) : kOutOfRange;
+    }
+  }
+
+  // the copy of issue_one for a K-tile inside K (0 <= t, 64 (t + 1) <= K),
+  // with no vector arithmetic: the lane's offset is voff[j] and the K-tile's
+  // start goes into the scalar offset (as LoaderKVec::issue_full)
+  __device__ __forceinline__ void issue_full(int32_t t, char* lds, int j) const {
+    const uint32_t v = voff[j];
+    const uint32_t s = (uint32_t)t * kstep;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (j * WAVES + wave) * 1024), 16, v, s, 0, 0);
   }
 
   // one copy instruction: the j-th 1 KiB block of this wave in K-tile t
