@@ -77,10 +77,45 @@ __device__ __forceinline__ void store_partial(const floatx4 (&acc)[FM][FN], cons
     }
 }
 
+// Epilogue of a wave's 128 x 16 FN block (FN = 8 or 4) through a private
+// LDS region of 64 rows x 16 FN fp32 (rows_load_c / rows_store_half): here
+// the accumulator-order writes, 16 rows x one 16-byte chunk per instruction
+// (accumulator (i, j) holds rows 16 i + lane % 16, columns 16 j + 4 (lane /
+// 16) .. + 3).  NT: non-temporal D stores.
+template <int DT, int FN, bool NT>
+__device__ __forceinline__ void epilogue_rows(const floatx4 (&acc)[8][FN], const GemmParams& p, int32_t batch,
+                                              int64_t m_base, int64_t n_base, int32_t lane, char* region) {
+  constexpr int COLS = 16 * FN;
+  const int32_t l0 = lane & 15, l1 = lane >> 4;
+  u16x4 cq[2][COLS / 4];
+  rows_load_c<COLS>(p, batch, m_base, n_base, lane, cq);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int32_t r = 16 * i + l0;
+        *(floatx4*)(region + rows_chunk<COLS>(r, 4 * j + l1)) = acc[4 * h + i][j];
+      }
+    rows_store_half<DT, COLS, NT>(p, batch, m_base + 64 * h, n_base, lane, region, cq[h]);
+  }
+}
+
+// the row epilogue's condition: every 256 x 256 tile full, D (and C if
+// present) in contiguous 8-byte aligned rows
+inline bool rows_epilogue_ok(const GemmParams& p) {
+  return p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) && (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
+}
+
 // PIPE 0: per k-slice, read the fragments then issue the MFMAs (latency is
 // covered by the other wave on the SIMD when WM*WN = 8).  PIPE 1: two
 // fragment sets, the next slice is read while the current one computes.
-template <int BM, int BN, int WM, int WN, int ALOAD, int BLOAD, int SHIFT, int PIPE, int DT = DT_F16>
+// ROWS (8 waves of 128 x 64, PIPE 0): every tile is full and C and D rows
+// are contiguous and 8-byte aligned, so the epilogue goes through LDS rows
+// (epilogue_rows, a 16 KiB region per wave in the stage buffers).
+template <int BM, int BN, int WM, int WN, int ALOAD, int BLOAD, int SHIFT, int PIPE, int DT = DT_F16,
+          bool ROWS = false>
 __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kernel(const GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -88,6 +123,8 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
   constexpr int ABYTES = BM * kRowBytes, BBYTES = BN * kRowBytes;
   constexpr int STAGE = ABYTES + BBYTES;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  static_assert(!ROWS || (FM == 8 && FN == 4 && PIPE == 0 && WM * WN * 64 * 64 * 4 <= 2 * STAGE),
+                "the row epilogue: 128 x 64 wave blocks, one 16 KiB region each in the stage buffers");
 
   const int32_t lane = threadIdx.x & 63;
   const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,7 +239,12 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_kerne
     }
   }
 
-  epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  if constexpr (ROWS) {
+    __syncthreads();  // every wave is done reading the stage buffers
+    epilogue_rows<DT, FN, false>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane, smem + wave * 16384);
+  } else {
+    epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
+  }
 }
 
 // Multi-stage variant for K-contiguous operands: K-tiles of RB/2 fp16 (LDS
@@ -304,28 +346,6 @@ __global__ __launch_bounds__(WM* WN * 64, (WM * WN + 3) / 4) void gemm_f16_ms_ke
     epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
 }
 
-// Epilogue of a wave's 128x128 block through a private 32 KiB LDS region
-// (rows_load_c / rows_store_half): here the accumulator-order writes, 16
-// rows x one 16-byte chunk per instruction.
-template <int DT>
-__device__ __forceinline__ void epilogue_rows(const floatx4 (&acc)[8][8], const GemmParams& p, int32_t batch,
-                                              int64_t m_base, int64_t n_base, int32_t lane, char* region) {
-  const int32_t l0 = lane & 15, l1 = lane >> 4;
-  u16x4 cq[2][32];
-  rows_load_c(p, batch, m_base, n_base, lane, cq);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int32_t r = 16 * i + l0;
-        *(floatx4*)(region + rows_chunk(r, 4 * j + l1)) = acc[4 * h + i][j];
-      }
-    rows_store_half<DT>(p, batch, m_base + 64 * h, n_base, lane, region, cq[h]);
-  }
-}
-
 // The ring kernel reads fragment r of a slice (rows row0 + 16 r ...) at the
 // lane's offset for r's parity plus 4096 (r / 2): with the chunk swizzle at
 // shift 0 a row's swizzle depends on its low three bits and bit 4, i.e. on
@@ -369,7 +389,10 @@ __device__ __forceinline__ void mfma_acc(floatx4& c, const half8& a, const half8
 // and three in flight fit the 160 KiB of a CU.  Requires at least one
 // K-tile.  ROWS (BN = 256 only): every tile is full and C and D rows are
 // contiguous and 8-byte aligned, so the epilogue goes through LDS
-// (epilogue_rows); otherwise the per-quad epilogue.  KFULL (K-contiguous
+// (epilogue_rows, its D stores non-temporal: with every workgroup of a
+// round storing at once this measured 1-6% faster on the one-round shapes
+// and no different on the larger ones); otherwise the per-quad epilogue.
+// KFULL (K-contiguous
 // operands, K a multiple of 64): every K-tile is whole, so every copy is
 // issue_full, with no vector arithmetic in front of it.
 //
@@ -590,7 +613,7 @@ __global__ __launch_bounds__(256, 1) void gemm_f16_w4r_kernel(const GemmParams p
     // every wave's copies have landed and its reads of the ring are done:
     // the LDS is free for the per-wave epilogue regions
     __syncthreads();
-    epilogue_rows<DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane, smem + wave * 32768);
+    epilogue_rows<DT, 8, true>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane, smem + wave * 32768);
   } else {
     epilogue<FM, FN, DT>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
   }
@@ -713,7 +736,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_w4r_kernel(const GemmParams
   pin();
   if constexpr (ROWS) {
     __syncthreads();
-    epilogue_rows<DT_F16>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane, smem + wave * 32768);
+    epilogue_rows<DT_F16, 8, false>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane, smem + wave * 32768);
   } else {
     epilogue<FM, FN, DT_F16>(acc, p, tc.batch, m0 + a_row0, n0 + b_row0, lane);
   }
@@ -1134,6 +1157,12 @@ template <int BM, int BN, int WM, int WN, int AL, int BL, int PIPE, int DT>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.batch * p.tiles_m * p.tiles_n;
   dim3 grid((uint32_t)total), block(WM * WN * 64);
+  if constexpr (BM == 256 && BN == 256 && WM == 2 && WN == 4 && PIPE == 0) {
+    if (rows_epilogue_ok(p)) {
+      hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, AL, BL, 0, PIPE, DT, true>), grid, block, 0, s, p);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, WM, WN, AL, BL, 0, PIPE, DT>), grid, block, 0, s, p);
   return hipGetLastError();
 }
@@ -1183,8 +1212,7 @@ template <int DT, int AL, int BL, int BN>
 hipError_t launch_ring(const GemmParams& p, hipStream_t s) {
   if (p.k_tiles < 1 || p.splits != 1) return hipErrorInvalidValue;
   const dim3 g((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), b(256);
-  const bool rows = BN == 256 && p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
-                    (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
+  const bool rows = BN == 256 && rows_epilogue_ok(p);
   if constexpr (AL == LOAD_KVEC && BL == LOAD_KVEC) {
     if (p.K % 64 == 0) {
       if constexpr (BN == 256) {
@@ -1254,8 +1282,7 @@ hipError_t launch_typed(const GemmParams& p, int32_t tile, int32_t a_load, int32
     if (tile == T256x256_W4R) {
       if (p.k_tiles < 1 || p.splits != 1) return hipErrorInvalidValue;
       const dim3 g((uint32_t)((int64_t)p.batch * p.tiles_m * p.tiles_n)), b(256);
-      const bool rows = p.M % 256 == 0 && p.N % 256 == 0 && (p.flags & F_D_VEC) &&
-                        (!(p.flags & F_HAS_C) || (p.flags & F_C_VEC));
+      const bool rows = rows_epilogue_ok(p);
       const bool pairs = a_load == LOAD_NVFP4_PAIRS;
       if (pairs && rows) hipLaunchKernelGGL((gemm_nvfp4_w4r_kernel<0, true, true>), g, b, 0, s, p);
       if (pairs && !rows) hipLaunchKernelGGL((gemm_nvfp4_w4r_kernel<0, true, false>), g, b, 0, s, p);

@@ -176,49 +176,64 @@ __device__ __forceinline__ void store_quad(const GemmParams& p, const uint16_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Row epilogue of a wave's 128x128 output block, for full tiles with
-// contiguous, 8-byte aligned C and D rows.  The block goes through a private
-// 32 KiB LDS region in two halves of 64 rows x 128 fp32, row-major with the
-// 16-byte chunk q of row r at chunk q ^ (r % 16) (rows_chunk): free of bank
-// conflicts both for accumulator-order writes (16 or 32 rows at one chunk)
-// and for row-order reads.  Read back one row-contiguous 16-byte piece per
-// lane (32 lanes per row), added to C and stored as 8 bytes, every C load
-// and D store instruction touches eight 64-byte lines; in accumulator order
-// one touches 16 or 32 rows.  All of the lane's C loads are issued first.
+// Row epilogue of a wave's 128 x COLS output block (COLS = 128 or 64), for
+// full tiles with contiguous, 8-byte aligned C and D rows.  The block goes
+// through a private LDS region of 64 rows x COLS fp32 (32 or 16 KiB) in two
+// halves of 64 rows, row-major with the 16-byte chunk q of row r at chunk
+// q ^ (r % 16) (rows_chunk): free of bank conflicts both for
+// accumulator-order writes (16 rows at one chunk per 16 lanes) and for
+// row-order reads.  Read back one row-contiguous 16-byte piece per lane
+// (COLS / 4 lanes per row, 256 / COLS rows per instruction), added to C and
+// stored as 8 bytes, every C load and D store instruction covers whole
+// 128-byte row segments; in accumulator order one touches 16 rows.  All of
+// the lane's C loads are issued first.  NT: the D stores carry the
+// non-temporal hint (D is not read again).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int32_t rows_chunk(int32_t r, int32_t q) { return r * 512 + 16 * (q ^ (r & 15)); }
+template <int COLS = 128>
+__device__ __forceinline__ int32_t rows_chunk(int32_t r, int32_t q) {
+  static_assert(COLS == 128 || COLS == 64, "row epilogue block width");
+  return r * (4 * COLS) + 16 * (q ^ (r & 15));
+}
 
-// C of the lane's row-order pieces of both halves (rows 2 it + lane / 32,
-// columns 4 (lane % 32) .. + 3); nothing when there is no C
+// C of the lane's row-order pieces of both halves (rows (256 / COLS) it +
+// lane / (COLS / 4), columns 4 (lane % (COLS / 4)) .. + 3); nothing when
+// there is no C
+template <int COLS = 128>
 __device__ __forceinline__ void rows_load_c(const GemmParams& p, int32_t batch, int64_t m_base, int64_t n_base,
-                                            int32_t lane, u16x4 (&cq)[2][32]) {
+                                            int32_t lane, u16x4 (&cq)[2][COLS / 4]) {
+  constexpr int LPR = COLS / 4, RPI = 64 / LPR;
   if (!(p.flags & F_HAS_C)) return;
   const uint16_t* C = (const uint16_t*)p.c + batch * p.c_bs;
-  const int32_t q = lane & 31, rl = lane >> 5;
+  const int32_t q = lane % LPR, rl = lane / LPR;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int it = 0; it < 32; ++it)
-      cq[h][it] = *(const u16x4*)(C + (m_base + 64 * h + 2 * it + rl) * p.c_rs + n_base + 4 * q);
+    for (int it = 0; it < LPR; ++it)
+      cq[h][it] = *(const u16x4*)(C + (m_base + 64 * h + RPI * it + rl) * p.c_rs + n_base + 4 * q);
 }
 
 // D rows m_base .. m_base + 63 from the region (+ C), one half
-template <int DT>
+template <int DT, int COLS = 128, bool NT = false>
 __device__ __forceinline__ void rows_store_half(const GemmParams& p, int32_t batch, int64_t m_base, int64_t n_base,
-                                                int32_t lane, const char* region, const u16x4 (&cq)[32]) {
+                                                int32_t lane, const char* region, const u16x4 (&cq)[COLS / 4]) {
+  constexpr int LPR = COLS / 4, RPI = 64 / LPR;
   uint16_t* D = (uint16_t*)p.d + batch * p.d_bs;
   const bool has_c = p.flags & F_HAS_C;
-  const int32_t q = lane & 31, rl = lane >> 5;
+  const int32_t q = lane % LPR, rl = lane / LPR;
 #pragma unroll
-  for (int it = 0; it < 32; ++it) {
-    const int32_t r = 2 * it + rl;
-    floatx4 v = *(const floatx4*)(region + rows_chunk(r, q));
+  for (int it = 0; it < LPR; ++it) {
+    const int32_t r = RPI * it + rl;
+    floatx4 v = *(const floatx4*)(region + rows_chunk<COLS>(r, q));
     if (has_c) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += to_f32<DT>(cq[it][e]);
     }
-    *(u16x4*)(D + (m_base + r) * p.d_rs + n_base + 4 * q) =
-        u16x4{from_f32<DT>(v[0]), from_f32<DT>(v[1]), from_f32<DT>(v[2]), from_f32<DT>(v[3])};
+    const u16x4 d = u16x4{from_f32<DT>(v[0]), from_f32<DT>(v[1]), from_f32<DT>(v[2]), from_f32<DT>(v[3])};
+    u16x4* dp = (u16x4*)(D + (m_base + r) * p.d_rs + n_base + 4 * q);
+    if constexpr (NT)
+      __builtin_nontemporal_store(d, dp);
+    else
+      *dp = d;
   }
 }
 

@@ -327,8 +327,9 @@ def test_ring_kernel_broadcast_a_and_c(api, M, N, monkeypatch):
 
 # zero strides inside the matrix dimensions: C as a bias row (0, 1) or a
 # column (1, 0), A or B with row stride 0 (every row the same), on full
-# 256 x 256 tiles (ring kernel: row epilogue and C-line prefetch) and on
-# ragged ones (per-quad epilogue); the planner's tile and the ring tile
+# 256 x 256 tiles (row epilogues; the ring kernel's C-line prefetch) and on
+# ragged ones (per-quad epilogue); the planner's tile, the 8-wave tile and
+# the ring tile
 ZERO_STRIDE = [
     # M, N, K, which operand broadcasts, how
     (512, 512, 576, "c", "row"),
@@ -343,7 +344,7 @@ ZERO_STRIDE = [
 ]
 
 
-@pytest.mark.parametrize("tile", [None, 19])
+@pytest.mark.parametrize("tile", [None, 4, 19])
 @pytest.mark.parametrize("case", ZERO_STRIDE, ids=lambda c: "x".join(map(str, c[:3])) + f"_{c[3]}_{c[4]}")
 def test_zero_stride_inside_the_matrix(api, case, tile, monkeypatch):
     """A zero stride inside a matrix dimension reads one element for every
@@ -355,7 +356,7 @@ def test_zero_stride_inside_the_matrix(api, case, tile, monkeypatch):
     M, N, K, which, how = case
     if tile is not None:
         if K < 64 or (M, N) == (264, 96):
-            pytest.skip("the ring tile is for outputs without a K-split")
+            pytest.skip("the forced tiles are for outputs without a K-split")
         monkeypatch.setenv("SL_TILE", str(tile))
     rng = np.random.default_rng(M + N + K + ord(which))
     A = rng.integers(-4, 5, (M, K)).astype(np.float16)
@@ -603,6 +604,8 @@ BF16_EXACT = [
     (1000, 776, 1032, 2, "row", "row", True, 19),
     (520, 300, 328, None, "row", "row", True, 20),
     (264, 520, 200, 2, "col", "row", True, 19),   # M-major A through the ring kernel's direct copies
+    (512, 512, 320, None, "col", "row", True, 4),  # 8-wave kernel, full tiles: row epilogue with C
+    (512, 256, 128, 2, "row", "row", True, 4),
 ]
 
 
