@@ -15,7 +15,12 @@ MXFP4; row and per-quad epilogues):
 - no vector-ALU write reaches an MFMA operand (data or scale) within 4
   instructions;
 - after the last MFMA, at least 18 wait states pass before the first
-  accumulator is read (the instruction's passes plus two need fewer).
+  accumulator is read (the instruction's passes plus two need fewer);
+- every s_barrier comes after a wait for all of the wave's LDS reads
+  (lgkmcnt(0)) with no LDS read between: after the barrier other waves
+  overwrite the ring slots this wave has just read.  The wait is issued
+  through the compiler's builtin, which its wait-count pass may merge with a
+  neighbouring wait; this checks that it survives as a full LDS wait.
 """
 
 import os
@@ -154,3 +159,83 @@ def test_ring_kernel_accumulator_discipline(code_objects, dtype):
     assert reads, "accumulators never read"
     nops = sum(int(o[1]) + 1 for o in ops[last + 1:reads[0]] if o[0] == "s_nop")
     assert nops >= 18, f"{nops} wait states before the first accumulator read ({L[reads[0]]})"
+
+
+
+def disassemble_cfg(cos, symbol):
+    """(instruction, successor indices) per instruction of the symbol, from
+    the disassembly's addresses and branch targets."""
+    for co in cos:
+        r = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", f"--disassemble-symbols={symbol}",
+                            co], check=True, capture_output=True, text=True)
+        ins = []
+        for line in r.stdout.splitlines():
+            m = re.match(r"\s+(\S.*?)\s*//\s*([0-9A-Fa-f]+):", line)
+            if m:
+                t = re.search(r"<[^>+]+\+0x([0-9a-fA-F]+)>", line)
+                ins.append((m.group(1).strip(), int(m.group(2), 16), int(t.group(1), 16) if t else None))
+        if any(i[0].startswith("v_mfma") for i in ins):
+            break
+    else:
+        raise AssertionError(f"{symbol} not found in the library's code objects")
+    base = ins[0][1]
+    at = {addr: k for k, (_, addr, _) in enumerate(ins)}
+    succ = []
+    for k, (text, addr, off) in enumerate(ins):
+        op = text.split()[0]
+        nxt = [] if op in ("s_branch", "s_endpgm", "s_setpc_b64") or k + 1 == len(ins) else [k + 1]
+        if op.startswith("s_cbranch") or op == "s_branch":
+            assert off is not None and base + off in at, f"branch target of {text} not found"
+            nxt.append(at[base + off])
+        succ.append(nxt)
+    return [i[0] for i in ins], succ
+
+
+def unwaited_lds_before(text, succ, b):
+    """An LDS instruction from which some path reaches instruction b without
+    passing an s_waitcnt with lgkmcnt(0), or None."""
+    pred = [[] for _ in text]
+    for k, ss in enumerate(succ):
+        for j in ss:
+            pred[j].append(k)
+    seen, stack = set(), list(pred[b])
+    while stack:
+        k = stack.pop()
+        if k in seen:
+            continue
+        seen.add(k)
+        t = text[k]
+        if t.startswith("s_waitcnt") and "lgkmcnt(0)" in t:
+            continue
+        if t.startswith("ds_"):
+            return t
+        stack.extend(pred[k])
+    return None
+
+
+def test_unwaited_lds_walk_on_small_graphs():
+    """The path walk on hand-made instruction lists: a straight line, a
+    branch around the wait, and a loop whose back edge skips it."""
+    line = ["ds_read_b128 v[0:3], v4", "s_waitcnt lgkmcnt(0)", "s_barrier"]
+    assert unwaited_lds_before(line, [[1], [2], []], 2) is None
+    assert unwaited_lds_before(["ds_read_b128 v[0:3], v4", "s_waitcnt lgkmcnt(1)", "s_barrier"], [[1], [2], []], 2)
+    # 0: read, 1: conditional branch to 3 (skips the wait at 2), 3: barrier
+    br = ["ds_read_b128 v[0:3], v4", "s_cbranch_scc1 1", "s_waitcnt lgkmcnt(0)", "s_barrier"]
+    assert unwaited_lds_before(br, [[1], [2, 3], [3], []], 3) == br[0]
+    # loop 0..3 with the barrier at its top: 0 barrier, 1 wait, 2 read, 3 branch back to 0
+    lp = ["s_barrier", "s_waitcnt lgkmcnt(0)", "ds_read_b128 v[0:3], v4", "s_cbranch_scc1 -4"]
+    assert unwaited_lds_before(lp, [[1], [2], [3], [0]], 0) == lp[2]
+    lp_ok = ["s_barrier", "ds_read_b128 v[0:3], v4", "s_waitcnt lgkmcnt(0)", "s_cbranch_scc1 -4"]
+    assert unwaited_lds_before(lp_ok, [[1], [2], [3], [0]], 0) is None
+
+
+@pytest.mark.parametrize("dtype", sorted(KERNELS))
+def test_ring_kernel_barriers_follow_lds_waits(code_objects, dtype):
+    text, succ = disassemble_cfg(code_objects, KERNELS[dtype][0])
+    bars = [k for k, t in enumerate(text) if t.split()[0] == "s_barrier"]
+    assert bars, "no barrier"
+    for b in bars:
+        # every path into the barrier passes a full LDS wait after its last
+        # LDS instruction (or has none)
+        t = unwaited_lds_before(text, succ, b)
+        assert t is None, f"a path reaches the barrier at {b} from {t} without an lgkmcnt(0) wait"
