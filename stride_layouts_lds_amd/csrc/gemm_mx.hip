@@ -458,7 +458,8 @@ __device__ __forceinline__ void mfma_scale_acc(floatx16& c, u32x4 a, u32x4 b, ui
 // the second half of the previous tile's last slice, the copy of B(t+1);
 // then every slice but the last with the reads of the next slice (and, in
 // slice 0, the copy of A(t+2)) interleaved; the first half of the last
-// slice; one barrier.  The ring takes all of the LDS, so the scales go
+// slice; one barrier.  (E2M1 spreads its copies over more slices: see
+// copies below.)  The ring takes all of the LDS, so the scales go
 // straight to registers: per TPC K-tiles each lane loads the 16-byte scale
 // chunk of each of its rows (4 of A, 4 of B; scale rows of a multiple of 16
 // blocks on 16-byte boundaries) into a second register set, issued two
@@ -597,6 +598,26 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
     if constexpr (KFULL) ld.issue_full(kt(u), dst, j);
     else ld.issue_one(kt(u), dst, j);
   };
+  // the copies of step g of phase ph of K-tile t (phase 0: part (1), phase
+  // s + 1: slice s with the reads of slice s + 1).  E4M3 and 6-bit data:
+  // B(t+1) over part (1), A(t+2) over slice 0, one per step.  E2M1 has four
+  // slices of 32-cycle MFMAs, so its part (1) holds a quarter of the MFMA
+  // cycles of E4M3's: its copies go every other step, B(t+1) over part (1)
+  // and slice 0, A(t+2) over slices 1 and 2 (2-3% faster; the same spread
+  // made 6-bit data 2% slower).  B's copies always precede A's, so the
+  // barrier's count of copies left in flight covers A's alone.
+  auto copies = [&](int ph, int g, int32_t t, int32_t s3, int32_t s4) {
+    if constexpr (F4) {
+      if (g % 2 == 0) {
+        if (ph <= 1) copy(lb, t + 1, slot(s3), 4 * ph + g / 2);
+        else copy(la, t + 2, slot(s4), 4 * (ph - 2) + g / 2);
+      }
+    } else {
+      if (ph == 0 && g < LOADS) copy(lb, t + 1, slot(s3), g);
+      if (ph == 1 && g < LOADS) copy(la, t + 2, slot(s4), g);
+    }
+  };
+  static_assert(!F4 || (LOADS == 8 && KS == 4), "E2M1 copy plan: 8 copies per operand over four slices");
   // fragment of k-slice ks for row block g of the wave (the probed operand
   // orders: E4M3 two 16-byte pieces K/2 apart; E2M1 the lane's 32
   // consecutive k in 16 bytes; 6-bit data its 32 consecutive k in 24 bytes,
@@ -716,7 +737,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
           fb[0][g] = rd(bB, g, 0);
         else
           fa[0][g - 4] = rd(bA, g - 4, 0);
-        if (g < LOADS) copy(lb, t + 1, slot(s3), g);
+        copies(0, g, t, s3, s4);
         const int i = FM / 2 + g / FN, j = g % FN;
         mfma_scale_acc<FMT, 1>(acc[i][j], fb[1][j], fa[1][i], sbp[j], sap[i]);
         __builtin_amdgcn_sched_barrier(0);
@@ -730,7 +751,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx_w4r_kernel(const GemmParams p)
             fb[(s + 1) % 2][g] = rd(bB, g, s + 1);
           else
             fa[(s + 1) % 2][g - 4] = rd(bA, g - 4, s + 1);
-          if (s == 0 && g < LOADS) copy(la, t + 2, slot(s4), g);
+          copies(s + 1, g, t, s3, s4);
           mfma_range(s_c, 2 * g, 2);
           __builtin_amdgcn_sched_barrier(0);
         }
