@@ -301,14 +301,15 @@ def test_broadcast_b_across_batch(api):
     assert np.array_equal(h.d_codes(out), d_ref)
 
 
+@pytest.mark.parametrize("tile", [19, 4])
 @pytest.mark.parametrize("M,N", [(512, 256), (300, 264)], ids=["rows", "quads"])
-def test_ring_kernel_broadcast_a_and_c(api, M, N, monkeypatch):
+def test_ring_kernel_broadcast_a_and_c(api, M, N, tile, monkeypatch):
     """A and C shared across a batch of B (batch stride 0 on both) through
-    the ring kernel, with the row epilogue (full tiles) and the per-quad one
-    (ragged edges)."""
+    the ring kernel (tile 19) and the 8-wave kernel (tile 4), with the row
+    epilogue (full tiles) and the per-quad one (ragged edges)."""
     import torch
     h = H()
-    monkeypatch.setenv("SL_TILE", "19")
+    monkeypatch.setenv("SL_TILE", str(tile))
     rng = np.random.default_rng(M + N)
     nb, K = 3, 576
     A = rng.integers(-4, 5, (M, K)).astype(np.float16)
