@@ -326,6 +326,38 @@ def test_ring_kernel_broadcast_a_and_c(api, M, N, tile, monkeypatch):
     assert np.array_equal(h.d_codes(out), d_ref)
 
 
+@pytest.mark.parametrize("with_c", [False, True], ids=["noc", "c"])
+@pytest.mark.parametrize("M,N", [(300, 261), (512, 387), (520, 384)])
+def test_ring_192_edges(api, M, N, with_c, monkeypatch):
+    """The 256 x 192 ring tile at the edges: M and N not multiples of the
+    tile, N not a multiple of 4 (D and C rows padded to a multiple of 4, so
+    the rows are vector-aligned while the quad that crosses N is stored
+    element by element); the padding columns are never written."""
+    import torch
+    h = H()
+    monkeypatch.setenv("SL_TILE", "20")
+    rng = np.random.default_rng(M * 7 + N)
+    K, NP = 200, (N + 3) // 4 * 4
+    A = rng.integers(-4, 5, (M, K)).astype(np.float16)
+    B = rng.integers(-4, 5, (N, K)).astype(np.float16)
+    Cf = rng.integers(-64, 65, (M, NP)).astype(np.float16)
+    c = torch.from_numpy(Cf).cuda()[:, :N] if with_c else None
+    dbuf = torch.full((M, NP), float("nan"), dtype=torch.float16, device="cuda")
+    out = dbuf[:, :N]
+    args = api.make_args(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), c, out)
+    plan = api.sl_gemm_plan(args)
+    h.log(f"ring 192 edges M={M} N={N} c={with_c} plan={plan}")
+    assert plan["tile_n"] == 192
+    api.gemm(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), c, out=out)
+    torch.cuda.synchronize()
+    from oracle import gemm as OG
+    cv = np.ascontiguousarray(Cf[:, :N]).view(np.uint16) if with_c else None
+    d_ref, _, _ = OG.gemm(A.view(np.uint16), B.view(np.uint16), cv)
+    assert np.array_equal(h.d_codes(out), d_ref[0])
+    # the padding columns are never written
+    assert torch.isnan(dbuf[:, N:]).all().item()
+
+
 # zero strides inside the matrix dimensions: C as a bias row (0, 1) or a
 # column (1, 0), A or B with row stride 0 (every row the same), on full
 # 256 x 256 tiles (row epilogues; the ring kernel's C-line prefetch) and on
@@ -345,7 +377,7 @@ ZERO_STRIDE = [
 ]
 
 
-@pytest.mark.parametrize("tile", [None, 4, 19])
+@pytest.mark.parametrize("tile", [None, 4, 19, 20])
 @pytest.mark.parametrize("case", ZERO_STRIDE, ids=lambda c: "x".join(map(str, c[:3])) + f"_{c[3]}_{c[4]}")
 def test_zero_stride_inside_the_matrix(api, case, tile, monkeypatch):
     """A zero stride inside a matrix dimension reads one element for every
