@@ -107,6 +107,7 @@ constexpr int32_t F_BF16 = 16;    // A, B, C and D are bf16 (else fp16)
 constexpr int32_t F_FP4 = 32;     // MX operands are packed E2M1 (MXFP4), else E4M3
 constexpr int32_t F_FP6 = 64;     // MX operands are packed 6-bit E2M3 (MXFP6)
 constexpr int32_t F_FP6_E3M2 = 128;  // MX operands are packed 6-bit E3M2 (MXFP6)
+constexpr int32_t kCUs = 256;     // compute units of an MI355X: one round of single-workgroup-per-CU tiles
 
 // element type of the 16-bit GEMM kernels (template argument)
 constexpr int DT_F16 = 0;
