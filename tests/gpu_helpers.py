@@ -135,10 +135,3 @@ def assert_within_bound(d: np.ndarray, d_ref: np.ndarray, absum: np.ndarray, wha
                              f"worst index {wi}: D={dd} Dref={rr} S={absum.ravel()[wi]} "
                              f"(error/bound {wr:.3g})")
 
-
-def dump(name: str, arr) -> None:
-    """Save an array under gpurun_out/ for offline reading (debug aid)."""
-    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
-    if os.environ.get("SL_DUMP"):
-        os.makedirs(d, exist_ok=True)
-        np.save(os.path.join(d, name + ".npy"), np.asarray(arr))

@@ -233,7 +233,7 @@ def test_fragment_reads_conflict_free_under_the_page_bank_model(api):
     """Under the data-layout page's bank model (32 banks x 4 B, 16-byte
     accesses served 8 lanes per pass) every ds_read_b128 of a fragment load
     takes the minimum 8 passes with the default swizzle, and 8x that
-    without it.  The gfx950 verdict is the hardware counter."""
+    without it.  On gfx950 the hardware counter decides."""
     addrs = api.query_fragment_addresses(1, 0).reshape(64, 8)[:, 0]
     assert L.bank_conflict_passes(addrs.tolist(), 16, 32, 4, 8) == 8
     plain = [r * 128 + c * 2 for _, v, r, c in L.MFMA16_F16_A.table() if v == 0]
