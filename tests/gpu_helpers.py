@@ -4,7 +4,6 @@ oracle (full or at sampled points)."""
 
 from __future__ import annotations
 
-import os
 import sys
 
 import numpy as np
