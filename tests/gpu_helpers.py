@@ -4,6 +4,7 @@ oracle (full or at sampled points)."""
 
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -134,3 +135,11 @@ def assert_within_bound(d: np.ndarray, d_ref: np.ndarray, absum: np.ndarray, wha
                              f"worst index {wi}: D={dd} Dref={rr} S={absum.ravel()[wi]} "
                              f"(error/bound {wr:.3g})")
 
+
+def dump(name: str, arr) -> None:
+    """Save an array as <name>.npy in the directory named by SL_DUMP, for
+    offline reading (a debug aid: nothing is written when it is unset)."""
+    d = os.environ.get("SL_DUMP")
+    if d:
+        os.makedirs(d, exist_ok=True)
+        np.save(os.path.join(d, name + ".npy"), np.asarray(arr))
