@@ -210,12 +210,14 @@ RING = [
     (520, 300, 328, None, True),
     (1000, 776, 1032, 2, True),
     (264, 520, 4104, None, False),
-    # with C at 2, 3 and 5 K-tiles: the C lines loaded ahead during the last
-    # four K-tiles (a window that starts before the first one, or not), full
-    # tiles for the row epilogue
+    # with C at 2, 3, 5, 8 and 9 K-tiles: the C lines loaded ahead during the
+    # last eight K-tiles (a window that starts before the first one, with it,
+    # or after it), full tiles for the row epilogue
     (512, 256, 128, None, True),
     (256, 512, 192, 2, True),
     (512, 512, 320, None, True),
+    (512, 256, 512, None, True),
+    (256, 512, 576, 2, True),
 ]
 
 
