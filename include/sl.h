@@ -199,6 +199,23 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream);
 #define SL_NO_ALLOC_SCRATCH_BYTES (32LL << 20)
 sl_status sl_gemm_no_alloc(const sl_gemm_args* args, void* stream);
 
+/*
+ * Planner overrides, read from the environment on every planning call (by
+ * sl_gemm, sl_gemm_no_alloc, sl_gemm_plan and the calls built on it).  They
+ * exist for measurement and tests; unset, the planner's own choices hold.
+ * A value a shape cannot use is replaced by the planner's choice.
+ *   SL_TILE=n       the library's tile configuration n, 0-20 (4: the 8-wave
+ *                   256x256 kernel, 19: the 4-wave 256x256 ring kernel, 20:
+ *                   the 256x192 ring kernel); the plan reports its tile_m/n/k
+ *   SL_GROUP_M=n    output-tile rows per group in each XCD's tile order
+ *                   (default 8, at least 1)
+ *   SL_SPLITK=n     split count of the split-K tiles (default: from the grid)
+ *   SL_SCALE16=0    MXFP8: no 16-byte scale chunks (so no 4-wave ring kernel)
+ *   SL_NV_PAIRS=0   NVFP4: fetch one K-tile per load instead of two
+ *   SL_MN_LOADER=1  8-wave 256x256 kernel: M/N-contiguous operands through
+ *                   the register-transposing loader instead of direct copies
+ */
+
 /* Validation and kernel selection only: fills *plan, launches nothing and
  * makes no HIP call.  Same status codes as sl_gemm, except that the
  * workspace fields are not checked. */
