@@ -344,6 +344,56 @@ def test_plan_split_k_for_skinny_outputs(api):
     assert p["split_k"] == 1
 
 
+def test_planner_environment_overrides(api, monkeypatch):
+    """The environment overrides sl.h lists change the plan as stated, and a
+    value a shape cannot use leaves the planner's own choice (SL_GROUP_M
+    changes only the tile order inside the kernels, which the plan does not
+    report)."""
+    sq = (rowmajor(BASE_A, (8192, 8192)), rowmajor(BASE_B, (8192, 8192)), None, rowmajor(BASE_D, (8192, 8192)))
+    base = plan(api, *sq)
+    assert base["threads"] == 256 and base["lds_bytes"] == 5 * 32768  # the 4-wave ring kernel
+    monkeypatch.setenv("SL_TILE", "4")
+    p = plan(api, *sq)
+    assert p["threads"] == 512 and (p["tile_m"], p["tile_n"]) == (256, 256)
+    monkeypatch.setenv("SL_TILE", "99")
+    assert plan(api, *sq) == base
+    monkeypatch.delenv("SL_TILE")
+
+    sk = (rowmajor(BASE_A, (8192, 8192)), rowmajor(BASE_B, (128, 8192)), None, rowmajor(BASE_D, (8192, 128)))
+    monkeypatch.setenv("SL_SPLITK", "2")
+    p = plan(api, *sk)
+    assert p["split_k"] == 2 and p["workspace_bytes"] == 2 * 8192 * 128 * 4
+    monkeypatch.delenv("SL_SPLITK")
+
+    # MXFP8 with 16 scale blocks per row: the ring kernel, or without
+    # 16-byte scale chunks the 8-wave one
+    E4, E8, M, K = 3, 4, 4096, 512
+    mx = ((BASE_A, E4, (M, K), (K, 1)), (BASE_B, E4, (M, K), (K, 1)), None, rowmajor(BASE_D, (M, M)),
+          (BASE_C, E8, (M, K // 32), (K // 32, 1)), (BASE_C + 0x100000, E8, (M, K // 32), (K // 32, 1)))
+    assert plan(api, *mx)["kernel"] == api.K_MX_W4R
+    monkeypatch.setenv("SL_SCALE16", "0")
+    assert plan(api, *mx)["kernel"] == api.K_MX_W8
+    monkeypatch.delenv("SL_SCALE16")
+
+    # NVFP4: the paired loader (5), or one K-tile per fetch (4)
+    E2, N, K = 6, 256, 1024
+    nv = ((BASE_A, E2, (512, K), (K, 1)), (BASE_B, E2, (N, K), (K, 1)), None, rowmajor(BASE_D, (512, N)),
+          (BASE_C, E4, (512, K // 16), (K // 16, 1)), (BASE_C + 0x100000, E4, (N, K // 16), (K // 16, 1)))
+    assert (plan(api, *nv, block_k=16)["a_load"]) == 5
+    monkeypatch.setenv("SL_NV_PAIRS", "0")
+    assert (plan(api, *nv, block_k=16)["a_load"]) == 4
+    monkeypatch.delenv("SL_NV_PAIRS")
+
+    # M- and N-contiguous operands of the 8-wave kernel: direct copies (3),
+    # or the register-transposing loader (1)
+    nb, M, N, K = 64, 512, 512, 512
+    mn = ((BASE_A, F16, (nb, M, K), (M * K, 1, M)), (BASE_B, F16, (nb, N, K), (N * K, 1, N)), None,
+          (BASE_D, F16, (nb, M, N), (M * N, N, 1)))
+    assert (plan(api, *mn)["a_load"], plan(api, *mn)["b_load"]) == (3, 3)
+    monkeypatch.setenv("SL_MN_LOADER", "1")
+    assert (plan(api, *mn)["a_load"], plan(api, *mn)["b_load"]) == (1, 1)
+
+
 def test_split_k_workspace_is_the_callers(api):
     """A split-K plan needs a caller workspace of splits * batch * M * N fp32:
     the plan and sl_gemm_workspace_bytes report its size, and sl_gemm
