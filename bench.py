@@ -4,8 +4,11 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-vendor]
 
 A step is one call of sl_gemm over the workload's operands, already resident
-in HBM.  W untimed steps, then K steps timed between two device
-synchronisations; HIP events on the launch stream give the kernel's
+in HBM.  W untimed steps (without --warmup: at least 10 steps and at least
+one second of them, so that the timed region runs at the clock the chip
+sustains under this load -- from idle it takes a fraction of a second to
+get there, and 10 warm-up steps of the 8192^3 default left the next 50
+3-4% slow), then K steps timed between two device synchronisations; HIP events on the launch stream give the kernel's
 average duration for the roofline object (for the HBM-bound workloads, the
 median of launches timed after a 512 MiB read, so that the inputs come from
 HBM rather than the Infinity Cache).  Prints one JSON line.
@@ -160,7 +163,8 @@ def vendor_timing(w, a, b, c, sfa, sfb, out, stream, reps: int = 20):
     context (not a baseline): torch.addmm / torch.mm for the single fp16
     products with K-contiguous A and B (C + A B^T), torch._scaled_mm with
     E8M0 block scales for MXFP8.  Average launch time over `reps` launches
-    between HIP events on the launch stream, and the relative Frobenius
+    between HIP events on the launch stream after at least a second of
+    back-to-back warm-up calls, and the relative Frobenius
     difference of its D from the library's (`out`, which holds the
     library's result).  None for the other workloads."""
     import torch
@@ -192,8 +196,14 @@ def vendor_timing(w, a, b, c, sfa, sfb, out, stream, reps: int = 20):
     ref = out.float()
     diff = ((r.float() - ref).norm() / ref.norm().clamp_min(1e-30)).item()
     del r
-    for _ in range(3):
-        fn()
+    # the same warm-up as the library's default: at least one second of
+    # back-to-back calls, so that both are timed at the sustained clock
+    n, t_w = 0, time.perf_counter()
+    while n < 10 or time.perf_counter() - t_w < 1.0:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -240,7 +250,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed region (default: at least 10 and at least 1 s of them)")
     ap.add_argument("--workload", default="fp16_8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-vendor", action="store_true",
@@ -289,9 +300,19 @@ def main():
     sid = stream.cuda_stream
 
     print(f"[bench] plan {plan}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        api.sl_gemm(margs, sid)
+    if args.warmup is None:
+        warmup, t_w = 0, time.perf_counter()
+        while warmup < 10 or time.perf_counter() - t_w < 1.0:
+            for _ in range(10):
+                api.sl_gemm(margs, sid)
+            warmup += 10
+            torch.cuda.synchronize()
+    else:
+        warmup = args.warmup
+        for _ in range(warmup):
+            api.sl_gemm(margs, sid)
     torch.cuda.synchronize()
+    print(f"[bench] {warmup} warm-up steps", file=sys.stderr, flush=True)
 
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -344,7 +365,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
