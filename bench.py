@@ -264,7 +264,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     rank = int(os.environ.get("RANK", "0"))

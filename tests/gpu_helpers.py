@@ -1,5 +1,5 @@
 """Shared helpers of the GPU tests: move seeded host operands to the device
-with their strides, run the library, and judge its output against the
+with their strides, run the library, and check its output against the
 oracle (full or at sampled points)."""
 
 from __future__ import annotations
