@@ -38,12 +38,15 @@
  *    gives D = C (or D = 0).
  *  - Ownership: the caller owns every buffer, the library allocates no
  *    device memory, and sl_gemm() keeps no pointer after it returns.  A
- *    split-K plan (sl_plan.split_k > 1) needs an fp32 workspace of
- *    sl_plan.workspace_bytes (also given by sl_gemm_workspace_bytes()),
- *    which the caller passes in sl_gemm_args.workspace: device memory,
- *    16-byte aligned, overlapping no operand, and not used by anything
- *    else until the call's kernels have finished on `stream`.  Plans
- *    without a split ignore the workspace fields.
+ *    plan with sl_plan.workspace_bytes > 0 (also given by
+ *    sl_gemm_workspace_bytes()) needs that much workspace, which the
+ *    caller passes in sl_gemm_args.workspace: device memory, 16-byte
+ *    aligned, overlapping no operand, and not used by anything else until
+ *    the call's kernels have finished on `stream`.  Two kinds of plan have
+ *    one: a split-K plan (sl_plan.split_k > 1) keeps its fp32 partial sums
+ *    there, and an NVFP4 plan that decodes its operands ahead (kernel 5
+ *    with a_load 0) keeps A and B there as fp16 rows.  Other plans ignore
+ *    the workspace fields.
  *  - Execution: validation runs on the host before any HIP call; a failure
  *    returns a negative sl_status and sets the thread-local message.  On
  *    success the kernel is launched asynchronously on `stream` (a
@@ -117,8 +120,9 @@ typedef struct {
   sl_tensor sfa;   /* (batch?, M, ceil(K/block_k)) e8m0 (MXFP8) or f8_e4m3 (NVFP4) */
   sl_tensor sfb;   /* (batch?, N, ceil(K/block_k)) same dtype as sfa       */
   int32_t block_k; /* 32 for MXFP8, 16 for NVFP4; ignored for f16 / bf16   */
-  void* workspace;          /* device memory for a split-K plan's fp32 partial
-                               sums (NULL when the plan has no split) */
+  void* workspace;          /* device memory for a plan's workspace: split-K
+                               fp32 partial sums or decoded NVFP4 operands
+                               (NULL when the plan needs none) */
   int64_t workspace_bytes;  /* its size in bytes */
 } sl_gemm_args;
 
@@ -128,7 +132,10 @@ typedef struct {
                          element loader, 3 mxfp8 (4 waves, 16x16x128
                          instruction), 4 mxfp8 (8 waves, 32x32x64 instruction,
                          scales staged in LDS), 5 nvfp4 (decoded to fp16 in
-                         the loader, fp16 instruction), 6 mxfp4 and 7 mxfp6
+                         the loader, fp16 instruction; from 2048^3 on, or
+                         with SL_NV_DECODE=1, and K % 64 == 0: decoded
+                         ahead into the workspace by a first kernel, then
+                         the fp16 4-wave ring kernel, a_load 0), 6 mxfp4 and 7 mxfp6
                          (32x32x64 scaled instruction with E2M1 or 6-bit
                          data: 4 waves on an LDS ring, scales in registers;
                          8 waves when K == 0 or tile 4 is asked for),
@@ -174,7 +181,7 @@ typedef struct {
  * span fewer than 2^31 bytes for the vector loaders of 16-bit operands
  * (else the slower element loader runs), and for packed 4/6-bit data and
  * scale tensors (else SL_ERR_SHAPE).
- * A split-K plan reads args->workspace: NULL returns SL_ERR_NULL, fewer
+ * A plan with a workspace reads args->workspace: NULL returns SL_ERR_NULL, fewer
  * than the plan's workspace bytes SL_ERR_SHAPE, an address not on a 16-byte
  * boundary SL_ERR_ALIGN, and a range overlapping an operand SL_ERR_ALIAS,
  * all before any HIP call.
@@ -187,7 +194,9 @@ sl_status sl_gemm(const sl_gemm_args* args, void* stream);
  * graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same validation, plans and kernels, but a split-K plan keeps its fp32
  * partial sums in a static device array of the library instead of the
- * caller's workspace (args->workspace and workspace_bytes are ignored).
+ * caller's workspace (args->workspace and workspace_bytes are ignored), and
+ * NVFP4 always runs the fused kernels (no decoded copies; its plan can
+ * differ from sl_gemm_plan's, with the same result bit for bit).
  * The call allocates nothing.  The array holds SL_NO_ALLOC_SCRATCH_BYTES
  * bytes on each GPU the library runs on and is held until the process ends;
  * a plan needing more (sl_plan.workspace_bytes) returns SL_ERR_SHAPE before
@@ -214,6 +223,8 @@ sl_status sl_gemm_no_alloc(const sl_gemm_args* args, void* stream);
  *   SL_NV_PAIRS=0   NVFP4: fetch one K-tile per load instead of two
  *   SL_MN_LOADER=1  8-wave 256x256 kernel: M/N-contiguous operands through
  *                   the register-transposing loader instead of direct copies
+ *   SL_NV_DECODE=0  NVFP4: never decode ahead into the workspace (=1: always,
+ *                   when K % 64 == 0; unset: from 2048^3 on, without SL_TILE)
  */
 
 /* Validation and kernel selection only: fills *plan, launches nothing and

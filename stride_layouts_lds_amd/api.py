@@ -235,9 +235,9 @@ def gemm(a, b, c=None, out=None, sfa=None, sfb=None, block_k: int = 32, stream: 
     """D = A B^T + C on torch tensors (any strides).  ``a``: (batch?, M, K)
     fp16, bf16 or float8_e4m3fn; ``b``: (batch?, N, K); ``c``: (batch?, M, N)
     of D's dtype (bf16 for bf16 operands, else fp16) or None; ``sfa``/``sfb``: float8_e8m0fnu scales (batch?, rows, K/32) for
-    the MX form.  A split-K plan's workspace is ``workspace`` (a device
-    tensor) or, when None, a torch allocation of the size the library asks
-    for.  Returns ``out`` (allocated by torch if None)."""
+    the MX form.  A plan's workspace (split-K partial sums, or NVFP4
+    operands decoded to fp16) is ``workspace`` (a device tensor) or, when
+    None, a torch allocation of the size the library asks for.  Returns ``out`` (allocated by torch if None)."""
     import torch
     if out is None:
         batch = max(x.shape[0] if x is not None and x.dim() == 3 else 0 for x in (a, b, c))

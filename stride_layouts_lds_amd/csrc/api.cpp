@@ -129,7 +129,10 @@ struct Plan {
   int32_t tile;
   bool mx;
   bool empty;
-  size_t ws_bytes;  // split-K partial sums (0: none)
+  size_t ws_bytes;  // workspace: split-K partial sums, or NVFP4 operands decoded to fp16 (0: none)
+  bool nv_dec;      // NVFP4 decoded ahead into the workspace, then the fp16 ring kernel
+  sl::Nvfp4Decode dec[2];  // A and B (out set at launch)
+  size_t dec_off_b, dec_bytes;  // B's offset in the workspace, and the total
   // byte ranges of the operands with data, for the workspace overlap check
   uintptr_t lo[6], hi[6];
   int32_t nranges;
@@ -176,7 +179,7 @@ double tile_cost(const sl::TileShape& t, int64_t batch, int64_t M, int64_t N, in
   return (double)waves * (double)t.bm * (double)t.bn * (double)std::max<int64_t>(K, 64) * per_cu / eff;
 }
 
-sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
+sl_status plan_gemm(const sl_gemm_args* args, Plan* out, bool allow_decode = true) {
   g_msg.clear();
   if (!args) return fail(SL_ERR_NULL, "args is NULL");
   const bool fp4 = args->a.dtype == SL_F4_E2M1;
@@ -363,14 +366,50 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
              (S.t->layout.rank == 2 || S.bs % 8 == 0);
     };
     const bool pairs = pair_rows(SA) && pair_rows(SB) && env_int("SL_NV_PAIRS", 1);
-    // the 8-wave kernel; the 4-wave ring schedule (tile 19, K > 0) only when
-    // asked for: with one wave per SIMD the decode between the MFMAs made
-    // it 25% slower on 8192^3
-    tile = K > 0 && tile == sl::T256x256_W4R ? sl::T256x256_W4R : sl::T256x256_W2x4;
-    P.pub.kernel = sl::K_NVFP4;
-    P.pub.a_load = P.pub.b_load = pairs ? sl::LOAD_NVFP4_PAIRS : sl::LOAD_NVFP4;
-    P.pub.tile_k = 64;
-    p.k_tiles = (int32_t)((K + 63) / 64);
+    // Products of 2048^3 and more: both operands decoded to fp16 rows in the
+    // caller's workspace by a first kernel, then the fp16 4-wave ring kernel
+    // on them (the fused 8-wave kernel below decodes in its loader and runs
+    // at the 8-wave kernel's pace; 8192^3 took 1006 us fused against 755
+    // decoded ahead).  SL_NV_DECODE=0 / 1 forbids / forces it; an SL_TILE
+    // choice keeps the fused kernels; sl_gemm_no_alloc never decodes ahead.
+    const int32_t dec_env = env_int("SL_NV_DECODE", -1);
+    const bool dec_ok = allow_decode && K > 0 && K % 64 == 0 && (int64_t)256 * K * 2 < ((int64_t)1 << 31);
+    const bool dec = dec_ok && (dec_env == 1 || (dec_env < 0 && tile < 0 &&
+                                                 (double)batch * (double)M * (double)N * (double)K >= 0x1p33));
+    if (dec) {
+      auto dec_of = [&](const View& X, const View& S, int64_t rows) {
+        sl::Nvfp4Decode d{};
+        d.x = (const uint8_t*)X.t->data;
+        d.s = (const uint8_t*)S.t->data;
+        d.rows = rows, d.K = K, d.rs = X.rs, d.bs = X.t->layout.rank == 3 ? X.bs : 0;
+        d.srs = S.rs, d.sks = S.cs, d.sbs = S.t->layout.rank == 3 ? S.bs : 0;
+        d.batch = (int32_t)batch;
+        return d;
+      };
+      P.nv_dec = true;
+      P.dec[0] = dec_of(A, SA, M);
+      P.dec[1] = dec_of(B, SB, N);
+      P.dec_off_b = ((size_t)batch * (size_t)M * (size_t)K * 2 + 255) & ~(size_t)255;
+      P.dec_bytes = P.dec_off_b + (size_t)batch * (size_t)N * (size_t)K * 2;
+      // the fp16 product over the decoded rows (pointers set at launch)
+      p.sfa = p.sfb = nullptr;
+      p.a_rs = K, p.a_ks = 1, p.a_bs = M * K;
+      p.b_rs = K, p.b_ks = 1, p.b_bs = N * K;
+      tile = sl::T256x256_W4R;
+      P.pub.kernel = sl::K_NVFP4;
+      P.pub.a_load = P.pub.b_load = sl::LOAD_KVEC;
+      P.pub.tile_k = 64;
+      p.k_tiles = (int32_t)(K / 64);
+    } else {
+      // the 8-wave kernel; the 4-wave ring schedule (tile 19, K > 0) only when
+      // asked for: with one wave per SIMD the decode between the MFMAs made
+      // it 25% slower on 8192^3
+      tile = K > 0 && tile == sl::T256x256_W4R ? sl::T256x256_W4R : sl::T256x256_W2x4;
+      P.pub.kernel = sl::K_NVFP4;
+      P.pub.a_load = P.pub.b_load = pairs ? sl::LOAD_NVFP4_PAIRS : sl::LOAD_NVFP4;
+      P.pub.tile_k = 64;
+      p.k_tiles = (int32_t)((K + 63) / 64);
+    }
   } else if (mxfp6) {
     // packed 6-bit rows in the 8-wave scaled-MFMA kernel: K-contiguous rows
     // a multiple of 64 elements (48 bytes) apart on 16-byte boundaries, so
@@ -559,7 +598,7 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   P.pub.threads = ts.wm * ts.wn * 64;
   P.pub.split_k = p.splits;
   P.pub.workgroups = total;
-  P.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)M * (size_t)N * sizeof(float) : 0;
+  P.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)M * (size_t)N * sizeof(float) : P.dec_bytes;
   P.pub.workspace_bytes = (int64_t)P.ws_bytes;
   P.pub.lds_bytes = ts.stages * (ts.bm + ts.bn) * P.pub.tile_k * (mx && !nvfp4 ? 1 : 2);
   if (P.pub.kernel == sl::K_MXFP4 || P.pub.kernel == sl::K_MXFP6)
@@ -567,19 +606,19 @@ sl_status plan_gemm(const sl_gemm_args* args, Plan* out) {
   if (P.pub.kernel == sl::K_MX_W8)
     P.pub.lds_bytes += (p.flags & sl::F_SCALE16) ? 2 * (ts.bm + ts.bn) * 16 : ts.stages * (ts.bm + ts.bn) * 4;
   if (tile == sl::T256x256_W4R || tile == sl::T256x192_W4R)
-    P.pub.lds_bytes = nvfp4 ? 2 * 512 * 128   // two fp16 stages (the packed data waits in registers)
-                            : 5 * 256 * 128;  // five 32 KiB operand K-tile slots
+    P.pub.lds_bytes = nvfp4 && !P.nv_dec ? 2 * 512 * 128   // two fp16 stages (the packed data waits in registers)
+                                         : 5 * 256 * 128;  // five 32 KiB operand K-tile slots
   return SL_OK;
 }
 
-// The caller's split-K workspace: present, large enough, 16-byte aligned
-// (the partial sums are stored 16 bytes at a time) and apart from every
-// operand (the reduction reads it while writing D).
+// The caller's workspace (split-K partial sums, or NVFP4 operands decoded
+// to fp16): present, large enough, 16-byte aligned (it is written 16 bytes
+// at a time) and apart from every operand (it is read while D is written).
 sl_status check_workspace(const sl_gemm_args* args, const Plan& P) {
   if (!P.ws_bytes) return SL_OK;
   if (!args->workspace)
-    return fail(SL_ERR_NULL, "the plan splits K %d ways and needs a workspace of %zu bytes; workspace is NULL",
-                P.pub.split_k, P.ws_bytes);
+    return fail(SL_ERR_NULL, "the plan needs a workspace of %zu bytes (%s); workspace is NULL", P.ws_bytes,
+                P.nv_dec ? "NVFP4 operands decoded to fp16" : "split-K partial sums");
   if (args->workspace_bytes < 0 || (uint64_t)args->workspace_bytes < (uint64_t)P.ws_bytes)
     return fail(SL_ERR_SHAPE, "workspace of %lld bytes, the plan needs %zu", (long long)args->workspace_bytes,
                 P.ws_bytes);
@@ -652,10 +691,20 @@ int64_t parse_int(const char* text) {
   return v;
 }
 
-// The plan's kernels on `stream`; a split-K plan's partial sums go to `ws`.
+// The plan's kernels on `stream`; a split-K plan's partial sums, or the
+// decoded NVFP4 operands, go to `ws`.
 sl_status launch_plan(Plan& P, void* ws, hipStream_t st) {
   hipError_t e;
-  if (P.pub.kernel == sl::K_NVFP4) {
+  if (P.nv_dec) {
+    sl::Nvfp4Decode da = P.dec[0], db = P.dec[1];
+    da.out = (uint16_t*)ws;
+    db.out = (uint16_t*)((char*)ws + P.dec_off_b);
+    P.p.a = da.out;
+    P.p.b = db.out;
+    e = sl::launch_nvfp4_decode(da, st);
+    if (e == hipSuccess) e = sl::launch_nvfp4_decode(db, st);
+    if (e == hipSuccess) e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
+  } else if (P.pub.kernel == sl::K_NVFP4) {
     e = sl::launch_gemm_f16(P.p, P.tile, P.pub.a_load, P.pub.b_load, st);
   } else if (P.mx) {
     e = sl::launch_gemm_mx(P.p, P.tile, st);
@@ -725,7 +774,7 @@ static_assert(sl::kScratchBytes == (size_t)SL_NO_ALLOC_SCRATCH_BYTES, "one scrat
 
 sl_status sl_gemm_no_alloc(const sl_gemm_args* args, void* stream) {
   Plan P;
-  sl_status s = plan_gemm(args, &P);
+  sl_status s = plan_gemm(args, &P, false);  // NVFP4: the fused kernels, no decoded copies
   if (s != SL_OK) return s;
   if (P.empty) return SL_OK;
   if (P.ws_bytes > sl::kScratchBytes)
@@ -921,6 +970,7 @@ sl_status sl_describe_plan(const sl_gemm_args* args, char* out, int64_t capacity
   in.bm = ts.bm, in.bn = ts.bn, in.bk = P.pub.tile_k;
   in.wm = ts.wm, in.wn = ts.wn, in.stages = ts.stages;
   in.ring = P.tile == sl::T256x256_W4R || P.tile == sl::T256x192_W4R;
+  in.nv_decoded = P.nv_dec;
   in.splits = p.splits, in.split_tiles = p.split_tiles, in.group_m = p.group_m;
   in.tiles_m = p.tiles_m, in.tiles_n = p.tiles_n;
   in.workgroups = P.pub.workgroups, in.batch = P.pub.batch, in.M = p.M, in.N = p.N, in.K = p.K;

@@ -317,7 +317,15 @@ std::string describe_plan(const DescribeInput& in) {
     o.line("SFA", T({R(in.M, in.sa_rs), R(kb, in.sa_cs)}), fmt("%s scale of A(m, %d j .. %d j + %d)", fmt_s,
                                                                 in.block_k, in.block_k, in.block_k - 1));
     o.line("SFB", T({R(in.N, in.sb_rs), R(kb, in.sb_cs)}), fmt("%s scale of B(n, block)", fmt_s));
-    if (in.kernel == K_NVFP4) {
+    if (in.kernel == K_NVFP4 && in.nv_decoded) {
+      const int64_t bytes_a = in.batch * in.M * in.K * 2;
+      o.line("A_decoded", T({R(in.M, in.K), R(in.K, 1), R(in.batch, in.M * in.K)}),
+             "fp16 (m, k, batch) in the workspace from byte 0: a first kernel turns each 16-value block into "
+             "E2M1 x its E4M3 scale (exact in fp16)");
+      o.line("B_decoded", T({R(in.N, in.K), R(in.K, 1), R(in.batch, in.N * in.K)}),
+             fmt("fp16 (n, k, batch) in the workspace from byte %lld; the stages above read these rows, not the "
+                 "packed operands", (long long)((bytes_a + 255) / 256 * 256)));
+    } else if (in.kernel == K_NVFP4) {
       o.note("NVFP4: each lane decodes 8 E2M1 values and multiplies them by their E4M3 scale into exact fp16 "
              "before the LDS write; the fp16 path follows");
     } else {

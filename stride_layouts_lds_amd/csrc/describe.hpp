@@ -22,6 +22,7 @@ struct DescribeInput {
   int32_t block_k;  // scale block (MX 32, NVFP4 16)
   int32_t lds_bytes;
   bool ring;  // LDS as a ring of five operand K-tiles (the 4-wave 256x256 kernel)
+  bool nv_decoded;  // NVFP4 operands decoded to fp16 rows in the workspace by a first kernel
 };
 
 // One line per stage: "name: layout  # note" (the layout parses back with

@@ -1342,6 +1342,42 @@ hipError_t launch_splitk_reduce(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// An NVFP4 operand decoded to fp16 ahead of the product: rows x K packed
+// E2M1 values (element (b, r, k) at byte (b bs + r rs + k) / 2, low nibble
+// first) with one E4M3 scale per 16 K (at s + b sbs + r srs + (k / 16) sks)
+// become fp16 rows of K contiguous values, batch after batch.  A thread turns
+// one scale block (8 bytes, 16 values) into 32 bytes of fp16 with the fused
+// loader's arithmetic (e2m1x8_to_half8, then an fp16 product with the
+// decoded scale: exact), so the fp16 kernel that follows computes the same
+// result bit for bit.  Consecutive threads take consecutive blocks of a row.
+__global__ __launch_bounds__(256) void nvfp4_decode_kernel(const Nvfp4Decode d) {
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  auto mul = [](uint32_t x, _Float16 sc) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, x) * half2v{sc, sc});
+  };
+  const int64_t nb = d.K / 16;
+  const int64_t total = (int64_t)d.batch * d.rows * nb;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t kb = i % nb, rb = i / nb;  // rb = b rows + r
+    const int64_t r = rb % d.rows, b = rb / d.rows;
+    const u32x2 w = *(const u32x2*)(d.x + (b * d.bs + r * d.rs) / 2 + kb * 8);
+    const _Float16 sc = e4m3_to_half(d.s[b * d.sbs + r * d.srs + kb * d.sks]);
+    const u32x4 lo = e2m1x8_to_half8(w[0]);
+    const u32x4 hi = e2m1x8_to_half8(w[1]);
+    u32x4* out = (u32x4*)(d.out + rb * d.K + kb * 16);
+    out[0] = u32x4{mul(lo[0], sc), mul(lo[1], sc), mul(lo[2], sc), mul(lo[3], sc)};
+    out[1] = u32x4{mul(hi[0], sc), mul(hi[1], sc), mul(hi[2], sc), mul(hi[3], sc)};
+  }
+}
+
+hipError_t launch_nvfp4_decode(const Nvfp4Decode& d, hipStream_t s) {
+  const int64_t total = (int64_t)d.batch * d.rows * (d.K / 16);
+  if (total <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(nvfp4_decode_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, int32_t b_load, hipStream_t s) {
   if (p.flags & F_BF16) return launch_typed<DT_BF16>(p, tile, a_load, b_load, s);
   return launch_typed<DT_F16>(p, tile, a_load, b_load, s);

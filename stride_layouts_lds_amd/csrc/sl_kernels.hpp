@@ -119,6 +119,18 @@ hipError_t launch_gemm_f16(const GemmParams& p, int32_t tile, int32_t a_load, in
                            hipStream_t stream);
 // D = C + sum over splits of ws (the second kernel of a split-K GEMM).
 hipError_t launch_splitk_reduce(const GemmParams& p, hipStream_t stream);
+// An NVFP4 operand decoded to fp16 rows (K contiguous, batch after batch)
+// ahead of an fp16 product: packed E2M1 x with strides rs, bs (elements)
+// and E4M3 scales s with strides srs, sks, sbs (one per 16 K); K % 32 == 0,
+// rows 16 bytes apart at least (rs % 32 == 0), x on a 16-byte boundary.
+struct Nvfp4Decode {
+  const uint8_t* x;
+  const uint8_t* s;
+  uint16_t* out;
+  int64_t rows, K, rs, bs, srs, sks, sbs;
+  int32_t batch;
+};
+hipError_t launch_nvfp4_decode(const Nvfp4Decode& d, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmParams& p, int32_t tile, hipStream_t stream);
 
 // The static device scratch behind sl_gemm_no_alloc (scratch.hip): its size

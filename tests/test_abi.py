@@ -392,6 +392,12 @@ def test_planner_environment_overrides(api, monkeypatch):
     assert (plan(api, *mn)["a_load"], plan(api, *mn)["b_load"]) == (3, 3)
     monkeypatch.setenv("SL_MN_LOADER", "1")
     assert (plan(api, *mn)["a_load"], plan(api, *mn)["b_load"]) == (1, 1)
+    monkeypatch.delenv("SL_MN_LOADER")
+
+    # NVFP4 decoded ahead (a_load 0, a workspace) when forced, else fused
+    monkeypatch.setenv("SL_NV_DECODE", "1")
+    p = plan(api, *nv, block_k=16)
+    assert p["a_load"] == 0 and p["workspace_bytes"] == 512 * 1024 * 2 + 256 * 1024 * 2
 
 
 def test_split_k_workspace_is_the_callers(api):
@@ -579,6 +585,49 @@ def test_nvfp4_plan_and_validation(api):
                block_k=16) == "SL_ERR_LAYOUT"
     assert err(api, a, (BASE_B, E2, (N, K), (1, N)), None, d, sa, sb, block_k=16) == "SL_ERR_LAYOUT"
     assert err(api, (BASE_A, E2, (M, K), (K + 16, 1)), b, None, d, sa, sb, block_k=16) == "SL_ERR_LAYOUT"
+
+
+def test_nvfp4_large_products_decode_ahead(api, monkeypatch):
+    """From 2048^3 on, NVFP4 operands are decoded to fp16 rows in the
+    caller's workspace (A, then B from the next 256-byte boundary) and the
+    fp16 ring kernel runs on them; SL_NV_DECODE=0, an SL_TILE choice, or K
+    not a multiple of 64 keep the fused kernels, and a missing workspace is
+    an error before any HIP call."""
+    E2, E4 = 6, 3
+
+    def nv(M, N, K, batch=None):
+        sh = lambda r, c: (r, c) if batch is None else (batch, r, c)
+        st = lambda r, c: (c, 1) if batch is None else (r * c, c, 1)
+        return ((BASE_A, E2, sh(M, K), st(M, K)), (BASE_B, E2, sh(N, K), st(N, K)), None,
+                (BASE_D, F16, sh(M, N), st(M, N)),
+                (BASE_C, E4, sh(M, K // 16), st(M, K // 16)),
+                (BASE_C + 0x40000000, E4, sh(N, K // 16), st(N, K // 16)))
+
+    big = nv(8192, 8192, 8192)
+    p = plan(api, *big, block_k=16)
+    assert p["kernel"] == api.K_NVFP4 and (p["a_load"], p["b_load"]) == (0, 0)
+    assert (p["threads"], p["lds_bytes"], p["workgroups"]) == (256, 5 * 32768, 1024)
+    assert p["workspace_bytes"] == 2 * 8192 * 8192 * 2
+    p = plan(api, *nv(2048, 2048, 2048), block_k=16)
+    assert p["a_load"] == 0 and p["workspace_bytes"] == 2 * 2048 * 2048 * 2
+    p = plan(api, *nv(2048, 2048, 1024), block_k=16)   # below 2^33 multiply-adds
+    assert p["a_load"] == 5 and p["workspace_bytes"] == 0
+    p = plan(api, *nv(300, 264, 512, batch=256), block_k=16)   # the batch counts: 2^33.2
+    assert p["a_load"] == 0 and p["workspace_bytes"] == (256 * 300 * 512 * 2 + 255) // 256 * 256 + 256 * 264 * 512 * 2
+    p = plan(api, *nv(4096, 4096, 4128), block_k=16)   # K % 64 != 0 (258-byte scale rows: loader 4)
+    assert p["a_load"] == 4 and p["workspace_bytes"] == 0
+    monkeypatch.setenv("SL_TILE", "19")
+    assert plan(api, *big, block_k=16)["a_load"] == 5
+    monkeypatch.delenv("SL_TILE")
+    monkeypatch.setenv("SL_NV_DECODE", "0")
+    assert plan(api, *big, block_k=16)["workspace_bytes"] == 0
+    monkeypatch.delenv("SL_NV_DECODE")
+    D = lambda x: api.desc(*x) if x is not None else None
+    args = api.make_args(*[D(x) for x in big], 16)
+    assert api.sl_gemm_workspace_bytes(args) == 2 * 8192 * 8192 * 2
+    with pytest.raises(api.SLError) as e:
+        api.sl_gemm(args, 0)
+    assert e.value.name == "SL_ERR_NULL"
 
 
 def test_mxfp6_plan(api):

@@ -179,7 +179,8 @@ def _plan(api, w):
     args = api.make_args(h.to_device(w.a), h.to_device(w.b), h.to_device(w.c), out, h.to_device(w.sfa),
                          h.to_device(w.sfb), w.block_k)
     p = api.sl_gemm_plan(args)
-    return {k: p[k] for k in ("kernel", "a_load", "b_load", "tile_m", "tile_n", "workgroups", "lds_bytes", "split_k")}
+    return {k: p[k] for k in ("kernel", "a_load", "b_load", "tile_m", "tile_n", "workgroups", "lds_bytes", "split_k",
+                                   "workspace_bytes")}
 
 
 def test_odd_strides_take_the_element_loader(api):
@@ -708,23 +709,31 @@ NVFP4_EXACT = [
 
 
 @pytest.mark.parametrize("case", NVFP4_EXACT, ids=lambda c: "x".join(map(str, c[:3])) + f"_b{c[3]}_c{int(c[4])}")
-@pytest.mark.parametrize("tile", [None, 19])
-def test_nvfp4_exact_parity(api, case, tile, monkeypatch):
+@pytest.mark.parametrize("mode", [None, 19, "decode"])
+def test_nvfp4_exact_parity(api, case, mode, monkeypatch):
     """Packed E2M1 data, E4M3 scales 2^[-2,2] x {1, 1.5}: every decoded
     product and partial sum is exact in fp32, so D must equal the oracle
-    bit for bit.  The automatic plan (the 8-wave kernel) and the 4-wave
-    ring schedule (tile 19, 128 KiB of LDS)."""
+    bit for bit.  The automatic plan at these sizes (the fused 8-wave
+    kernel), the fused 4-wave ring schedule (tile 19, 128 KiB of LDS), and
+    the operands decoded ahead into the workspace followed by the fp16 ring
+    kernel (forced here; the automatic plan from 2048^3 on), which needs K a
+    multiple of 64 and otherwise keeps the fused kernel."""
     h = H()
-    if tile is not None:
-        monkeypatch.setenv("SL_TILE", str(tile))
+    if mode == 19:
+        monkeypatch.setenv("SL_TILE", "19")
+    elif mode == "decode":
+        monkeypatch.setenv("SL_NV_DECODE", "1")
     M, N, K, batch, with_c = case
     w = I.nvfp4_workload("nvfp4_exact", M, N, K, seed=M + K, batch=batch, with_c=with_c, exact=True)
     plan = _plan(api, w)
-    h.log(f"nvfp4 exact {case} plan={plan}")
+    h.log(f"nvfp4 exact {case} {mode} plan={plan}")
     # scale rows of a multiple of 8 bytes take the paired loader (5), others the per-tile one (4)
     kind = 5 if (K // 16) % 8 == 0 and os.environ.get("SL_NV_PAIRS", "1") != "0" else 4
-    assert plan["kernel"] == api.K_NVFP4 and plan["a_load"] == plan["b_load"] == kind
-    assert plan["lds_bytes"] == (131072 if tile == 19 and K > 0 else 2 * 512 * 128)
+    decoded = mode == "decode" and K % 64 == 0
+    nb = batch or 1
+    assert plan["kernel"] == api.K_NVFP4 and plan["a_load"] == plan["b_load"] == (0 if decoded else kind)
+    assert plan["lds_bytes"] == (163840 if decoded else 131072 if mode == 19 and K > 0 else 2 * 512 * 128)
+    assert plan["workspace_bytes"] == ((nb * M * K * 2 + 255) // 256 * 256 + nb * N * K * 2 if decoded else 0)
     d = h.d_codes(h.run_library(w))
     d_ref, _, _ = h.oracle_full(w)
     mism = np.count_nonzero(d.reshape(d_ref.shape) != d_ref)
