@@ -703,6 +703,7 @@ NVFP4_EXACT = [
     (256, 256, 64, None, False),
     (300, 264, 512, None, True),
     (136, 72, 96, 2, True),      # K ends half way through a 64-wide K-tile
+    (136, 72, 128, 3, True),     # batched, K whole K-tiles (decoded ahead when forced)
     (520, 300, 1024, None, False),
     (512, 512, 320, None, True),   # full tiles with C: the row epilogue; an odd number of K-tiles
 ]
