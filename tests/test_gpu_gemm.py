@@ -741,6 +741,34 @@ def test_nvfp4_exact_parity(api, case, mode, monkeypatch):
     assert mism == 0, f"{mism} elements differ"
 
 
+@pytest.mark.parametrize("mode", [None, "decode"])
+def test_nvfp4_column_major_scales(api, mode, monkeypatch):
+    """E4M3 scales held column-major (the K block the fast index is not):
+    the fused kernel's per-tile loader and the decode-ahead kernel both
+    address them through their strides; D equals the oracle bit for bit."""
+    import torch
+    h = H()
+    if mode == "decode":
+        monkeypatch.setenv("SL_NV_DECODE", "1")
+    M, N, K = 264, 136, 512
+    w = I.nvfp4_workload("nvfp4_cm_scales", M, N, K, seed=11, with_c=True, exact=True)
+    a, b, c = h.to_device(w.a), h.to_device(w.b), h.to_device(w.c)
+    sfa, sfb = h.to_device(w.sfa), h.to_device(w.sfb)
+    cm = lambda x: x.t().contiguous().t()  # same values, strides (1, rows)
+    sfa_cm, sfb_cm = cm(sfa), cm(sfb)
+    assert sfa_cm.stride() == (1, M) and torch.equal(sfa_cm.view(torch.uint8), sfa.view(torch.uint8))
+    out = torch.full(w.d_shape, float("nan"), dtype=torch.float16, device="cuda")
+    args = api.make_args(a, b, c, out, sfa_cm, sfb_cm, w.block_k)
+    plan = api.sl_gemm_plan(args)
+    h.log(f"nvfp4 column-major scales {mode} plan={plan}")
+    assert plan["a_load"] == (0 if mode == "decode" else 4)
+    api.gemm(a, b, c, out=out, sfa=sfa_cm, sfb=sfb_cm, block_k=w.block_k)
+    torch.cuda.synchronize()
+    d_ref, _, _ = h.oracle_full(w)
+    got = h.d_codes(out)
+    assert np.array_equal(got.reshape(d_ref.shape), d_ref), f"{np.count_nonzero(got.reshape(d_ref.shape) != d_ref)} differ"
+
+
 def test_nvfp4_bounded_and_sampled_8192(api):
     h = H()
     w = I.nvfp4_workload("nvfp4_1024", 1024, 520, 2048, seed=3, with_c=True)
