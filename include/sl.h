@@ -45,7 +45,9 @@
  *    the call's kernels have finished on `stream`.  Two kinds of plan have
  *    one: a split-K plan (sl_plan.split_k > 1) keeps its fp32 partial sums
  *    there, and an NVFP4 plan that decodes its operands ahead (kernel 5
- *    with a_load 0) keeps A and B there as fp16 rows.  Other plans ignore
+ *    with a_load 0) keeps A and B there as fp16 rows of K contiguous
+ *    values (batch * M * K * 2 bytes of A, then B from the next 256-byte
+ *    boundary: about (M + N) * K * 2 bytes per batch).  Other plans ignore
  *    the workspace fields.
  *  - Execution: validation runs on the host before any HIP call; a failure
  *    returns a negative sl_status and sets the thread-local message.  On
